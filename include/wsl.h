@@ -1,0 +1,183 @@
+/*
+ * wsl.h -- C ABI of the weight-streaming linear library for AMD Instinct MI355X (gfx950).
+ *
+ * The library computes the linear layers y = W x of a decoder whose weights W
+ * are held either as plain bf16 or as packed NF4 (4-bit codes in groups of 64
+ * along K plus one fp16 scale per group).  NF4 weights stay packed in device
+ * memory and are dequantized in registers inside the linear kernels; no dense
+ * copy of W is ever written back.  Sources:
+ *   - deep-fold README, "Метод" section: codes and scales live in video
+ *     memory; linear kernels restore only the fragment of the current tile
+ *     and never write a dense weight matrix back; a group of 64 weights holds
+ *     4-bit NF4 codes and one FP16 scale; prefill is a GEMM that restores
+ *     into BF16 register fragments for batches of up to 32 positions, decode
+ *     an N=1 GEMV; both paths share one compressed representation (Figure 1).
+ *   - TCPP README, "What exact means here": bf16 weights used as stored, no
+ *     dequantization; "Quickstart"/"Performance": batch verification scores
+ *     every position of a K-token context in one sweep (a wide GEMM).
+ *   - IPE page, "What is built": a decode step indexes preallocated buffers
+ *     with host integers and never reads device values back; "How it is
+ *     checked": zero host-device synchronizations and zero allocator growth.
+ *
+ * Conventions for every entry point:
+ *   - Shapes are int64_t.  W is [n_out][k] row-major (k contiguous), like a
+ *     torch Linear weight; y = W x has n_out entries; the GEMM computes
+ *     Y[m][n_out] = X[m][k] * W^T for m token positions.
+ *   - Pointers named d_* or documented "device" are caller-owned device
+ *     memory; "host" pointers are ordinary host memory.  The library never
+ *     allocates, frees, copies or synchronizes: every call only validates its
+ *     arguments on the host and enqueues kernels on `stream` (a hipStream_t;
+ *     NULL means the default stream), so calls are legal inside HIP stream or
+ *     graph capture.
+ *   - Argument errors are returned synchronously, before anything is
+ *     enqueued (nothing is launched).  Launch failures are reported as
+ *     WSL_E_LAUNCH (from hipGetLastError, which does not synchronize).
+ *     Errors in the *data* (non-finite weights) are reported through an
+ *     optional device status word (nf4_pack only).
+ *   - The library refuses any device other than gfx950 (WSL_E_DEVICE).
+ *   - Results are deterministic: no floating-point atomics; the same inputs
+ *     give the same bits on every run.
+ *   - Calls that share output buffers and overlap on one device race; calls
+ *     on the same stream are ordered.
+ */
+#ifndef WSL_H
+#define WSL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+enum {
+    WSL_OK = 0,
+    WSL_E_NULL = 1,    /* a required pointer is NULL */
+    WSL_E_SHAPE = 2,   /* a size <= 0 (or < 0 where 0 is allowed), k % 64 != 0, or a size overflow */
+    WSL_E_ALIGN = 3,   /* a pointer or leading dimension breaks the documented alignment */
+    WSL_E_FORMAT = 4,  /* unknown weight or output format */
+    WSL_E_DEVICE = 5,  /* current device is not gfx950, or the device query failed */
+    WSL_E_LAUNCH = 6,  /* a kernel launch failed */
+    WSL_E_RANGE = 7    /* a tile or workspace lies outside its matrix or buffer */
+};
+
+/* Weight formats. */
+enum { WSL_W_BF16 = 0, WSL_W_NF4 = 1 };
+/* Output formats. */
+enum { WSL_OUT_F32 = 0, WSL_OUT_BF16 = 1 };
+
+/* Bits OR-ed into nf4_pack's optional device status word. */
+#define WSL_STATUS_NONFINITE 1u   /* a group held a NaN or an infinity */
+#define WSL_STATUS_OVERFLOW  2u   /* a group's absmax rounds to +inf in fp16 (>= 65520) */
+
+/*
+ * nf4_packed_bytes -- size in bytes of one packed NF4 matrix.
+ *   = n_out*k/2 (codes, 4 bits each) + n_out*(k/64)*2 (fp16 scales),
+ *   i.e. 17/32 byte per weight (deep-fold README, "Метод": the payload is
+ *   about 3.76x smaller than BF16 for aligned matrices).
+ *   Returns 0 if n_out <= 0, k <= 0, k % 64 != 0 or the size overflows.
+ */
+size_t nf4_packed_bytes(int64_t n_out, int64_t k);
+
+/*
+ * nf4_codebook -- copies the 16 binary32 NF4 levels (ascending; c[0] = -1,
+ * c[7] = +0, c[15] = +1) into host memory out_host[0..15].  The levels are
+ * normal quantiles with an exact zero, scaled to [-1, 1] (NF4 as introduced
+ * in QLoRA, credited in deep-fold README, "Метод").  Returns WSL_E_NULL if
+ * out_host is NULL.
+ */
+int nf4_codebook(float *out_host);
+
+/*
+ * nf4_pack -- encode a bf16 weight matrix into the packed NF4 device layout.
+ *   (deep-fold README, "Метод": per group of 64 weights, 4-bit NF4 codes and
+ *   one FP16 scale; the compressor there runs offline on the CPU.)
+ * d_w       device, bf16 [n_out][k], 16-byte aligned (read only).
+ * n_out, k  n_out >= 1, k >= 64, k % 64 == 0.
+ * d_packed  device, nf4_packed_bytes(n_out, k) bytes, 16-byte aligned (written).
+ * d_status  device uint32 or NULL.  If non-NULL, the kernel ORs
+ *           WSL_STATUS_* bits into it for groups it cannot encode (the
+ *           caller zeroes it first).  Such a group is written as s = +0 with
+ *           every code 7, i.e. as zeros.
+ * Encoding per row and group of 64 consecutive k: s = fp16_RNE(max|w|);
+ * code = nearest level to w/s with ties to the lower index, decided
+ * exactly as #{i : w > m_i * s} in fp64, m_i = (c_i + c_{i+1}) / 2; an
+ * all-zero or fp16-underflowing group stores s = +0 and codes 7.
+ * Layout written:
+ *   codes  bytes [0, n_out*k/2): row-major, two codes per byte (even k in the
+ *          low nibble), and every aligned little-endian 32-bit word (codes
+ *          k = 8j..8j+7 of a row) rotated left by 2 bits;
+ *   scales fp16 following the codes; rows in blocks of 16 (the last block
+ *          may have rb < 16 rows), ordered [group][row] inside a block:
+ *          scale(n, g) at index (n/16)*16*(k/64) + g*rb + n%16.
+ * Bit-exact and deterministic.
+ */
+int nf4_pack(const void *d_w, int64_t n_out, int64_t k, void *d_packed,
+             uint32_t *d_status, void *stream);
+
+/*
+ * nf4_dequant_tile -- restore a rectangular tile of a packed NF4 matrix to bf16.
+ *   (deep-fold README, "Метод": kernels restore only the current tile's
+ *   fragment into BF16.)  A test and diagnostic export: the linear kernels
+ *   restore tiles in registers and never call it.
+ * Value written for (r, c): bf16_RNE(fp32_RN(level[code] * s)) of weight
+ * (row0 + r, k0 + c).  Tile: rows x cols at d_tile[r*ld_tile + c] (bf16).
+ * Requires 0 <= row0, rows >= 1, row0 + rows <= n_out, 0 <= k0, cols >= 1,
+ * k0 + cols <= k (else WSL_E_RANGE), ld_tile >= cols, d_tile 2-byte aligned.
+ */
+int nf4_dequant_tile(const void *d_packed, int64_t n_out, int64_t k,
+                     int64_t row0, int64_t k0, int64_t rows, int64_t cols,
+                     void *d_tile, int64_t ld_tile, void *stream);
+
+/*
+ * linear_gemv -- decode (one position): y[n] = sum_k W[n][k] * x[k], fp32 result.
+ *   (deep-fold README, "Метод" table: decode is an N=1 NF4 GEMV; TCPP
+ *   README: bf16 weights used as stored.)
+ * wfmt      WSL_W_BF16: d_w is bf16 [n_out][k], 16-byte aligned;
+ *           WSL_W_NF4 : d_w is a packed NF4 matrix (nf4_pack layout).
+ * d_x       device bf16 [k], 16-byte aligned.   d_y device fp32 [n_out], 4-byte aligned.
+ * n_out >= 1; k >= 64 and k % 64 == 0 for NF4; k >= 8 and k % 8 == 0 for bf16.
+ * Accumulation is fp32.  NF4 multiplies the binary32 level by x and applies
+ * the fp32 scale once per group partial sum; each row satisfies
+ * |y - y_exact| <= 1e-4 * sum_k |w_hat x| with w_hat = level * s exactly.
+ */
+int linear_gemv(int wfmt, const void *d_w, int64_t n_out, int64_t k,
+                const void *d_x, float *d_y, void *stream);
+
+/*
+ * linear_gemm_workspace_bytes -- workspace linear_gemm can use for a shape
+ * (0 if it would not split the reduction).  Passing a smaller (or NULL)
+ * workspace is legal and only selects a path with less parallelism.
+ */
+size_t linear_gemm_workspace_bytes(int wfmt, int64_t n_out, int64_t k, int64_t m);
+
+/*
+ * linear_gemm -- prefill / batch verification: Y[i][n] = sum_k X[i][k] * T[n][k].
+ *   (deep-fold README, "Метод" table: prefill is an NF4 GEMM that restores
+ *   weights into BF16 register fragments; TCPP README, "Quickstart" and
+ *   "Performance": batch verification over thousands of positions.)
+ * T is the bf16 weight (WSL_W_BF16) or the restored bf16 tile value
+ * bf16_RNE(fp32_RN(level * s)) (WSL_W_NF4).  Products are accumulated in fp32
+ * on the matrix cores (MFMA); Y is written as fp32 (WSL_OUT_F32) or rounded
+ * once to bf16 (WSL_OUT_BF16, round to nearest even).
+ * d_x       device bf16 [m][ldx], ldx >= k, ldx % 8 == 0, 16-byte aligned.
+ * d_y       device [m][ldy] of the output type, ldy >= n_out, ldy % 8 == 0, 16-byte aligned.
+ * m >= 1.   n_out, k as for linear_gemv (k % 64 == 0 for both formats).
+ * d_ws      optional device workspace (16-byte aligned) of ws_bytes bytes.
+ *           It holds split-reduction partials; its contents on entry do not
+ *           matter.  Calls that share a workspace and overlap race.
+ */
+int linear_gemm(int wfmt, const void *d_w, int64_t n_out, int64_t k,
+                const void *d_x, int64_t m, int64_t ldx,
+                void *d_y, int ofmt, int64_t ldy,
+                void *d_ws, size_t ws_bytes, void *stream);
+
+/* wsl_strerror -- static description of a status code (never NULL). */
+const char *wsl_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WSL_H */

@@ -1,0 +1,53 @@
+// Host-only driver for the argument-validation unit, built with g++ under
+// AddressSanitizer and UndefinedBehaviorSanitizer by tests/test_abi.py.
+#include <cstdint>
+#include <cstdio>
+
+#include "../../include/wsl.h"
+#include "../../weight_streaming_linear_amd/csrc/validate.h"
+
+static int fails = 0;
+#define EXPECT(cond)                                                  \
+    do {                                                              \
+        if (!(cond)) {                                                \
+            std::printf("FAIL line %d: %s\n", __LINE__, #cond);       \
+            ++fails;                                                  \
+        }                                                             \
+    } while (0)
+
+int main() {
+    alignas(16) static char buf[256];
+    void *p = buf;
+    void *odd = buf + 2;
+    EXPECT(wsl::nf4_bytes(4096, 4096) == 8912896u);
+    EXPECT(wsl::nf4_bytes(1, 64) == 34u);
+    EXPECT(wsl::nf4_bytes(0, 64) == 0u);
+    EXPECT(wsl::nf4_bytes(4, 63) == 0u);
+    EXPECT(wsl::nf4_bytes(-1, 64) == 0u);
+    EXPECT(wsl::nf4_bytes(INT64_MAX, 64) == 0u);
+    EXPECT(wsl::nf4_bytes(int64_t(1) << 30, int64_t(1) << 30) != 0u);
+    EXPECT(wsl::check_pack(nullptr, 4, 64, p) == WSL_E_NULL);
+    EXPECT(wsl::check_pack(p, 4, 100, p) == WSL_E_SHAPE);
+    EXPECT(wsl::check_pack(odd, 4, 64, p) == WSL_E_ALIGN);
+    EXPECT(wsl::check_pack(p, 4, 64, p) == WSL_OK);
+    EXPECT(wsl::check_dequant_tile(p, 4, 64, 3, 0, 2, 8, p, 8) == WSL_E_RANGE);
+    EXPECT(wsl::check_dequant_tile(p, 4, 64, 0, 60, 1, 8, p, 8) == WSL_E_RANGE);
+    EXPECT(wsl::check_dequant_tile(p, 4, 64, 0, 0, 1, 8, p, 4) == WSL_E_SHAPE);
+    EXPECT(wsl::check_dequant_tile(p, 4, 64, 0, 0, 4, 64, p, 64) == WSL_OK);
+    EXPECT(wsl::check_dequant_tile(p, 4, 64, INT64_MAX, 0, 1, 1, p, 1) == WSL_E_RANGE);
+    EXPECT(wsl::check_gemv(7, p, 4, 64, p, p) == WSL_E_FORMAT);
+    EXPECT(wsl::check_gemv(WSL_W_NF4, p, 4, 96, p, p) == WSL_E_SHAPE);
+    EXPECT(wsl::check_gemv(WSL_W_BF16, p, 4, 12, p, p) == WSL_E_SHAPE);
+    EXPECT(wsl::check_gemv(WSL_W_BF16, p, 4, 16, p, p) == WSL_OK);
+    EXPECT(wsl::check_gemv(WSL_W_BF16, p, 4, 16, odd, p) == WSL_E_ALIGN);
+    EXPECT(wsl::check_gemv(WSL_W_BF16, p, INT64_MAX, INT64_MAX, p, p) == WSL_E_SHAPE);
+    EXPECT(wsl::check_gemm(WSL_W_BF16, p, 4, 64, p, 3, 64, p, 9, 8, nullptr, 0) == WSL_E_FORMAT);
+    EXPECT(wsl::check_gemm(WSL_W_BF16, p, 4, 64, p, 3, 60, p, WSL_OUT_F32, 8, nullptr, 0) == WSL_E_SHAPE);
+    EXPECT(wsl::check_gemm(WSL_W_BF16, p, 4, 64, p, 3, 68, p, WSL_OUT_F32, 8, nullptr, 0) == WSL_E_ALIGN);
+    EXPECT(wsl::check_gemm(WSL_W_BF16, p, 4, 64, p, 3, 64, p, WSL_OUT_F32, 8, nullptr, 0) == WSL_OK);
+    EXPECT(wsl::check_gemm(WSL_W_NF4, p, 4, 64, p, 0, 64, p, WSL_OUT_F32, 8, nullptr, 0) == WSL_E_SHAPE);
+    EXPECT(wsl::check_gemm(WSL_W_NF4, p, 4, 64, p, 3, 64, p, WSL_OUT_F32, 8, odd, 64) == WSL_E_ALIGN);
+    EXPECT(wsl::check_gemm(WSL_W_NF4, p, 4, 64, p, INT64_MAX / 2, 64, p, WSL_OUT_F32, 8, nullptr, 0) == WSL_E_SHAPE);
+    std::printf("%s (%d failures)\n", fails ? "FAILED" : "ok", fails);
+    return fails ? 1 : 0;
+}

@@ -1,0 +1,75 @@
+"""The C-ABI library without a GPU: load, exported symbols, constants, argument checks."""
+
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+import weight_streaming_linear_amd as wsl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wsl.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = wsl.lib()
+    names = declared_functions()
+    assert set(names) == set(wsl.EXPORTED)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_codebook_bits_match_oracle():
+    lv = np.array(wsl.nf4_codebook(), dtype=np.float32)
+    assert np.array_equal(lv.view(np.uint32), oracle.nf4_levels_f32().view(np.uint32))
+
+
+@pytest.mark.parametrize("n_out,k", [(4096, 4096), (1, 64), (17, 192), (27648, 5120), (6144, 16384)])
+def test_packed_bytes_formula(n_out, k):
+    assert wsl.nf4_packed_bytes(n_out, k) == oracle.packed_bytes(n_out, k) == n_out * k * 17 // 32
+
+
+def test_packed_bytes_invalid():
+    assert wsl.nf4_packed_bytes(0, 64) == 0
+    assert wsl.nf4_packed_bytes(4, 65) == 0
+    assert wsl.nf4_packed_bytes(-3, 64) == 0
+
+
+def test_argument_errors_return_before_any_launch():
+    L = wsl.lib()
+    a = ctypes.c_void_p(4096)     # aligned, never dereferenced: validation fails first
+    odd = ctypes.c_void_p(4098)
+    assert L.linear_gemv(wsl.WSL_W_NF4, None, 4, 64, a, a, None) == 1
+    assert L.linear_gemv(wsl.WSL_W_NF4, a, 4, 96, a, a, None) == 2
+    assert L.linear_gemv(wsl.WSL_W_NF4, odd, 4, 64, a, a, None) == 3
+    assert L.linear_gemv(5, a, 4, 64, a, a, None) == 4
+    assert L.linear_gemm(wsl.WSL_W_BF16, a, 4, 64, a, 3, 64, a, 7, 8, None, 0, None) == 4
+    assert L.linear_gemm(wsl.WSL_W_BF16, a, 4, 64, a, 3, 32, a, 0, 8, None, 0, None) == 2
+    assert L.nf4_pack(a, 4, 100, a, None, None) == 2
+    assert L.nf4_dequant_tile(a, 4, 64, 4, 0, 1, 1, a, 1, None) == 7
+    assert wsl.wsl_strerror(7).startswith("tile")
+    assert L.nf4_codebook(None) == 1
+
+
+def test_validation_unit_under_sanitizers(tmp_path):
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("g++ not available")
+    exe = str(tmp_path / "validate_asan")
+    srcs = [os.path.join(ROOT, "tests", "cpp", "validate_main.cpp"),
+            os.path.join(ROOT, "weight_streaming_linear_amd", "csrc", "validate.cpp")]
+    subprocess.run([gxx, "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined",
+                    "-fno-sanitize-recover=all", *srcs, "-o", exe], check=True)
+    r = subprocess.run([exe], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr

@@ -1,0 +1,176 @@
+"""linear_gemm on the GPU against the fp64 CPU oracle.
+
+NF4: the reference multiplies the restored bf16 tile T = bf16(fp32(c * s)); bf16:
+the weight as stored.  fp32 output: |Y - Y_ref| <= 1e-4 * S elementwise; bf16 output:
+one more bf16 ulp of |Y_ref|.  Full BASELINE shapes are checked on sampled rows and
+columns, including tile edges.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+import weight_streaming_linear_amd as wsl
+from gpu_common import to_dev_bf16, bits_of, f64, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _tile_f64(wb):
+    codes, scales = oracle.pack_codes(f64(wb))
+    return f64(oracle.dequant_tile_bits(codes, scales))
+
+
+def _check(y_dev, y_ref, s_ref, ofmt):
+    if ofmt == wsl.WSL_OUT_F32:
+        return oracle.check_rows_f32(y_dev.cpu().numpy(), y_ref, s_ref)
+    return oracle.check_bf16(bits_of(y_dev), y_ref, s_ref)
+
+
+@pytest.mark.parametrize("m,n_out,k", [(5, 100, 192), (32, 96, 640), (70, 33, 128), (130, 160, 256), (1, 32, 64),
+                                       (32, 1000, 5120)])
+@pytest.mark.parametrize("ofmt", [wsl.WSL_OUT_F32, wsl.WSL_OUT_BF16])
+@pytest.mark.parametrize("use_ws", [False, True])
+def test_gemm_nf4_small(m, n_out, k, ofmt, use_ws):
+    import torch
+    say(f"gemm nf4 m={m} n={n_out} k={k} ofmt={ofmt} ws={use_ws}")
+    wb = synth.weight_bits(97, n_out, n_out, k)
+    xb = synth.act_bits(97, 1000 + m, (m, k))
+    packed = wsl.nf4_pack(to_dev_bf16(wb))
+    ws = None
+    if use_ws:
+        nb = wsl.linear_gemm_workspace_bytes(wsl.WSL_W_NF4, n_out, k, m)
+        ws = torch.full((max(nb, 16) // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    y = wsl.linear_gemm(packed, to_dev_bf16(xb), wfmt=wsl.WSL_W_NF4, n_out=n_out, k=k, ofmt=ofmt, workspace=ws)
+    torch.cuda.synchronize()
+    y_ref, s_ref = oracle.gemm_ref(f64(xb), _tile_f64(wb))
+    ok, worst, i = _check(y, y_ref, s_ref, ofmt)
+    assert ok, f"elem {i}: worst ratio {worst}"
+
+
+@pytest.mark.parametrize("m,n_out,k", [(5, 100, 192), (130, 200, 320), (128, 128, 64), (257, 129, 576), (1, 8, 64)])
+@pytest.mark.parametrize("ofmt", [wsl.WSL_OUT_F32, wsl.WSL_OUT_BF16])
+def test_gemm_bf16_small(m, n_out, k, ofmt):
+    import torch
+    say(f"gemm bf16 m={m} n={n_out} k={k} ofmt={ofmt}")
+    wb = synth.weight_bits(98, n_out, n_out, k)
+    xb = synth.act_bits(98, 1000 + m, (m, k))
+    y = wsl.linear_gemm(to_dev_bf16(wb), to_dev_bf16(xb), ofmt=ofmt)
+    torch.cuda.synchronize()
+    y_ref, s_ref = oracle.gemm_ref(f64(xb), f64(wb))
+    ok, worst, i = _check(y, y_ref, s_ref, ofmt)
+    assert ok, f"elem {i}: worst ratio {worst}"
+
+
+def test_gemm_strided_x_and_y():
+    """Leading dimensions larger than the logical widths."""
+    import torch
+    m, n_out, k = 40, 72, 192
+    wb = synth.weight_bits(99, 0, n_out, k)
+    xb = synth.act_bits(99, 1, (m, k + 16))
+    x = to_dev_bf16(xb)[:, :k]
+    y = torch.full((m, n_out + 8), float("nan"), dtype=torch.float32, device="cuda")
+    wsl.linear_gemm(to_dev_bf16(wb), x, y=y[:, :n_out])
+    packed = wsl.nf4_pack(to_dev_bf16(wb))
+    y2 = torch.full((m, n_out + 8), float("nan"), dtype=torch.float32, device="cuda")
+    wsl.linear_gemm(packed, x, y=y2[:, :n_out], wfmt=wsl.WSL_W_NF4, n_out=n_out, k=k)
+    torch.cuda.synchronize()
+    xf = f64(xb)[:, :k]
+    y_ref, s_ref = oracle.gemm_ref(xf, f64(wb))
+    assert oracle.check_rows_f32(y[:, :n_out].cpu().numpy(), y_ref, s_ref)[0]
+    assert torch.isnan(y[:, n_out:]).all()
+    y_ref2, s_ref2 = oracle.gemm_ref(xf, _tile_f64(wb))
+    assert oracle.check_rows_f32(y2[:, :n_out].cpu().numpy(), y_ref2, s_ref2)[0]
+    assert torch.isnan(y2[:, n_out:]).all()
+
+
+@pytest.mark.parametrize("j", [0, 31, 32, 63, 191])
+def test_gemm_one_hot_restores_tile_column(j):
+    """A one-hot row of X picks column j of the bf16 tile exactly (NF4) / of W (bf16)."""
+    import torch
+    m, n_out, k = 3, 96, 192
+    wb = synth.weight_bits(100, 0, n_out, k)
+    x = np.zeros((m, k), np.float32)
+    x[1, j] = 1.0
+    x[2, j] = -2.0
+    xb = oracle.bf16_bits_from_f32(x)
+    packed = wsl.nf4_pack(to_dev_bf16(wb))
+    y = wsl.linear_gemm(packed, to_dev_bf16(xb), wfmt=wsl.WSL_W_NF4, n_out=n_out, k=k)
+    yb = wsl.linear_gemm(to_dev_bf16(wb), to_dev_bf16(xb))
+    torch.cuda.synchronize()
+    t = _tile_f64(wb)
+    got = y.cpu().numpy()
+    assert np.all(got[0] == 0)
+    assert np.array_equal(got[1].astype(np.float64), t[:, j])
+    assert np.array_equal(got[2].astype(np.float64), -2.0 * t[:, j])
+    assert np.array_equal(yb.cpu().numpy()[1].astype(np.float64), f64(wb)[:, j])
+
+
+def _sample_idx(n, tile, rng, count):
+    edges = [0, n - 1] + [v for t in range(tile, n, tile) for v in (t - 1, t)][:16]
+    return np.unique(np.concatenate([np.array(edges), rng.integers(0, n, count)]))
+
+
+# configs[3]: NF4 prefill GEMM, 32 positions, 32B-class FFN (up 5120 -> 27648, down 27648 -> 5120)
+@pytest.mark.parametrize("n_out,k,tid", [(27648, 5120, 0), (5120, 27648, 1)])
+def test_gemm_nf4_cfg3_full_shape_sampled(n_out, k, tid):
+    import torch
+    say(f"gemm nf4 cfg3 {n_out}x{k}")
+    m = 32
+    wb = synth.weight_bits(3, tid, n_out, k)
+    xb = synth.act_bits(3, 2 + tid, (m, k))
+    w_dev = to_dev_bf16(wb)
+    packed = wsl.nf4_pack(w_dev)
+    del w_dev
+    nb = wsl.linear_gemm_workspace_bytes(wsl.WSL_W_NF4, n_out, k, m)
+    ws = torch.empty(max(nb, 16), dtype=torch.uint8, device="cuda")
+    y = wsl.linear_gemm(packed, to_dev_bf16(xb), wfmt=wsl.WSL_W_NF4, n_out=n_out, k=k, workspace=ws)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(41 + tid)
+    cols = _sample_idx(n_out, 128, rng, 200)
+    # packed bytes of the sampled rows are bit-exact
+    cb, sc = oracle.canonical_from_device(packed.cpu().numpy(), n_out, k)
+    codes, scales = oracle.pack_codes(f64(wb[cols]))
+    assert np.array_equal(cb[cols], oracle.codes_to_bytes(codes))
+    assert np.array_equal(sc[cols].view(np.uint16), scales.view(np.uint16))
+    t = f64(oracle.dequant_tile_bits(codes, scales))
+    y_ref, s_ref = oracle.gemm_ref(f64(xb), t)
+    ok, worst, i = oracle.check_rows_f32(y.cpu().numpy()[:, cols], y_ref, s_ref)
+    assert ok, f"elem {i}: worst ratio {worst}"
+
+
+# configs[4]: bf16 batch verification, M = 8192 positions, gate (5120 -> 17408) and down (17408 -> 5120)
+@pytest.mark.parametrize("n_out,k,tid", [(17408, 5120, 0), (5120, 17408, 1)])
+def test_gemm_bf16_cfg4_full_shape_sampled(n_out, k, tid):
+    import torch
+    say(f"gemm bf16 cfg4 {n_out}x{k}")
+    m = 8192
+    wb = synth.weight_bits(4, tid, n_out, k)
+    xb = synth.act_bits(4, 2 + tid, (m, k))
+    y = wsl.linear_gemm(to_dev_bf16(wb), to_dev_bf16(xb), ofmt=wsl.WSL_OUT_BF16)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(43 + tid)
+    rows = _sample_idx(m, 128, rng, 48)
+    cols = _sample_idx(n_out, 128, rng, 160)
+    y_ref, s_ref = oracle.gemm_ref(f64(xb[rows]), f64(wb[cols]))
+    got = bits_of(y)[np.ix_(rows, cols)]
+    ok, worst, i = oracle.check_bf16(got, y_ref, s_ref)
+    assert ok, f"elem {i}: worst ratio {worst}"
+
+
+def test_gemm_deterministic():
+    import torch
+    m, n_out, k = 32, 5120, 27648 // 4
+    wb = synth.weight_bits(101, 0, n_out, k)
+    xb = synth.act_bits(101, 1, (m, k))
+    packed = wsl.nf4_pack(to_dev_bf16(wb))
+    x = to_dev_bf16(xb)
+    nb = wsl.linear_gemm_workspace_bytes(wsl.WSL_W_NF4, n_out, k, m)
+    ws = torch.empty(max(nb, 16), dtype=torch.uint8, device="cuda")
+    a = wsl.linear_gemm(packed, x, wfmt=wsl.WSL_W_NF4, n_out=n_out, k=k, workspace=ws)
+    b = wsl.linear_gemm(packed, x, wfmt=wsl.WSL_W_NF4, n_out=n_out, k=k, workspace=ws)
+    c = wsl.linear_gemm(to_dev_bf16(wb), x)
+    d = wsl.linear_gemm(to_dev_bf16(wb), x)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(c, d)

@@ -1,0 +1,152 @@
+"""linear_gemv on the GPU against the fp64 CPU oracle.
+
+Tolerance (per row): |y - y_ref| <= 1e-4 * sum_j |w_hat_ij x_j|, with w_hat the
+exact dequantized weight c * s (NF4) or the bf16 weight.  Exact special cases
+(small integers, one-hot x, power-of-two scaling) must match bit for bit.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+import weight_streaming_linear_amd as wsl
+from gpu_common import to_dev_bf16, to_dev_u8, f64, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _nf4_case(n_out, k, cfg, tid_w, tid_x):
+    import torch
+    wb = synth.weight_bits(cfg, tid_w, n_out, k)
+    xb = synth.act_bits(cfg, tid_x, (k,))
+    packed = wsl.nf4_pack(to_dev_bf16(wb))
+    y = wsl.linear_gemv(packed, to_dev_bf16(xb), wfmt=wsl.WSL_W_NF4, n_out=n_out, k=k)
+    torch.cuda.synchronize()
+    codes, scales = oracle.pack_codes(f64(wb))
+    y_ref, s_ref = oracle.gemv_ref(oracle.dequant_exact(codes, scales), f64(xb))
+    return y.cpu().numpy(), y_ref, s_ref
+
+
+@pytest.mark.parametrize("n_out,k", [(4096, 4096), (37, 192), (1, 64), (130, 2112), (257, 6144), (64, 16384),
+                                     (9, 4160)])
+def test_gemv_nf4_tolerance(n_out, k):
+    say(f"gemv nf4 {n_out}x{k}")
+    y, y_ref, s_ref = _nf4_case(n_out, k, 0 if (n_out, k) == (4096, 4096) else 94, 0, 1)
+    ok, worst, i = oracle.check_rows_f32(y, y_ref, s_ref)
+    assert ok, f"row {i}: worst ratio {worst}"
+
+
+def _bf16_case(n_out, k, cfg, tid_w, tid_x):
+    import torch
+    wb = synth.weight_bits(cfg, tid_w, n_out, k)
+    xb = synth.act_bits(cfg, tid_x, (k,))
+    y = wsl.linear_gemv(to_dev_bf16(wb), to_dev_bf16(xb))
+    torch.cuda.synchronize()
+    y_ref, s_ref = oracle.gemv_ref(f64(wb), f64(xb))
+    return y.cpu().numpy(), y_ref, s_ref
+
+
+# configs[1]: one dense decoder layer, hidden 5120, k/v 1024 rows, gate/up 17408, down k = 17408
+@pytest.mark.parametrize("n_out,k,tid", [(5120, 5120, 0), (1024, 5120, 1), (17408, 5120, 4), (5120, 17408, 6),
+                                         (7168, 5120, 10), (3, 8, 11), (5, 520, 12), (1, 4104, 13), (333, 1000, 14)])
+def test_gemv_bf16_tolerance(n_out, k, tid):
+    say(f"gemv bf16 {n_out}x{k}")
+    y, y_ref, s_ref = _bf16_case(n_out, k, 1, tid, 100 + tid)
+    ok, worst, i = oracle.check_rows_f32(y, y_ref, s_ref)
+    assert ok, f"row {i}: worst ratio {worst}"
+
+
+def test_gemv_nf4_exact_cases():
+    """Codes in {0, 7, 15} (levels -1, 0, +1), power-of-two scales, small integer x: every
+    partial sum is an exact integer multiple of the scale, so y must equal the exact result."""
+    import torch
+    rng = np.random.default_rng(31)
+    n_out, k = 70, 4160
+    lv = rng.integers(-1, 2, size=(n_out, k)).astype(np.float64)
+    e = rng.integers(-3, 4, size=(n_out, k // 64))
+    s = np.repeat(np.exp2(e), 64, axis=1)
+    lv[:, ::64] = 1.0                                        # every group holds +s: scale is exactly s
+    w = lv * s
+    wb = oracle.bf16_bits_from_f32(w.astype(np.float32))
+    x = rng.integers(-4, 5, size=k).astype(np.float64)
+    xb = oracle.bf16_bits_from_f32(x.astype(np.float32))
+    packed = wsl.nf4_pack(to_dev_bf16(wb))
+    y = wsl.linear_gemv(packed, to_dev_bf16(xb), wfmt=wsl.WSL_W_NF4, n_out=n_out, k=k)
+    # x scaled by 2^5 must scale y by exactly 2^5
+    x2b = oracle.bf16_bits_from_f32((x * 32).astype(np.float32))
+    y2 = wsl.linear_gemv(packed, to_dev_bf16(x2b), wfmt=wsl.WSL_W_NF4, n_out=n_out, k=k)
+    torch.cuda.synchronize()
+    codes, scales = oracle.pack_codes(f64(wb))
+    assert set(np.unique(codes).tolist()) <= {0, 7, 15}
+    y_ref, _ = oracle.gemv_ref(oracle.dequant_exact(codes, scales), x)
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), y_ref)
+    assert np.array_equal(y2.cpu().numpy(), y.cpu().numpy() * np.float32(32))
+
+
+@pytest.mark.parametrize("j", [0, 63, 64, 2047, 2048, 4159])
+def test_gemv_nf4_one_hot(j):
+    """x = e_j gives y = fp32(c * s) of column j (one fp32 rounding of the exact product)."""
+    import torch
+    n_out, k = 50, 4160
+    wb = synth.weight_bits(95, 0, n_out, k)
+    x = np.zeros(k, np.float32)
+    x[j] = 1.0
+    packed = wsl.nf4_pack(to_dev_bf16(wb))
+    y = wsl.linear_gemv(packed, to_dev_bf16(oracle.bf16_bits_from_f32(x)), wfmt=wsl.WSL_W_NF4, n_out=n_out, k=k)
+    torch.cuda.synchronize()
+    codes, scales = oracle.pack_codes(f64(wb))
+    want = oracle.dequant_exact(codes, scales)[:, j].astype(np.float32)
+    assert np.array_equal(y.cpu().numpy(), want)
+
+
+def test_gemv_bf16_exact_integers():
+    import torch
+    rng = np.random.default_rng(37)
+    n_out, k = 301, 5120
+    w = rng.integers(-16, 17, size=(n_out, k)).astype(np.float32)
+    x = rng.integers(-16, 17, size=k).astype(np.float32)
+    y = wsl.linear_gemv(to_dev_bf16(oracle.bf16_bits_from_f32(w)), to_dev_bf16(oracle.bf16_bits_from_f32(x)))
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), w.astype(np.float64) @ x.astype(np.float64))
+
+
+def test_gemv_zero_weights_give_zero():
+    import torch
+    n_out, k = 40, 640
+    wb = np.zeros((n_out, k), np.uint16)
+    xb = synth.act_bits(96, 0, (k,))
+    packed = wsl.nf4_pack(to_dev_bf16(wb))
+    y = wsl.linear_gemv(packed, to_dev_bf16(xb), wfmt=wsl.WSL_W_NF4, n_out=n_out, k=k)
+    y2 = wsl.linear_gemv(to_dev_bf16(wb), to_dev_bf16(xb))
+    torch.cuda.synchronize()
+    assert np.all(y.cpu().numpy() == 0) and np.all(y2.cpu().numpy() == 0)
+
+
+def test_gemv_deterministic_and_graph_capturable():
+    """Same bits on repeated calls; a captured graph replays to the eager result (the call
+    neither synchronizes nor allocates, or capture would fail)."""
+    import torch
+    n_out, k = 4096, 4096
+    wb = synth.weight_bits(0, 0, n_out, k)
+    xb = synth.act_bits(0, 1, (k,))
+    packed = wsl.nf4_pack(to_dev_bf16(wb))
+    x = to_dev_bf16(xb)
+    y1 = wsl.linear_gemv(packed, x, wfmt=wsl.WSL_W_NF4, n_out=n_out, k=k)
+    y2 = wsl.linear_gemv(packed, x, wfmt=wsl.WSL_W_NF4, n_out=n_out, k=k)
+    yg = torch.empty(n_out, dtype=torch.float32, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        wsl.linear_gemv(packed, x, y=yg, wfmt=wsl.WSL_W_NF4, n_out=n_out, k=k)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        wsl.linear_gemv(packed, x, y=yg, wfmt=wsl.WSL_W_NF4, n_out=n_out, k=k)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        yg.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(yg, y1)
+    assert torch.equal(y1, y2)

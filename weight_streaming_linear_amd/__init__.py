@@ -1,0 +1,165 @@
+"""Weight-streaming linear layers for AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over the C ABI of ``libwsl.so`` (declared in
+``include/wsl.h``).  Every step of the computation runs in the library's HIP
+kernels; this module only marshals arguments: it takes torch tensors (device
+memory) and the current torch stream, passes raw pointers and sizes, and turns
+status codes into exceptions.  There is no fallback: if the library is not
+built, every call raises.
+
+Entry points (same names as the C ABI):
+  nf4_packed_bytes, nf4_codebook, nf4_pack, nf4_dequant_tile,
+  linear_gemv, linear_gemm, linear_gemm_workspace_bytes, wsl_strerror
+"""
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libwsl.so")
+
+WSL_OK = 0
+WSL_W_BF16 = 0
+WSL_W_NF4 = 1
+WSL_OUT_F32 = 0
+WSL_OUT_BF16 = 1
+WSL_STATUS_NONFINITE = 1
+WSL_STATUS_OVERFLOW = 2
+
+EXPORTED = [
+    "nf4_packed_bytes", "nf4_codebook", "nf4_pack", "nf4_dequant_tile", "linear_gemv",
+    "linear_gemm_workspace_bytes", "linear_gemm", "wsl_strerror",
+]
+
+
+class WSLError(RuntimeError):
+    def __init__(self, code, where):
+        self.code = code
+        super().__init__(f"{where}: status {code} ({wsl_strerror(code)})")
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libwsl.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libwsl.so is not built ({LIB_PATH}); run __graft_entry__.build() "
+                           "or python -m weight_streaming_linear_amd.build")
+    L = ctypes.CDLL(LIB_PATH)
+    i64, vp, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+    L.nf4_packed_bytes.argtypes = [i64, i64]
+    L.nf4_packed_bytes.restype = sz
+    L.nf4_codebook.argtypes = [ctypes.POINTER(ctypes.c_float)]
+    L.nf4_codebook.restype = ctypes.c_int
+    L.nf4_pack.argtypes = [vp, i64, i64, vp, vp, vp]
+    L.nf4_pack.restype = ctypes.c_int
+    L.nf4_dequant_tile.argtypes = [vp, i64, i64, i64, i64, i64, i64, vp, i64, vp]
+    L.nf4_dequant_tile.restype = ctypes.c_int
+    L.linear_gemv.argtypes = [ctypes.c_int, vp, i64, i64, vp, vp, vp]
+    L.linear_gemv.restype = ctypes.c_int
+    L.linear_gemm_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i64]
+    L.linear_gemm_workspace_bytes.restype = sz
+    L.linear_gemm.argtypes = [ctypes.c_int, vp, i64, i64, vp, i64, i64, vp, ctypes.c_int, i64, vp, sz, vp]
+    L.linear_gemm.restype = ctypes.c_int
+    L.wsl_strerror.argtypes = [ctypes.c_int]
+    L.wsl_strerror.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def wsl_strerror(code):
+    return lib().wsl_strerror(int(code)).decode()
+
+
+def _check(rc, where):
+    if rc != WSL_OK:
+        raise WSLError(rc, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+# ---------------------------------------------------------------- format helpers
+def nf4_packed_bytes(n_out, k):
+    return int(lib().nf4_packed_bytes(int(n_out), int(k)))
+
+
+def nf4_codebook():
+    """The 16 binary32 levels the kernels use (a Python list of floats)."""
+    buf = (ctypes.c_float * 16)()
+    _check(lib().nf4_codebook(buf), "nf4_codebook")
+    return [float(v) for v in buf]
+
+
+# ---------------------------------------------------------------- entry points
+def nf4_pack(w, packed=None, status=None, stream=None):
+    """Encode a bf16 [n_out][k] device tensor into a packed NF4 uint8 device tensor."""
+    import torch
+    n_out, k = w.shape
+    nbytes = nf4_packed_bytes(n_out, k)
+    if packed is None:
+        packed = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=w.device)
+    rc = lib().nf4_pack(_ptr(w), n_out, k, _ptr(packed), _ptr(status), _stream(stream))
+    _check(rc, "nf4_pack")
+    return packed
+
+
+def nf4_dequant_tile(packed, n_out, k, row0, k0, rows, cols, tile=None, ld_tile=None, stream=None):
+    """Restore the bf16 tile [rows][cols] at (row0, k0) of a packed NF4 matrix."""
+    import torch
+    if tile is None:
+        tile = torch.empty((rows, cols), dtype=torch.bfloat16, device=packed.device)
+        ld_tile = cols
+    if ld_tile is None:
+        ld_tile = tile.stride(0)
+    rc = lib().nf4_dequant_tile(_ptr(packed), n_out, k, row0, k0, rows, cols, _ptr(tile), ld_tile, _stream(stream))
+    _check(rc, "nf4_dequant_tile")
+    return tile
+
+
+def linear_gemv(w, x, y=None, wfmt=None, n_out=None, k=None, stream=None):
+    """y = W x (fp32).  w: bf16 [n_out][k] or packed NF4 uint8 (give n_out and k)."""
+    import torch
+    if wfmt is None:
+        wfmt = WSL_W_NF4 if w.dtype == torch.uint8 else WSL_W_BF16
+    if n_out is None or k is None:
+        n_out, k = w.shape
+    if y is None:
+        y = torch.empty(n_out, dtype=torch.float32, device=x.device)
+    rc = lib().linear_gemv(int(wfmt), _ptr(w), n_out, k, _ptr(x), _ptr(y), _stream(stream))
+    _check(rc, "linear_gemv")
+    return y
+
+
+def linear_gemm_workspace_bytes(wfmt, n_out, k, m):
+    return int(lib().linear_gemm_workspace_bytes(int(wfmt), int(n_out), int(k), int(m)))
+
+
+def linear_gemm(w, x, y=None, wfmt=None, n_out=None, k=None, ofmt=WSL_OUT_F32, workspace=None, stream=None):
+    """Y = X W^T.  x: bf16 [m][k] (row stride = x.stride(0)); y fp32 or bf16 [m][n_out]."""
+    import torch
+    if wfmt is None:
+        wfmt = WSL_W_NF4 if w.dtype == torch.uint8 else WSL_W_BF16
+    if n_out is None or k is None:
+        n_out, k = w.shape
+    m = x.shape[0]
+    if y is None:
+        dt = torch.float32 if ofmt == WSL_OUT_F32 else torch.bfloat16
+        y = torch.empty((m, n_out), dtype=dt, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib().linear_gemm(int(wfmt), _ptr(w), n_out, k, _ptr(x), m, x.stride(0), _ptr(y), int(ofmt), y.stride(0),
+                           _ptr(workspace), ws_bytes, _stream(stream))
+    _check(rc, "linear_gemm")
+    return y

@@ -1,0 +1,117 @@
+// C ABI entry points (include/wsl.h): validate on the host, check the device,
+// enqueue on the caller's stream, report launch errors without synchronizing.
+#include <atomic>
+#include <cstring>
+
+#include "device_common.h"
+#include "validate.h"
+
+namespace wsl {
+int launch_pack(const void *w, int64_t n_out, int64_t k, void *packed, uint32_t *status, hipStream_t s);
+int launch_dequant_tile(const void *packed, int64_t n_out, int64_t k, int64_t row0, int64_t k0, int64_t rows,
+                        int64_t cols, void *tile, int64_t ld, hipStream_t s);
+int launch_gemv_bf16(const void *w, int64_t n_out, int64_t k, const void *x, float *y, hipStream_t s);
+int launch_gemv_nf4(const void *w, int64_t n_out, int64_t k, const void *x, float *y, hipStream_t s);
+int launch_gemm_bf16(const void *w, int64_t n_out, int64_t k, const void *x, int64_t m, int64_t ldx, void *y,
+                     int ofmt, int64_t ldy, hipStream_t s);
+int launch_gemm_nf4(const void *w, int64_t n_out, int64_t k, const void *x, int64_t m, int64_t ldx, void *y,
+                    int ofmt, int64_t ldy, void *ws, size_t ws_bytes, hipStream_t s);
+size_t gemm_ws_bytes(int wfmt, int64_t n_out, int64_t k, int64_t m);
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// 0 = not yet checked, 1 = gfx950, 2 = something else.
+std::atomic<int> g_arch[kMaxDevices];
+
+int device_ok() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return WSL_E_DEVICE;
+    if (dev >= kMaxDevices) return WSL_E_DEVICE;
+    int st = g_arch[dev].load(std::memory_order_acquire);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return WSL_E_DEVICE;
+        st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+        g_arch[dev].store(st, std::memory_order_release);
+    }
+    return st == 1 ? WSL_OK : WSL_E_DEVICE;
+}
+
+int after_launch(int rc) {
+    if (rc != WSL_OK) return rc;
+    return hipGetLastError() == hipSuccess ? WSL_OK : WSL_E_LAUNCH;
+}
+
+hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+}  // namespace wsl
+
+extern "C" {
+
+size_t nf4_packed_bytes(int64_t n_out, int64_t k) { return wsl::nf4_bytes(n_out, k); }
+
+int nf4_codebook(float *out_host) {
+    if (!out_host) return WSL_E_NULL;
+    for (int i = 0; i < 16; ++i) std::memcpy(&out_host[i], &wsl::kLevelBits[i], sizeof(float));
+    return WSL_OK;
+}
+
+int nf4_pack(const void *d_w, int64_t n_out, int64_t k, void *d_packed, uint32_t *d_status, void *stream) {
+    int rc = wsl::check_pack(d_w, n_out, k, d_packed);
+    if (rc != WSL_OK) return rc;
+    if ((rc = wsl::device_ok()) != WSL_OK) return rc;
+    return wsl::after_launch(wsl::launch_pack(d_w, n_out, k, d_packed, d_status, wsl::as_stream(stream)));
+}
+
+int nf4_dequant_tile(const void *d_packed, int64_t n_out, int64_t k, int64_t row0, int64_t k0, int64_t rows,
+                     int64_t cols, void *d_tile, int64_t ld_tile, void *stream) {
+    int rc = wsl::check_dequant_tile(d_packed, n_out, k, row0, k0, rows, cols, d_tile, ld_tile);
+    if (rc != WSL_OK) return rc;
+    if ((rc = wsl::device_ok()) != WSL_OK) return rc;
+    return wsl::after_launch(
+        wsl::launch_dequant_tile(d_packed, n_out, k, row0, k0, rows, cols, d_tile, ld_tile, wsl::as_stream(stream)));
+}
+
+int linear_gemv(int wfmt, const void *d_w, int64_t n_out, int64_t k, const void *d_x, float *d_y, void *stream) {
+    int rc = wsl::check_gemv(wfmt, d_w, n_out, k, d_x, d_y);
+    if (rc != WSL_OK) return rc;
+    if ((rc = wsl::device_ok()) != WSL_OK) return rc;
+    if (wfmt == WSL_W_NF4) return wsl::after_launch(wsl::launch_gemv_nf4(d_w, n_out, k, d_x, d_y, wsl::as_stream(stream)));
+    return wsl::after_launch(wsl::launch_gemv_bf16(d_w, n_out, k, d_x, d_y, wsl::as_stream(stream)));
+}
+
+size_t linear_gemm_workspace_bytes(int wfmt, int64_t n_out, int64_t k, int64_t m) {
+    if (wfmt != WSL_W_BF16 && wfmt != WSL_W_NF4) return 0;
+    if (n_out <= 0 || k <= 0 || m <= 0 || (k % 64) != 0) return 0;
+    if (n_out > wsl::kMaxDim || k > wsl::kMaxDim || m > wsl::kMaxDim) return 0;
+    return wsl::gemm_ws_bytes(wfmt, n_out, k, m);
+}
+
+int linear_gemm(int wfmt, const void *d_w, int64_t n_out, int64_t k, const void *d_x, int64_t m, int64_t ldx,
+                void *d_y, int ofmt, int64_t ldy, void *d_ws, size_t ws_bytes, void *stream) {
+    int rc = wsl::check_gemm(wfmt, d_w, n_out, k, d_x, m, ldx, d_y, ofmt, ldy, d_ws, ws_bytes);
+    if (rc != WSL_OK) return rc;
+    if ((rc = wsl::device_ok()) != WSL_OK) return rc;
+    if (wfmt == WSL_W_NF4)
+        return wsl::after_launch(
+            wsl::launch_gemm_nf4(d_w, n_out, k, d_x, m, ldx, d_y, ofmt, ldy, d_ws, ws_bytes, wsl::as_stream(stream)));
+    return wsl::after_launch(wsl::launch_gemm_bf16(d_w, n_out, k, d_x, m, ldx, d_y, ofmt, ldy, wsl::as_stream(stream)));
+}
+
+const char *wsl_strerror(int code) {
+    switch (code) {
+        case WSL_OK: return "ok";
+        case WSL_E_NULL: return "a required pointer is NULL";
+        case WSL_E_SHAPE: return "invalid shape (non-positive size, k not a multiple of 64, or size overflow)";
+        case WSL_E_ALIGN: return "misaligned pointer or leading dimension";
+        case WSL_E_FORMAT: return "unknown weight or output format";
+        case WSL_E_DEVICE: return "current device is not gfx950 (MI355X) or could not be queried";
+        case WSL_E_LAUNCH: return "kernel launch failed";
+        case WSL_E_RANGE: return "tile or workspace outside its matrix or buffer";
+        default: return "unknown status code";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,84 @@
+// Host-side argument validation of the C ABI (no HIP dependency).
+#include "validate.h"
+
+#include "../../include/wsl.h"
+
+namespace wsl {
+namespace {
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool mul_ok(int64_t a, int64_t b, int64_t *out) {
+    if (a < 0 || b < 0) return false;
+    if (a != 0 && b > INT64_MAX / a) return false;
+    *out = a * b;
+    return true;
+}
+
+}  // namespace
+
+size_t nf4_bytes(int64_t n_out, int64_t k) {
+    if (n_out <= 0 || k <= 0 || (k % kGroup) != 0) return 0;
+    if (n_out > kMaxDim || k > kMaxDim) return 0;
+    int64_t codes = 0, scales = 0;
+    if (!mul_ok(n_out, k / 2, &codes)) return 0;
+    if (!mul_ok(n_out, (k / kGroup) * 2, &scales)) return 0;
+    if (codes > INT64_MAX - scales) return 0;
+    return static_cast<size_t>(codes + scales);
+}
+
+int check_pack(const void *w, int64_t n_out, int64_t k, const void *packed) {
+    if (!w || !packed) return WSL_E_NULL;
+    if (nf4_bytes(n_out, k) == 0) return WSL_E_SHAPE;
+    int64_t elems = 0;
+    if (!mul_ok(n_out, k, &elems)) return WSL_E_SHAPE;
+    if (!aligned(w, 16) || !aligned(packed, 16)) return WSL_E_ALIGN;
+    return WSL_OK;
+}
+
+int check_dequant_tile(const void *packed, int64_t n_out, int64_t k, int64_t row0, int64_t k0,
+                       int64_t rows, int64_t cols, const void *tile, int64_t ld_tile) {
+    if (!packed || !tile) return WSL_E_NULL;
+    if (nf4_bytes(n_out, k) == 0) return WSL_E_SHAPE;
+    if (rows <= 0 || cols <= 0 || ld_tile <= 0) return WSL_E_SHAPE;
+    if (rows > kMaxDim || cols > kMaxDim || ld_tile > kMaxDim) return WSL_E_SHAPE;
+    if (ld_tile < cols) return WSL_E_SHAPE;
+    if (row0 < 0 || k0 < 0 || row0 > n_out - rows || k0 > k - cols) return WSL_E_RANGE;
+    int64_t t = 0;
+    if (!mul_ok(rows, ld_tile, &t)) return WSL_E_SHAPE;
+    if (!aligned(packed, 16) || !aligned(tile, 2)) return WSL_E_ALIGN;
+    return WSL_OK;
+}
+
+int check_gemv(int wfmt, const void *w, int64_t n_out, int64_t k, const void *x, const void *y) {
+    if (wfmt != WSL_W_BF16 && wfmt != WSL_W_NF4) return WSL_E_FORMAT;
+    if (!w || !x || !y) return WSL_E_NULL;
+    if (n_out <= 0 || k <= 0 || n_out > kMaxDim || k > kMaxDim) return WSL_E_SHAPE;
+    if (wfmt == WSL_W_NF4) {
+        if (nf4_bytes(n_out, k) == 0) return WSL_E_SHAPE;
+    } else {
+        int64_t e = 0;
+        if ((k % 8) != 0 || !mul_ok(n_out, k, &e) || e > INT64_MAX / 2) return WSL_E_SHAPE;
+    }
+    if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4)) return WSL_E_ALIGN;
+    return WSL_OK;
+}
+
+int check_gemm(int wfmt, const void *w, int64_t n_out, int64_t k, const void *x, int64_t m,
+               int64_t ldx, const void *y, int ofmt, int64_t ldy, const void *ws, size_t ws_bytes) {
+    if (wfmt != WSL_W_BF16 && wfmt != WSL_W_NF4) return WSL_E_FORMAT;
+    if (ofmt != WSL_OUT_F32 && ofmt != WSL_OUT_BF16) return WSL_E_FORMAT;
+    if (!w || !x || !y) return WSL_E_NULL;
+    if (n_out <= 0 || k <= 0 || m <= 0) return WSL_E_SHAPE;
+    if (n_out > kMaxDim || k > kMaxDim || m > kMaxDim || ldx > kMaxDim || ldy > kMaxDim) return WSL_E_SHAPE;
+    if ((k % kGroup) != 0) return WSL_E_SHAPE;
+    if (ldx < k || ldy < n_out) return WSL_E_SHAPE;
+    int64_t e = 0;
+    if (!mul_ok(m, ldx, &e) || !mul_ok(m, ldy, &e) || !mul_ok(n_out, k, &e)) return WSL_E_SHAPE;
+    if ((ldx % 8) != 0 || (ldy % 8) != 0) return WSL_E_ALIGN;
+    if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 16)) return WSL_E_ALIGN;
+    if (ws && ws_bytes && !aligned(ws, 16)) return WSL_E_ALIGN;
+    return WSL_OK;
+}
+
+}  // namespace wsl

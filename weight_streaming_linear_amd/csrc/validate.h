@@ -1,0 +1,31 @@
+// Host-side argument validation of the C ABI (no HIP dependency).
+//
+// Every entry point validates its arguments here before it enqueues anything,
+// so a caller error returns a status code and launches nothing.  This unit is
+// plain C++ so it can be built with g++ and exercised under AddressSanitizer
+// and UndefinedBehaviorSanitizer on a machine without a GPU.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace wsl {
+
+constexpr int64_t kGroup = 64;          // NF4 group size along k
+constexpr int64_t kScaleRowBlock = 16;  // rows per scale block in the device layout
+
+// Size of a packed NF4 matrix, or 0 if the shape is invalid or the size overflows.
+size_t nf4_bytes(int64_t n_out, int64_t k);
+
+int check_pack(const void *w, int64_t n_out, int64_t k, const void *packed);
+int check_dequant_tile(const void *packed, int64_t n_out, int64_t k, int64_t row0, int64_t k0,
+                       int64_t rows, int64_t cols, const void *tile, int64_t ld_tile);
+int check_gemv(int wfmt, const void *w, int64_t n_out, int64_t k, const void *x, const void *y);
+int check_gemm(int wfmt, const void *w, int64_t n_out, int64_t k, const void *x, int64_t m,
+               int64_t ldx, const void *y, int ofmt, int64_t ldy, const void *ws, size_t ws_bytes);
+
+// Upper bound on any single dimension accepted by the library (keeps every
+// derived index within int64 and every per-row byte offset within int32).
+constexpr int64_t kMaxDim = int64_t(1) << 30;
+
+}  // namespace wsl
