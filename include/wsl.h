@@ -162,7 +162,7 @@ size_t linear_gemm_workspace_bytes(int wfmt, int64_t n_out, int64_t k, int64_t m
  * on the matrix cores (MFMA); Y is written as fp32 (WSL_OUT_F32) or rounded
  * once to bf16 (WSL_OUT_BF16, round to nearest even).
  * d_x       device bf16 [m][ldx], ldx >= k, ldx % 8 == 0, 16-byte aligned.
- * d_y       device [m][ldy] of the output type, ldy >= n_out, ldy % 8 == 0, 16-byte aligned.
+ * d_y       device [m][ldy] of the output type, ldy >= n_out, aligned to its element size.
  * m >= 1.   n_out, k as for linear_gemv (k % 64 == 0 for both formats).
  * d_ws      optional device workspace (16-byte aligned) of ws_bytes bytes.
  *           It holds split-reduction partials; its contents on entry do not

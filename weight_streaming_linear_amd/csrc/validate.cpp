@@ -75,8 +75,9 @@ int check_gemm(int wfmt, const void *w, int64_t n_out, int64_t k, const void *x,
     if (ldx < k || ldy < n_out) return WSL_E_SHAPE;
     int64_t e = 0;
     if (!mul_ok(m, ldx, &e) || !mul_ok(m, ldy, &e) || !mul_ok(n_out, k, &e)) return WSL_E_SHAPE;
-    if ((ldx % 8) != 0 || (ldy % 8) != 0) return WSL_E_ALIGN;
-    if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 16)) return WSL_E_ALIGN;
+    if ((ldx % 8) != 0) return WSL_E_ALIGN;
+    if (!aligned(w, 16) || !aligned(x, 16)) return WSL_E_ALIGN;
+    if (!aligned(y, ofmt == WSL_OUT_F32 ? 4 : 2)) return WSL_E_ALIGN;
     if (ws && ws_bytes && !aligned(ws, 16)) return WSL_E_ALIGN;
     return WSL_OK;
 }
