@@ -19,51 +19,99 @@ namespace wsl {
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // ---------------------------------------------------------------- bf16, LDS-tiled
-// Workgroup tile 128 (m) x 128 (n) x 64 (k); 4 waves in 2 x 2, each 64 x 64 as
-// 2 x 2 blocks of 32 x 32.  LDS rows of 64 bf16 (128 B) hold 8 chunks of 16 B;
-// chunk c of row r is stored at c ^ (r & 7) so that the 32 lanes reading one
-// chunk column from 32 consecutive rows hit distinct banks.
-constexpr int kBM = 128, kBN = 128, kBK = 64;
+// Workgroup tile 256 (m) x 256 (n), 8 waves in 2 (m) x 4 (n), each owning a
+// 128 x 64 block as 4 x 2 v_mfma_f32_32x32x16_bf16 tiles (128 fp32
+// accumulators per lane; two waves per SIMD).
+// The k loop runs over 32-k stages held in a 4-deep LDS ring (4 x 32 KB).
+// Operands go global -> LDS directly (global_load_lds_dwordx4: a wave-wide
+// load writes 1 KB of LDS, lane L at byte 16L), so no registers are spent on
+// staging and three stages (96 KB per CU) stay in flight: enough bytes in
+// flight to cover the L2/MALL latency at the operand rate a 256 x 256 tile
+// needs.  Per stage: wait for the oldest copies (s_waitcnt vmcnt), one
+// barrier, refill the stage freed by the previous iteration, then 2 x 8 MFMAs.
+// LDS rows are 32 bf16 = 64 B = 4 chunks of 16 B; chunk c of row r sits at
+// c ^ ((r >> 1) & 3) ^ ((r >> 3) & 1): the fragment reads (32 rows, one chunk
+// column) are free of bank conflicts for 32 and for 64 banks.  Because a
+// lane's LDS slot is fixed by its lane index, the swizzle is applied by
+// choosing which global chunk each lane copies.
+// Workgroups map to tiles XCD-aware: each of the 8 XCDs takes a contiguous
+// range of tiles, ordered in bands of 8 m-tiles, so tiles sharing rows of X or
+// of W run on the same XCD (one L2) at about the same time.
+constexpr int kBM = 256, kBN = 256, kBK = 32, kStages = 4;
+constexpr int kStageBytes = (kBM + kBN) * kBK * 2;   // 32 KB
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+__device__ __forceinline__ int chunk_swz(int row, int chunk) { return chunk ^ ((row >> 1) & 3) ^ ((row >> 3) & 1); }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 64 + (chunk_swz(row, chunk) << 4); }
 
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt with vmcnt <= N and the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// The four ring stages are separate LDS objects and the k loop is unrolled by
+// four, so every copy and every fragment read names its stage at compile time;
+// the compiler can then tell that reading stage s does not alias the copies
+// still in flight into the other stages, and does not drain them.
+__global__ __launch_bounds__(512) void gemm_bf16_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
                                                         int64_t m, int64_t n_out, int64_t k, int64_t ldx,
-                                                        void *__restrict__ y, int ofmt, int64_t ldy) {
-    __shared__ __attribute__((aligned(16))) char sa[kBM * 128];
-    __shared__ __attribute__((aligned(16))) char sb[kBN * 128];
+                                                        void *__restrict__ y, int ofmt, int64_t ldy,
+                                                        int tiles_m, int tiles_n) {
+    __shared__ __attribute__((aligned(1024))) char st0[kStageBytes];
+    __shared__ __attribute__((aligned(1024))) char st1[kStageBytes];
+    __shared__ __attribute__((aligned(1024))) char st2[kStageBytes];
+    __shared__ __attribute__((aligned(1024))) char st3[kStageBytes];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int64_t m0 = static_cast<int64_t>(blockIdx.y) * kBM;
-    const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kBN;
+    const int wm = wave >> 2, wn = wave & 3;
 
-    // global -> register staging: 4 chunks of A and 4 of B per thread
-    uint4 ra[4], rb[4];
-    auto load_tile = [&](int64_t k0) {
+    // XCD-aware tile order (a bijection of [0, tiles)): XCD x = bid % 8 gets
+    // tiles [start(x), start(x) + count(x)) in its dispatch order bid / 8.
+    const int ntiles = tiles_m * tiles_n;
+    const int bid = blockIdx.x;
+    const int per_xcd = ntiles >> 3, rem = ntiles & 7;
+    const int xcd = bid & 7, slot = bid >> 3;
+    const int t = xcd * per_xcd + (xcd < rem ? xcd : rem) + slot;
+    const int band = 8;
+    const int band_tiles = band * tiles_n;
+    const int b_idx = t / band_tiles, in_band = t - b_idx * band_tiles;
+    const int band_rows = (tiles_m - b_idx * band) < band ? (tiles_m - b_idx * band) : band;
+    const int tm = b_idx * band + in_band % band_rows;
+    const int tn = in_band / band_rows;
+    const int64_t m0 = static_cast<int64_t>(tm) * kBM;
+    const int64_t n0 = static_cast<int64_t>(tn) * kBN;
+
+    // Copies: wave w issues wave-loads g = 2w, 2w+1 of each operand; load g
+    // covers tile rows 16g .. 16g+15, lane L row 16g + L/4, LDS slot L % 4.
+    // Rows outside the matrix are clamped (they only feed discarded outputs).
+    const uint16_t *asrc[2];
+    const uint16_t *bsrc[2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int id = tid + 256 * i;
-            const int row = id >> 3, c = id & 7;
-            const int64_t gm = m0 + row, gn = n0 + row;
-            ra[i] = (gm < m) ? *reinterpret_cast<const uint4 *>(x + gm * ldx + k0 + c * 8) : make_uint4(0, 0, 0, 0);
-            rb[i] = (gn < n_out) ? *reinterpret_cast<const uint4 *>(w + gn * k + k0 + c * 8) : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < 2; ++i) {
+        const int row = 16 * (2 * wave + i) + (lane >> 2);
+        const int c = chunk_swz(row, lane & 3);                 // global chunk landing in slot lane % 4
+        const int64_t gm = (m0 + row < m) ? m0 + row : m - 1;
+        const int64_t gn = (n0 + row < n_out) ? n0 + row : n_out - 1;
+        asrc[i] = x + gm * ldx + c * 8;
+        bsrc[i] = w + gn * k + c * 8;
+    }
+    auto copy_stage = [&](int64_t kt, char *sa) {
+        char *sb = sa + kBM * kBK * 2;
+        const int64_t k0 = kt * kBK;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int g = 2 * wave + i;
+            __builtin_amdgcn_global_load_lds(asrc[i] + k0, (lds_void *)(sa + g * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(bsrc[i] + k0, (lds_void *)(sb + g * 1024), 16, 0, 0);
         }
     };
-    auto store_tile = [&]() {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int id = tid + 256 * i;
-            const int row = id >> 3, c = id & 7;
-            *reinterpret_cast<uint4 *>(sa + swz(row, c)) = ra[i];
-            *reinterpret_cast<uint4 *>(sb + swz(row, c)) = rb[i];
-        }
-    };
 
-    f32x16 acc[2][2];
+    f32x16 acc[4][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -71,45 +119,61 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t *__restri
 
     const int half = lane >> 5, l32 = lane & 31;
     const int64_t ktiles = k / kBK;
-    load_tile(0);
-    store_tile();
-    __syncthreads();
-    for (int64_t kt = 0; kt < ktiles; ++kt) {
-        if (kt + 1 < ktiles) load_tile((kt + 1) * kBK);
+    auto compute_stage = [&](const char *sa) {
+        const char *sb = sa + kBM * kBK * 2;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
+        for (int ks = 0; ks < 2; ++ks) {
             const int chunk = ks * 2 + half;
-            bf16x8 a[2], b[2];
+            uint4 fa[4], fb[2];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int ra_row = wm * 64 + i * 32 + l32;
-                a[i] = as_bf16x8(*reinterpret_cast<const uint4 *>(sa + swz(ra_row, chunk)));
-                const int rb_row = wn * 64 + i * 32 + l32;
-                b[i] = as_bf16x8(*reinterpret_cast<const uint4 *>(sb + swz(rb_row, chunk)));
-            }
+            for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const uint4 *>(sa + swz(wm * 128 + i * 32 + l32, chunk));
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int j = 0; j < 2; ++j) fb[j] = *reinterpret_cast<const uint4 *>(sb + swz(wn * 64 + j * 32 + l32, chunk));
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa[i]), as_bf16x8(fb[j]), acc[i][j],
+                                                                        0, 0, 0);
         }
-        __syncthreads();
-        if (kt + 1 < ktiles) {
-            store_tile();
-            __syncthreads();
-        }
+    };
+    // One k-stage: wait for this wave's copies of stage kt (copies of kt+1 and
+    // kt+2, 4 wave-loads each, may stay in flight), a bare barrier (no memory
+    // fence, which would also wait for those), refill the stage freed by the
+    // previous iteration with k-tile kt+3, multiply stage kt.
+    auto step = [&](int64_t kt, char *cur, char *refill) {
+        const int64_t ahead = ktiles - 1 - kt;
+        if (ahead >= 2) wait_vmcnt<8>();
+        else if (ahead == 1) wait_vmcnt<4>();
+        else wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        if (kt + 3 < ktiles) copy_stage(kt + 3, refill);
+        compute_stage(cur);
+    };
+    if (0 < ktiles) copy_stage(0, st0);
+    if (1 < ktiles) copy_stage(1, st1);
+    if (2 < ktiles) copy_stage(2, st2);
+    int64_t kt = 0;
+    for (; kt + 4 <= ktiles; kt += 4) {
+        step(kt + 0, st0, st3);
+        step(kt + 1, st1, st0);
+        step(kt + 2, st2, st1);
+        step(kt + 3, st3, st2);
     }
+    if (kt + 0 < ktiles) step(kt + 0, st0, st3);
+    if (kt + 1 < ktiles) step(kt + 1, st1, st0);
+    if (kt + 2 < ktiles) step(kt + 2, st2, st1);
 
     // 32x32 accumulator layout: element e of lane l is row 8*(e/4) + 4*(l/32) + e%4, column l%32.
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int64_t col = n0 + wn * 64 + j * 32 + l32;
             if (col >= n_out) continue;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int64_t row = m0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
+                const int64_t row = m0 + wm * 128 + i * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
                 if (row >= m) continue;
                 if (ofmt == WSL_OUT_F32) {
                     static_cast<float *>(y)[row * ldy + col] = acc[i][j][e];
@@ -122,26 +186,58 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t *__restri
 }
 
 // ---------------------------------------------------------------- NF4, weight-stationary
-// Each wave owns 32 weight rows (n) and a k range; it restores 8 codes at a
-// time into one bf16 B fragment (t = bf16(fp32(level * s))) and multiplies it
-// against MB blocks of 32 positions.  Lane l serves row n0 + l%32 and k half
-// h = l/32: per 64-k step it loads the 16-byte run of codes for k in
-// [kc + 32h, kc + 32h + 32) -- four MFMA k-steps of 8 -- all inside group kc/64.
-// The matching A fragments are X[row][kc + 32h + 8t .. +8].
-template <int MB>
+// Each wave owns NB blocks of 32 weight rows (n) and a k range of its split.
+// Lane l serves rows n0 + 32j + l%32 (j < NB) and k half h = l/32.  Per 256-k
+// step the lane reads, for each of its rows, one contiguous 64-byte run of codes
+// (k in [kc + 128h, kc + 128h + 128): 128 codes, two groups), restores 8 codes
+// at a time into a bf16 B fragment t = bf16(fp32(level * s)) and issues one
+// v_mfma_f32_32x32x16_bf16 per fragment and block; the A fragment (8 positions'
+// worth of X for the same 8 k) is loaded once and shared by the NB blocks.
+// A k tail shorter than 256 is done in 64-k steps (lane: 32 codes at
+// kc + 32h), with the same rule that A and B use one k assignment per MFMA.
+__device__ __forceinline__ uint4 dequant8(uint32_t w, float s, const char *lut) {
+    const uint32_t wo = rotr32(w, 4);
+    uint4 r;
+    r.x = pack_bf16x2(*reinterpret_cast<const float *>(lut + (w & 0x3cu)) * s,
+                      *reinterpret_cast<const float *>(lut + (wo & 0x3cu)) * s);
+    r.y = pack_bf16x2(*reinterpret_cast<const float *>(lut + ((w >> 8) & 0x3cu)) * s,
+                      *reinterpret_cast<const float *>(lut + ((wo >> 8) & 0x3cu)) * s);
+    r.z = pack_bf16x2(*reinterpret_cast<const float *>(lut + ((w >> 16) & 0x3cu)) * s,
+                      *reinterpret_cast<const float *>(lut + ((wo >> 16) & 0x3cu)) * s);
+    r.w = pack_bf16x2(*reinterpret_cast<const float *>(lut + (w >> 24 & 0x3cu)) * s,
+                      *reinterpret_cast<const float *>(lut + ((wo >> 24) & 0x3cu)) * s);
+    return r;
+}
+
+// NF4 GEMM kernel (32 positions per z block).  Every wave is independent: it
+// owns NB blocks of 32 weight rows and the k range of its split (blockIdx.y).
+// Per 128-k chunk a wave
+//   1. copies X[32 positions][128 k] into its private 8 KB LDS buffer with fully
+//      coalesced loads (one wave-wide load = 4 rows x 256 B), 16-byte chunks of
+//      each row stored at chunk ^ (row & 15) so the fragment reads below hit
+//      distinct banks;
+//   2. for its NB row blocks reads the codes (lane (n, h): 64 codes of row n at
+//      k in [kc + 64h, kc + 64h + 64)), restores 8 at a time into a bf16 B
+//      fragment t = bf16(fp32(level * s)), and issues one MFMA per fragment and
+//      block, the A fragment X[m][kc + 64h + 8t .. +8] (read once from LDS) being
+//      shared by the NB blocks.
+// The wave writes its 32 x 32NB result to Y, or to the split workspace.
+template <int NB>
 __global__ __launch_bounds__(256) void gemm_nf4_kernel(const uint8_t *__restrict__ packed, int64_t n_out,
                                                        int64_t k, const uint16_t *__restrict__ x, int64_t m,
                                                        int64_t ldx, void *__restrict__ y, int ofmt, int64_t ldy,
                                                        float *__restrict__ ws, int64_t k_per_split) {
     __shared__ float lut[16];
+    __shared__ __attribute__((aligned(16))) char xs_all[4][32 * 256];
     if (threadIdx.x < 16) lut[threadIdx.x] = level(threadIdx.x);
     __syncthreads();
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int half = lane >> 5, l32 = lane & 31;
-    const int64_t n0 = (static_cast<int64_t>(blockIdx.x) * 4 + wave) * 32;
-    const int64_t n = (n0 + l32 < n_out) ? n0 + l32 : n_out - 1;
-    const int64_t mbase = static_cast<int64_t>(blockIdx.z) * 32 * MB;
+    char *xs = xs_all[wave];
+    const int64_t n0 = (static_cast<int64_t>(blockIdx.x) * 4 + wave) * 32 * NB;
+    if (n0 >= n_out) return;                               // no barrier follows
+    const int64_t mbase = static_cast<int64_t>(blockIdx.z) * 32;
     const int64_t kbeg = static_cast<int64_t>(blockIdx.y) * k_per_split;
     const int64_t kend = (kbeg + k_per_split < k) ? kbeg + k_per_split : k;
     const int64_t groups = k >> 6;
@@ -149,57 +245,75 @@ __global__ __launch_bounds__(256) void gemm_nf4_kernel(const uint8_t *__restrict
     const uint16_t *scales = reinterpret_cast<const uint16_t *>(packed + n_out * rowbytes);
     const char *lutp = reinterpret_cast<const char *>(lut);
 
-    const uint16_t *xrow[MB];
-    bool xok[MB];
+    int64_t rows[NB];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-        const int64_t r = mbase + mb * 32 + l32;
-        xok[mb] = r < m;
-        xrow[mb] = x + (xok[mb] ? r : 0) * ldx;
+    for (int j = 0; j < NB; ++j) {
+        const int64_t n = n0 + 32 * j + l32;
+        rows[j] = n < n_out ? n : n_out - 1;
     }
-    f32x16 acc[MB];
+    f32x16 acc[NB];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[mb][e] = 0.f;
+        for (int e = 0; e < 16; ++e) acc[j][e] = 0.f;
 
-    if (n0 < n_out) {
-        for (int64_t kc = kbeg; kc < kend; kc += 64) {
-            const uint4 q = load_stream16(packed + n * rowbytes + ((kc + 32 * half) >> 1));
-            const float s = f16_to_f32(scales[scale_index(n, kc >> 6, groups, n_out)]);
-            const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
+    // staging: load i (0..7) covers X rows 4i + lane/16, 16-byte chunk lane%16
+    const int srow = lane >> 4, schunk = lane & 15;
+    for (int64_t kc = kbeg; kc < kend; kc += 128) {
+        const int64_t kw = (kend - kc < 128) ? (kend - kc) : 128;   // 64 or 128
+        uint4 xv[8];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const uint32_t we = wd[t], wo = rotr32(wd[t], 4);
-                uint4 bv;
-                uint32_t *bp = reinterpret_cast<uint32_t *>(&bv);
+        for (int i = 0; i < 8; ++i) {
+            const int64_t r = mbase + 4 * i + srow;
+            const bool ok = (r < m) && (schunk * 8 < kw);
+            xv[i] = ok ? *reinterpret_cast<const uint4 *>(x + r * ldx + kc + schunk * 8) : make_uint4(0, 0, 0, 0);
+        }
+        uint4 q[NB][2];
+        float s[NB];
 #pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const float le = *reinterpret_cast<const float *>(lutp + ((we >> (8 * b)) & 0x3cu));
-                    const float lo = *reinterpret_cast<const float *>(lutp + ((wo >> (8 * b)) & 0x3cu));
-                    bp[b] = pack_bf16x2(le * s, lo * s);
-                }
-                const bf16x8 bf = as_bf16x8(bv);
-                const int64_t kk = kc + 32 * half + 8 * t;
+        for (int j = 0; j < NB; ++j) {
+            const int64_t kl = kc + 64 * half;
+            if (kl < kend) {
+                const uint8_t *src = packed + rows[j] * rowbytes + (kl >> 1);
+                q[j][0] = *reinterpret_cast<const uint4 *>(src);
+                q[j][1] = *reinterpret_cast<const uint4 *>(src + 16);
+                s[j] = f16_to_f32(scales[scale_index(rows[j], kl >> 6, groups, n_out)]);
+            } else {
+                q[j][0] = q[j][1] = make_uint4(0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u);
+                s[j] = 0.f;
+            }
+        }
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb) {
-                    const uint4 av = xok[mb] ? *reinterpret_cast<const uint4 *>(xrow[mb] + kk) : make_uint4(0, 0, 0, 0);
-                    acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), bf, acc[mb], 0, 0, 0);
-                }
+        for (int i = 0; i < 8; ++i) {
+            const int r = 4 * i + srow;
+            *reinterpret_cast<uint4 *>(xs + r * 256 + ((schunk ^ (r & 15)) << 4)) = xv[i];
+        }
+        // the wave reads back what its own lanes wrote: LDS ops of one wave are
+        // ordered, so no barrier is needed
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int c = 8 * half + t;                      // 16-byte chunk of k = kc + 64h + 8t
+            const uint4 av = *reinterpret_cast<const uint4 *>(xs + l32 * 256 + ((c ^ (l32 & 15)) << 4));
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                const uint4 qq = q[j][t >> 2];
+                const uint32_t wd = (t & 3) == 0 ? qq.x : (t & 3) == 1 ? qq.y : (t & 3) == 2 ? qq.z : qq.w;
+                const uint4 bv = dequant8(wd, s[j], lutp);
+                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(bv), acc[j], 0, 0, 0);
             }
         }
     }
 
-    // Output element e of lane l: position row mbase + mb*32 + 8*(e/4) + 4*h + e%4, column n0 + l%32.
-    const int64_t col = n0 + l32;
-    if (col >= n_out) return;
+    // Output element e of lane l: position mbase + 8*(e/4) + 4*h + e%4, column n0 + 32j + l%32.
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    for (int j = 0; j < NB; ++j) {
+        const int64_t col = n0 + 32 * j + l32;
+        if (col >= n_out) continue;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            const int64_t row = mbase + mb * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
+            const int64_t row = mbase + 8 * (e >> 2) + 4 * half + (e & 3);
             if (row >= m) continue;
-            const float v = acc[mb][e];
+            const float v = acc[j][e];
             if (ws != nullptr) {
                 ws[(static_cast<int64_t>(blockIdx.y) * m + row) * n_out + col] = v;
             } else if (ofmt == WSL_OUT_F32) {
@@ -208,6 +322,7 @@ __global__ __launch_bounds__(256) void gemm_nf4_kernel(const uint8_t *__restrict
                 static_cast<uint16_t *>(y)[row * ldy + col] = static_cast<uint16_t>(pack_bf16x2(v, 0.f) & 0xffffu);
             }
         }
+    }
 }
 
 // Sum split partials in split order (fixed, so the result is deterministic).
@@ -225,13 +340,23 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float *__restri
 }
 
 // ---------------------------------------------------------------- planning / launch
+// NF4 GEMM plan: NB = 1 (32 rows per wave), 4 waves per workgroup; split k
+// across workgroups (each split a multiple of 128 k) only as far as needed to
+// give about 2 waves per SIMD, and only when the caller passes a workspace.
+constexpr int kNf4Nb = 1;
+constexpr int64_t kNf4RowsPerWg = 4 * 32 * kNf4Nb;
+
 static int nf4_splits(int64_t n_out, int64_t k, int64_t m) {
-    const int64_t wgs = (n_out + 127) / 128;
-    const int64_t mchunks = (m + 127) / 128;
+    const int64_t waves = ((n_out + 32 * kNf4Nb - 1) / (32 * kNf4Nb)) * ((m + 31) / 32);
+    const int64_t chunks = (k + 127) / 128;
     int64_t splits = 1;
-    const int64_t kgroups = k / 64;
-    while (wgs * mchunks * splits < 512 && splits * 2 <= kgroups && splits < 16) splits *= 2;
+    while (waves * splits < 2048 && splits * 2 * 4 <= chunks && splits < 16) splits *= 2;
     return static_cast<int>(splits);
+}
+
+static int64_t nf4_k_per_split(int64_t k, int splits) {
+    const int64_t chunks = (k + 127) / 128;
+    return ((chunks + splits - 1) / splits) * 128;
 }
 
 size_t gemm_ws_bytes(int wfmt, int64_t n_out, int64_t k, int64_t m) {
@@ -243,11 +368,11 @@ size_t gemm_ws_bytes(int wfmt, int64_t n_out, int64_t k, int64_t m) {
 
 int launch_gemm_bf16(const void *w, int64_t n_out, int64_t k, const void *x, int64_t m, int64_t ldx, void *y,
                      int ofmt, int64_t ldy, hipStream_t s) {
-    const int64_t gx = (n_out + kBN - 1) / kBN, gy = (m + kBM - 1) / kBM;
-    if (gx > 0x7fffffff || gy > 65535) return WSL_E_SHAPE;
-    hipLaunchKernelGGL(gemm_bf16_kernel, dim3(static_cast<unsigned>(gx), static_cast<unsigned>(gy)), dim3(256), 0, s,
+    const int64_t tn = (n_out + kBN - 1) / kBN, tm = (m + kBM - 1) / kBM;
+    if (tn * tm > 0x7fffffff / 2) return WSL_E_SHAPE;
+    hipLaunchKernelGGL(gemm_bf16_kernel, dim3(static_cast<unsigned>(tn * tm)), dim3(512), 0, s,
                        static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(w), m, n_out, k, ldx, y, ofmt,
-                       ldy);
+                       ldy, static_cast<int>(tm), static_cast<int>(tn));
     return WSL_OK;
 }
 
@@ -255,22 +380,14 @@ int launch_gemm_nf4(const void *w, int64_t n_out, int64_t k, const void *x, int6
                     int ofmt, int64_t ldy, void *ws, size_t ws_bytes, hipStream_t s) {
     int splits = nf4_splits(n_out, k, m);
     if (splits > 1 && (ws == nullptr || ws_bytes < gemm_ws_bytes(WSL_W_NF4, n_out, k, m))) splits = 1;
-    const int64_t kgroups = k / 64;
-    const int64_t kps = ((kgroups + splits - 1) / splits) * 64;
-    const int64_t gx = (n_out + 127) / 128;
-    const int mb = (m >= 128) ? 4 : static_cast<int>((m + 31) / 32);
-    const int64_t gz = (m + 32 * mb - 1) / (32 * mb);
+    const int64_t kps = nf4_k_per_split(k, splits);
+    const int64_t gx = (n_out + kNf4RowsPerWg - 1) / kNf4RowsPerWg;
+    const int64_t gz = (m + 31) / 32;
     if (gx > 0x7fffffff || gz > 65535) return WSL_E_SHAPE;
     const dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(splits), static_cast<unsigned>(gz));
     float *wsp = splits > 1 ? static_cast<float *>(ws) : nullptr;
-    const auto *wp = static_cast<const uint8_t *>(w);
-    const auto *xp = static_cast<const uint16_t *>(x);
-    switch (mb) {
-        case 1: hipLaunchKernelGGL((gemm_nf4_kernel<1>), grid, dim3(256), 0, s, wp, n_out, k, xp, m, ldx, y, ofmt, ldy, wsp, kps); break;
-        case 2: hipLaunchKernelGGL((gemm_nf4_kernel<2>), grid, dim3(256), 0, s, wp, n_out, k, xp, m, ldx, y, ofmt, ldy, wsp, kps); break;
-        case 3: hipLaunchKernelGGL((gemm_nf4_kernel<3>), grid, dim3(256), 0, s, wp, n_out, k, xp, m, ldx, y, ofmt, ldy, wsp, kps); break;
-        default: hipLaunchKernelGGL((gemm_nf4_kernel<4>), grid, dim3(256), 0, s, wp, n_out, k, xp, m, ldx, y, ofmt, ldy, wsp, kps); break;
-    }
+    hipLaunchKernelGGL((gemm_nf4_kernel<kNf4Nb>), grid, dim3(256), 0, s, static_cast<const uint8_t *>(w), n_out, k,
+                       static_cast<const uint16_t *>(x), m, ldx, y, ofmt, ldy, wsp, kps);
     if (splits > 1) {
         const int64_t total = m * n_out;
         int64_t blocks = (total + 255) / 256;
