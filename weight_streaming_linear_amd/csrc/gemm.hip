@@ -37,7 +37,7 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast
 // Workgroups map to tiles XCD-aware: each of the 8 XCDs takes a contiguous
 // range of tiles, ordered in bands of 8 m-tiles, so tiles sharing rows of X or
 // of W run on the same XCD (one L2) at about the same time.
-constexpr int kBM = 256, kBN = 256, kBK = 32, kStages = 4;
+constexpr int kBM = 256, kBN = 256, kBK = 32;
 constexpr int kStageBytes = (kBM + kBN) * kBK * 2;   // 32 KB
 
 __device__ __forceinline__ int chunk_swz(int row, int chunk) { return chunk ^ ((row >> 1) & 3) ^ ((row >> 3) & 1); }
@@ -119,29 +119,64 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(const uint16_t *__restri
 
     const int half = lane >> 5, l32 = lane & 31;
     const int64_t ktiles = k / kBK;
-    auto compute_stage = [&](const char *sa) {
-        const char *sb = sa + kBM * kBK * 2;
+    // Fragment reads: the lane's 4 A rows (and 2 B rows) are 32 rows apart and
+    // share their swizzled chunk, so one base address plus immediate offsets
+    // (2048 B apart) covers the six 16-byte reads of a 16-k step.  They are
+    // issued from inline asm with their own lgkmcnt wait: the compiler then
+    // has no LDS read of its own there to order against the copies still in
+    // flight into the other stages (it cannot prove those disjoint across the
+    // loop back-edge and would drain every copy).
+    uint32_t offa[2], offb[2];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int chunk = ks * 2 + half;
-            uint4 fa[4], fb[2];
+    for (int ks = 0; ks < 2; ++ks) {
+        offa[ks] = static_cast<uint32_t>(swz(wm * 128 + l32, ks * 2 + half));
+        offb[ks] = static_cast<uint32_t>(kBM * kBK * 2 + swz(wn * 64 + l32, ks * 2 + half));
+    }
+    // Per stage: issue the reads of step 0, wait; issue the reads of step 1,
+    // run the 8 MFMAs of step 0 while they are in flight, wait; run step 1.
+    // The wait is a separate asm statement that takes the fragments as in/out
+    // operands, so no MFMA can use them before it.
+    auto issue = [&](uint32_t a_addr, uint32_t b_addr, u32x4 (&f)[6]) {
+        asm volatile(
+            "ds_read_b128 %0, %6\n\t"
+            "ds_read_b128 %1, %6 offset:2048\n\t"
+            "ds_read_b128 %2, %6 offset:4096\n\t"
+            "ds_read_b128 %3, %6 offset:6144\n\t"
+            "ds_read_b128 %4, %7\n\t"
+            "ds_read_b128 %5, %7 offset:2048"
+            : "=&v"(f[0]), "=&v"(f[1]), "=&v"(f[2]), "=&v"(f[3]), "=&v"(f[4]), "=&v"(f[5])
+            : "v"(a_addr), "v"(b_addr));
+    };
+    auto landed = [&](u32x4 (&f)[6]) {
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]), "+v"(f[4]), "+v"(f[5]));
+    };
+    auto mfmas = [&](const u32x4 (&f)[6]) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const uint4 *>(sa + swz(wm * 128 + i * 32 + l32, chunk));
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j) fb[j] = *reinterpret_cast<const uint4 *>(sb + swz(wn * 64 + j * 32 + l32, chunk));
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa[i]), as_bf16x8(fb[j]), acc[i][j],
-                                                                        0, 0, 0);
-        }
+            for (int j = 0; j < 2; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f[i]),
+                                                                    __builtin_bit_cast(bf16x8, f[4 + j]), acc[i][j], 0, 0, 0);
+    };
+    auto compute_stage = [&](uint32_t base) {
+        u32x4 f0[6], f1[6];
+        issue(base + offa[0], base + offb[0], f0);
+        landed(f0);
+        issue(base + offa[1], base + offb[1], f1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(f0);
+        __builtin_amdgcn_sched_barrier(0);
+        landed(f1);
+        mfmas(f1);
     };
     // One k-stage: wait for this wave's copies of stage kt (copies of kt+1 and
     // kt+2, 4 wave-loads each, may stay in flight), a bare barrier (no memory
     // fence, which would also wait for those), refill the stage freed by the
     // previous iteration with k-tile kt+3, multiply stage kt.
-    auto step = [&](int64_t kt, char *cur, char *refill) {
+    auto lds_addr = [](char *p) { return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void *)p)); };
+    const uint32_t a0 = lds_addr(st0), a1 = lds_addr(st1), a2 = lds_addr(st2), a3 = lds_addr(st3);
+    auto step = [&](int64_t kt, uint32_t cur, char *refill) {
         const int64_t ahead = ktiles - 1 - kt;
         if (ahead >= 2) wait_vmcnt<8>();
         else if (ahead == 1) wait_vmcnt<4>();
@@ -155,14 +190,14 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(const uint16_t *__restri
     if (2 < ktiles) copy_stage(2, st2);
     int64_t kt = 0;
     for (; kt + 4 <= ktiles; kt += 4) {
-        step(kt + 0, st0, st3);
-        step(kt + 1, st1, st0);
-        step(kt + 2, st2, st1);
-        step(kt + 3, st3, st2);
+        step(kt + 0, a0, st3);
+        step(kt + 1, a1, st0);
+        step(kt + 2, a2, st1);
+        step(kt + 3, a3, st2);
     }
-    if (kt + 0 < ktiles) step(kt + 0, st0, st3);
-    if (kt + 1 < ktiles) step(kt + 1, st1, st0);
-    if (kt + 2 < ktiles) step(kt + 2, st2, st1);
+    if (kt + 0 < ktiles) step(kt + 0, a0, st3);
+    if (kt + 1 < ktiles) step(kt + 1, a1, st0);
+    if (kt + 2 < ktiles) step(kt + 2, a2, st1);
 
     // 32x32 accumulator layout: element e of lane l is row 8*(e/4) + 4*(l/32) + e%4, column l%32.
 #pragma unroll
