@@ -37,6 +37,41 @@ def test_gemv_nf4_tolerance(n_out, k):
     assert ok, f"row {i}: worst ratio {worst}"
 
 
+@pytest.mark.parametrize("n_out,k", [(4099, 2112), (37, 32832), (130, 40960), (20, 2048), (16, 64)])
+def test_gemv_nf4_plan_edges(n_out, k):
+    """Row counts that leave a partial 16-row block and row groups outside the pipelined
+    loop; k > 32768 (several slices per wave); k = 2048 (one full slice)."""
+    say(f"gemv nf4 {n_out}x{k}")
+    y, y_ref, s_ref = _nf4_case(n_out, k, 97, 0, 1)
+    ok, worst, i = oracle.check_rows_f32(y, y_ref, s_ref)
+    assert ok, f"row {i}: worst ratio {worst}"
+
+
+def _sample_rows(n, rng, count):
+    edges = [0, 1, 2, 3, n - 4, n - 3, n - 2, n - 1] + [v for t in range(16, n, 16) for v in (t - 1, t)][:24]
+    return np.unique(np.clip(np.concatenate([np.array(edges), rng.integers(0, n, count)]), 0, n - 1))
+
+
+# Decode sweep with hidden size 6144: gate/up 6144 -> 32768 and down 16384 -> 6144; plus ragged
+# large shapes (odd row count, k not a multiple of 2048).  These take the pair-table kernel.
+@pytest.mark.parametrize("n_out,k,tid", [(32768, 6144, 0), (6144, 16384, 1), (8195, 6208, 2), (20000, 2112, 3)])
+def test_gemv_nf4_large_sampled(n_out, k, tid):
+    import torch
+    say(f"gemv nf4 large {n_out}x{k}")
+    wb = synth.weight_bits(98, tid, n_out, k)
+    xb = synth.act_bits(98, 10 + tid, (k,))
+    w_dev = to_dev_bf16(wb)
+    packed = wsl.nf4_pack(w_dev)
+    del w_dev
+    y = wsl.linear_gemv(packed, to_dev_bf16(xb), wfmt=wsl.WSL_W_NF4, n_out=n_out, k=k)
+    torch.cuda.synchronize()
+    rows = _sample_rows(n_out, np.random.default_rng(50 + tid), 120)
+    codes, scales = oracle.pack_codes(f64(wb[rows]))
+    y_ref, s_ref = oracle.gemv_ref(oracle.dequant_exact(codes, scales), f64(xb))
+    ok, worst, i = oracle.check_rows_f32(y.cpu().numpy()[rows], y_ref, s_ref)
+    assert ok, f"row {rows[i]}: worst ratio {worst}"
+
+
 def _bf16_case(n_out, k, cfg, tid_w, tid_x):
     import torch
     wb = synth.weight_bits(cfg, tid_w, n_out, k)

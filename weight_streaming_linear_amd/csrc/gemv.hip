@@ -13,12 +13,14 @@
 //     and the per-wave partials meet in LDS in a fixed order -- deterministic,
 //     no atomics;
 //   * x (<= 64 KB) is read through the cache hierarchy;
-//   * NF4 codes become levels through a 16-entry fp32 table in LDS (16
-//     distinct banks: lanes reading one entry broadcast, lanes reading
-//     different entries never conflict).  The device layout rotates each
-//     32-bit code word left by 2 bits, so one AND with 0x3C on a byte (and,
-//     for the odd codes, on the word rotated right by 4) is already the byte
-//     address code*4 of the table entry.
+//   * NF4 codes become fp32 levels through a table in LDS.  Small matrices use
+//     a 16-entry table (one read per code; the device layout's 2-bit word
+//     rotation makes the byte address a single SDWA AND); large ones a 64 KB
+//     table of level pairs indexed by a whole code byte and replicated per
+//     lane so that no read ever meets a bank conflict (one 8-byte read per
+//     two codes, about half the VALU work per code).  With the loads
+//     prefetched one row group ahead, the lookups and multiply-adds are what
+//     bounds the NF4 kernel, not HBM.
 #include "device_common.h"
 
 namespace wsl {
@@ -169,26 +171,17 @@ __device__ __forceinline__ void load_scales(const uint16_t *__restrict__ scales,
                                             int64_t row0, int64_t g, int64_t groups, int64_t n_out, float (&s)[R]) {
     if (vec) {
         const uint16_t *p = scales + scale_index(row0, g, groups, n_out);
-        if constexpr (R == 8) {
-            const uint4 v = *reinterpret_cast<const uint4 *>(p);
-            const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                s[2 * i] = f16_to_f32(u[i] & 0xffffu);
-                s[2 * i + 1] = f16_to_f32(u[i] >> 16);
-            }
-        } else if constexpr (R == 4) {
+        if constexpr (R == 4) {
             const uint2 v = *reinterpret_cast<const uint2 *>(p);
             s[0] = f16_to_f32(v.x & 0xffffu);
             s[1] = f16_to_f32(v.x >> 16);
             s[2] = f16_to_f32(v.y & 0xffffu);
             s[3] = f16_to_f32(v.y >> 16);
-        } else if constexpr (R == 2) {
+        } else {
+            static_assert(R == 2, "R must be 2 or 4");
             const uint32_t v = *reinterpret_cast<const uint32_t *>(p);
             s[0] = f16_to_f32(v & 0xffffu);
             s[1] = f16_to_f32(v >> 16);
-        } else {
-            s[0] = f16_to_f32(*p);
         }
     } else {
 #pragma unroll
@@ -196,8 +189,26 @@ __device__ __forceinline__ void load_scales(const uint16_t *__restrict__ scales,
     }
 }
 
-// Byte B of a device-layout word, ANDed with 0x3C: the byte address code*4 of the
-// table entry of the code sitting at bits 2..5 of that byte (one SDWA AND).
+// Raw fp16 scale bits of R consecutive rows of one group, kept packed until the
+// multiply so that a prefetch of the next row group is never waited on early.
+template <int R> struct ScaleBits;
+template <> struct ScaleBits<2> { typedef uint32_t T; };
+template <> struct ScaleBits<4> { typedef uint2 T; };
+
+template <int R>
+__device__ __forceinline__ float scale_at(const typename ScaleBits<R>::T &v, int r) {
+    if constexpr (R == 2) {
+        return f16_to_f32(r == 0 ? (v & 0xffffu) : (v >> 16));
+    } else {
+        const uint32_t w = (r < 2) ? v.x : v.y;
+        return f16_to_f32((r & 1) ? (w >> 16) : (w & 0xffffu));
+    }
+}
+
+// --- table lookups
+// 16-entry table (64 B, one ds_read_b32 per code).  Byte B of a device-layout word,
+// ANDed with 0x3C, is the byte address code*4 of the entry of the code at bits 2..5
+// of that byte (one SDWA AND); the odd codes come from the word rotated right by 4.
 template <int B>
 __device__ __forceinline__ uint32_t lut_addr(uint32_t w, uint32_t m60) {
     uint32_t r;
@@ -225,8 +236,8 @@ __device__ __forceinline__ void nf4_byte(uint32_t we, uint32_t wo, uint32_t m60,
     p1 = __builtin_fmaf(lo, xf[2 * B + 1], p1);
 }
 
-// Dot product of 32 codes (one 16-byte device-layout load) with 32 fp32 x: per 8
-// codes one rotate and eight SDWA ANDs give the table addresses.
+// Dot product of 32 codes (one 16-byte device-layout load) with 32 fp32 x through
+// the 16-entry table.  Even codes accumulate in p0, odd codes in p1.
 __device__ __forceinline__ float nf4_dot32(const uint4 q, const float (&xf)[32], const char *lut, uint32_t m60) {
     const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
     float p0 = 0.f, p1 = 0.f;
@@ -238,6 +249,50 @@ __device__ __forceinline__ float nf4_dot32(const uint4 q, const float (&xf)[32],
         nf4_byte<1>(we, wo, m60, lut, &xf[8 * i], p0, p1);
         nf4_byte<2>(we, wo, m60, lut, &xf[8 * i], p0, p1);
         nf4_byte<3>(we, wo, m60, lut, &xf[8 * i], p0, p1);
+    }
+    return p0 + p1;
+}
+
+// Pair table (64 KB, one ds_read_b64 per two codes).  Entry of byte value b (the
+// codes of two consecutive k, even k in the low nibble) = (level(b & 15),
+// level(b >> 4)), replicated 32 times: lane l reads copy l % 32 at byte offset
+// b * 256 + (l % 32) * 8, so the 32 lanes served together touch 32 distinct
+// 8-byte bank pairs whatever the codes are.  The address is one SDWA move that
+// writes byte B of the (un-rotated) code word into bits 8..15 of a register whose
+// low byte already holds the lane's copy offset.
+constexpr int kPairTableBytes = 256 * 32 * 8;
+
+template <int B>
+__device__ __forceinline__ void pair_addr(uint32_t &a, uint32_t w) {
+    if constexpr (B == 0)
+        asm("v_mov_b32_sdwa %0, %1 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_0" : "+v"(a) : "v"(w));
+    else if constexpr (B == 1)
+        asm("v_mov_b32_sdwa %0, %1 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_1" : "+v"(a) : "v"(w));
+    else if constexpr (B == 2)
+        asm("v_mov_b32_sdwa %0, %1 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_2" : "+v"(a) : "v"(w));
+    else
+        asm("v_mov_b32_sdwa %0, %1 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_3" : "+v"(a) : "v"(w));
+}
+
+__device__ __forceinline__ float nf4_dot32_pair(const uint4 q, const float (&xf)[32], const char *tab,
+                                                uint32_t (&ad)[4]) {
+    const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
+    float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t w = rotr32(wd[i], 2);   // undo the layout's rotation: byte B = codes 2B, 2B+1
+        pair_addr<0>(ad[0], w);
+        pair_addr<1>(ad[1], w);
+        pair_addr<2>(ad[2], w);
+        pair_addr<3>(ad[3], w);
+        float2 l[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) l[b] = *reinterpret_cast<const float2 *>(tab + ad[b]);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            p0 = __builtin_fmaf(l[b].x, xf[8 * i + 2 * b], p0);
+            p1 = __builtin_fmaf(l[b].y, xf[8 * i + 2 * b + 1], p1);
+        }
     }
     return p0 + p1;
 }
@@ -260,18 +315,167 @@ __device__ __forceinline__ void load_x32(const uint16_t *__restrict__ x, int64_t
     }
 }
 
-// NF4 GEMV.  Lane slice: 32 consecutive codes (16 B, half a group); a k-slice of
-// a row is 2048 codes (1 KB, one wave-wide load).  The workgroup has W waves and
-// wave w owns k-slices w, w+W, ...; when there are at most W slices (ONE = true)
-// each wave keeps its 32 x values in registers for the whole kernel.
-// Workgroups are persistent over row groups of R rows (row group rg = blockIdx.x,
-// blockIdx.x + gridDim.x, ...), and the next row group's codes and scales are
-// loaded before the current one is multiplied, so every wave keeps two groups
-// of loads in flight.  Per row group the W per-wave row sums meet in LDS
-// (double-buffered by iteration parity, one barrier per row group).
-template <int R, bool ONE>
-__global__ __launch_bounds__(1024) void gemv_nf4_kernel(const uint8_t *__restrict__ packed, int64_t n_out, int64_t k,
-                                                        const uint16_t *__restrict__ x, float *__restrict__ y) {
+// Contiguous chunk of `total` work items owned by XCD `xcd` (of 8).
+__device__ __forceinline__ void xcd_chunk(int64_t total, int xcd, int64_t &first, int64_t &count) {
+    const int64_t per = total >> 3, rem = total & 7;
+    first = xcd * per + (xcd < rem ? xcd : rem);
+    count = per + (xcd < rem ? 1 : 0);
+}
+
+// NF4 GEMV for k <= 32768.  A lane owns 32 consecutive codes (16 B, half a group) of
+// a row; a wave covers a 2048-code k-slice.  A workgroup holds T teams of S waves,
+// S = ceil(k / 2048): the S waves of a team split the row into slices and keep their
+// 32 x values in registers for the whole kernel; team t works on row group
+// sg * T + t of super-group sg (R rows per row group).
+// Super-groups of full row groups (every row present, scales of the R rows
+// contiguous) are split into 8 contiguous chunks, one per XCD (workgroup b runs on
+// XCD b % 8), so the rows that share a 16-row scale block are read through one L2
+// and each XCD streams a contiguous range.  Workgroups are persistent over their
+// chunk, and the codes and scales of the next super-group are loaded before the
+// current one is multiplied; the scales stay raw fp16 until they are used.
+// Row sums: transposed wave reduction, then the S per-wave partials of each row meet
+// in LDS in a fixed order (one barrier per super-group, double-buffered) -- the
+// result is deterministic.  Rows of a last partial 16-row block whose size is not a
+// multiple of R, and super-groups left incomplete, are done at the end with per-row
+// loads.  TAB selects the 16-entry table (0) or the replicated pair table (1).
+template <int R, int TAB>
+__global__ __launch_bounds__(1024) void gemv_nf4_team_kernel(const uint8_t *__restrict__ packed, int64_t n_out,
+                                                             int64_t k, const uint16_t *__restrict__ x,
+                                                             float *__restrict__ y, int S) {
+    typedef typename ScaleBits<R>::T SB;
+    __shared__ __align__(16) char tab[TAB == 0 ? 64 : kPairTableBytes];
+    __shared__ float red[2][16][R];
+    if constexpr (TAB == 0) {
+        if (threadIdx.x < 16) reinterpret_cast<float *>(tab)[threadIdx.x] = level(threadIdx.x);
+    } else {
+        for (int i = threadIdx.x; i < kPairTableBytes / 8; i += blockDim.x) {
+            const int b = i >> 5;
+            reinterpret_cast<float2 *>(tab)[i] = make_float2(level(b & 15), level(b >> 4));
+        }
+    }
+    __syncthreads();
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int T = (blockDim.x >> 6) / S;
+    const int team = wave / S;
+    const int slice = wave - team * S;
+    const int64_t groups = k >> 6;
+    const int64_t rowbytes = k >> 1;
+    const int64_t row_groups = (n_out + R - 1) / R;
+    const int64_t full_rg = (n_out % R == 0) ? row_groups : ((n_out >> 4) << 4) / R;
+    const int64_t supers = full_rg / T;
+    const uint16_t *scales = reinterpret_cast<const uint16_t *>(packed + n_out * rowbytes);
+    const uint32_t m60 = 0x3c;
+    uint32_t ad[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ad[i] = static_cast<uint32_t>(lane & 31) << 3;
+    constexpr int span = 64 / R;
+
+    // Lanes past k read valid codes of the row's last group and multiply them by x = 0.
+    const int64_t kk0 = static_cast<int64_t>(slice) * 2048 + lane * 32;
+    const bool active = kk0 < k;
+    const int64_t kkl = active ? kk0 : k - 32;
+    const uint32_t coff = static_cast<uint32_t>(kkl >> 1);
+    const uint32_t gl = static_cast<uint32_t>(kkl >> 6);
+    float xf[32];
+    load_x32(x, kkl, active, xf);
+
+    auto dot = [&](const uint4 &q) -> float {
+        if constexpr (TAB == 0) return nf4_dot32(q, xf, tab, m60);
+        else return nf4_dot32_pair(q, xf, tab, ad);
+    };
+    auto fetch = [&](int64_t sg, uint4 (&q)[R], SB &sb) {
+        const int64_t row0 = (sg * T + team) * R;
+        const uint8_t *rowp = packed + row0 * rowbytes;
+#pragma unroll
+        for (int r = 0; r < R; ++r) q[r] = load_stream16(rowp + r * rowbytes + coff);
+        const int64_t blk = row0 >> 4;
+        const int64_t rem = n_out - (blk << 4);
+        const uint32_t rb = static_cast<uint32_t>(rem < 16 ? rem : 16);
+        const uint16_t *sp = scales + blk * 16 * groups + (row0 & 15);
+        sb = *reinterpret_cast<const SB *>(reinterpret_cast<const char *>(sp) + gl * rb * 2u);
+        __builtin_amdgcn_sched_barrier(0);   // the whole prefetch is issued before the math below
+    };
+    // Fold the S slice partials of every team's R rows; row0 = first row of team 0.
+    auto reduce_store = [&](const float (&acc)[R], int64_t row0, int it) {
+        const float v = reduce_rows<R>(acc, lane);
+        if ((lane % span) == 0) red[it & 1][wave][lane / span] = v;
+        __syncthreads();
+        if (threadIdx.x < T * R) {
+            const int tm = threadIdx.x / R, r = threadIdx.x - tm * R;
+            float t = red[it & 1][tm * S][r];
+            for (int s = 1; s < S; ++s) t += red[it & 1][tm * S + s][r];
+            const int64_t row = row0 + tm * R + r;
+            if (row < n_out) y[row] = t;
+        }
+    };
+    auto consume = [&](int64_t sg, const uint4 (&q)[R], const SB &sb, int it) {
+        float acc[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] = scale_at<R>(sb, r) * dot(q[r]);
+        reduce_store(acc, sg * T * R, it);
+    };
+
+    const int xcd = blockIdx.x & 7;
+    const int64_t nloc = gridDim.x >> 3;   // the grid is a multiple of 8
+    int64_t first, count;
+    xcd_chunk(supers, xcd, first, count);
+    int it = 0;
+    int64_t i = blockIdx.x >> 3;
+    uint4 qa[R], qb[R];
+    SB sa, sb;
+    if (i < count) {
+        fetch(first + i, qa, sa);
+        for (;;) {   // unrolled by two so that the two buffers swap without copies
+            const int64_t i1 = i + nloc;
+            if (i1 >= count) {
+                consume(first + i, qa, sa, it++);
+                break;
+            }
+            fetch(first + i1, qb, sb);
+            consume(first + i, qa, sa, it++);
+            const int64_t i2 = i1 + nloc;
+            if (i2 >= count) {
+                consume(first + i1, qb, sb, it++);
+                break;
+            }
+            fetch(first + i2, qa, sa);
+            consume(first + i1, qb, sb, it++);
+            i = i2;
+        }
+    }
+    // Leftover row groups [supers * T, row_groups): T per workgroup, one per team,
+    // rows clamped to the matrix and scales read one row at a time.
+    const int64_t left0 = supers * T;
+    const int64_t nleft = row_groups - left0;
+    for (int64_t b = blockIdx.x; b * T < nleft; b += gridDim.x) {
+        const int64_t rg = left0 + b * T + team;
+        float acc[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] = 0.f;
+        if (rg < row_groups) {
+            const int64_t row0 = rg * R;
+            uint4 q[R];
+            float s[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int64_t row = (row0 + r < n_out) ? row0 + r : n_out - 1;
+                q[r] = load_stream16(packed + row * rowbytes + coff);
+                s[r] = f16_to_f32(scales[scale_index(row, gl, groups, n_out)]);
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r) acc[r] = s[r] * dot(q[r]);
+        }
+        reduce_store(acc, (left0 + b * T) * R, it++);
+    }
+}
+
+// NF4 GEMV for k > 32768: a workgroup of 16 waves per row group of R rows; wave w
+// takes the 2048-code slices w, w + 16, ... and reloads its x slice each time.
+template <int R>
+__global__ __launch_bounds__(1024) void gemv_nf4_wide_kernel(const uint8_t *__restrict__ packed, int64_t n_out,
+                                                             int64_t k, const uint16_t *__restrict__ x,
+                                                             float *__restrict__ y) {
     __shared__ float lut[16];
     __shared__ float red[2][16][R];
     if (threadIdx.x < 16) lut[threadIdx.x] = level(threadIdx.x);
@@ -286,13 +490,10 @@ __global__ __launch_bounds__(1024) void gemv_nf4_kernel(const uint8_t *__restric
     const char *lutp = reinterpret_cast<const char *>(lut);
     const uint32_t m60 = 0x3c;
     constexpr int span = 64 / R;
-
-    const int64_t kk0 = static_cast<int64_t>(wave) * 2048 + lane * 32;   // this lane's codes in slice `wave`
     const int64_t kstep = static_cast<int64_t>(2048) * waves;
-    float xf[32];
-    if constexpr (ONE) load_x32(x, kk0, kk0 < k, xf);
 
-    auto fetch = [&](int64_t rg, int64_t kk, uint4 (&q)[R], float (&s)[R]) {
+    int it = 0;
+    for (int64_t rg = blockIdx.x; rg < row_groups; rg += gridDim.x, ++it) {
         const int64_t row0 = rg * R;
         const int64_t rem = n_out - ((row0 >> 4) << 4);
         const int64_t rb = rem < 16 ? rem : 16;
@@ -300,51 +501,19 @@ __global__ __launch_bounds__(1024) void gemv_nf4_kernel(const uint8_t *__restric
         int64_t rows[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) rows[r] = (row0 + r < n_out) ? row0 + r : n_out - 1;
-        if (kk < k) {
-#pragma unroll
-            for (int r = 0; r < R; ++r) q[r] = load_stream16(packed + rows[r] * rowbytes + (kk >> 1));
-            load_scales<R>(scales, vec, rows, row0, kk >> 6, groups, n_out, s);
-        } else {
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                q[r] = make_uint4(0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u);   // never used
-                s[r] = 0.f;
-            }
-        }
-    };
-
-    int64_t rg = blockIdx.x;
-    uint4 q[R];
-    float s[R];
-    if (ONE && rg < row_groups) fetch(rg, kk0, q, s);
-    for (int it = 0; rg < row_groups; ++it, rg += gridDim.x) {
         float acc[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[r] = 0.f;
-        if constexpr (ONE) {
-            uint4 qn[R];
-            float sn[R];
-            const int64_t rgn = rg + gridDim.x;
-            if (rgn < row_groups) fetch(rgn, kk0, qn, sn);
-            if (kk0 < k) {
+        for (int64_t kk = static_cast<int64_t>(wave) * 2048 + lane * 32; kk < k; kk += kstep) {
+            uint4 q[R];
+            float s[R];
 #pragma unroll
-                for (int r = 0; r < R; ++r) acc[r] = s[r] * nf4_dot32(q[r], xf, lutp, m60);
-            }
+            for (int r = 0; r < R; ++r) q[r] = load_stream16(packed + rows[r] * rowbytes + (kk >> 1));
+            load_scales<R>(scales, vec, rows, row0, kk >> 6, groups, n_out, s);
+            float xf[32];
+            load_x32(x, kk, true, xf);
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                q[r] = qn[r];
-                s[r] = sn[r];
-            }
-        } else {
-            for (int64_t kk = kk0; kk < k; kk += kstep) {
-                uint4 qc[R];
-                float sc[R];
-                fetch(rg, kk, qc, sc);
-                float xc[32];
-                load_x32(x, kk, true, xc);
-#pragma unroll
-                for (int r = 0; r < R; ++r) acc[r] = __builtin_fmaf(sc[r], nf4_dot32(qc[r], xc, lutp, m60), acc[r]);
-            }
+            for (int r = 0; r < R; ++r) acc[r] = __builtin_fmaf(s[r], nf4_dot32(q[r], xf, lutp, m60), acc[r]);
         }
         const float v = reduce_rows<R>(acc, lane);
         if ((lane % span) == 0) red[it & 1][wave][lane / span] = v;
@@ -352,8 +521,7 @@ __global__ __launch_bounds__(1024) void gemv_nf4_kernel(const uint8_t *__restric
         if (threadIdx.x < R) {
             float t = red[it & 1][0][threadIdx.x];
             for (int w = 1; w < waves; ++w) t += red[it & 1][w][threadIdx.x];
-            const int64_t row = rg * R + threadIdx.x;
-            if (row < n_out) y[row] = t;
+            if (row0 + threadIdx.x < n_out) y[row0 + threadIdx.x] = t;
         }
     }
 }
@@ -394,40 +562,65 @@ int launch_gemv_bf16(const void *w, int64_t n_out, int64_t k, const void *x, flo
     return WSL_OK;
 }
 
-// NF4 plan: W = number of 2048-code k-slices (at most 16), R rows per row group,
-// and a persistent grid of about `per_cu` resident waves per CU.
-struct Nf4Plan {
-    int rows, waves;
+// NF4 plan.  k <= 32768: the team kernel with S = ceil(k / 2048) waves per team.
+// Large matrices (>= 40 Mi weights) take the pair table, 2 rows per row group and
+// 16 / S teams in one workgroup per CU (the 64 KB table leaves room for one); the
+// others the 16-entry table, 4 rows (2 below 4096 rows), at most 2 teams and two
+// workgroups per CU.  The grid is a multiple of 8 (one share per XCD) and never
+// larger than needed.  k > 32768: the wide kernel.
+struct Nf4GemvPlan {
+    bool wide, pair;
+    int rows, S, T;
     int64_t grid;
-    bool one;
 };
 
-static Nf4Plan plan_nf4(int64_t n_out, int64_t k) {
+static Nf4GemvPlan plan_gemv_nf4(int64_t n_out, int64_t k) {
+    Nf4GemvPlan p{};
     const int64_t slices = (k + 2047) / 2048;
-    Nf4Plan p;
-    p.waves = static_cast<int>(slices < 16 ? slices : 16);
-    p.one = slices <= 16;
-    p.rows = (n_out >= 16384) ? 4 : 2;
-    const int64_t row_groups = (n_out + p.rows - 1) / p.rows;
-    const int64_t per_cu = 24;
-    int64_t wgs = 256 * ((per_cu + p.waves - 1) / p.waves);
-    if (wgs > row_groups) wgs = row_groups;
-    p.grid = wgs;
+    if (slices > 16) {
+        p.wide = true;
+        p.rows = n_out >= 16384 ? 4 : 2;
+        p.S = 16;
+        p.T = 1;
+        const int64_t rg = (n_out + p.rows - 1) / p.rows;
+        p.grid = rg < 512 ? rg : 512;
+        return p;
+    }
+    p.wide = false;
+    p.S = static_cast<int>(slices);
+    int64_t per_cu;
+    if (n_out * k >= (static_cast<int64_t>(40) << 20)) {
+        p.pair = true;
+        p.rows = 2;
+        p.T = 16 / p.S;
+        per_cu = 1;
+    } else {
+        p.pair = false;
+        p.rows = n_out >= 4096 ? 4 : 2;
+        p.T = 16 / p.S < 2 ? 1 : 2;
+        per_cu = 2;
+    }
+    const int64_t rg = (n_out + p.rows - 1) / p.rows;
+    const int64_t full = (n_out % p.rows == 0) ? rg : ((n_out >> 4) << 4) / p.rows;
+    const int64_t supers = full / p.T;
+    const int64_t need = ((supers > 0 ? supers : 1) + 7) / 8 * 8;
+    p.grid = 256 * per_cu < need ? 256 * per_cu : need;
     return p;
 }
 
 int launch_gemv_nf4(const void *w, int64_t n_out, int64_t k, const void *x, float *y, hipStream_t s) {
-    const Nf4Plan p = plan_nf4(n_out, k);
-    if (p.grid > 0x7fffffff) return WSL_E_SHAPE;
+    const Nf4GemvPlan p = plan_gemv_nf4(n_out, k);
     const auto *wp = static_cast<const uint8_t *>(w);
     const auto *xp = static_cast<const uint16_t *>(x);
-    const dim3 g(static_cast<unsigned>(p.grid)), b(64 * p.waves);
-    if (p.one) {
-        if (p.rows == 4) hipLaunchKernelGGL((gemv_nf4_kernel<4, true>), g, b, 0, s, wp, n_out, k, xp, y);
-        else hipLaunchKernelGGL((gemv_nf4_kernel<2, true>), g, b, 0, s, wp, n_out, k, xp, y);
+    const dim3 g(static_cast<unsigned>(p.grid)), b(64 * p.S * p.T);
+    if (p.wide) {
+        if (p.rows == 4) hipLaunchKernelGGL((gemv_nf4_wide_kernel<4>), g, b, 0, s, wp, n_out, k, xp, y);
+        else hipLaunchKernelGGL((gemv_nf4_wide_kernel<2>), g, b, 0, s, wp, n_out, k, xp, y);
+    } else if (p.pair) {
+        hipLaunchKernelGGL((gemv_nf4_team_kernel<2, 1>), g, b, 0, s, wp, n_out, k, xp, y, p.S);
     } else {
-        if (p.rows == 4) hipLaunchKernelGGL((gemv_nf4_kernel<4, false>), g, b, 0, s, wp, n_out, k, xp, y);
-        else hipLaunchKernelGGL((gemv_nf4_kernel<2, false>), g, b, 0, s, wp, n_out, k, xp, y);
+        if (p.rows == 4) hipLaunchKernelGGL((gemv_nf4_team_kernel<4, 0>), g, b, 0, s, wp, n_out, k, xp, y, p.S);
+        else hipLaunchKernelGGL((gemv_nf4_team_kernel<2, 0>), g, b, 0, s, wp, n_out, k, xp, y, p.S);
     }
     return WSL_OK;
 }
