@@ -1,27 +1,38 @@
 #!/usr/bin/env python3
 """Benchmark of the weight-streaming linear layers on one MI355X.
 
-Headline workload (the ``value``): batch-1 bf16 decode GEMV over one dense
-decoder layer with hidden size 5120 -- q/k/v fused into one 7168x5120 matrix,
-o 5120x5120, gate/up fused into one 34816x5120 matrix, down 5120x17408 --
-launched in decoder order (qkv, o, gate_up, down), four launches per step.
-``value`` is the effective weight stream: weight bytes read per step / wall
-time per step (GB/s, 1e9 B/s), with every input resident in HBM before the
-timed region starts.  Weights rotate through two distinct layer copies
-(1.32 GB) so the 256 MB last-level cache cannot serve them.
+Headline workload (``value``): batch-1 bf16 decode GEMV over one dense decoder
+layer with hidden size 5120 -- q/k/v fused into one 7168x5120 matrix, o
+5120x5120, gate/up fused into one 34816x5120 matrix, down 5120x17408 -- four
+launches per step in decoder order, each step replayed as one captured HIP
+graph.  ``value`` is the effective weight stream: weight bytes read per step /
+wall time per step (GB/s, 1e9 B/s), every input resident in HBM before the
+timed region starts.  Steps alternate between two distinct copies of the layer
+(1.32 GB) so that the 256 MB last-level cache cannot serve the weights.
 
-The same run also measures the other workloads of the hot path (reported
-under ``paths``): the NF4 GEMV 4096x4096, the 48-layer NF4 decode sweep
-(hidden 6144), the NF4 prefill GEMM at 32 positions (5120 <-> 27648) and the
-bf16 batch-verification GEMM at 8192 positions (5120 <-> 17408).
+``roofline`` describes the dominant kernel, the gate/up GEMV (34816x5120, the
+largest matrix of the step): its algorithmic bytes per launch divided by its
+average launch duration, measured as a block of K back-to-back launches
+(alternating the two copies) between one pair of HIP events on the launch
+stream.  ``traffic`` is the
+HBM bytes per launch read from rocprofv3 FETCH_SIZE/WRITE_SIZE counter runs of
+this script (``--traffic-probe``), scaled by what the same counters read for a
+plain copy of known size; it is null when the kernel source changed since the
+counters were taken.
+
+The same run measures the other workloads of the hot path (under ``paths``):
+the NF4 GEMV 4096x4096, the 48-layer NF4 decode sweep (hidden 6144), the NF4
+prefill GEMM at 32 positions (5120 <-> 27648) and the bf16 batch-verification
+GEMM at 8192 positions (5120 <-> 17408).
 
 Protocol (IPE page, "How it is benchmarked"; deep-fold README, lab-plate
 rules): a failed correctness check stops the run before timing; warm-up and
-graph capture are outside every timer; per-launch durations come from HIP
-events recorded on the stream the kernels run on.
+graph capture are outside every timer.
 """
 
 import argparse
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -36,6 +47,10 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, 8 TB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, 2.5 PFLOP/s
 METRIC = "GEMV effective weight GB/s (% of HBM peak); GEMM TFLOP/s (% of MFMA peak)"
+GEMV_SRC = os.path.join(ROOT, "weight_streaming_linear_amd", "csrc", "gemv.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_bf16_gate_up_34816x5120.json")
+DOMINANT = "gate_up"
+CALIB_BYTES = 1 << 30            # plain copy used to calibrate the byte counters
 
 
 def log(msg):
@@ -50,203 +65,65 @@ class Launch:
         self.fn, self.nbytes, self.flops, self.name = fn, nbytes, flops, name
 
 
-def time_steps(steps_fn, k_steps, warmup, per_launch_events=True):
-    """Run warmup steps untimed, then exactly k_steps timed ones.
+_SPIN = {}
 
-    steps_fn(i) returns the list of Launch objects of step i.  Returns (wall_ms_total,
-    per-launch durations in ms as a list of (launch, ms))."""
+
+def spin_cycles_per_ms():
+    """Rate of torch's spin kernel (torch.cuda._sleep), measured once with HIP events."""
+    import torch
+    if "rate" not in _SPIN:
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(1000)
+        a.record()
+        torch.cuda._sleep(4_000_000)
+        b.record()
+        torch.cuda.synchronize()
+        _SPIN["rate"] = 4_000_000 / max(a.elapsed_time(b), 1e-3)
+    return _SPIN["rate"]
+
+
+def time_block(launches, reps, warmup):
+    """Average duration of one launch: `warmup` untimed launches, then `reps` launches back to
+    back (cycling through `launches`) between one pair of HIP events on the current stream,
+    the one the launches use.  A spin kernel queued first keeps the GPU busy while the host
+    enqueues the block, so the span holds the kernels and nothing of the host.  (An event
+    pair around every single launch would add about 2 us of command-processor overhead to
+    each measured launch on this platform.)  Returns microseconds per launch."""
     import torch
     for i in range(warmup):
-        for l in steps_fn(i):
-            l.fn()
+        launches[i % len(launches)].fn()
     torch.cuda.synchronize()
-    recs = []
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    launches[0].fn()
     torch.cuda.synchronize()
-    t0.record()
-    for i in range(k_steps):
-        for l in steps_fn(warmup + i):
-            if per_launch_events:
-                a = torch.cuda.Event(enable_timing=True)
-                b = torch.cuda.Event(enable_timing=True)
-                a.record()
-                l.fn()
-                b.record()
-                recs.append((l, a, b))
-            else:
-                l.fn()
-    t1.record()
+    host_ms = 1e3 * (time.perf_counter() - t0)
+    torch.cuda._sleep(int((2.0 * host_ms * reps + 2.0) * spin_cycles_per_ms()))
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(reps):
+        launches[(warmup + i) % len(launches)].fn()
+    b.record()
     torch.cuda.synchronize()
-    wall = t0.elapsed_time(t1)
-    return wall, [(l, a.elapsed_time(b)) for (l, a, b) in recs]
+    return 1e3 * a.elapsed_time(b) / reps
 
 
-def summarize(wall_ms, recs, k_steps):
-    nbytes = sum(l.nbytes for l, _ in recs)
-    flops = sum(l.flops for l, _ in recs)
-    ksum = sum(ms for _, ms in recs)
-    return {
-        "ms_per_step": wall_ms / k_steps,
-        "kernel_ms_per_step": ksum / k_steps,
-        "launches_per_step": len(recs) // k_steps,
-        "bytes_per_step": nbytes // k_steps,
-        "flops_per_step": flops // k_steps,
-        "avg_launch_us": 1e3 * ksum / max(1, len(recs)),
-        "kernel_gbs": (nbytes / 1e9) / (ksum / 1e3) if ksum > 0 else 0.0,
-        "wall_gbs": (nbytes / 1e9) / (wall_ms / 1e3),
-        "kernel_tflops": (flops / 1e12) / (ksum / 1e3) if ksum > 0 else 0.0,
-        "wall_tflops": (flops / 1e12) / (wall_ms / 1e3),
-    }
+def time_step_launches(steps, k_steps, warmup):
+    """Per-kernel average durations for a step made of several kinds of launch: launches of
+    the same name (one per step copy) are timed together as one block of k_steps launches.
+    Returns {name: (avg_us, launch)}."""
+    kinds = {}
+    for st in steps:
+        for l in st:
+            kinds.setdefault(l.name, []).append(l)
+    return {name: (time_block(ls, k_steps, warmup), ls[0]) for name, ls in kinds.items()}
 
 
-# ---------------------------------------------------------------- parity gates
-def gate_rows(name, y_dev, w_rows_f64, x_f64, rows):
-    import oracle
-    y = y_dev.cpu().numpy()[rows]
-    y_ref, s_ref = oracle.gemv_ref(w_rows_f64, x_f64)
-    ok, worst, _ = oracle.check_rows_f32(y, y_ref, s_ref)
-    if not ok:
-        raise SystemExit(f"parity check failed for {name}: worst ratio {worst}; refusing to time")
-    return worst
-
-
-def bf16_rows_to_host(t, rows):
+def capture(launches):
+    """One HIP graph replaying `launches` in order (captured on a side stream after one
+    eager run on it, as torch requires)."""
     import torch
-    return t[torch.as_tensor(rows, device=t.device)].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-
-
-def sample_rows(n, count, seed):
-    rng = np.random.default_rng(seed)
-    return np.unique(np.concatenate([[0, n - 1], rng.integers(0, n, count)]))
-
-
-# ---------------------------------------------------------------- workloads
-CFG1_MATS = [("qkv", 7168, 5120), ("o", 5120, 5120), ("gate_up", 34816, 5120), ("down", 5120, 17408)]
-
-
-def setup_cfg1(copies=2):
-    """One dense decoder layer (hidden 5120) in bf16, `copies` distinct copies."""
-    import torch
-    import synth
-    layers = []
-    for c in range(copies):
-        mats = [synth.device_weight(1, 10 * c + j, n, k) for j, (_, n, k) in enumerate(CFG1_MATS)]
-        layers.append(mats)
-    xs = [synth.device_normal_bf16(1, 100 + j, (k,)) for j, (_, n, k) in enumerate(CFG1_MATS)]
-    ys = [torch.empty(n, dtype=torch.float32, device="cuda") for (_, n, _) in CFG1_MATS]
-    return layers, xs, ys
-
-
-def cfg1_steps(layers, xs, ys):
-    import weight_streaming_linear_amd as wsl
-    steps = []
-    for mats in layers:
-        st = []
-        for j, (name, n, k) in enumerate(CFG1_MATS):
-            st.append(Launch(lambda w=mats[j], x=xs[j], y=ys[j]: wsl.linear_gemv(w, x, y=y),
-                             nbytes=2 * n * k, flops=2 * n * k, name=f"bf16_gemv_{name}"))
-        steps.append(st)
-    return lambda i: steps[i % len(steps)]
-
-
-def gate_cfg1(layers, xs, ys):
-    import torch
-    import oracle
-    import weight_streaming_linear_amd as wsl
-    worst = 0.0
-    for j, (name, n, k) in enumerate(CFG1_MATS):
-        wsl.linear_gemv(layers[0][j], xs[j], y=ys[j])
-        torch.cuda.synchronize()
-        rows = sample_rows(n, 48, 7 + j)
-        wb = bf16_rows_to_host(layers[0][j], rows)
-        xb = xs[j].view(torch.int16).cpu().numpy().view(np.uint16)
-        worst = max(worst, gate_rows(f"cfg1/{name}", ys[j], oracle.f32_from_bf16_bits(wb).astype(np.float64),
-                                     oracle.f32_from_bf16_bits(xb).astype(np.float64), rows))
-    return worst
-
-
-def nf4_gate_rows(name, w_bf16_rows_bits, packed_rows_y, x_bits):
-    import oracle
-    wf = oracle.f32_from_bf16_bits(w_bf16_rows_bits).astype(np.float64)
-    codes, scales = oracle.pack_codes(wf)
-    y_ref, s_ref = oracle.gemv_ref(oracle.dequant_exact(codes, scales),
-                                   oracle.f32_from_bf16_bits(x_bits).astype(np.float64))
-    ok, worst, _ = oracle.check_rows_f32(packed_rows_y, y_ref, s_ref)
-    if not ok:
-        raise SystemExit(f"parity check failed for {name}: worst ratio {worst}; refusing to time")
-    return worst
-
-
-def run_cfg0(k_steps, warmup, copies=128):
-    """NF4 GEMV 4096x4096 (configs[0]), 128 packed copies (1.14 GB) in rotation."""
-    import torch
-    import synth
-    import weight_streaming_linear_amd as wsl
-    n, k = 4096, 4096
-    x = synth.device_normal_bf16(0, 1, (k,))
-    y = torch.empty(n, dtype=torch.float32, device="cuda")
-    packs = []
-    for c in range(copies):
-        w = synth.device_weight(0, 1000 + c, n, k)
-        packs.append(wsl.nf4_pack(w))
-        if c == 0:
-            rows = sample_rows(n, 64, 3)
-            wrows = bf16_rows_to_host(w, rows)
-        del w
-    wsl.linear_gemv(packs[0], x, y=y, wfmt=wsl.WSL_W_NF4, n_out=n, k=k)
-    torch.cuda.synchronize()
-    xb = x.view(torch.int16).cpu().numpy().view(np.uint16)
-    worst = nf4_gate_rows("cfg0", wrows, y.cpu().numpy()[rows], xb)
-    nb = wsl.nf4_packed_bytes(n, k)
-    steps = [[Launch(lambda p=p: wsl.linear_gemv(p, x, y=y, wfmt=wsl.WSL_W_NF4, n_out=n, k=k), nbytes=nb,
-                     flops=2 * n * k, name="nf4_gemv")] for p in packs]
-    wall, recs = time_steps(lambda i: steps[i % copies], k_steps, warmup)
-    out = summarize(wall, recs, k_steps)
-    out.update({"workload": "NF4 GEMV 4096x4096, fp32 out", "rotation_copies": copies, "parity_worst_ratio": worst,
-                "frac_hbm": out["kernel_gbs"] / HBM_PEAK_GBS})
-    del packs
-    torch.cuda.empty_cache()
-    return out
-
-
-CFG2_STAGES = [("qkv", 8192, 6144), ("o", 6144, 6144), ("gate_up", 32768, 6144), ("down", 6144, 16384)]
-
-
-def run_cfg2(k_steps, warmup, layers=48):
-    """48-layer NF4 decode sweep, hidden 6144 (configs[2]): 192 launches per token."""
-    import torch
-    import synth
-    import weight_streaming_linear_amd as wsl
-    xs = [synth.device_normal_bf16(2, 1000 + j, (k,)) for j, (_, n, k) in enumerate(CFG2_STAGES)]
-    ys = [torch.empty(n, dtype=torch.float32, device="cuda") for (_, n, _) in CFG2_STAGES]
-    packs = []
-    gate_src = {}
-    t_setup = time.time()
-    for l in range(layers):
-        for j, (name, n, k) in enumerate(CFG2_STAGES):
-            w = synth.device_weight(2, 16 * l + j, n, k)
-            packs.append((wsl.nf4_pack(w), n, k, j))
-            if l == 0:
-                rows = sample_rows(n, 32, 11 + j)
-                gate_src[j] = (rows, bf16_rows_to_host(w, rows))
-            del w
-    torch.cuda.synchronize()
-    log(f"cfg2: packed {layers} layers in {time.time() - t_setup:.1f}s")
-    worst = 0.0
-    for j, (name, n, k) in enumerate(CFG2_STAGES):
-        p = packs[j][0]
-        wsl.linear_gemv(p, xs[j], y=ys[j], wfmt=wsl.WSL_W_NF4, n_out=n, k=k)
-        torch.cuda.synchronize()
-        rows, wrows = gate_src[j]
-        xb = xs[j].view(torch.int16).cpu().numpy().view(np.uint16)
-        worst = max(worst, nf4_gate_rows(f"cfg2/{name}", wrows, ys[j].cpu().numpy()[rows], xb))
-    launches = [Launch(lambda p=p, n=n, k=k, j=j: wsl.linear_gemv(p, xs[j], y=ys[j], wfmt=wsl.WSL_W_NF4, n_out=n, k=k),
-                       nbytes=wsl.nf4_packed_bytes(n, k), flops=2 * n * k, name=f"nf4_gemv_{CFG2_STAGES[j][0]}")
-                for (p, n, k, j) in packs]
-    wall, recs = time_steps(lambda i: launches, k_steps, warmup)
-    out = summarize(wall, recs, k_steps)
-    # the same sweep replayed as one captured graph per token
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -257,23 +134,211 @@ def run_cfg2(k_steps, warmup, layers=48):
     with torch.cuda.graph(g):
         for l in launches:
             l.fn()
-    for _ in range(warmup):
-        g.replay()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graphs(graphs, k_steps, warmup):
+    """Replay graphs[i % len] for `warmup` untimed and k_steps timed steps; wall ms."""
+    import torch
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
     torch.cuda.synchronize()
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
     a.record()
-    for _ in range(k_steps):
-        g.replay()
+    for i in range(k_steps):
+        graphs[(warmup + i) % len(graphs)].replay()
     b.record()
     torch.cuda.synchronize()
-    graph_ms = a.elapsed_time(b) / k_steps
+    return a.elapsed_time(b)
+
+
+def summarize(per_kind, counts=None):
+    """Step totals from {name: (avg_us, launch)}; counts[name] = launches of that name per
+    step (default 1)."""
+    counts = counts or {}
+    us = sum(t * counts.get(n, 1) for n, (t, _) in per_kind.items())
+    nbytes = sum(l.nbytes * counts.get(n, 1) for n, (_, l) in per_kind.items())
+    flops = sum(l.flops * counts.get(n, 1) for n, (_, l) in per_kind.items())
+    launches = {}
+    for name, (t, l) in per_kind.items():
+        e = {"avg_us": round(t, 3), "gbs": round(l.nbytes / 1e3 / t, 1)}
+        if l.flops and l.nbytes and l.flops / l.nbytes > 10:
+            e["tflops"] = round(l.flops / 1e6 / t, 1)
+        launches[name] = e
+    return {
+        "kernel_ms_per_step": us / 1e3,
+        "launches_per_step": sum(counts.get(n, 1) for n in per_kind),
+        "bytes_per_step": nbytes,
+        "flops_per_step": flops,
+        "kernel_gbs": nbytes / 1e3 / us if us > 0 else 0.0,
+        "kernel_tflops": flops / 1e6 / us if us > 0 else 0.0,
+        "launches": launches,
+    }
+
+
+# ---------------------------------------------------------------- sanity gates
+# Parity with the CPU oracle is proven by the test suite.  Before timing, the bench only
+# checks sampled outputs against torch fp32 products on the GPU (for NF4, of the tiles the
+# library restores with nf4_dequant_tile), and refuses to time anything that fails.
+def refuse(name, worst):
+    raise SystemExit(f"sanity check failed for {name}: worst ratio {worst}; refusing to time")
+
+
+def sample_rows(n, count, seed):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, n - 1], rng.integers(0, n, count)]))
+
+
+def check_close(name, got, ref, scale, rel, ulp_rel=0.0):
+    """|got - ref| <= rel * scale + ulp_rel * |ref| elementwise (torch tensors, any device)."""
+    import torch
+    got = got.double()
+    ref = ref.double()
+    bound = rel * scale.double() + ulp_rel * ref.abs()
+    if not bool(torch.isfinite(got).all()):
+        refuse(name, float("inf"))
+    ratio = ((got - ref).abs() / bound.clamp_min(1e-300)).max().item()
+    if ratio > 1.0:
+        refuse(name, ratio)
+    return ratio
+
+
+def nf4_rows_tile(packed, n_out, k, rows):
+    """bf16 tiles of the given rows, restored by the library (one nf4_dequant_tile per row)."""
+    import torch
+    import weight_streaming_linear_amd as wsl
+    t = torch.empty((len(rows), k), dtype=torch.bfloat16, device="cuda")
+    for i, r in enumerate(rows):
+        wsl.nf4_dequant_tile(packed, n_out, k, int(r), 0, 1, k, tile=t[i:i + 1], ld_tile=k)
+    return t
+
+
+def gate_gemv(name, y, w_rows, x, rel):
+    """y[rows] against w_rows (bf16 [r][k]) times x in fp32."""
+    wf = w_rows.float()
+    xf = x.float()
+    return check_close(name, y, wf @ xf, wf.abs() @ xf.abs(), rel)
+
+
+# ---------------------------------------------------------------- headline: bf16 decode layer
+LAYER_5120 = [("qkv", 7168, 5120), ("o", 5120, 5120), ("gate_up", 34816, 5120), ("down", 5120, 17408)]
+
+
+def setup_layer_5120(copies=2):
+    """One dense decoder layer (hidden 5120) in bf16, `copies` distinct copies."""
+    import torch
+    import synth
+    import weight_streaming_linear_amd as wsl
+    layers = [[synth.device_weight(1, 10 * c + j, n, k) for j, (_, n, k) in enumerate(LAYER_5120)]
+              for c in range(copies)]
+    xs = [synth.device_normal_bf16(1, 100 + j, (k,)) for j, (_, n, k) in enumerate(LAYER_5120)]
+    ys = [torch.empty(n, dtype=torch.float32, device="cuda") for (_, n, _) in LAYER_5120]
+    steps = [[Launch(lambda w=mats[j], x=xs[j], y=ys[j]: wsl.linear_gemv(w, x, y=y), nbytes=2 * n * k,
+                     flops=2 * n * k, name=name) for j, (name, n, k) in enumerate(LAYER_5120)] for mats in layers]
+    return layers, xs, ys, steps
+
+
+def gate_layer_5120(layers, xs, ys):
+    import torch
+    import weight_streaming_linear_amd as wsl
+    worst = 0.0
+    for c, mats in enumerate(layers):
+        for j, (name, n, k) in enumerate(LAYER_5120):
+            wsl.linear_gemv(mats[j], xs[j], y=ys[j])
+            rows = torch.as_tensor(sample_rows(n, 48, 7 + j + 10 * c), device="cuda")
+            worst = max(worst, gate_gemv(f"bf16 decode layer copy {c} {name}", ys[j][rows], mats[j][rows], xs[j],
+                                         1e-4))
+    torch.cuda.synchronize()
+    return worst
+
+
+def measure_headline(k_steps, warmup):
+    import torch
+    layers, xs, ys, steps = setup_layer_5120(copies=2)
+    worst = gate_layer_5120(layers, xs, ys)
+    log(f"bf16 decode layer parity ok (worst ratio {worst:.3g})")
+    graphs = [capture(st) for st in steps]
+    gwall = time_graphs(graphs, k_steps, warmup)
+    per_kind = time_step_launches(steps, k_steps, warmup)
+    per_launch = summarize(per_kind)
+    out = {"ms_per_step": gwall / k_steps, "sanity_worst_ratio": worst, "per_launch": per_launch,
+           "dominant_avg_us": per_kind[DOMINANT][0], "dominant_bytes": per_kind[DOMINANT][1].nbytes}
+    del graphs, steps, layers
+    torch.cuda.empty_cache()
+    return out
+
+
+# ---------------------------------------------------------------- other workloads
+def run_nf4_gemv_4096(k_steps, warmup, copies=128):
+    """NF4 GEMV 4096x4096, 128 packed copies (1.14 GB) in rotation."""
+    import torch
+    import synth
+    import weight_streaming_linear_amd as wsl
+    n, k = 4096, 4096
+    x = synth.device_normal_bf16(0, 1, (k,))
+    y = torch.empty(n, dtype=torch.float32, device="cuda")
+    packs = []
+    for c in range(copies):
+        w = synth.device_weight(0, 1000 + c, n, k)
+        packs.append(wsl.nf4_pack(w))
+        del w
+    wsl.linear_gemv(packs[0], x, y=y, wfmt=wsl.WSL_W_NF4, n_out=n, k=k)
+    rows = sample_rows(n, 64, 3)
+    # the GEMV multiplies the exact c*s, the tile is bf16(c*s): 2^-8 relative per weight at most
+    worst = gate_gemv("nf4 gemv 4096", y[torch.as_tensor(rows, device="cuda")], nf4_rows_tile(packs[0], n, k, rows),
+                      x, 4e-3)
+    nb = wsl.nf4_packed_bytes(n, k)
+    steps = [[Launch(lambda p=p: wsl.linear_gemv(p, x, y=y, wfmt=wsl.WSL_W_NF4, n_out=n, k=k), nbytes=nb,
+                     flops=2 * n * k, name="nf4_gemv_4096")] for p in packs]
+    out = summarize(time_step_launches(steps, k_steps, warmup))
+    out.update({"workload": "NF4 GEMV 4096x4096, fp32 out", "rotation_copies": copies, "sanity_worst_ratio": worst,
+                "frac_hbm": out["kernel_gbs"] / HBM_PEAK_GBS})
+    del packs
+    torch.cuda.empty_cache()
+    return out
+
+
+SWEEP_6144 = [("qkv", 8192, 6144), ("o", 6144, 6144), ("gate_up", 32768, 6144), ("down", 6144, 16384)]
+
+
+def run_nf4_decode_sweep(k_steps, warmup, layers=48):
+    """48-layer NF4 decode sweep, hidden 6144: 192 launches per token, replayed as one captured
+    graph per token; per-stage kernel durations from blocks of launches."""
+    import torch
+    import synth
+    import weight_streaming_linear_amd as wsl
+    xs = [synth.device_normal_bf16(2, 1000 + j, (k,)) for j, (_, n, k) in enumerate(SWEEP_6144)]
+    ys = [torch.empty(n, dtype=torch.float32, device="cuda") for (_, n, _) in SWEEP_6144]
+    packs = []
+    t_setup = time.time()
+    for l in range(layers):
+        for j, (name, n, k) in enumerate(SWEEP_6144):
+            w = synth.device_weight(2, 16 * l + j, n, k)
+            packs.append((wsl.nf4_pack(w), n, k, j))
+            del w
+    torch.cuda.synchronize()
+    log(f"nf4 decode sweep: packed {layers} layers in {time.time() - t_setup:.1f}s")
+    worst = 0.0
+    for j, (name, n, k) in enumerate(SWEEP_6144):
+        wsl.linear_gemv(packs[j][0], xs[j], y=ys[j], wfmt=wsl.WSL_W_NF4, n_out=n, k=k)
+        rows = sample_rows(n, 32, 11 + j)
+        worst = max(worst, gate_gemv(f"nf4 decode sweep {name}", ys[j][torch.as_tensor(rows, device="cuda")],
+                                     nf4_rows_tile(packs[j][0], n, k, rows), xs[j], 4e-3))
+    launches = [Launch(lambda p=p, n=n, k=k, j=j: wsl.linear_gemv(p, xs[j], y=ys[j], wfmt=wsl.WSL_W_NF4, n_out=n, k=k),
+                       nbytes=wsl.nf4_packed_bytes(n, k), flops=2 * n * k, name=f"nf4_gemv_{SWEEP_6144[j][0]}")
+                for (p, n, k, j) in packs]
+    g = capture(launches)
+    graph_ms = time_graphs([g], k_steps, warmup) / k_steps
+    # per stage: one block of launches over the 48 layers' matrices of that stage
+    out = summarize(time_step_launches([launches], 2 * layers, 4), {f"nf4_gemv_{st[0]}": layers for st in SWEEP_6144})
     out.update({
         "workload": "NF4 decode sweep, 48 layers x (qkv 8192x6144, o 6144x6144, gate_up 32768x6144, down 6144x16384)",
-        "parity_worst_ratio": worst, "frac_hbm": out["kernel_gbs"] / HBM_PEAK_GBS,
+        "sanity_worst_ratio": worst, "frac_hbm_kernels": out["kernel_gbs"] / HBM_PEAK_GBS,
         "graph_ms_per_token": graph_ms, "graph_tokens_per_s": 1e3 / graph_ms,
         "graph_gbs": out["bytes_per_step"] / 1e9 / (graph_ms / 1e3),
-        "eager_tokens_per_s": 1e3 / out["ms_per_step"],
+        "frac_hbm_graph": out["bytes_per_step"] / 1e9 / (graph_ms / 1e3) / HBM_PEAK_GBS,
         "launch_gap_us_per_launch": 1e3 * (graph_ms - out["kernel_ms_per_step"]) / out["launches_per_step"],
     })
     del g, packs, launches
@@ -281,8 +346,8 @@ def run_cfg2(k_steps, warmup, layers=48):
     return out
 
 
-def run_cfg3(k_steps, warmup, copies=16):
-    """NF4 prefill GEMM, 32 positions, 32B-class FFN (configs[3])."""
+def run_nf4_prefill_gemm(k_steps, warmup, copies=16):
+    """NF4 prefill GEMM, 32 positions, 32B-class FFN: up 27648x5120 and down 5120x27648."""
     import torch
     import synth
     import weight_streaming_linear_amd as wsl
@@ -300,19 +365,12 @@ def run_cfg3(k_steps, warmup, copies=16):
             w = synth.device_weight(3, 100 * c + j, n, k)
             p = wsl.nf4_pack(w)
             if c == 0:
-                import oracle
                 wsl.linear_gemm(p, xs[j], y=ys[j], wfmt=wsl.WSL_W_NF4, n_out=n, k=k, workspace=wss[j])
-                torch.cuda.synchronize()
                 cols = sample_rows(n, 48, 21 + j)
-                wf = oracle.f32_from_bf16_bits(bf16_rows_to_host(w, cols)).astype(np.float64)
-                codes, scales = oracle.pack_codes(wf)
-                t = oracle.f32_from_bf16_bits(oracle.dequant_tile_bits(codes, scales)).astype(np.float64)
-                xf = oracle.f32_from_bf16_bits(xs[j].view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
-                y_ref, s_ref = oracle.gemm_ref(xf, t)
-                ok, wr, _ = oracle.check_rows_f32(ys[j].cpu().numpy()[:, cols], y_ref, s_ref)
-                if not ok:
-                    raise SystemExit(f"parity check failed for cfg3/{name}: worst {wr}; refusing to time")
-                worst = max(worst, wr)
+                t = nf4_rows_tile(p, n, k, cols).float()
+                xf = xs[j].float()
+                worst = max(worst, check_close(f"nf4 prefill gemm {name}", ys[j][:, torch.as_tensor(cols, device="cuda")],
+                                               xf @ t.t().contiguous(), xf.abs() @ t.abs().t().contiguous(), 1e-4))
             pc.append(p)
             del w
         packs.append(pc)
@@ -320,12 +378,11 @@ def run_cfg3(k_steps, warmup, copies=16):
                                                                       k=k, workspace=wss[j]),
                      nbytes=wsl.nf4_packed_bytes(n, k), flops=2 * m * n * k, name=f"nf4_gemm_{name}")
               for j, (name, n, k) in enumerate(mats)] for pc in packs]
-    wall, recs = time_steps(lambda i: steps[i % copies], k_steps, warmup)
-    out = summarize(wall, recs, k_steps)
+    out = summarize(time_step_launches(steps, k_steps, warmup))
     ai = out["flops_per_step"] / out["bytes_per_step"]
     roof = min(MFMA_BF16_PEAK_TFLOPS, ai * HBM_PEAK_GBS / 1e3)
     out.update({"workload": "NF4 GEMM M=32: up 27648x5120 and down 5120x27648, fp32 out", "rotation_copies": copies,
-                "parity_worst_ratio": worst, "frac_mfma": out["kernel_tflops"] / MFMA_BF16_PEAK_TFLOPS,
+                "sanity_worst_ratio": worst, "frac_mfma": out["kernel_tflops"] / MFMA_BF16_PEAK_TFLOPS,
                 "roofline_tflops": roof, "frac_roofline": out["kernel_tflops"] / roof,
                 "frac_hbm": out["kernel_gbs"] / HBM_PEAK_GBS})
     del packs
@@ -333,11 +390,10 @@ def run_cfg3(k_steps, warmup, copies=16):
     return out
 
 
-def run_cfg4(k_steps, warmup, copies=2):
-    """bf16 batch-verification GEMM, 8192 positions (configs[4]), bf16 out."""
+def run_bf16_verify_gemm(k_steps, warmup, copies=2):
+    """bf16 batch-verification GEMM, 8192 positions: gate 17408x5120 and down 5120x17408, bf16 out."""
     import torch
     import synth
-    import oracle
     import weight_streaming_linear_amd as wsl
     m = 8192
     mats = [("gate", 17408, 5120), ("down", 5120, 17408)]
@@ -347,27 +403,26 @@ def run_cfg4(k_steps, warmup, copies=2):
     worst = 0.0
     for j, (name, n, k) in enumerate(mats):
         wsl.linear_gemm(ws[0][j], xs[j], y=ys[j], ofmt=wsl.WSL_OUT_BF16)
-        torch.cuda.synchronize()
-        rows = sample_rows(m, 24, 31 + j)
-        cols = sample_rows(n, 48, 41 + j)
-        xf = oracle.f32_from_bf16_bits(bf16_rows_to_host(xs[j], rows)).astype(np.float64)
-        wf = oracle.f32_from_bf16_bits(bf16_rows_to_host(ws[0][j], cols)).astype(np.float64)
-        y_ref, s_ref = oracle.gemm_ref(xf, wf)
-        got = ys[j].view(torch.int16).cpu().numpy().view(np.uint16)[np.ix_(rows, cols)]
-        ok, wr, _ = oracle.check_bf16(got, y_ref, s_ref)
-        if not ok:
-            raise SystemExit(f"parity check failed for cfg4/{name}: worst {wr}; refusing to time")
-        worst = max(worst, wr)
+        rows = torch.as_tensor(sample_rows(m, 24, 31 + j), device="cuda")
+        cols = torch.as_tensor(sample_rows(n, 48, 41 + j), device="cuda")
+        xf = xs[j][rows].float()
+        wf = ws[0][j][cols].float()
+        got = ys[j][rows][:, cols]
+        worst = max(worst, check_close(f"bf16 verify gemm {name}", got, xf @ wf.t().contiguous(),
+                                       xf.abs() @ wf.abs().t().contiguous(), 1e-4, ulp_rel=2.0 ** -8))
     steps = [[Launch(lambda w=wc[j], j=j: wsl.linear_gemm(w, xs[j], y=ys[j], ofmt=wsl.WSL_OUT_BF16),
                      nbytes=2 * n * k, flops=2 * m * n * k, name=f"bf16_gemm_{name}")
               for j, (name, n, k) in enumerate(mats)] for wc in ws]
-    wall, recs = time_steps(lambda i: steps[i % copies], k_steps, warmup)
-    out = summarize(wall, recs, k_steps)
+    out = summarize(time_step_launches(steps, k_steps, warmup))
     out.update({"workload": "bf16 GEMM M=8192: gate 17408x5120 and down 5120x17408, bf16 out",
-                "parity_worst_ratio": worst, "frac_mfma": out["kernel_tflops"] / MFMA_BF16_PEAK_TFLOPS})
+                "sanity_worst_ratio": worst, "frac_mfma": out["kernel_tflops"] / MFMA_BF16_PEAK_TFLOPS})
     del ws, xs, ys
     torch.cuda.empty_cache()
     return out
+
+
+PATHS = [("nf4_gemv_4096", run_nf4_gemv_4096), ("nf4_decode_sweep_48x6144", run_nf4_decode_sweep),
+         ("nf4_prefill_gemm_m32", run_nf4_prefill_gemm), ("bf16_verify_gemm_m8192", run_bf16_verify_gemm)]
 
 
 # ---------------------------------------------------------------- CPU baseline (oracle)
@@ -382,7 +437,7 @@ def cpu_baseline(budget_s=12.0):
     except Exception:
         blas_threads = None
     cores = len(os.sched_getaffinity(0))
-    mats = [(synth.weight_bits(1, j, n, k), synth.act_bits(1, 100 + j, (k,))) for j, (_, n, k) in enumerate(CFG1_MATS)]
+    mats = [(synth.weight_bits(1, j, n, k), synth.act_bits(1, 100 + j, (k,))) for j, (_, n, k) in enumerate(LAYER_5120)]
     done_bytes = 0
     t0 = time.perf_counter()
     passes = 0
@@ -399,6 +454,87 @@ def cpu_baseline(budget_s=12.0):
                       f"through oracle.gemv_ref (bf16->fp64 + fp64 BLAS matvec), {dt:.1f} s; host has {cores} cores"}
 
 
+# ---------------------------------------------------------------- HBM traffic from rocprofv3 counters
+def source_sha():
+    return hashlib.sha256(open(GEMV_SRC, "rb").read()).hexdigest()
+
+
+def traffic_probe():
+    """The launches that a counter run of this script sees: 3 elementwise copies of CALIB_BYTES
+    (torch.neg into a second buffer: a kernel that reads and writes exactly CALIB_BYTES), then
+    4 eager steps of the headline layer.  No timing, no oracle."""
+    import torch
+    src = torch.empty(CALIB_BYTES // 2, dtype=torch.bfloat16, device="cuda").normal_()
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    _, _, _, steps = setup_layer_5120(copies=2)
+    for i in range(4):
+        for l in steps[i % 2]:
+            l.fn()
+    torch.cuda.synchronize()
+    print("traffic probe done", flush=True)
+
+
+def _counter_rows(run_dir, counter):
+    """(kernel name, dispatch id, value) for every dispatch in a rocprofv3 counter CSV."""
+    import csv
+    rows = []
+    for path in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") == counter:
+                    rows.append((r.get("Kernel_Name", ""), r.get("Dispatch_Id", ""), float(r["Counter_Value"])))
+    return rows
+
+
+def _per_dispatch(rows, match):
+    acc = {}
+    for name, disp, v in rows:
+        if match(name):
+            acc[disp] = acc.get(disp, 0.0) + v
+    return list(acc.values())
+
+
+def traffic_summarize(fetch_dir, write_dir, commands):
+    """Per-launch HBM bytes of the dominant kernel from two counter runs of --traffic-probe."""
+    # calibration: the elementwise negation of CALIB_BYTES (reads and writes CALIB_BYTES)
+    is_calib = lambda n: "neg_kernel" in n
+    is_dom = lambda n: "gemv_bf16_kernel" in n and ("<8>" in n or "ILi8E" in n)
+    out = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _counter_rows(d, counter)
+        calib = _per_dispatch(rows, is_calib)
+        dom = _per_dispatch(rows, is_dom)
+        if not calib or not dom:
+            raise SystemExit(f"{counter}: no calibration copy ({len(calib)}) or dominant kernel ({len(dom)}) rows")
+        factor = (np.mean(calib) * 1024) / CALIB_BYTES
+        out[counter] = {"kib_per_dispatch_raw": float(np.mean(dom)), "dispatches": len(dom),
+                        "calibration_copy_kib": float(np.mean(calib)), "factor": float(factor),
+                        "bytes_per_launch": float(np.mean(dom) * 1024 / factor)}
+    algo = 2 * 34816 * 5120
+    res = {"kernel": "gemv_bf16_kernel<8> (gate_up 34816x5120)", "kernel_source_sha256": source_sha(),
+           "algorithmic_bytes_per_launch": algo, "counters": out,
+           "bytes_per_launch": out["FETCH_SIZE"]["bytes_per_launch"] + out["WRITE_SIZE"]["bytes_per_launch"],
+           "commands": commands}
+    res["ratio_to_algorithmic"] = res["bytes_per_launch"] / algo
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(res, f, indent=1)
+    print(json.dumps(res, indent=1))
+
+
+def traffic_from_file():
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+        return t["bytes_per_launch"] if t.get("kernel_source_sha256") == source_sha() else None
+    except Exception:
+        return None
+
+
 # ---------------------------------------------------------------- main
 def main():
     ap = argparse.ArgumentParser()
@@ -407,57 +543,44 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-paths", action="store_true", help="only the headline workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", default="", help="comma list of paths to run (cfg0,cfg2,cfg3,cfg4)")
+    ap.add_argument("--only", default="", help="comma list of paths: " + ",".join(n for n, _ in PATHS))
+    ap.add_argument("--traffic-probe", action="store_true", help="launch sequence for rocprofv3 counter runs")
+    ap.add_argument("--traffic-summarize", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--traffic-commands", default="", help="the counter commands, recorded with the summary")
     args = ap.parse_args()
+    if args.traffic_summarize:
+        traffic_summarize(*args.traffic_summarize, args.traffic_commands)
+        return
     if args.gpus != 1:
-        print("bench.py measures one GPU only: the weight-streaming kernels run on a single MI355X; "
-              "multi-GPU sharding is described in DESIGN.md but not built. Use --gpus 1.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build measures the kernels on a "
+              "single MI355X and has no multi-GPU path. Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
     import weight_streaming_linear_amd as wsl
     wsl.lib()
+    if args.traffic_probe:
+        traffic_probe()
+        return
     props = torch.cuda.get_device_properties(0)
     log(f"device {props.name} ({getattr(props, 'gcnArchName', '?')}), {props.multi_processor_count} CUs")
 
-    # headline: configs[1]
-    layers, xs, ys = setup_cfg1(copies=2)
-    worst = gate_cfg1(layers, xs, ys)
-    log(f"cfg1 parity ok (worst ratio {worst:.3g})")
-    steps_fn = cfg1_steps(layers, xs, ys)
-    wall, recs = time_steps(steps_fn, args.steps, args.warmup)
-    head = summarize(wall, recs, args.steps)
-    value = head["bytes_per_step"] / 1e9 / (head["ms_per_step"] / 1e3)
-    avg_launch_s = head["avg_launch_us"] / 1e6
-    bytes_per_launch = head["bytes_per_step"] / head["launches_per_step"]
-    achieved = bytes_per_launch / 1e9 / avg_launch_s
-    log(f"cfg1: {head['ms_per_step'] * 1e3:.1f} us/step, {value:.0f} GB/s wall, {achieved:.0f} GB/s kernel")
-    del layers
-    torch.cuda.empty_cache()
+    head = measure_headline(args.steps, args.warmup)
+    per_launch = head["per_launch"]
+    value = per_launch["bytes_per_step"] / 1e9 / (head["ms_per_step"] / 1e3)
+    achieved = head["dominant_bytes"] / 1e3 / head["dominant_avg_us"]
+    log(f"bf16 decode layer: {head['ms_per_step'] * 1e3:.1f} us/step (graph), {value:.0f} GB/s; "
+        f"kernels {per_launch['kernel_ms_per_step'] * 1e3:.1f} us/step; gate_up kernel {achieved:.0f} GB/s")
 
     paths = {}
     if not args.no_paths:
         only = set(filter(None, args.only.split(",")))
-        for name, fn in [("cfg0", run_cfg0), ("cfg2", run_cfg2), ("cfg3", run_cfg3), ("cfg4", run_cfg4)]:
+        for name, fn in PATHS:
             if only and name not in only:
                 continue
             log(f"{name} ...")
             paths[name] = fn(20, 5)
             log(f"{name}: {json.dumps({k: v for k, v in paths[name].items() if isinstance(v, float)})}")
-
-    traffic = None
-    tfile = os.path.join(ROOT, "profiles", "traffic_gemv_bf16_cfg1.json")
-    if os.path.exists(tfile):
-        try:
-            t = json.load(open(tfile))
-            src_hash = t.get("kernel_source_sha256")
-            import hashlib
-            cur = hashlib.sha256(open(os.path.join(ROOT, "weight_streaming_linear_amd", "csrc", "gemv.hip"),
-                                      "rb").read()).hexdigest()
-            if src_hash == cur:
-                traffic = t.get("bytes_per_launch")
-        except Exception:
-            traffic = None
 
     out = {
         "metric": METRIC,
@@ -474,9 +597,10 @@ def main():
         "data": "synthetic (seeded N(0,0.02) weights, N(0,1) activations; drawn on the device)",
         "config": {
             "workload": "bf16 decode GEMV, batch 1, one dense decoder layer, hidden 5120: "
-                        "qkv 7168x5120, o 5120x5120, gate_up 34816x5120, down 5120x17408 (4 launches/step)",
-            "weight_bytes_per_step": head["bytes_per_step"],
-            "rotation_bytes": 2 * head["bytes_per_step"],
+                        "qkv 7168x5120, o 5120x5120, gate_up 34816x5120, down 5120x17408 (4 launches/step, "
+                        "one graph replay per step)",
+            "weight_bytes_per_step": per_launch["bytes_per_step"],
+            "rotation_bytes": 2 * per_launch["bytes_per_step"],
             "parallelism": "single GPU",
             "device": props.name,
         },
@@ -486,10 +610,15 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic,
-            "kernel": "gemv_bf16_kernel",
-            "bytes_per_launch": bytes_per_launch,
-            "avg_launch_us": round(head["avg_launch_us"], 3),
+            "traffic": traffic_from_file(),
+            "kernel": "gemv_bf16_kernel<8> (gate_up 34816x5120)",
+            "bytes_per_launch": head["dominant_bytes"],
+            "avg_launch_us": round(head["dominant_avg_us"], 3),
+        },
+        "headline_detail": {
+            "sanity_worst_ratio": head["sanity_worst_ratio"],
+            "kernel_ms_per_step": round(per_launch["kernel_ms_per_step"], 6),
+            "launches": per_launch["launches"],
         },
         "paths": paths,
     }

@@ -9,7 +9,7 @@ of code plus 16 bits of scale per 64 weights); the kernels restore only the
 current tile's fragment; prefill restores into BF16 fragments.  deep-fold's
 "Контрибьюторы" table: compression is checked by a CPU round trip.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
 * weights are y = W x with W stored [n_out][k], k contiguous; a group is 64
   consecutive k of one row, so k must be a multiple of 64;
 * scale s = fp16_RNE(max |w|) over the group; codes are chosen against the

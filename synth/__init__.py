@@ -10,11 +10,12 @@ Recipe (stand-ins for the trained weights and hidden states of the dense
 * weights: float32 standard normal * float32(0.02), cast to bf16;
 * activations: float32 standard normal, cast to bf16.
 
-Host draws use numpy's PCG64 seeded with [2026, cfg, tensor_id]; device draws
-(for the 48-layer sweep, too large to draw on the host) use torch's generator
-on the device, seeded with 2026 * 1_000_003 + cfg * 1_000 + tensor_id.  A
-tensor is always drawn the same way for a given (cfg, tensor_id), so a host
-copy of a device draw is the same tensor.
+Host draws use numpy's PCG64 seeded with [2026, stream, tensor_id], where
+`stream` numbers a family of inputs (one per workload, 0-4, and others for
+test fixtures); device draws (for the 48-layer sweep, too large to draw on the
+host) use torch's generator on the device, seeded with
+2026 * 1_000_003 + stream * 1_000 + tensor_id.  A tensor is always drawn the
+same way for a given (stream, tensor_id).
 """
 
 import numpy as np
@@ -23,8 +24,8 @@ WEIGHT_STD = np.float32(0.02)
 SEED = 2026
 
 
-def _rng(cfg, tensor_id):
-    return np.random.default_rng([SEED, int(cfg), int(tensor_id)])
+def _rng(stream, tensor_id):
+    return np.random.default_rng([SEED, int(stream), int(tensor_id)])
 
 
 def _bf16_bits_torch(f32):
@@ -33,38 +34,38 @@ def _bf16_bits_torch(f32):
     return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
-def host_normal_f32(cfg, tensor_id, shape, scale=None):
-    g = _rng(cfg, tensor_id)
+def host_normal_f32(stream, tensor_id, shape, scale=None):
+    g = _rng(stream, tensor_id)
     a = g.standard_normal(size=shape, dtype=np.float32)
     if scale is not None:
         a = (a * np.float32(scale)).astype(np.float32)
     return a
 
 
-def weight_bits(cfg, tensor_id, n_out, k):
+def weight_bits(stream, tensor_id, n_out, k):
     """bf16 bit patterns (uint16 [n_out][k]) of a seeded ~N(0, 0.02) weight matrix."""
-    return _bf16_bits_torch(host_normal_f32(cfg, tensor_id, (n_out, k), WEIGHT_STD))
+    return _bf16_bits_torch(host_normal_f32(stream, tensor_id, (n_out, k), WEIGHT_STD))
 
 
-def act_bits(cfg, tensor_id, shape):
+def act_bits(stream, tensor_id, shape):
     """bf16 bit patterns of seeded ~N(0, 1) activations of the given shape."""
-    return _bf16_bits_torch(host_normal_f32(cfg, tensor_id, shape))
+    return _bf16_bits_torch(host_normal_f32(stream, tensor_id, shape))
 
 
-def device_seed(cfg, tensor_id):
-    return SEED * 1_000_003 + int(cfg) * 1_000 + int(tensor_id)
+def device_seed(stream, tensor_id):
+    return SEED * 1_000_003 + int(stream) * 1_000 + int(tensor_id)
 
 
-def device_normal_bf16(cfg, tensor_id, shape, scale=None, device="cuda"):
+def device_normal_bf16(stream, tensor_id, shape, scale=None, device="cuda"):
     """A seeded bf16 tensor drawn on the device (torch generator on that device)."""
     import torch
     g = torch.Generator(device=device)
-    g.manual_seed(device_seed(cfg, tensor_id))
+    g.manual_seed(device_seed(stream, tensor_id))
     a = torch.randn(shape, generator=g, dtype=torch.float32, device=device)
     if scale is not None:
         a.mul_(float(np.float32(scale)))
     return a.to(torch.bfloat16)
 
 
-def device_weight(cfg, tensor_id, n_out, k, device="cuda"):
-    return device_normal_bf16(cfg, tensor_id, (n_out, k), WEIGHT_STD, device)
+def device_weight(stream, tensor_id, n_out, k, device="cuda"):
+    return device_normal_bf16(stream, tensor_id, (n_out, k), WEIGHT_STD, device)

@@ -2,8 +2,8 @@
 
 NF4: the reference multiplies the restored bf16 tile T = bf16(fp32(c * s)); bf16:
 the weight as stored.  fp32 output: |Y - Y_ref| <= 1e-4 * S elementwise; bf16 output:
-one more bf16 ulp of |Y_ref|.  Full BASELINE shapes are checked on sampled rows and
-columns, including tile edges.
+one more bf16 ulp of |Y_ref|.  The full prefill and batch-verification shapes are checked
+on sampled rows and columns, including tile edges.
 """
 
 import numpy as np
@@ -112,11 +112,11 @@ def _sample_idx(n, tile, rng, count):
     return np.unique(np.concatenate([np.array(edges), rng.integers(0, n, count)]))
 
 
-# configs[3]: NF4 prefill GEMM, 32 positions, 32B-class FFN (up 5120 -> 27648, down 27648 -> 5120)
+# NF4 prefill GEMM, 32 positions, 32B-class FFN (up 5120 -> 27648, down 27648 -> 5120).
 @pytest.mark.parametrize("n_out,k,tid", [(27648, 5120, 0), (5120, 27648, 1)])
-def test_gemm_nf4_cfg3_full_shape_sampled(n_out, k, tid):
+def test_gemm_nf4_prefill_m32_full_shape_sampled(n_out, k, tid):
     import torch
-    say(f"gemm nf4 cfg3 {n_out}x{k}")
+    say(f"gemm nf4 prefill m=32 {n_out}x{k}")
     m = 32
     wb = synth.weight_bits(3, tid, n_out, k)
     xb = synth.act_bits(3, 2 + tid, (m, k))
@@ -140,11 +140,11 @@ def test_gemm_nf4_cfg3_full_shape_sampled(n_out, k, tid):
     assert ok, f"elem {i}: worst ratio {worst}"
 
 
-# configs[4]: bf16 batch verification, M = 8192 positions, gate (5120 -> 17408) and down (17408 -> 5120)
+# bf16 batch verification, M = 8192 positions, gate (5120 -> 17408) and down (17408 -> 5120).
 @pytest.mark.parametrize("n_out,k,tid", [(17408, 5120, 0), (5120, 17408, 1)])
-def test_gemm_bf16_cfg4_full_shape_sampled(n_out, k, tid):
+def test_gemm_bf16_verify_m8192_full_shape_sampled(n_out, k, tid):
     import torch
-    say(f"gemm bf16 cfg4 {n_out}x{k}")
+    say(f"gemm bf16 verify m=8192 {n_out}x{k}")
     m = 8192
     wb = synth.weight_bits(4, tid, n_out, k)
     xb = synth.act_bits(4, 2 + tid, (m, k))

@@ -16,10 +16,10 @@ from gpu_common import to_dev_bf16, to_dev_u8, f64, say
 pytestmark = pytest.mark.gpu
 
 
-def _nf4_case(n_out, k, cfg, tid_w, tid_x):
+def _nf4_case(n_out, k, stream, tid_w, tid_x):
     import torch
-    wb = synth.weight_bits(cfg, tid_w, n_out, k)
-    xb = synth.act_bits(cfg, tid_x, (k,))
+    wb = synth.weight_bits(stream, tid_w, n_out, k)
+    xb = synth.act_bits(stream, tid_x, (k,))
     packed = wsl.nf4_pack(to_dev_bf16(wb))
     y = wsl.linear_gemv(packed, to_dev_bf16(xb), wfmt=wsl.WSL_W_NF4, n_out=n_out, k=k)
     torch.cuda.synchronize()
@@ -72,17 +72,17 @@ def test_gemv_nf4_large_sampled(n_out, k, tid):
     assert ok, f"row {rows[i]}: worst ratio {worst}"
 
 
-def _bf16_case(n_out, k, cfg, tid_w, tid_x):
+def _bf16_case(n_out, k, stream, tid_w, tid_x):
     import torch
-    wb = synth.weight_bits(cfg, tid_w, n_out, k)
-    xb = synth.act_bits(cfg, tid_x, (k,))
+    wb = synth.weight_bits(stream, tid_w, n_out, k)
+    xb = synth.act_bits(stream, tid_x, (k,))
     y = wsl.linear_gemv(to_dev_bf16(wb), to_dev_bf16(xb))
     torch.cuda.synchronize()
     y_ref, s_ref = oracle.gemv_ref(f64(wb), f64(xb))
     return y.cpu().numpy(), y_ref, s_ref
 
 
-# configs[1]: one dense decoder layer, hidden 5120, k/v 1024 rows, gate/up 17408, down k = 17408
+# One dense decoder layer with hidden size 5120: k/v 1024 rows, gate/up 17408 rows, down k = 17408.
 @pytest.mark.parametrize("n_out,k,tid", [(5120, 5120, 0), (1024, 5120, 1), (17408, 5120, 4), (5120, 17408, 6),
                                          (7168, 5120, 10), (3, 8, 11), (5, 520, 12), (1, 4104, 13), (333, 1000, 14)])
 def test_gemv_bf16_tolerance(n_out, k, tid):

@@ -11,12 +11,12 @@ from gpu_common import to_dev_bf16, to_dev_u8, bits_of, f64, say
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("n_out,k,cfg,tid", [(4096, 4096, 0, 0), (17, 192, 90, 1), (1, 64, 90, 2),
+@pytest.mark.parametrize("n_out,k,stream,tid", [(4096, 4096, 0, 0), (17, 192, 90, 1), (1, 64, 90, 2),
                                              (33, 320, 90, 3), (16, 128, 90, 4), (100, 2112, 90, 5)])
-def test_pack_bit_exact(n_out, k, cfg, tid):
+def test_pack_bit_exact(n_out, k, stream, tid):
     import torch
     say(f"pack {n_out}x{k}")
-    wb = synth.weight_bits(cfg, tid, n_out, k)
+    wb = synth.weight_bits(stream, tid, n_out, k)
     packed = wsl.nf4_pack(to_dev_bf16(wb))
     torch.cuda.synchronize()
     ref = oracle.pack_device(f64(wb))
