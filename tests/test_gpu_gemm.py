@@ -28,8 +28,11 @@ def _check(y_dev, y_ref, s_ref, ofmt):
     return oracle.check_bf16(bits_of(y_dev), y_ref, s_ref)
 
 
+# k % 256 == 0 with m <= 32 takes the shared-X kernel (ragged row counts, one chunk, many
+# splits, m < 32); the others the general kernel.
 @pytest.mark.parametrize("m,n_out,k", [(5, 100, 192), (32, 96, 640), (70, 33, 128), (130, 160, 256), (1, 32, 64),
-                                       (32, 1000, 5120)])
+                                       (32, 1000, 5120), (7, 300, 512), (32, 257, 1024), (1, 16, 256),
+                                       (19, 4109, 2304), (33, 64, 512)])
 @pytest.mark.parametrize("ofmt", [wsl.WSL_OUT_F32, wsl.WSL_OUT_BF16])
 @pytest.mark.parametrize("use_ws", [False, True])
 def test_gemm_nf4_small(m, n_out, k, ofmt, use_ws):
@@ -63,10 +66,11 @@ def test_gemm_bf16_small(m, n_out, k, ofmt):
     assert ok, f"elem {i}: worst ratio {worst}"
 
 
-def test_gemm_strided_x_and_y():
+@pytest.mark.parametrize("m,k", [(40, 192), (20, 512)])
+def test_gemm_strided_x_and_y(m, k):
     """Leading dimensions larger than the logical widths."""
     import torch
-    m, n_out, k = 40, 72, 192
+    n_out = 72
     wb = synth.weight_bits(99, 0, n_out, k)
     xb = synth.act_bits(99, 1, (m, k + 16))
     x = to_dev_bf16(xb)[:, :k]
@@ -85,11 +89,13 @@ def test_gemm_strided_x_and_y():
     assert torch.isnan(y2[:, n_out:]).all()
 
 
-@pytest.mark.parametrize("j", [0, 31, 32, 63, 191])
-def test_gemm_one_hot_restores_tile_column(j):
-    """A one-hot row of X picks column j of the bf16 tile exactly (NF4) / of W (bf16)."""
+@pytest.mark.parametrize("j,k", [(0, 192), (31, 192), (32, 192), (63, 192), (191, 192), (0, 512), (127, 512),
+                                 (128, 512), (255, 512), (300, 512), (511, 512)])
+def test_gemm_one_hot_restores_tile_column(j, k):
+    """A one-hot row of X picks column j of the bf16 tile exactly (NF4) / of W (bf16).  k = 512
+    runs the shared-X kernel, whose lanes take 128-code runs in a permuted k order."""
     import torch
-    m, n_out, k = 3, 96, 192
+    m, n_out = 3, 96
     wb = synth.weight_bits(100, 0, n_out, k)
     x = np.zeros((m, k), np.float32)
     x[1, j] = 1.0

@@ -38,12 +38,13 @@ __device__ __forceinline__ float f16_to_f32(uint32_t h) {
     return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
 }
 
-// Round-to-nearest-even binary32 -> bf16 (hardware conversion, finite inputs).
+// Round-to-nearest-even binary32 -> bf16 of two values, lo in bits 0..15 (one
+// v_cvt_pk_bf16_f32; finite inputs).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    __bf16 a = static_cast<__bf16>(lo);
-    __bf16 b = static_cast<__bf16>(hi);
-    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
-           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
+    const f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v));
 }
 
 // Index (in fp16 elements) of scale (row n, group g) in the device layout:
@@ -57,6 +58,36 @@ __device__ __forceinline__ int64_t scale_index(int64_t n, int64_t g, int64_t gro
 
 __device__ __forceinline__ uint32_t rotl32(uint32_t v, int s) { return (v << s) | (v >> (32 - s)); }
 __device__ __forceinline__ uint32_t rotr32(uint32_t v, int s) { return (v >> s) | (v << (32 - s)); }
+
+// Pair table (64 KB, one ds_read_b64 per two codes).  Entry of byte value b (the
+// codes of two consecutive k, even k in the low nibble) = (level(b & 15),
+// level(b >> 4)), replicated 32 times: lane l reads copy l % 32 at byte offset
+// b * 256 + (l % 32) * 8, so the 32 lanes served together touch 32 distinct
+// 8-byte bank pairs whatever the codes are.  The address is one SDWA move that
+// writes byte B of the (un-rotated) code word into bits 8..15 of a register whose
+// low byte already holds the lane's copy offset.
+constexpr int kPairTableBytes = 256 * 32 * 8;
+
+template <int B>
+__device__ __forceinline__ void pair_addr(uint32_t &a, uint32_t w) {
+    if constexpr (B == 0)
+        asm("v_mov_b32_sdwa %0, %1 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_0" : "+v"(a) : "v"(w));
+    else if constexpr (B == 1)
+        asm("v_mov_b32_sdwa %0, %1 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_1" : "+v"(a) : "v"(w));
+    else if constexpr (B == 2)
+        asm("v_mov_b32_sdwa %0, %1 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_2" : "+v"(a) : "v"(w));
+    else
+        asm("v_mov_b32_sdwa %0, %1 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_3" : "+v"(a) : "v"(w));
+}
+
+// Fill the pair table (kPairTableBytes of LDS at `tab`) cooperatively; the caller
+// synchronizes the workgroup before the first lookup.
+__device__ __forceinline__ void fill_pair_table(char *tab) {
+    for (int i = threadIdx.x; i < kPairTableBytes / 8; i += blockDim.x) {
+        const int b = i >> 5;
+        reinterpret_cast<float2 *>(tab)[i] = make_float2(level(b & 15), level(b >> 4));
+    }
+}
 
 // Sum across the 64 lanes of a wavefront; every lane gets the total.
 __device__ __forceinline__ float wave_sum(float v) {

@@ -360,6 +360,154 @@ __global__ __launch_bounds__(256) void gemm_nf4_kernel(const uint8_t *__restrict
     }
 }
 
+// ---------------------------------------------------------------- NF4, shared X, M <= 32
+// The prefill kernel for up to 32 positions and k a multiple of 256.  A
+// workgroup of 8 waves owns 256 weight rows (wave w: rows 32w .. 32w+31, lane l
+// row l % 32) and the k range of its split.  Per 256-k chunk:
+//   * the workgroup stages X[32 positions][256 k] (16 KB) once in LDS (two
+//     buffers; row i at i * 512, 16-byte chunk c at c ^ (i % 32) so that the
+//     fragment reads of a 32-lane half are free of bank conflicts), instead of
+//     every wave reading its own copy;
+//   * lane (n, h) holds the 64 bytes of codes of row n for k in
+//     [kc + 128h, kc + 128h + 128) -- 16 MFMA k-steps of 8 codes -- and the two
+//     scales of those groups, loaded one chunk ahead.  Each load instruction
+//     touches 32 rows; the four that cover a 128-byte line of a row are issued
+//     back to back as ordinary (L1-allocating) loads, so the line is fetched
+//     from L2 once;
+//   * each k-step restores 8 codes through the replicated pair table into a
+//     bf16 B fragment t = bf16(fp32(level * s)) and issues one
+//     v_mfma_f32_32x32x16_bf16 against the A fragment X[i][same 8 k] from LDS.
+// The barrier that publishes a staged chunk is an asm statement with a memory
+// clobber and no vmcnt wait, so the next chunk's loads stay in flight across it
+// and the compiler cannot move LDS accesses over it.  The wave writes its
+// 32 x 32 result to Y, or to the split workspace.
+constexpr int kX32Chunk = 256;
+constexpr int kX32Stage = 32 * kX32Chunk * 2;
+constexpr int kX32Rows = 256;
+
+__global__ __launch_bounds__(512) void gemm_nf4_x32_kernel(const uint8_t *__restrict__ packed, int64_t n_out,
+                                                           int64_t k, const uint16_t *__restrict__ x, int64_t m,
+                                                           int64_t ldx, void *__restrict__ y, int ofmt, int64_t ldy,
+                                                           float *__restrict__ ws, int64_t k_per_split) {
+    __shared__ __align__(16) char tab[kPairTableBytes];
+    __shared__ __align__(16) char xst[2][kX32Stage];
+    fill_pair_table(tab);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int half = lane >> 5, l32 = lane & 31;
+    const int64_t groups = k >> 6;
+    const int64_t rowbytes = k >> 1;
+    const uint16_t *scales = reinterpret_cast<const uint16_t *>(packed + n_out * rowbytes);
+    const int64_t rowt = static_cast<int64_t>(blockIdx.x) * kX32Rows + wave * 32 + l32;
+    const int64_t row = rowt < n_out ? rowt : n_out - 1;
+    const int64_t kbeg = static_cast<int64_t>(blockIdx.y) * k_per_split;
+    const int64_t kend = (kbeg + k_per_split < k) ? kbeg + k_per_split : k;
+    const int nch = kend > kbeg ? static_cast<int>((kend - kbeg) / kX32Chunk) : 0;
+    uint32_t ad[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ad[i] = static_cast<uint32_t>(lane & 31) << 3;
+    const uint8_t *crow = packed + row * rowbytes + 64 * half;
+    const int64_t srem = n_out - ((row >> 4) << 4);
+    const int64_t srb = srem < 16 ? srem : 16;
+    const uint16_t *srow = scales + (row >> 4) * 16 * groups + (row & 15);   // scale (row, g) at srow[g * srb]
+    // X staging: thread t moves the 16-byte chunks (row t / 32, chunk t % 32) and (row t / 32 + 16, same chunk).
+    const int xi0 = tid >> 5, xi1 = xi0 + 16, xcc = tid & 31;
+    const uint16_t *xrow0 = x + (xi0 < m ? xi0 : m - 1) * ldx + xcc * 8;
+    const uint16_t *xrow1 = x + (xi1 < m ? xi1 : m - 1) * ldx + xcc * 8;
+    const int xoff0 = xi0 * 512 + ((xcc ^ xi0) << 4);
+    const int xoff1 = xi1 * 512 + ((xcc ^ xi1) << 4);
+
+    auto fetch = [&](int c, uint4 (&q)[4], uint32_t (&sr)[2], uint4 &xv0, uint4 &xv1) {
+        const int64_t kc = kbeg + static_cast<int64_t>(c) * kX32Chunk;
+        xv0 = *reinterpret_cast<const uint4 *>(xrow0 + kc);
+        xv1 = *reinterpret_cast<const uint4 *>(xrow1 + kc);
+        const uint8_t *src = crow + (kc >> 1);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) q[j] = *reinterpret_cast<const uint4 *>(src + 16 * j);
+        const int64_t g0 = (kc >> 6) + 2 * half;
+        sr[0] = srow[g0 * srb];
+        sr[1] = srow[(g0 + 1) * srb];
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto stage_x = [&](char *st, const uint4 &xv0, const uint4 &xv1) {
+        *reinterpret_cast<uint4 *>(st + xoff0) = xv0;
+        *reinterpret_cast<uint4 *>(st + xoff1) = xv1;
+    };
+    f32x16 acc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+    auto compute = [&](const char *st, const uint4 (&q)[4], const uint32_t (&sr)[2]) {
+        const float s0 = f16_to_f32(sr[0]), s1 = f16_to_f32(sr[1]);
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            const int c = 16 * half + t;   // 16-byte chunk of k = kc + 128h + 8t
+            const uint4 av = *reinterpret_cast<const uint4 *>(st + l32 * 512 + ((c ^ l32) << 4));
+            const uint4 qq = q[t >> 2];
+            const uint32_t wn = rotr32((t & 3) == 0 ? qq.x : (t & 3) == 1 ? qq.y : (t & 3) == 2 ? qq.z : qq.w, 2);
+            const float s = t < 8 ? s0 : s1;
+            pair_addr<0>(ad[0], wn);
+            pair_addr<1>(ad[1], wn);
+            pair_addr<2>(ad[2], wn);
+            pair_addr<3>(ad[3], wn);
+            const float2 l0 = *reinterpret_cast<const float2 *>(tab + ad[0]);
+            const float2 l1 = *reinterpret_cast<const float2 *>(tab + ad[1]);
+            const float2 l2 = *reinterpret_cast<const float2 *>(tab + ad[2]);
+            const float2 l3 = *reinterpret_cast<const float2 *>(tab + ad[3]);
+            const uint4 bv = make_uint4(pack_bf16x2(l0.x * s, l0.y * s), pack_bf16x2(l1.x * s, l1.y * s),
+                                        pack_bf16x2(l2.x * s, l2.y * s), pack_bf16x2(l3.x * s, l3.y * s));
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(bv), acc, 0, 0, 0);
+        }
+    };
+    auto sync = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+
+    uint4 qa[4], qb[4], xa0, xa1, xb0, xb1;
+    uint32_t sa[2], sb[2];
+    __syncthreads();   // pair table complete
+    // Chunk c lives in buffer A and LDS stage 0 when c is even, in B and stage 1 when odd.
+    // Inside the loop the prefetch of the next chunk is unconditional (the last chunk is
+    // peeled), so the compiler waits for exactly the loads of the chunk being used.  A
+    // stage is rewritten only after the barrier that follows every wave's use of it.
+    if (nch > 0) {
+        fetch(0, qa, sa, xa0, xa1);
+        for (int c = 0;; c += 2) {
+            stage_x(xst[0], xa0, xa1);
+            if (c + 1 >= nch) {
+                sync();
+                compute(xst[0], qa, sa);
+                break;
+            }
+            fetch(c + 1, qb, sb, xb0, xb1);
+            sync();
+            compute(xst[0], qa, sa);
+            stage_x(xst[1], xb0, xb1);
+            if (c + 2 >= nch) {
+                sync();
+                compute(xst[1], qb, sb);
+                break;
+            }
+            fetch(c + 2, qa, sa, xa0, xa1);
+            sync();
+            compute(xst[1], qb, sb);
+        }
+    }
+    // Output element e of lane l: position 8*(e/4) + 4*h + e%4, column rowt.
+    if (rowt < n_out) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int64_t p = 8 * (e >> 2) + 4 * half + (e & 3);
+            if (p >= m) continue;
+            const float v = acc[e];
+            if (ws != nullptr) {
+                ws[(static_cast<int64_t>(blockIdx.y) * m + p) * n_out + rowt] = v;
+            } else if (ofmt == WSL_OUT_F32) {
+                static_cast<float *>(y)[p * ldy + rowt] = v;
+            } else {
+                static_cast<uint16_t *>(y)[p * ldy + rowt] = static_cast<uint16_t>(pack_bf16x2(v, 0.f) & 0xffffu);
+            }
+        }
+    }
+}
+
 // Sum split partials in split order (fixed, so the result is deterministic).
 __global__ __launch_bounds__(256) void split_reduce_kernel(const float *__restrict__ ws, int splits, int64_t m,
                                                            int64_t n_out, void *__restrict__ y, int ofmt, int64_t ldy) {
@@ -375,13 +523,27 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float *__restri
 }
 
 // ---------------------------------------------------------------- planning / launch
-// NF4 GEMM plan: NB = 1 (32 rows per wave), 4 waves per workgroup; split k
-// across workgroups (each split a multiple of 128 k) only as far as needed to
-// give about 2 waves per SIMD, and only when the caller passes a workspace.
+// NF4 GEMM plans.  M <= 32 with k % 256 == 0: the shared-X kernel, 256 rows per
+// workgroup (one workgroup per CU: 96 KB of LDS), k split into as many ranges
+// of whole 256-k chunks as keep the grid within one pass over the 256 CUs.
+// Otherwise the general kernel: NB = 1 (32 rows per wave), 4 waves per
+// workgroup, 32 positions per grid z, k split (multiples of 128) as far as
+// needed for about 2 waves per SIMD.  Splits need the caller's workspace.
 constexpr int kNf4Nb = 1;
 constexpr int64_t kNf4RowsPerWg = 4 * 32 * kNf4Nb;
 
+static bool use_x32(int64_t k, int64_t m) { return m <= 32 && (k % kX32Chunk) == 0; }
+
 static int nf4_splits(int64_t n_out, int64_t k, int64_t m) {
+    if (use_x32(k, m)) {
+        const int64_t blocks = (n_out + kX32Rows - 1) / kX32Rows;
+        const int64_t chunks = k / kX32Chunk;
+        int64_t splits = 256 / blocks;
+        if (splits < 1) splits = 1;
+        if (splits > chunks) splits = chunks;
+        if (splits > 64) splits = 64;
+        return static_cast<int>(splits);
+    }
     const int64_t waves = ((n_out + 32 * kNf4Nb - 1) / (32 * kNf4Nb)) * ((m + 31) / 32);
     const int64_t chunks = (k + 127) / 128;
     int64_t splits = 1;
@@ -389,9 +551,10 @@ static int nf4_splits(int64_t n_out, int64_t k, int64_t m) {
     return static_cast<int>(splits);
 }
 
-static int64_t nf4_k_per_split(int64_t k, int splits) {
-    const int64_t chunks = (k + 127) / 128;
-    return ((chunks + splits - 1) / splits) * 128;
+static int64_t nf4_k_per_split(int64_t k, int64_t m, int splits) {
+    const int64_t unit = use_x32(k, m) ? kX32Chunk : 128;
+    const int64_t chunks = (k + unit - 1) / unit;
+    return ((chunks + splits - 1) / splits) * unit;
 }
 
 size_t gemm_ws_bytes(int wfmt, int64_t n_out, int64_t k, int64_t m) {
@@ -415,14 +578,24 @@ int launch_gemm_nf4(const void *w, int64_t n_out, int64_t k, const void *x, int6
                     int ofmt, int64_t ldy, void *ws, size_t ws_bytes, hipStream_t s) {
     int splits = nf4_splits(n_out, k, m);
     if (splits > 1 && (ws == nullptr || ws_bytes < gemm_ws_bytes(WSL_W_NF4, n_out, k, m))) splits = 1;
-    const int64_t kps = nf4_k_per_split(k, splits);
-    const int64_t gx = (n_out + kNf4RowsPerWg - 1) / kNf4RowsPerWg;
-    const int64_t gz = (m + 31) / 32;
-    if (gx > 0x7fffffff || gz > 65535) return WSL_E_SHAPE;
-    const dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(splits), static_cast<unsigned>(gz));
+    int64_t kps = nf4_k_per_split(k, m, splits);
+    splits = static_cast<int>((k + kps - 1) / kps);   // no empty trailing split
     float *wsp = splits > 1 ? static_cast<float *>(ws) : nullptr;
-    hipLaunchKernelGGL((gemm_nf4_kernel<kNf4Nb>), grid, dim3(256), 0, s, static_cast<const uint8_t *>(w), n_out, k,
-                       static_cast<const uint16_t *>(x), m, ldx, y, ofmt, ldy, wsp, kps);
+    const auto *wp = static_cast<const uint8_t *>(w);
+    const auto *xp = static_cast<const uint16_t *>(x);
+    if (use_x32(k, m)) {
+        const int64_t gx = (n_out + kX32Rows - 1) / kX32Rows;
+        if (gx > 0x7fffffff) return WSL_E_SHAPE;
+        hipLaunchKernelGGL(gemm_nf4_x32_kernel, dim3(static_cast<unsigned>(gx), static_cast<unsigned>(splits)),
+                           dim3(512), 0, s, wp, n_out, k, xp, m, ldx, y, ofmt, ldy, wsp, kps);
+    } else {
+        const int64_t gx = (n_out + kNf4RowsPerWg - 1) / kNf4RowsPerWg;
+        const int64_t gz = (m + 31) / 32;
+        if (gx > 0x7fffffff || gz > 65535) return WSL_E_SHAPE;
+        const dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(splits), static_cast<unsigned>(gz));
+        hipLaunchKernelGGL((gemm_nf4_kernel<kNf4Nb>), grid, dim3(256), 0, s, wp, n_out, k, xp, m, ldx, y, ofmt, ldy,
+                           wsp, kps);
+    }
     if (splits > 1) {
         const int64_t total = m * n_out;
         int64_t blocks = (total + 255) / 256;

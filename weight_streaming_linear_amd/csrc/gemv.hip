@@ -253,27 +253,6 @@ __device__ __forceinline__ float nf4_dot32(const uint4 q, const float (&xf)[32],
     return p0 + p1;
 }
 
-// Pair table (64 KB, one ds_read_b64 per two codes).  Entry of byte value b (the
-// codes of two consecutive k, even k in the low nibble) = (level(b & 15),
-// level(b >> 4)), replicated 32 times: lane l reads copy l % 32 at byte offset
-// b * 256 + (l % 32) * 8, so the 32 lanes served together touch 32 distinct
-// 8-byte bank pairs whatever the codes are.  The address is one SDWA move that
-// writes byte B of the (un-rotated) code word into bits 8..15 of a register whose
-// low byte already holds the lane's copy offset.
-constexpr int kPairTableBytes = 256 * 32 * 8;
-
-template <int B>
-__device__ __forceinline__ void pair_addr(uint32_t &a, uint32_t w) {
-    if constexpr (B == 0)
-        asm("v_mov_b32_sdwa %0, %1 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_0" : "+v"(a) : "v"(w));
-    else if constexpr (B == 1)
-        asm("v_mov_b32_sdwa %0, %1 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_1" : "+v"(a) : "v"(w));
-    else if constexpr (B == 2)
-        asm("v_mov_b32_sdwa %0, %1 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_2" : "+v"(a) : "v"(w));
-    else
-        asm("v_mov_b32_sdwa %0, %1 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_3" : "+v"(a) : "v"(w));
-}
-
 __device__ __forceinline__ float nf4_dot32_pair(const uint4 q, const float (&xf)[32], const char *tab,
                                                 uint32_t (&ad)[4]) {
     const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
@@ -348,10 +327,7 @@ __global__ __launch_bounds__(1024) void gemv_nf4_team_kernel(const uint8_t *__re
     if constexpr (TAB == 0) {
         if (threadIdx.x < 16) reinterpret_cast<float *>(tab)[threadIdx.x] = level(threadIdx.x);
     } else {
-        for (int i = threadIdx.x; i < kPairTableBytes / 8; i += blockDim.x) {
-            const int b = i >> 5;
-            reinterpret_cast<float2 *>(tab)[i] = make_float2(level(b & 15), level(b >> 4));
-        }
+        fill_pair_table(tab);
     }
     __syncthreads();
     const int lane = threadIdx.x & 63;
