@@ -421,8 +421,39 @@ def run_bf16_verify_gemm(k_steps, warmup, copies=2):
     return out
 
 
+def run_nf4_embed_rows(k_steps, warmup):
+    """Packed embedding rows: restore 1 row (a decode step) and 2048 rows (a prefill) of a
+    packed NF4 [128000][5120] table to bf16; ids are random and change every launch."""
+    import torch
+    import synth
+    import weight_streaming_linear_amd as wsl
+    n_rows, k = 128000, 5120
+    w = synth.device_weight(5, 0, n_rows, k)
+    packed = wsl.nf4_pack(w)
+    del w
+    out = {}
+    for count in (1, 2048):
+        idss = [torch.randint(0, n_rows, (count,), dtype=torch.int64, device="cuda",
+                              generator=torch.Generator(device="cuda").manual_seed(c)) for c in range(8)]
+        ys = torch.empty((count, k), dtype=torch.bfloat16, device="cuda")
+        wsl.nf4_embed_rows(packed, n_rows, k, idss[0], out=ys)
+        t = nf4_rows_tile(packed, n_rows, k, idss[0].cpu().numpy()[:4])
+        if not torch.equal(ys[:4], t):
+            refuse(f"nf4 embed rows count {count}", float("inf"))
+        nbytes = count * (k // 2 + (k // 64) * 2) + count * k * 2      # packed rows read + bf16 rows written
+        launches = [Launch(lambda ids=ids: wsl.nf4_embed_rows(packed, n_rows, k, ids, out=ys), nbytes=nbytes,
+                           name=f"rows_{count}") for ids in idss]
+        us = time_block(launches, k_steps, warmup)
+        out[f"rows_{count}"] = {"avg_us": round(us, 3), "gbs": round(nbytes / 1e3 / us, 1)}
+    out["workload"] = "NF4 embedding row gather, table 128000x5120 (348 MB packed), bf16 out"
+    del packed
+    torch.cuda.empty_cache()
+    return out
+
+
 PATHS = [("nf4_gemv_4096", run_nf4_gemv_4096), ("nf4_decode_sweep_48x6144", run_nf4_decode_sweep),
-         ("nf4_prefill_gemm_m32", run_nf4_prefill_gemm), ("bf16_verify_gemm_m8192", run_bf16_verify_gemm)]
+         ("nf4_prefill_gemm_m32", run_nf4_prefill_gemm), ("bf16_verify_gemm_m8192", run_bf16_verify_gemm),
+         ("nf4_embed_rows_128000x5120", run_nf4_embed_rows)]
 
 
 # ---------------------------------------------------------------- CPU baseline (oracle)

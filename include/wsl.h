@@ -70,6 +70,7 @@ enum { WSL_OUT_F32 = 0, WSL_OUT_BF16 = 1 };
 /* Bits OR-ed into nf4_pack's optional device status word. */
 #define WSL_STATUS_NONFINITE 1u   /* a group held a NaN or an infinity */
 #define WSL_STATUS_OVERFLOW  2u   /* a group's absmax rounds to +inf in fp16 (>= 65520) */
+#define WSL_STATUS_INDEX     4u   /* nf4_embed_rows: a requested row index was outside the matrix */
 
 /*
  * nf4_packed_bytes -- size in bytes of one packed NF4 matrix.
@@ -172,6 +173,29 @@ int linear_gemm(int wfmt, const void *d_w, int64_t n_out, int64_t k,
                 const void *d_x, int64_t m, int64_t ldx,
                 void *d_y, int ofmt, int64_t ldy,
                 void *d_ws, size_t ws_bytes, void *stream);
+
+/*
+ * nf4_embed_rows -- restore only the requested rows of a packed NF4 matrix (a
+ * packed embedding table [n_rows][k]).
+ *   (deep-fold README, introduction and Figure 1: embeddings stay packed and
+ *   only the rows that are asked for are restored, separately from the linear
+ *   kernels.)
+ * d_packed  device, nf4_pack layout of an [n_rows][k] matrix, 16-byte aligned.
+ * d_ids     device int64 [count], the rows to restore (any order, repeats allowed),
+ *           8-byte aligned.  Read by the kernel only: indices are never copied
+ *           to the host.
+ * count     >= 0 (0 launches nothing; d_ids and d_out may then be NULL).
+ * d_out     device [count][ld_out], 16-byte aligned; row i receives row d_ids[i]:
+ *           WSL_OUT_BF16: bf16_RNE(fp32_RN(level * s)) (the restored tile value,
+ *                         bit-identical to nf4_dequant_tile), ld_out % 8 == 0;
+ *           WSL_OUT_F32 : fp32_RN(level * s), ld_out % 4 == 0.
+ *           ld_out >= k; entries past k are not written.
+ * d_status  device uint32 or NULL.  An index outside [0, n_rows) gives an
+ *           all-zero output row and ORs WSL_STATUS_INDEX into *d_status.
+ * Bit-exact and deterministic.
+ */
+int nf4_embed_rows(const void *d_packed, int64_t n_rows, int64_t k, const int64_t *d_ids, int64_t count,
+                   void *d_out, int ofmt, int64_t ld_out, uint32_t *d_status, void *stream);
 
 /* wsl_strerror -- static description of a status code (never NULL). */
 const char *wsl_strerror(int code);

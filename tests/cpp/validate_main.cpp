@@ -48,6 +48,19 @@ int main() {
     EXPECT(wsl::check_gemm(WSL_W_NF4, p, 4, 64, p, 0, 64, p, WSL_OUT_F32, 8, nullptr, 0) == WSL_E_SHAPE);
     EXPECT(wsl::check_gemm(WSL_W_NF4, p, 4, 64, p, 3, 64, p, WSL_OUT_F32, 8, odd, 64) == WSL_E_ALIGN);
     EXPECT(wsl::check_gemm(WSL_W_NF4, p, 4, 64, p, INT64_MAX / 2, 64, p, WSL_OUT_F32, 8, nullptr, 0) == WSL_E_SHAPE);
+    EXPECT(wsl::check_embed(p, 4, 64, p, 2, p, 9, 64) == WSL_E_FORMAT);
+    EXPECT(wsl::check_embed(p, 4, 64, nullptr, 2, p, WSL_OUT_BF16, 64) == WSL_E_NULL);
+    EXPECT(wsl::check_embed(p, 4, 60, p, 2, p, WSL_OUT_BF16, 64) == WSL_E_SHAPE);
+    EXPECT(wsl::check_embed(p, 4, 64, p, -1, p, WSL_OUT_BF16, 64) == WSL_E_SHAPE);
+    EXPECT(wsl::check_embed(p, 4, 64, p, 2, p, WSL_OUT_BF16, 32) == WSL_E_SHAPE);
+    EXPECT(wsl::check_embed(p, 4, 64, p, 2, p, WSL_OUT_BF16, 68) == WSL_E_ALIGN);
+    EXPECT(wsl::check_embed(p, 4, 64, p, 2, p, WSL_OUT_F32, 68) == WSL_OK);
+    EXPECT(wsl::check_embed(p, 4, 64, odd, 2, p, WSL_OUT_F32, 64) == WSL_E_ALIGN);
+    EXPECT(wsl::check_embed(p, 4, 64, p, 2, odd, WSL_OUT_F32, 64) == WSL_E_ALIGN);
+    EXPECT(wsl::check_embed(p, 4, 64, p, 0, p, WSL_OUT_BF16, 64) == WSL_OK);
+    EXPECT(wsl::check_embed(p, 4, 64, nullptr, 0, nullptr, WSL_OUT_BF16, 64) == WSL_OK);
+    EXPECT(wsl::check_embed(nullptr, 4, 64, p, 1, p, WSL_OUT_BF16, 64) == WSL_E_NULL);
+    EXPECT(wsl::check_embed(p, 4, 64, p, INT64_MAX, p, WSL_OUT_BF16, 64) == WSL_E_SHAPE);
     std::printf("%s (%d failures)\n", fails ? "FAILED" : "ok", fails);
     return fails ? 1 : 0;
 }

@@ -58,6 +58,10 @@ def test_argument_errors_return_before_any_launch():
     assert L.linear_gemm(wsl.WSL_W_BF16, a, 4, 64, a, 3, 32, a, 0, 8, None, 0, None) == 2
     assert L.nf4_pack(a, 4, 100, a, None, None) == 2
     assert L.nf4_dequant_tile(a, 4, 64, 4, 0, 1, 1, a, 1, None) == 7
+    assert L.nf4_embed_rows(a, 4, 64, None, 2, a, wsl.WSL_OUT_BF16, 64, None, None) == 1
+    assert L.nf4_embed_rows(a, 4, 64, a, 2, a, 9, 64, None, None) == 4
+    assert L.nf4_embed_rows(a, 4, 64, a, 2, a, wsl.WSL_OUT_BF16, 68, None, None) == 3
+    assert L.nf4_embed_rows(a, 4, 96, a, 2, a, wsl.WSL_OUT_BF16, 96, None, None) == 2
     assert wsl.wsl_strerror(7).startswith("tile")
     assert L.nf4_codebook(None) == 1
 

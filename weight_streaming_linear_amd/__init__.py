@@ -28,7 +28,7 @@ WSL_STATUS_OVERFLOW = 2
 
 EXPORTED = [
     "nf4_packed_bytes", "nf4_codebook", "nf4_pack", "nf4_dequant_tile", "linear_gemv",
-    "linear_gemm_workspace_bytes", "linear_gemm", "wsl_strerror",
+    "linear_gemm_workspace_bytes", "linear_gemm", "nf4_embed_rows", "wsl_strerror",
 ]
 
 
@@ -65,6 +65,8 @@ def lib():
     L.linear_gemm_workspace_bytes.restype = sz
     L.linear_gemm.argtypes = [ctypes.c_int, vp, i64, i64, vp, i64, i64, vp, ctypes.c_int, i64, vp, sz, vp]
     L.linear_gemm.restype = ctypes.c_int
+    L.nf4_embed_rows.argtypes = [vp, i64, i64, vp, i64, vp, ctypes.c_int, i64, vp, vp]
+    L.nf4_embed_rows.restype = ctypes.c_int
     L.wsl_strerror.argtypes = [ctypes.c_int]
     L.wsl_strerror.restype = ctypes.c_char_p
     _lib = L
@@ -127,6 +129,19 @@ def nf4_dequant_tile(packed, n_out, k, row0, k0, rows, cols, tile=None, ld_tile=
     rc = lib().nf4_dequant_tile(_ptr(packed), n_out, k, row0, k0, rows, cols, _ptr(tile), ld_tile, _stream(stream))
     _check(rc, "nf4_dequant_tile")
     return tile
+
+
+def nf4_embed_rows(packed, n_rows, k, ids, out=None, ofmt=WSL_OUT_BF16, status=None, stream=None):
+    """Restore rows ids (int64 device tensor) of a packed NF4 [n_rows][k] matrix into out [count][>= k]."""
+    import torch
+    count = int(ids.numel())
+    if out is None:
+        dt = torch.bfloat16 if ofmt == WSL_OUT_BF16 else torch.float32
+        out = torch.empty((count, k), dtype=dt, device=packed.device)
+    rc = lib().nf4_embed_rows(_ptr(packed), n_rows, k, _ptr(ids), count, _ptr(out), int(ofmt), out.stride(0),
+                              _ptr(status), _stream(stream))
+    _check(rc, "nf4_embed_rows")
+    return out
 
 
 def linear_gemv(w, x, y=None, wfmt=None, n_out=None, k=None, stream=None):

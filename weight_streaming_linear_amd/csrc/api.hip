@@ -17,6 +17,8 @@ int launch_gemm_bf16(const void *w, int64_t n_out, int64_t k, const void *x, int
 int launch_gemm_nf4(const void *w, int64_t n_out, int64_t k, const void *x, int64_t m, int64_t ldx, void *y,
                     int ofmt, int64_t ldy, void *ws, size_t ws_bytes, hipStream_t s);
 size_t gemm_ws_bytes(int wfmt, int64_t n_out, int64_t k, int64_t m);
+int launch_embed_rows(const void *packed, int64_t n_rows, int64_t k, const int64_t *ids, int64_t count, void *out,
+                      int ofmt, int64_t ld_out, uint32_t *status, hipStream_t s);
 
 namespace {
 
@@ -98,6 +100,15 @@ int linear_gemm(int wfmt, const void *d_w, int64_t n_out, int64_t k, const void 
         return wsl::after_launch(
             wsl::launch_gemm_nf4(d_w, n_out, k, d_x, m, ldx, d_y, ofmt, ldy, d_ws, ws_bytes, wsl::as_stream(stream)));
     return wsl::after_launch(wsl::launch_gemm_bf16(d_w, n_out, k, d_x, m, ldx, d_y, ofmt, ldy, wsl::as_stream(stream)));
+}
+
+int nf4_embed_rows(const void *d_packed, int64_t n_rows, int64_t k, const int64_t *d_ids, int64_t count,
+                   void *d_out, int ofmt, int64_t ld_out, uint32_t *d_status, void *stream) {
+    int rc = wsl::check_embed(d_packed, n_rows, k, d_ids, count, d_out, ofmt, ld_out);
+    if (rc != WSL_OK) return rc;
+    if ((rc = wsl::device_ok()) != WSL_OK) return rc;
+    return wsl::after_launch(wsl::launch_embed_rows(d_packed, n_rows, k, d_ids, count, d_out, ofmt, ld_out, d_status,
+                                                    wsl::as_stream(stream)));
 }
 
 const char *wsl_strerror(int code) {

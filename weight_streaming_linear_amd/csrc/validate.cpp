@@ -82,4 +82,17 @@ int check_gemm(int wfmt, const void *w, int64_t n_out, int64_t k, const void *x,
     return WSL_OK;
 }
 
+int check_embed(const void *packed, int64_t n_rows, int64_t k, const void *ids, int64_t count, const void *out,
+                int ofmt, int64_t ld_out) {
+    if (ofmt != WSL_OUT_F32 && ofmt != WSL_OUT_BF16) return WSL_E_FORMAT;
+    if (!packed || (count != 0 && (!ids || !out))) return WSL_E_NULL;   // ids and out may be NULL when count == 0
+    if (nf4_bytes(n_rows, k) == 0) return WSL_E_SHAPE;
+    if (count < 0 || count > kMaxDim || ld_out < k || ld_out > kMaxDim) return WSL_E_SHAPE;
+    int64_t e = 0;
+    if (!mul_ok(count, ld_out, &e)) return WSL_E_SHAPE;
+    if ((ld_out % (ofmt == WSL_OUT_F32 ? 4 : 8)) != 0) return WSL_E_ALIGN;
+    if (!aligned(packed, 16) || !aligned(ids, 8) || !aligned(out, 16)) return WSL_E_ALIGN;
+    return WSL_OK;
+}
+
 }  // namespace wsl

@@ -23,6 +23,8 @@ int check_dequant_tile(const void *packed, int64_t n_out, int64_t k, int64_t row
 int check_gemv(int wfmt, const void *w, int64_t n_out, int64_t k, const void *x, const void *y);
 int check_gemm(int wfmt, const void *w, int64_t n_out, int64_t k, const void *x, int64_t m,
                int64_t ldx, const void *y, int ofmt, int64_t ldy, const void *ws, size_t ws_bytes);
+int check_embed(const void *packed, int64_t n_rows, int64_t k, const void *ids, int64_t count, const void *out,
+                int ofmt, int64_t ld_out);
 
 // Upper bound on any single dimension accepted by the library (keeps every
 // derived index within int64 and every per-row byte offset within int32).
