@@ -451,9 +451,95 @@ def run_nf4_embed_rows(k_steps, warmup):
     return out
 
 
+def run_copyring_decode_sweep(k_steps, warmup, layers=48, resident_layers=29):
+    """The 48-layer NF4 decode sweep with the packed matrices in page-locked host memory,
+    streamed through two device slots (linear_gemv_streamed): every layer from the host, and
+    a split with the first `resident_layers` layers on the device (about 6/10 of the weight
+    bytes, like a model that overflows the device budget).  Tokens are timed between events on
+    the compute stream; the host-to-device rate of a plain 1 GiB pinned copy is the reference."""
+    import torch
+    import synth
+    import weight_streaming_linear_amd as wsl
+    xs = [synth.device_normal_bf16(2, 1000 + j, (k,)) for j, (_, n, k) in enumerate(SWEEP_6144)]
+    ys = [torch.empty(n, dtype=torch.float32, device="cuda") for (_, n, _) in SWEEP_6144]
+    t0 = time.time()
+    host, dev = [], []
+    for l in range(layers):
+        for j, (name, n, k) in enumerate(SWEEP_6144):
+            w = synth.device_weight(2, 16 * l + j, n, k)
+            p = wsl.nf4_pack(w)
+            del w
+            host.append((wsl.to_pinned(p), n, k))
+            dev.append(p if l < resident_layers else None)
+    torch.cuda.synchronize()
+    log(f"copy ring: {layers} layers packed and pinned in {time.time() - t0:.1f}s")
+    # reference: plain pinned host -> device copy of 1 GiB
+    hbuf = torch.empty(1 << 30, dtype=torch.uint8, pin_memory=True)
+    dbuf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    for _ in range(2):
+        dbuf.copy_(hbuf, non_blocking=True)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(4):
+        dbuf.copy_(hbuf, non_blocking=True)
+    b.record()
+    torch.cuda.synchronize()
+    h2d_gbs = 4 * (1 << 30) / 1e6 / a.elapsed_time(b)
+    del hbuf, dbuf
+    slot = max(wsl.nf4_packed_bytes(n, k) for _, n, k in SWEEP_6144)
+    ring = wsl.CopyRing(slot)
+    token_bytes = sum(wsl.nf4_packed_bytes(n, k) for _, n, k in host)
+    stream_xs = [xs[i % 4] for i in range(len(host))]
+    stream_ys = [ys[i % 4] for i in range(len(host))]
+
+    # sanity: one streamed layer equals the resident result
+    ring.gemv(host[:4], xs, ys)
+    got = [y.clone() for y in ys]
+    for j, (_, n, k) in enumerate(SWEEP_6144):
+        wsl.linear_gemv(dev[j], xs[j], y=ys[j], wfmt=wsl.WSL_W_NF4, n_out=n, k=k)
+    torch.cuda.synchronize()
+    if not all(torch.equal(g, y) for g, y in zip(got, ys)):
+        refuse("copy ring decode sweep", float("inf"))
+
+    def all_streamed():
+        ring.gemv(host, stream_xs, stream_ys)
+
+    nres = 4 * resident_layers
+
+    def split():
+        for i in range(nres):
+            _, n, k = host[i]
+            wsl.linear_gemv(dev[i], xs[i % 4], y=ys[i % 4], wfmt=wsl.WSL_W_NF4, n_out=n, k=k)
+        ring.gemv(host[nres:], stream_xs[nres:], stream_ys[nres:])
+
+    out = {"workload": "NF4 decode sweep, 48 layers of hidden 6144, packed weights in page-locked host memory, "
+                       "two device slots", "h2d_copy_gbs": round(h2d_gbs, 1), "token_bytes": token_bytes}
+    for name, fn, host_bytes in (("all_streamed", all_streamed, token_bytes),
+                                 ("split", split, sum(wsl.nf4_packed_bytes(n, k) for _, n, k in host[nres:]))):
+        for _ in range(max(1, warmup // 2)):
+            fn()
+        torch.cuda.synchronize()
+        steps = max(2, k_steps // 4)
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / steps
+        out[name] = {"ms_per_token": round(ms, 3), "tokens_per_s": round(1e3 / ms, 2),
+                     "host_bytes_per_token": host_bytes, "host_gbs": round(host_bytes / 1e6 / ms, 1),
+                     "frac_of_h2d_copy": round(host_bytes / 1e6 / ms / h2d_gbs, 3)}
+    del host, dev, ring
+    torch.cuda.empty_cache()
+    return out
+
+
 PATHS = [("nf4_gemv_4096", run_nf4_gemv_4096), ("nf4_decode_sweep_48x6144", run_nf4_decode_sweep),
          ("nf4_prefill_gemm_m32", run_nf4_prefill_gemm), ("bf16_verify_gemm_m8192", run_bf16_verify_gemm),
-         ("nf4_embed_rows_128000x5120", run_nf4_embed_rows)]
+         ("nf4_embed_rows_128000x5120", run_nf4_embed_rows),
+         ("copyring_nf4_decode_sweep_48x6144", run_copyring_decode_sweep)]
 
 
 # ---------------------------------------------------------------- CPU baseline (oracle)

@@ -59,7 +59,8 @@ enum {
     WSL_E_FORMAT = 4,  /* unknown weight or output format */
     WSL_E_DEVICE = 5,  /* current device is not gfx950, or the device query failed */
     WSL_E_LAUNCH = 6,  /* a kernel launch failed */
-    WSL_E_RANGE = 7    /* a tile or workspace lies outside its matrix or buffer */
+    WSL_E_RANGE = 7,   /* a tile or workspace lies outside its matrix or buffer */
+    WSL_E_MEMORY = 8   /* a host buffer of a streamed call is not pinned (page-locked) host memory */
 };
 
 /* Weight formats. */
@@ -196,6 +197,48 @@ int linear_gemm(int wfmt, const void *d_w, int64_t n_out, int64_t k,
  */
 int nf4_embed_rows(const void *d_packed, int64_t n_rows, int64_t k, const int64_t *d_ids, int64_t count,
                    void *d_out, int ofmt, int64_t ld_out, uint32_t *d_status, void *stream);
+
+/*
+ * linear_gemv_streamed / linear_gemm_streamed -- the linear kernels over matrices
+ * that live in pinned host memory, brought to the device through two reusable
+ * caller-owned device slots (a copy ring).
+ *   (deep-fold README, "Метод" table and Figure 1: a model larger than the GPU
+ *   budget keeps selected packed matrices in pinned host memory and passes them
+ *   through two reusable device slots to the same kernels; the 32B model of the
+ *   results keeps 9.5 GiB resident and 6.7 GiB in pinned host memory.)
+ * For matrix i (slot s = i % 2) the call enqueues, without waiting:
+ *   copy_stream:    wait events[2 + s]; copy h_w[i] -> d_slot[s]; record events[s];
+ *   compute_stream: wait events[s]; linear_gemv / linear_gemm on d_slot[s];
+ *                   record events[2 + s].
+ * So the copy of matrix i + 1 runs while matrix i is multiplied, and a slot is
+ * overwritten only after the kernel that read it finished (also across calls,
+ * since the events carry over).
+ * wfmt          WSL_W_NF4 or WSL_W_BF16, the format of every h_w[i].
+ * count         number of matrices (>= 0; 0 enqueues nothing).
+ * h_w           host array of count pointers to page-locked host buffers (allocated
+ *               with hipHostMalloc; any other host memory gives WSL_E_MEMORY), each
+ *               holding a matrix in its device format (nf4_pack layout, or bf16
+ *               [n_out][k]).  They must stay allocated until the copies complete.
+ * n_out, k      host arrays of count shapes (as for linear_gemv / linear_gemm).
+ * d_x, d_y      host arrays of count device pointers: GEMV x bf16 [k] and y fp32
+ *               [n_out]; GEMM X bf16 [m][ldx] and Y [m][ldy] of type ofmt.
+ * m, ldx, ldy, ofmt, d_ws, ws_bytes   GEMM only, shared by every matrix (the
+ *               workspace is used by one kernel at a time: all run on compute_stream).
+ * d_slot        host array of 2 device pointers, 16-byte aligned, slot_bytes each;
+ *               every matrix must fit (else WSL_E_RANGE).
+ * copy_stream, compute_stream   hipStream_t (NULL = default stream); inputs and
+ *               outputs are ordered on compute_stream.
+ * events        host array of 4 hipEvent_t created by the caller.
+ * Every argument is validated before anything is enqueued; a HIP error while
+ * enqueuing returns WSL_E_LAUNCH (earlier matrices may already be enqueued).
+ */
+int linear_gemv_streamed(int wfmt, int64_t count, const void *const *h_w, const int64_t *n_out, const int64_t *k,
+                         const void *const *d_x, float *const *d_y, void *const *d_slot, size_t slot_bytes,
+                         void *copy_stream, void *compute_stream, void *const *events);
+int linear_gemm_streamed(int wfmt, int64_t count, const void *const *h_w, const int64_t *n_out, const int64_t *k,
+                         const void *const *d_x, int64_t m, int64_t ldx, void *const *d_y, int ofmt, int64_t ldy,
+                         void *d_ws, size_t ws_bytes, void *const *d_slot, size_t slot_bytes,
+                         void *copy_stream, void *compute_stream, void *const *events);
 
 /* wsl_strerror -- static description of a status code (never NULL). */
 const char *wsl_strerror(int code);

@@ -61,6 +61,26 @@ int main() {
     EXPECT(wsl::check_embed(p, 4, 64, nullptr, 0, nullptr, WSL_OUT_BF16, 64) == WSL_OK);
     EXPECT(wsl::check_embed(nullptr, 4, 64, p, 1, p, WSL_OUT_BF16, 64) == WSL_E_NULL);
     EXPECT(wsl::check_embed(p, 4, 64, p, INT64_MAX, p, WSL_OUT_BF16, 64) == WSL_E_SHAPE);
+    {
+        const void *hw[2] = {p, p};
+        const void *xs[2] = {p, p};
+        const void *ys[2] = {p, p};
+        const void *slots[2] = {p, p};
+        const void *evs[4] = {p, p, p, p};
+        const int64_t ns[2] = {4, 8}, ks[2] = {64, 128};
+        EXPECT(wsl::check_ring(WSL_W_NF4, 2, hw, ns, ks, xs, -1, 0, ys, 0, 0, nullptr, 0, slots, 1024, evs) == WSL_OK);
+        EXPECT(wsl::check_ring(WSL_W_NF4, 2, hw, ns, ks, xs, -1, 0, ys, 0, 0, nullptr, 0, slots, 543, evs) == WSL_E_RANGE);
+        EXPECT(wsl::check_ring(WSL_W_BF16, 2, hw, ns, ks, xs, -1, 0, ys, 0, 0, nullptr, 0, slots, 1024, evs) == WSL_E_RANGE);
+        EXPECT(wsl::check_ring(WSL_W_BF16, 2, hw, ns, ks, xs, -1, 0, ys, 0, 0, nullptr, 0, slots, 2048, evs) == WSL_OK);
+        EXPECT(wsl::check_ring(WSL_W_NF4, 2, hw, ns, ks, xs, 3, 128, ys, WSL_OUT_F32, 8, nullptr, 0, slots, 1024, evs) == WSL_OK);
+        EXPECT(wsl::check_ring(WSL_W_NF4, 2, hw, ns, ks, xs, 3, 64, ys, WSL_OUT_F32, 8, nullptr, 0, slots, 1024, evs) == WSL_E_SHAPE);
+        const void *badslots[2] = {p, odd};
+        EXPECT(wsl::check_ring(WSL_W_NF4, 2, hw, ns, ks, xs, -1, 0, ys, 0, 0, nullptr, 0, badslots, 1024, evs) == WSL_E_ALIGN);
+        const void *hw0[2] = {p, nullptr};
+        EXPECT(wsl::check_ring(WSL_W_NF4, 2, hw0, ns, ks, xs, -1, 0, ys, 0, 0, nullptr, 0, slots, 1024, evs) == WSL_E_NULL);
+        EXPECT(wsl::check_ring(WSL_W_NF4, 0, nullptr, nullptr, nullptr, nullptr, -1, 0, nullptr, 0, 0, nullptr, 0,
+                               nullptr, 0, nullptr) == WSL_OK);
+    }
     std::printf("%s (%d failures)\n", fails ? "FAILED" : "ok", fails);
     return fails ? 1 : 0;
 }

@@ -62,6 +62,17 @@ def test_argument_errors_return_before_any_launch():
     assert L.nf4_embed_rows(a, 4, 64, a, 2, a, 9, 64, None, None) == 4
     assert L.nf4_embed_rows(a, 4, 64, a, 2, a, wsl.WSL_OUT_BF16, 68, None, None) == 3
     assert L.nf4_embed_rows(a, 4, 96, a, 2, a, wsl.WSL_OUT_BF16, 96, None, None) == 2
+    one = (ctypes.c_void_p * 1)(4096)
+    two = (ctypes.c_void_p * 2)(4096, 8192)
+    four = (ctypes.c_void_p * 4)(1, 2, 3, 4)
+    shp = (ctypes.c_int64 * 1)(64)
+    assert L.linear_gemv_streamed(wsl.WSL_W_NF4, 0, None, None, None, None, None, None, 0, None, None, None) == 0
+    assert L.linear_gemv_streamed(wsl.WSL_W_NF4, -1, one, shp, shp, one, one, two, 4096, None, None, four) == 2
+    assert L.linear_gemv_streamed(9, 1, one, shp, shp, one, one, two, 4096, None, None, four) == 4
+    assert L.linear_gemv_streamed(wsl.WSL_W_NF4, 1, one, shp, shp, one, one, two, 4096, None, None, None) == 1
+    assert L.linear_gemv_streamed(wsl.WSL_W_NF4, 1, one, shp, shp, one, one, two, 100, None, None, four) == 7
+    assert L.linear_gemm_streamed(wsl.WSL_W_NF4, 1, one, shp, shp, one, 0, 64, one, 0, 64, None, 0, two, 4096,
+                                  None, None, four) == 2
     assert wsl.wsl_strerror(7).startswith("tile")
     assert L.nf4_codebook(None) == 1
 

@@ -28,7 +28,8 @@ WSL_STATUS_OVERFLOW = 2
 
 EXPORTED = [
     "nf4_packed_bytes", "nf4_codebook", "nf4_pack", "nf4_dequant_tile", "linear_gemv",
-    "linear_gemm_workspace_bytes", "linear_gemm", "nf4_embed_rows", "wsl_strerror",
+    "linear_gemm_workspace_bytes", "linear_gemm", "nf4_embed_rows", "linear_gemv_streamed",
+    "linear_gemm_streamed", "wsl_strerror",
 ]
 
 
@@ -67,6 +68,11 @@ def lib():
     L.linear_gemm.restype = ctypes.c_int
     L.nf4_embed_rows.argtypes = [vp, i64, i64, vp, i64, vp, ctypes.c_int, i64, vp, vp]
     L.nf4_embed_rows.restype = ctypes.c_int
+    L.linear_gemv_streamed.argtypes = [ctypes.c_int, i64, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
+    L.linear_gemv_streamed.restype = ctypes.c_int
+    L.linear_gemm_streamed.argtypes = [ctypes.c_int, i64, vp, vp, vp, vp, i64, i64, vp, ctypes.c_int, i64, vp, sz, vp,
+                                       sz, vp, vp, vp]
+    L.linear_gemm_streamed.restype = ctypes.c_int
     L.wsl_strerror.argtypes = [ctypes.c_int]
     L.wsl_strerror.restype = ctypes.c_char_p
     _lib = L
@@ -178,3 +184,72 @@ def linear_gemm(w, x, y=None, wfmt=None, n_out=None, k=None, ofmt=WSL_OUT_F32, w
                            _ptr(workspace), ws_bytes, _stream(stream))
     _check(rc, "linear_gemm")
     return y
+
+
+# ---------------------------------------------------------------- copy ring
+def to_pinned(t):
+    """A page-locked host copy (uint8) of a device or host tensor's bytes."""
+    import torch
+    src = t.contiguous().view(torch.uint8).reshape(-1)
+    h = torch.empty(src.numel(), dtype=torch.uint8, pin_memory=True)
+    h.copy_(src)
+    return h
+
+
+def _ptr_array(items):
+    arr = (ctypes.c_void_p * max(1, len(items)))()
+    for i, t in enumerate(items):
+        arr[i] = t if isinstance(t, int) else t.data_ptr()
+    return arr
+
+
+def _i64_array(vals):
+    arr = (ctypes.c_int64 * max(1, len(vals)))()
+    for i, v in enumerate(vals):
+        arr[i] = int(v)
+    return arr
+
+
+class CopyRing:
+    """Two device slots, a copy stream and four events for linear_*_streamed.
+
+    Matrices stay in page-locked host memory (see to_pinned); each call copies them one
+    by one into the slots on the ring's copy stream while the kernels run on the compute
+    stream (torch's current stream unless given)."""
+
+    def __init__(self, slot_bytes, device="cuda"):
+        import torch
+        self.slot_bytes = int(slot_bytes)
+        self.slots = [torch.empty(max(self.slot_bytes, 16), dtype=torch.uint8, device=device) for _ in range(2)]
+        self.copy_stream = torch.cuda.Stream(device=device)
+        self.events = [torch.cuda.Event() for _ in range(4)]
+        for e in self.events:
+            e.record()          # creates the events; a recorded, completed event is a no-op to wait on
+
+    def _common(self, mats):
+        hs = _ptr_array([h for h, _, _ in mats])
+        ns = _i64_array([n for _, n, _ in mats])
+        ks = _i64_array([k for _, _, k in mats])
+        slots = _ptr_array(self.slots)
+        evs = _ptr_array([e.cuda_event for e in self.events])
+        return hs, ns, ks, slots, evs
+
+    def gemv(self, mats, xs, ys, wfmt=WSL_W_NF4, stream=None):
+        """mats: [(pinned host tensor, n_out, k)]; xs: bf16 [k] device tensors; ys: fp32 [n_out]."""
+        hs, ns, ks, slots, evs = self._common(mats)
+        rc = lib().linear_gemv_streamed(int(wfmt), len(mats), hs, ns, ks, _ptr_array(xs), _ptr_array(ys), slots,
+                                        self.slot_bytes, ctypes.c_void_p(self.copy_stream.cuda_stream),
+                                        _stream(stream), evs)
+        _check(rc, "linear_gemv_streamed")
+        return ys
+
+    def gemm(self, mats, xs, ys, m, ldx, ldy, wfmt=WSL_W_NF4, ofmt=WSL_OUT_F32, workspace=None, stream=None):
+        hs, ns, ks, slots, evs = self._common(mats)
+        nb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        rc = lib().linear_gemm_streamed(int(wfmt), len(mats), hs, ns, ks, _ptr_array(xs), int(m), int(ldx),
+                                        _ptr_array(ys), int(ofmt), int(ldy), _ptr(workspace), nb, slots,
+                                        self.slot_bytes, ctypes.c_void_p(self.copy_stream.cuda_stream),
+                                        _stream(stream), evs)
+        _check(rc, "linear_gemm_streamed")
+        return ys
+

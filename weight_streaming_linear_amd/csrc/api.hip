@@ -17,6 +17,13 @@ int launch_gemm_bf16(const void *w, int64_t n_out, int64_t k, const void *x, int
 int launch_gemm_nf4(const void *w, int64_t n_out, int64_t k, const void *x, int64_t m, int64_t ldx, void *y,
                     int ofmt, int64_t ldy, void *ws, size_t ws_bytes, hipStream_t s);
 size_t gemm_ws_bytes(int wfmt, int64_t n_out, int64_t k, int64_t m);
+int check_pinned(int64_t count, const void *const *h_w);
+int ring_gemv(int wfmt, int64_t count, const void *const *h_w, const int64_t *n_out, const int64_t *k,
+              const void *const *x, float *const *y, void *const *slot, hipStream_t copy, hipStream_t compute,
+              void *const *events);
+int ring_gemm(int wfmt, int64_t count, const void *const *h_w, const int64_t *n_out, const int64_t *k,
+              const void *const *x, int64_t m, int64_t ldx, void *const *y, int ofmt, int64_t ldy, void *ws,
+              size_t ws_bytes, void *const *slot, hipStream_t copy, hipStream_t compute, void *const *events);
 int launch_embed_rows(const void *packed, int64_t n_rows, int64_t k, const int64_t *ids, int64_t count, void *out,
                       int ofmt, int64_t ld_out, uint32_t *status, hipStream_t s);
 
@@ -111,6 +118,32 @@ int nf4_embed_rows(const void *d_packed, int64_t n_rows, int64_t k, const int64_
                                                     wsl::as_stream(stream)));
 }
 
+int linear_gemv_streamed(int wfmt, int64_t count, const void *const *h_w, const int64_t *n_out, const int64_t *k,
+                         const void *const *d_x, float *const *d_y, void *const *d_slot, size_t slot_bytes,
+                         void *copy_stream, void *compute_stream, void *const *events) {
+    int rc = wsl::check_ring(wfmt, count, h_w, n_out, k, d_x, -1, 0, reinterpret_cast<const void *const *>(d_y), 0,
+                             0, nullptr, 0, d_slot, slot_bytes, events);
+    if (rc != WSL_OK || count == 0) return rc;
+    if ((rc = wsl::device_ok()) != WSL_OK) return rc;
+    if ((rc = wsl::check_pinned(count, h_w)) != WSL_OK) return rc;
+    return wsl::ring_gemv(wfmt, count, h_w, n_out, k, d_x, d_y, d_slot, wsl::as_stream(copy_stream),
+                          wsl::as_stream(compute_stream), events);
+}
+
+int linear_gemm_streamed(int wfmt, int64_t count, const void *const *h_w, const int64_t *n_out, const int64_t *k,
+                         const void *const *d_x, int64_t m, int64_t ldx, void *const *d_y, int ofmt, int64_t ldy,
+                         void *d_ws, size_t ws_bytes, void *const *d_slot, size_t slot_bytes,
+                         void *copy_stream, void *compute_stream, void *const *events) {
+    int rc = wsl::check_ring(wfmt, count, h_w, n_out, k, d_x, m < 0 ? 0 : m, ldx,
+                             reinterpret_cast<const void *const *>(d_y), ofmt, ldy, d_ws, ws_bytes, d_slot,
+                             slot_bytes, events);
+    if (rc != WSL_OK || count == 0) return rc;
+    if ((rc = wsl::device_ok()) != WSL_OK) return rc;
+    if ((rc = wsl::check_pinned(count, h_w)) != WSL_OK) return rc;
+    return wsl::ring_gemm(wfmt, count, h_w, n_out, k, d_x, m, ldx, d_y, ofmt, ldy, d_ws, ws_bytes, d_slot,
+                          wsl::as_stream(copy_stream), wsl::as_stream(compute_stream), events);
+}
+
 const char *wsl_strerror(int code) {
     switch (code) {
         case WSL_OK: return "ok";
@@ -121,6 +154,7 @@ const char *wsl_strerror(int code) {
         case WSL_E_DEVICE: return "current device is not gfx950 (MI355X) or could not be queried";
         case WSL_E_LAUNCH: return "kernel launch failed";
         case WSL_E_RANGE: return "tile or workspace outside its matrix or buffer";
+        case WSL_E_MEMORY: return "host buffer is not pinned (page-locked) host memory";
         default: return "unknown status code";
     }
 }

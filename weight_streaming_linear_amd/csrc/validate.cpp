@@ -82,6 +82,35 @@ int check_gemm(int wfmt, const void *w, int64_t n_out, int64_t k, const void *x,
     return WSL_OK;
 }
 
+int check_ring(int wfmt, int64_t count, const void *const *h_w, const int64_t *n_out, const int64_t *k,
+               const void *const *x, int64_t m, int64_t ldx, const void *const *y, int ofmt, int64_t ldy,
+               const void *ws, size_t ws_bytes, const void *const *slot, size_t slot_bytes, const void *const *events) {
+    if (wfmt != WSL_W_BF16 && wfmt != WSL_W_NF4) return WSL_E_FORMAT;
+    if (count < 0 || count > kMaxDim) return WSL_E_SHAPE;
+    if (count == 0) return WSL_OK;
+    if (!h_w || !n_out || !k || !x || !y || !slot || !events) return WSL_E_NULL;
+    if (!slot[0] || !slot[1]) return WSL_E_NULL;
+    if (!events[0] || !events[1] || !events[2] || !events[3]) return WSL_E_NULL;
+    if (!aligned(slot[0], 16) || !aligned(slot[1], 16)) return WSL_E_ALIGN;
+    for (int64_t i = 0; i < count; ++i) {
+        if (!h_w[i]) return WSL_E_NULL;
+        int rc = (m < 0) ? check_gemv(wfmt, slot[0], n_out[i], k[i], x[i], y[i])
+                         : check_gemm(wfmt, slot[0], n_out[i], k[i], x[i], m, ldx, y[i], ofmt, ldy, ws, ws_bytes);
+        if (rc != WSL_OK) return rc;
+        size_t bytes = 0;
+        if (wfmt == WSL_W_NF4) {
+            bytes = nf4_bytes(n_out[i], k[i]);
+        } else {
+            int64_t e = 0;
+            if (!mul_ok(n_out[i], k[i], &e) || e > INT64_MAX / 2) return WSL_E_SHAPE;
+            bytes = static_cast<size_t>(e) * 2;
+        }
+        if (bytes == 0) return WSL_E_SHAPE;
+        if (bytes > slot_bytes) return WSL_E_RANGE;
+    }
+    return WSL_OK;
+}
+
 int check_embed(const void *packed, int64_t n_rows, int64_t k, const void *ids, int64_t count, const void *out,
                 int ofmt, int64_t ld_out) {
     if (ofmt != WSL_OUT_F32 && ofmt != WSL_OUT_BF16) return WSL_E_FORMAT;
