@@ -536,9 +536,49 @@ def run_copyring_decode_sweep(k_steps, warmup, layers=48, resident_layers=29):
     return out
 
 
+def run_nf4_verify_gemm(k_steps, warmup, copies=2):
+    """NF4 batch-verification GEMM, 8192 positions: gate 17408x5120 and down 5120x17408 held as
+    packed NF4, bf16 out (the restored tiles go straight into MFMA fragments)."""
+    import torch
+    import synth
+    import weight_streaming_linear_amd as wsl
+    m = 8192
+    mats = [("gate", 17408, 5120), ("down", 5120, 17408)]
+    xs = [synth.device_normal_bf16(4, 2 + j, (m, k)) for j, (_, n, k) in enumerate(mats)]
+    ys = [torch.empty((m, n), dtype=torch.bfloat16, device="cuda") for (_, n, _) in mats]
+    packs = []
+    for c in range(copies):
+        pc = []
+        for j, (_, n, k) in enumerate(mats):
+            w = synth.device_weight(4, 10 * c + j, n, k)
+            pc.append(wsl.nf4_pack(w))
+            del w
+        packs.append(pc)
+    worst = 0.0
+    for j, (name, n, k) in enumerate(mats):
+        wsl.linear_gemm(packs[0][j], xs[j], y=ys[j], wfmt=wsl.WSL_W_NF4, n_out=n, k=k, ofmt=wsl.WSL_OUT_BF16)
+        rows = torch.as_tensor(sample_rows(m, 24, 51 + j), device="cuda")
+        cols = sample_rows(n, 48, 61 + j)
+        t = nf4_rows_tile(packs[0][j], n, k, cols).float()
+        xf = xs[j][rows].float()
+        got = ys[j][rows][:, torch.as_tensor(cols, device="cuda")]
+        worst = max(worst, check_close(f"nf4 verify gemm {name}", got, xf @ t.t().contiguous(),
+                                       xf.abs() @ t.abs().t().contiguous(), 1e-4, ulp_rel=2.0 ** -8))
+    steps = [[Launch(lambda p=pc[j], j=j, n=n, k=k: wsl.linear_gemm(p, xs[j], y=ys[j], wfmt=wsl.WSL_W_NF4, n_out=n,
+                                                                      k=k, ofmt=wsl.WSL_OUT_BF16),
+                     nbytes=wsl.nf4_packed_bytes(n, k), flops=2 * m * n * k, name=f"nf4_gemm_{name}")
+              for j, (name, n, k) in enumerate(mats)] for pc in packs]
+    out = summarize(time_step_launches(steps, max(2, k_steps // 4), 2))
+    out.update({"workload": "NF4 GEMM M=8192: gate 17408x5120 and down 5120x17408, bf16 out",
+                "sanity_worst_ratio": worst, "frac_mfma": out["kernel_tflops"] / MFMA_BF16_PEAK_TFLOPS})
+    del packs, xs, ys
+    torch.cuda.empty_cache()
+    return out
+
+
 PATHS = [("nf4_gemv_4096", run_nf4_gemv_4096), ("nf4_decode_sweep_48x6144", run_nf4_decode_sweep),
          ("nf4_prefill_gemm_m32", run_nf4_prefill_gemm), ("bf16_verify_gemm_m8192", run_bf16_verify_gemm),
-         ("nf4_embed_rows_128000x5120", run_nf4_embed_rows),
+         ("nf4_verify_gemm_m8192", run_nf4_verify_gemm), ("nf4_embed_rows_128000x5120", run_nf4_embed_rows),
          ("copyring_nf4_decode_sweep_48x6144", run_copyring_decode_sweep)]
 
 

@@ -165,6 +165,42 @@ def test_gemm_bf16_verify_m8192_full_shape_sampled(n_out, k, tid):
     assert ok, f"elem {i}: worst ratio {worst}"
 
 
+# NF4 batch verification (M = 8192) on the gate and down shapes: the tiled NF4 kernel.
+@pytest.mark.parametrize("n_out,k,tid", [(17408, 5120, 0), (5120, 17408, 1)])
+def test_gemm_nf4_verify_m8192_full_shape_sampled(n_out, k, tid):
+    import torch
+    say(f"gemm nf4 verify m=8192 {n_out}x{k}")
+    m = 8192
+    wb = synth.weight_bits(108, tid, n_out, k)
+    xb = synth.act_bits(108, 2 + tid, (m, k))
+    w_dev = to_dev_bf16(wb)
+    packed = wsl.nf4_pack(w_dev)
+    del w_dev
+    y = wsl.linear_gemm(packed, to_dev_bf16(xb), wfmt=wsl.WSL_W_NF4, n_out=n_out, k=k, ofmt=wsl.WSL_OUT_BF16)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(47 + tid)
+    rows = _sample_idx(m, 256, rng, 40)
+    cols = _sample_idx(n_out, 256, rng, 120)
+    y_ref, s_ref = oracle.gemm_ref(f64(xb[rows]), _tile_f64(wb[cols]))
+    ok, worst, i = oracle.check_bf16(bits_of(y)[np.ix_(rows, cols)], y_ref, s_ref)
+    assert ok, f"elem {i}: worst ratio {worst}"
+
+
+@pytest.mark.parametrize("m,n_out,k", [(64, 300, 512), (200, 1000, 1024), (257, 130, 2048), (513, 260, 64)])
+@pytest.mark.parametrize("ofmt", [wsl.WSL_OUT_F32, wsl.WSL_OUT_BF16])
+def test_gemm_nf4_tiled_mid_m(m, n_out, k, ofmt):
+    import torch
+    say(f"gemm nf4 tiled m={m} n={n_out} k={k} ofmt={ofmt}")
+    wb = synth.weight_bits(109, n_out, n_out, k)
+    xb = synth.act_bits(109, 1000 + m, (m, k))
+    packed = wsl.nf4_pack(to_dev_bf16(wb))
+    y = wsl.linear_gemm(packed, to_dev_bf16(xb), wfmt=wsl.WSL_W_NF4, n_out=n_out, k=k, ofmt=ofmt)
+    torch.cuda.synchronize()
+    y_ref, s_ref = oracle.gemm_ref(f64(xb), _tile_f64(wb))
+    ok, worst, i = _check(y, y_ref, s_ref, ofmt)
+    assert ok, f"elem {i}: worst ratio {worst}"
+
+
 def test_gemm_deterministic():
     import torch
     m, n_out, k = 32, 5120, 27648 // 4

@@ -508,6 +508,199 @@ __global__ __launch_bounds__(512) void gemm_nf4_x32_kernel(const uint8_t *__rest
     }
 }
 
+// ---------------------------------------------------------------- NF4, tiled, M > 32
+// NF4 GEMM over many positions (batch verification, long prefill): the bf16
+// kernel's 256 x 256 tiles, 8 waves of 128 x 64 and 4-stage ring, but the weight
+// half of each 32-k stage is restored on the way in.  X tiles still arrive by
+// direct global -> LDS copies three stages ahead.  Thread t restores row t/2,
+// k [16 (t % 2), +16) of the weight stage: its 8 code bytes and the group's scale
+// are loaded three stages ahead into registers, and at step kt the codes of stage
+// kt + 1 are turned into t = bf16(fp32(level * s)) through a 16-entry LDS table
+// (the four 32 KB stages leave no room for the 64 KB pair table) and written into
+// that stage's weight half.  Weight halves live in LDS arrays of their own,
+// separate from the arrays the copies fill, so the compiler sees that these
+// writes cannot alias copies in flight.  Per step: wait until the X copy of stage
+// kt and the codes of stage kt + 1 have landed (vmcnt 6 / 2 / 0 as 2, 1, 0 stages
+// remain), one barrier (an asm statement with a memory clobber, so no LDS access
+// moves across it), issue the codes and X copy of stage kt + 3, restore stage
+// kt + 1, multiply stage kt.  Each weight tile is restored once per 256 positions.
+__global__ __launch_bounds__(512) void gemm_nf4_tiled_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ packed,
+                                                      int64_t m, int64_t n_out, int64_t k, int64_t ldx,
+                                                      void *__restrict__ y, int ofmt, int64_t ldy, int tiles_m, int tiles_n) {
+    constexpr int kHalf = kBM * kBK * 2;   // 16 KB per operand per stage
+    __shared__ __attribute__((aligned(1024))) char sa0[kHalf];
+    __shared__ __attribute__((aligned(1024))) char sa1[kHalf];
+    __shared__ __attribute__((aligned(1024))) char sa2[kHalf];
+    __shared__ __attribute__((aligned(1024))) char sa3[kHalf];
+    __shared__ __attribute__((aligned(1024))) char sb0[kHalf];
+    __shared__ __attribute__((aligned(1024))) char sb1[kHalf];
+    __shared__ __attribute__((aligned(1024))) char sb2[kHalf];
+    __shared__ __attribute__((aligned(1024))) char sb3[kHalf];
+    __shared__ float lut[16];
+    const int tid = threadIdx.x;
+    if (tid < 16) lut[tid] = level(tid);
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave >> 2, wn = wave & 3;
+    const int ntiles = tiles_m * tiles_n;
+    const int bid = blockIdx.x;
+    const int per_xcd = ntiles >> 3, rem = ntiles & 7;
+    const int xcd = bid & 7, slot = bid >> 3;
+    const int t = xcd * per_xcd + (xcd < rem ? xcd : rem) + slot;
+    const int band = 8;
+    const int band_tiles = band * tiles_n;
+    const int b_idx = t / band_tiles, in_band = t - b_idx * band_tiles;
+    const int band_rows = (tiles_m - b_idx * band) < band ? (tiles_m - b_idx * band) : band;
+    const int tm = b_idx * band + in_band % band_rows;
+    const int tn = in_band / band_rows;
+    const int64_t m0 = static_cast<int64_t>(tm) * kBM;
+    const int64_t n0 = static_cast<int64_t>(tn) * kBN;
+
+    const uint16_t *asrc[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int row = 16 * (2 * wave + i) + (lane >> 2);
+        const int c = chunk_swz(row, lane & 3);
+        const int64_t gm = (m0 + row < m) ? m0 + row : m - 1;
+        asrc[i] = x + gm * ldx + c * 8;
+    }
+    // B producer: thread t restores row t/2, k [16*(t%2), +16) of the 32-k stage.
+    const int brow = tid >> 1, bhp = tid & 1;
+    const int64_t gn = (n0 + brow < n_out) ? n0 + brow : n_out - 1;
+    const int64_t groups = k >> 6;
+    const uint8_t *crow = packed + gn * (k >> 1) + 8 * bhp;          // + k0/2
+    const uint16_t *scales = reinterpret_cast<const uint16_t *>(packed + n_out * (k >> 1));
+    const int64_t srem = n_out - ((gn >> 4) << 4);
+    const int64_t srb = srem < 16 ? srem : 16;
+    const uint16_t *srow = scales + (gn >> 4) * 16 * groups + (gn & 15);
+    const uint32_t boff0 = static_cast<uint32_t>(swz(brow, 2 * bhp));
+    const uint32_t boff1 = static_cast<uint32_t>(swz(brow, 2 * bhp + 1));
+    const char *lutp = reinterpret_cast<const char *>(lut);
+
+    auto copy_a = [&](int64_t kt, char *sa) {
+        const int64_t k0 = kt * kBK;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int g = 2 * wave + i;
+            __builtin_amdgcn_global_load_lds(asrc[i] + k0, (lds_void *)(sa + g * 1024), 16, 0, 0);
+        }
+    };
+    auto load_codes = [&](int64_t kt, uint2 &q, uint32_t &sraw) {
+        const int64_t k0 = kt * kBK;
+        q = *reinterpret_cast<const uint2 *>(crow + (k0 >> 1));
+        sraw = srow[((k0 >> 6)) * srb];
+    };
+    auto put_b = [&](char *sb, const uint2 &q, uint32_t sraw) {
+        const float s = f16_to_f32(sraw);
+        const uint4 v0 = dequant8(q.x, s, lutp);
+        const uint4 v1 = dequant8(q.y, s, lutp);
+        *reinterpret_cast<uint4 *>(sb + boff0) = v0;
+        *reinterpret_cast<uint4 *>(sb + boff1) = v1;
+    };
+
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+    const int half = lane >> 5, l32 = lane & 31;
+    const int64_t ktiles = k / kBK;
+    uint32_t offa[2], offb[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        offa[ks] = static_cast<uint32_t>(swz(wm * 128 + l32, ks * 2 + half));
+        offb[ks] = static_cast<uint32_t>(swz(wn * 64 + l32, ks * 2 + half));
+    }
+    auto issue = [&](uint32_t a_addr, uint32_t b_addr, u32x4 (&f)[6]) {
+        asm volatile(
+            "ds_read_b128 %0, %6\n\t"
+            "ds_read_b128 %1, %6 offset:2048\n\t"
+            "ds_read_b128 %2, %6 offset:4096\n\t"
+            "ds_read_b128 %3, %6 offset:6144\n\t"
+            "ds_read_b128 %4, %7\n\t"
+            "ds_read_b128 %5, %7 offset:2048"
+            : "=&v"(f[0]), "=&v"(f[1]), "=&v"(f[2]), "=&v"(f[3]), "=&v"(f[4]), "=&v"(f[5])
+            : "v"(a_addr), "v"(b_addr));
+    };
+    auto landed = [&](u32x4 (&f)[6]) {
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]), "+v"(f[4]), "+v"(f[5]));
+    };
+    auto mfmas = [&](const u32x4 (&f)[6]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f[i]),
+                                                                    __builtin_bit_cast(bf16x8, f[4 + j]), acc[i][j], 0, 0, 0);
+    };
+    auto compute_stage = [&](uint32_t abase, uint32_t bbase) {
+        u32x4 f0[6], f1[6];
+        issue(abase + offa[0], bbase + offb[0], f0);
+        landed(f0);
+        issue(abase + offa[1], bbase + offb[1], f1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(f0);
+        __builtin_amdgcn_sched_barrier(0);
+        landed(f1);
+        mfmas(f1);
+    };
+    auto lds_addr = [](char *p) { return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void *)p)); };
+    const uint32_t A0 = lds_addr(sa0), A1 = lds_addr(sa1), A2 = lds_addr(sa2), A3 = lds_addr(sa3);
+    const uint32_t B0 = lds_addr(sb0), B1 = lds_addr(sb1), B2 = lds_addr(sb2), B3 = lds_addr(sb3);
+    uint2 q0, q1, q2, q3;
+    uint32_t r0, r1, r2, r3;
+    // step kt: wait (A(kt) and the codes of kt+1 landed), barrier, issue codes(kt+3) then A(kt+3),
+    // restore B(kt+1), multiply stage kt.
+    auto step = [&](int64_t kt, uint32_t acur, uint32_t bcur, char *arefill, uint2 &qload, uint32_t &rload,
+                    char *bnext, const uint2 &qnext, const uint32_t &rnext) {
+        const int64_t ahead = ktiles - 1 - kt;
+        if (ahead >= 2) wait_vmcnt<6>();
+        else if (ahead == 1) wait_vmcnt<2>();
+        else wait_vmcnt<0>();
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if (kt + 3 < ktiles) {
+            load_codes(kt + 3, qload, rload);
+            copy_a(kt + 3, arefill);
+        }
+        if (kt + 1 < ktiles) put_b(bnext, qnext, rnext);
+        compute_stage(acur, bcur);
+    };
+    __syncthreads();   // lut
+    // prologue: codes and A for stages 0, 1, 2; restore B(0)
+    if (0 < ktiles) { load_codes(0, q0, r0); copy_a(0, sa0); }
+    if (1 < ktiles) { load_codes(1, q1, r1); copy_a(1, sa1); }
+    if (2 < ktiles) { load_codes(2, q2, r2); copy_a(2, sa2); }
+    if (ktiles > 0) put_b(sb0, q0, r0);
+    int64_t kt = 0;
+    for (; kt + 4 <= ktiles; kt += 4) {
+        step(kt + 0, A0, B0, sa3, q3, r3, sb1, q1, r1);
+        step(kt + 1, A1, B1, sa0, q0, r0, sb2, q2, r2);
+        step(kt + 2, A2, B2, sa1, q1, r1, sb3, q3, r3);
+        step(kt + 3, A3, B3, sa2, q2, r2, sb0, q0, r0);
+    }
+    if (kt + 0 < ktiles) step(kt + 0, A0, B0, sa3, q3, r3, sb1, q1, r1);
+    if (kt + 1 < ktiles) step(kt + 1, A1, B1, sa0, q0, r0, sb2, q2, r2);
+    if (kt + 2 < ktiles) step(kt + 2, A2, B2, sa1, q1, r1, sb3, q3, r3);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int64_t col = n0 + wn * 64 + j * 32 + l32;
+            if (col >= n_out) continue;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int64_t row = m0 + wm * 128 + i * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
+                if (row >= m) continue;
+                if (ofmt == WSL_OUT_F32) static_cast<float *>(y)[row * ldy + col] = acc[i][j][e];
+                else static_cast<uint16_t *>(y)[row * ldy + col] = static_cast<uint16_t>(pack_bf16x2(acc[i][j][e], 0.f) & 0xffffu);
+            }
+        }
+}
+
 // Sum split partials in split order (fixed, so the result is deterministic).
 __global__ __launch_bounds__(256) void split_reduce_kernel(const float *__restrict__ ws, int splits, int64_t m,
                                                            int64_t n_out, void *__restrict__ y, int ofmt, int64_t ldy) {
@@ -523,18 +716,21 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float *__restri
 }
 
 // ---------------------------------------------------------------- planning / launch
-// NF4 GEMM plans.  M <= 32 with k % 256 == 0: the shared-X kernel, 256 rows per
-// workgroup (one workgroup per CU: 96 KB of LDS), k split into as many ranges
-// of whole 256-k chunks as keep the grid within one pass over the 256 CUs.
-// Otherwise the general kernel: NB = 1 (32 rows per wave), 4 waves per
-// workgroup, 32 positions per grid z, k split (multiples of 128) as far as
-// needed for about 2 waves per SIMD.  Splits need the caller's workspace.
+// NF4 GEMM plans.  M > 32: the tiled kernel (no workspace).  M <= 32 with
+// k % 256 == 0: the shared-X kernel, 256 rows per workgroup (one workgroup per
+// CU: 96 KB of LDS), k split into as many ranges of whole 256-k chunks as keep
+// the grid within one pass over the 256 CUs.  Otherwise the general kernel:
+// NB = 1 (32 rows per wave), 4 waves per workgroup, 32 positions per grid z, k
+// split (multiples of 128) as far as needed for about 2 waves per SIMD.  Splits
+// need the caller's workspace.
 constexpr int kNf4Nb = 1;
 constexpr int64_t kNf4RowsPerWg = 4 * 32 * kNf4Nb;
 
 static bool use_x32(int64_t k, int64_t m) { return m <= 32 && (k % kX32Chunk) == 0; }
+static bool use_tiled(int64_t m) { return m > 32; }
 
 static int nf4_splits(int64_t n_out, int64_t k, int64_t m) {
+    if (use_tiled(m)) return 1;
     if (use_x32(k, m)) {
         const int64_t blocks = (n_out + kX32Rows - 1) / kX32Rows;
         const int64_t chunks = k / kX32Chunk;
@@ -576,6 +772,14 @@ int launch_gemm_bf16(const void *w, int64_t n_out, int64_t k, const void *x, int
 
 int launch_gemm_nf4(const void *w, int64_t n_out, int64_t k, const void *x, int64_t m, int64_t ldx, void *y,
                     int ofmt, int64_t ldy, void *ws, size_t ws_bytes, hipStream_t s) {
+    if (use_tiled(m)) {
+        const int64_t tn = (n_out + kBN - 1) / kBN, tm = (m + kBM - 1) / kBM;
+        if (tn * tm > 0x7fffffff / 2) return WSL_E_SHAPE;
+        hipLaunchKernelGGL(gemm_nf4_tiled_kernel, dim3(static_cast<unsigned>(tn * tm)), dim3(512), 0, s,
+                           static_cast<const uint16_t *>(x), static_cast<const uint8_t *>(w), m, n_out, k, ldx, y,
+                           ofmt, ldy, static_cast<int>(tm), static_cast<int>(tn));
+        return WSL_OK;
+    }
     int splits = nf4_splits(n_out, k, m);
     if (splits > 1 && (ws == nullptr || ws_bytes < gemm_ws_bytes(WSL_W_NF4, n_out, k, m))) splits = 1;
     int64_t kps = nf4_k_per_split(k, m, splits);
