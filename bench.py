@@ -331,6 +331,20 @@ def run_nf4_decode_sweep(k_steps, warmup, layers=48):
                 for (p, n, k, j) in packs]
     g = capture(launches)
     graph_ms = time_graphs([g], k_steps, warmup) / k_steps
+    # the same token step preceded by the packed-embedding gather of a device-resident token id
+    # (hidden 6144 table of 128000 rows), the id advanced on the device inside the graph
+    emb_n = 128000
+    wemb = synth.device_weight(2, 999, emb_n, 6144)
+    emb = wsl.nf4_pack(wemb)
+    del wemb
+    tok = torch.zeros(1, dtype=torch.int64, device="cuda")
+    hid = torch.empty((1, 6144), dtype=torch.bfloat16, device="cuda")
+    step_launches = [Launch(lambda: wsl.nf4_embed_rows(emb, emb_n, 6144, tok, out=hid))] + launches + \
+        [Launch(lambda: tok.add_(1))]
+    g2 = capture(step_launches)
+    before = torch.cuda.memory_allocated()
+    step_ms = time_graphs([g2], k_steps, warmup) / k_steps
+    grew = torch.cuda.memory_allocated() - before
     # per stage: one block of launches over the 48 layers' matrices of that stage
     out = summarize(time_step_launches([launches], 2 * layers, 4), {f"nf4_gemv_{st[0]}": layers for st in SWEEP_6144})
     out.update({
@@ -340,8 +354,11 @@ def run_nf4_decode_sweep(k_steps, warmup, layers=48):
         "graph_gbs": out["bytes_per_step"] / 1e9 / (graph_ms / 1e3),
         "frac_hbm_graph": out["bytes_per_step"] / 1e9 / (graph_ms / 1e3) / HBM_PEAK_GBS,
         "launch_gap_us_per_launch": 1e3 * (graph_ms - out["kernel_ms_per_step"]) / out["launches_per_step"],
+        "decode_step_graph": {"ms_per_token": step_ms, "tokens_per_s": 1e3 / step_ms,
+                              "what": "embedding gather (device-resident token id) + 192 GEMVs + id advance, one graph",
+                              "allocator_growth_bytes": grew},
     })
-    del g, packs, launches
+    del g, g2, packs, launches, step_launches, emb
     torch.cuda.empty_cache()
     return out
 
