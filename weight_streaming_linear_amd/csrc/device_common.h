@@ -82,12 +82,27 @@ __device__ __forceinline__ void pair_addr(uint32_t &a, uint32_t w) {
 
 // Fill the pair table (kPairTableBytes of LDS at `tab`) cooperatively; the caller
 // synchronizes the workgroup before the first lookup.
+// The 16 levels into lut[0..15] (LDS).  Lane c < 16 selects its level from the
+// literals with compare-selects, so no memory load sits in a kernel prologue.
+__device__ __forceinline__ void write_levels(float *lut) {
+    if (threadIdx.x < 16) {
+        uint32_t v = kLevelBits[0];
+#pragma unroll
+        for (int c = 1; c < 16; ++c) v = (threadIdx.x == static_cast<unsigned>(c)) ? kLevelBits[c] : v;
+        lut[threadIdx.x] = __builtin_bit_cast(float, v);
+    }
+}
+
 __device__ __forceinline__ void fill_pair_table(char *tab) {
     for (int i = threadIdx.x; i < kPairTableBytes / 8; i += blockDim.x) {
         const int b = i >> 5;
         reinterpret_cast<float2 *>(tab)[i] = make_float2(level(b & 15), level(b >> 4));
     }
 }
+
+// Workgroup barrier that orders LDS accesses only: waits for this wave's LDS
+// operations, not for its global loads still in flight.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Sum across the 64 lanes of a wavefront; every lane gets the total.
 __device__ __forceinline__ float wave_sum(float v) {

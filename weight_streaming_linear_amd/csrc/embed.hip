@@ -16,7 +16,7 @@ __global__ __launch_bounds__(256) void nf4_embed_rows_kernel(const uint8_t *__re
                                                              int64_t count, void *__restrict__ out, int ofmt,
                                                              int64_t ld_out, uint32_t *__restrict__ status) {
     __shared__ float lut[16];
-    if (threadIdx.x < 16) lut[threadIdx.x] = level(threadIdx.x);
+    write_levels(lut);
     __syncthreads();
     const int64_t wpr = k >> 3;                    // device words per row
     const int64_t groups = k >> 6;

@@ -264,7 +264,7 @@ __global__ __launch_bounds__(256) void gemm_nf4_kernel(const uint8_t *__restrict
                                                        float *__restrict__ ws, int64_t k_per_split) {
     __shared__ float lut[16];
     __shared__ __attribute__((aligned(16))) char xs_all[4][32 * 256];
-    if (threadIdx.x < 16) lut[threadIdx.x] = level(threadIdx.x);
+    write_levels(lut);
     __syncthreads();
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -436,26 +436,45 @@ __global__ __launch_bounds__(512) void gemm_nf4_x32_kernel(const uint8_t *__rest
     f32x16 acc;
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+    // Each k-step: the four pair-table reads of its code word and the X fragment
+    // read are issued one step ahead (two register sets), so the LDS latency of a
+    // step is covered by the previous step's multiplies and MFMA.
+    uint32_t adb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) adb[i] = ad[i];
     auto compute = [&](const char *st, const uint4 (&q)[4], const uint32_t (&sr)[2]) {
         const float s0 = f16_to_f32(sr[0]), s1 = f16_to_f32(sr[1]);
-#pragma unroll
-        for (int t = 0; t < 16; ++t) {
-            const int c = 16 * half + t;   // 16-byte chunk of k = kc + 128h + 8t
-            const uint4 av = *reinterpret_cast<const uint4 *>(st + l32 * 512 + ((c ^ l32) << 4));
+        float2 la[4], lb[4];
+        uint4 ava, avb;
+        auto issue = [&](int t, uint32_t (&a4)[4], float2 (&l)[4], uint4 &av) {
             const uint4 qq = q[t >> 2];
             const uint32_t wn = rotr32((t & 3) == 0 ? qq.x : (t & 3) == 1 ? qq.y : (t & 3) == 2 ? qq.z : qq.w, 2);
-            const float s = t < 8 ? s0 : s1;
-            pair_addr<0>(ad[0], wn);
-            pair_addr<1>(ad[1], wn);
-            pair_addr<2>(ad[2], wn);
-            pair_addr<3>(ad[3], wn);
-            const float2 l0 = *reinterpret_cast<const float2 *>(tab + ad[0]);
-            const float2 l1 = *reinterpret_cast<const float2 *>(tab + ad[1]);
-            const float2 l2 = *reinterpret_cast<const float2 *>(tab + ad[2]);
-            const float2 l3 = *reinterpret_cast<const float2 *>(tab + ad[3]);
-            const uint4 bv = make_uint4(pack_bf16x2(l0.x * s, l0.y * s), pack_bf16x2(l1.x * s, l1.y * s),
-                                        pack_bf16x2(l2.x * s, l2.y * s), pack_bf16x2(l3.x * s, l3.y * s));
+            pair_addr<0>(a4[0], wn);
+            pair_addr<1>(a4[1], wn);
+            pair_addr<2>(a4[2], wn);
+            pair_addr<3>(a4[3], wn);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) l[i] = *reinterpret_cast<const float2 *>(tab + a4[i]);
+            const int c = 16 * half + t;   // 16-byte chunk of k = kc + 128h + 8t
+            av = *reinterpret_cast<const uint4 *>(st + l32 * 512 + ((c ^ l32) << 4));
+        };
+        auto finish = [&](int t, const float2 (&l)[4], const uint4 &av) {
+            const float sc = t < 8 ? s0 : s1;
+            const uint4 bv = make_uint4(pack_bf16x2(l[0].x * sc, l[0].y * sc), pack_bf16x2(l[1].x * sc, l[1].y * sc),
+                                        pack_bf16x2(l[2].x * sc, l[2].y * sc), pack_bf16x2(l[3].x * sc, l[3].y * sc));
             acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(bv), acc, 0, 0, 0);
+        };
+        issue(0, ad, la, ava);
+#pragma unroll
+        for (int t = 0; t < 16; t += 2) {
+            issue(t + 1, adb, lb, avb);
+            __builtin_amdgcn_sched_barrier(0);
+            finish(t, la, ava);
+            __builtin_amdgcn_sched_barrier(0);
+            if (t + 2 < 16) issue(t + 2, ad, la, ava);
+            __builtin_amdgcn_sched_barrier(0);
+            finish(t + 1, lb, avb);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
     auto sync = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
@@ -538,7 +557,7 @@ __global__ __launch_bounds__(512) void gemm_nf4_tiled_kernel(const uint16_t *__r
     __shared__ __attribute__((aligned(1024))) char sb3[kHalf];
     __shared__ float lut[16];
     const int tid = threadIdx.x;
-    if (tid < 16) lut[tid] = level(tid);
+    write_levels(lut);
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wm = wave >> 2, wn = wave & 3;

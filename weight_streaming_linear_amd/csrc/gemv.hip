@@ -311,12 +311,17 @@ __device__ __forceinline__ void xcd_chunk(int64_t total, int xcd, int64_t &first
 // XCD b % 8), so the rows that share a 16-row scale block are read through one L2
 // and each XCD streams a contiguous range.  Workgroups are persistent over their
 // chunk, and the codes and scales of the next super-group are loaded before the
-// current one is multiplied; the scales stay raw fp16 until they are used.
+// current one is multiplied; the scales stay raw fp16 until they are used.  The
+// last super-group of a round is peeled, so no load is issued past it.
 // Row sums: transposed wave reduction, then the S per-wave partials of each row meet
-// in LDS in a fixed order (one barrier per super-group, double-buffered) -- the
-// result is deterministic.  Rows of a last partial 16-row block whose size is not a
+// in LDS in a fixed order (one LDS-only barrier per super-group, double-buffered) --
+// the result is deterministic.  A workgroup with four or more super-groups parks the
+// finished sums of a round in LDS and writes them to y after the round, so no global
+// store sits between the loads of its loop.  Rows of a last partial 16-row block whose size is not a
 // multiple of R, and super-groups left incomplete, are done at the end with per-row
 // loads.  TAB selects the 16-entry table (0) or the replicated pair table (1).
+constexpr int kRowSumCap = 2048;   // finished row sums parked per round
+
 template <int R, int TAB>
 __global__ __launch_bounds__(1024) void gemv_nf4_team_kernel(const uint8_t *__restrict__ packed, int64_t n_out,
                                                              int64_t k, const uint16_t *__restrict__ x,
@@ -324,6 +329,7 @@ __global__ __launch_bounds__(1024) void gemv_nf4_team_kernel(const uint8_t *__re
     typedef typename ScaleBits<R>::T SB;
     __shared__ __align__(16) char tab[TAB == 0 ? 64 : kPairTableBytes];
     __shared__ float red[2][16][R];
+    __shared__ float yl[kRowSumCap];
     if constexpr (TAB == 0) {
         if (threadIdx.x < 16) reinterpret_cast<float *>(tab)[threadIdx.x] = level(threadIdx.x);
     } else {
@@ -360,8 +366,21 @@ __global__ __launch_bounds__(1024) void gemv_nf4_team_kernel(const uint8_t *__re
         if constexpr (TAB == 0) return nf4_dot32(q, xf, tab, m60);
         else return nf4_dot32_pair(q, xf, tab, ad);
     };
-    auto fetch = [&](int64_t sg, uint4 (&q)[R], SB &sb) {
-        const int64_t row0 = (sg * T + team) * R;
+    // This workgroup's super-groups: first + i0 + j * nloc, j = 0 .. n - 1.
+    const int xcd = blockIdx.x & 7;
+    const int64_t nloc = gridDim.x >> 3;   // the grid is a multiple of 8
+    int64_t first, count;
+    xcd_chunk(supers, xcd, first, count);
+    const int64_t i0 = blockIdx.x >> 3;
+    const int64_t n = i0 < count ? (count - i0 + nloc - 1) / nloc : 0;
+    const int64_t cap = kRowSumCap / (T * R);
+    // Parking pays off once a workgroup owns several super-groups; with one or two
+    // the two extra barriers of the flush cost more than the stores they move.
+    const bool park = n >= 4;
+
+    int64_t jend = 0;   // end of the current round
+    auto fetch = [&](int64_t j, uint4 (&q)[R], SB &sb) {
+        const int64_t row0 = ((first + i0 + j * nloc) * T + team) * R;
         const uint8_t *rowp = packed + row0 * rowbytes;
 #pragma unroll
         for (int r = 0; r < R; ++r) q[r] = load_stream16(rowp + r * rowbytes + coff);
@@ -372,58 +391,59 @@ __global__ __launch_bounds__(1024) void gemv_nf4_team_kernel(const uint8_t *__re
         sb = *reinterpret_cast<const SB *>(reinterpret_cast<const char *>(sp) + gl * rb * 2u);
         __builtin_amdgcn_sched_barrier(0);   // the whole prefetch is issued before the math below
     };
-    // Fold the S slice partials of every team's R rows; row0 = first row of team 0.
-    auto reduce_store = [&](const float (&acc)[R], int64_t row0, int it) {
-        const float v = reduce_rows<R>(acc, lane);
-        if ((lane % span) == 0) red[it & 1][wave][lane / span] = v;
-        __syncthreads();
-        if (threadIdx.x < T * R) {
-            const int tm = threadIdx.x / R, r = threadIdx.x - tm * R;
-            float t = red[it & 1][tm * S][r];
-            for (int s = 1; s < S; ++s) t += red[it & 1][tm * S + s][r];
-            const int64_t row = row0 + tm * R + r;
-            if (row < n_out) y[row] = t;
-        }
-    };
-    auto consume = [&](int64_t sg, const uint4 (&q)[R], const SB &sb, int it) {
+    int ph = 0;
+    int64_t jbeg = 0;
+    auto consume = [&](int64_t j, const uint4 (&q)[R], const SB &sb) {
         float acc[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[r] = scale_at<R>(sb, r) * dot(q[r]);
-        reduce_store(acc, sg * T * R, it);
+        const float v = reduce_rows<R>(acc, lane);
+        if ((lane % span) == 0) red[ph][wave][lane / span] = v;
+        lds_barrier();
+        if (threadIdx.x < T * R) {
+            const int tm = threadIdx.x / R, r = threadIdx.x - tm * R;
+            float t = red[ph][tm * S][r];
+            for (int s = 1; s < S; ++s) t += red[ph][tm * S + s][r];
+            if (park) yl[(j - jbeg) * T * R + threadIdx.x] = t;
+            else y[(first + i0 + j * nloc) * T * R + threadIdx.x] = t;
+        }
+        ph ^= 1;
     };
 
-    const int xcd = blockIdx.x & 7;
-    const int64_t nloc = gridDim.x >> 3;   // the grid is a multiple of 8
-    int64_t first, count;
-    xcd_chunk(supers, xcd, first, count);
-    int it = 0;
-    int64_t i = blockIdx.x >> 3;
     uint4 qa[R], qb[R];
     SB sa, sb;
-    if (i < count) {
-        fetch(first + i, qa, sa);
-        for (;;) {   // unrolled by two so that the two buffers swap without copies
-            const int64_t i1 = i + nloc;
-            if (i1 >= count) {
-                consume(first + i, qa, sa, it++);
+    for (jbeg = 0; jbeg < n; jbeg += cap) {
+        jend = (jbeg + cap < n) ? jbeg + cap : n;
+        fetch(jbeg, qa, sa);
+        for (int64_t j = jbeg;; j += 2) {   // unrolled by two so that the two buffers swap without copies
+            if (j + 1 >= jend) {
+                consume(j, qa, sa);
                 break;
             }
-            fetch(first + i1, qb, sb);
-            consume(first + i, qa, sa, it++);
-            const int64_t i2 = i1 + nloc;
-            if (i2 >= count) {
-                consume(first + i1, qb, sb, it++);
+            fetch(j + 1, qb, sb);
+            consume(j, qa, sa);
+            if (j + 2 >= jend) {
+                consume(j + 1, qb, sb);
                 break;
             }
-            fetch(first + i2, qa, sa);
-            consume(first + i1, qb, sb, it++);
-            i = i2;
+            fetch(j + 2, qa, sa);
+            consume(j + 1, qb, sb);
+        }
+        if (park) {
+            __syncthreads();
+            for (int64_t e = threadIdx.x; e < (jend - jbeg) * T * R; e += blockDim.x) {
+                const int64_t jj = jbeg + e / (T * R);
+                const int64_t rest = e - (e / (T * R)) * (T * R);
+                y[(first + i0 + jj * nloc) * T * R + rest] = yl[e];
+            }
+            __syncthreads();
         }
     }
     // Leftover row groups [supers * T, row_groups): T per workgroup, one per team,
     // rows clamped to the matrix and scales read one row at a time.
     const int64_t left0 = supers * T;
     const int64_t nleft = row_groups - left0;
+    int it = 0;
     for (int64_t b = blockIdx.x; b * T < nleft; b += gridDim.x) {
         const int64_t rg = left0 + b * T + team;
         float acc[R];
@@ -442,7 +462,17 @@ __global__ __launch_bounds__(1024) void gemv_nf4_team_kernel(const uint8_t *__re
 #pragma unroll
             for (int r = 0; r < R; ++r) acc[r] = s[r] * dot(q[r]);
         }
-        reduce_store(acc, (left0 + b * T) * R, it++);
+        const float v = reduce_rows<R>(acc, lane);
+        if ((lane % span) == 0) red[it & 1][wave][lane / span] = v;
+        __syncthreads();
+        if (threadIdx.x < T * R) {
+            const int tm = threadIdx.x / R, r = threadIdx.x - tm * R;
+            float t = red[it & 1][tm * S][r];
+            for (int s = 1; s < S; ++s) t += red[it & 1][tm * S + s][r];
+            const int64_t row = (left0 + b * T) * R + tm * R + r;
+            if (row < n_out) y[row] = t;
+        }
+        ++it;
     }
 }
 
@@ -454,7 +484,7 @@ __global__ __launch_bounds__(1024) void gemv_nf4_wide_kernel(const uint8_t *__re
                                                              float *__restrict__ y) {
     __shared__ float lut[16];
     __shared__ float red[2][16][R];
-    if (threadIdx.x < 16) lut[threadIdx.x] = level(threadIdx.x);
+    write_levels(lut);
     __syncthreads();
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
