@@ -52,6 +52,25 @@ def test_gemm_nf4_small(m, n_out, k, ofmt, use_ws):
     assert ok, f"elem {i}: worst ratio {worst}"
 
 
+# At least 192 blocks of 128 rows: the shared-X kernel in its 128-row form (two waves per
+# 32-row group, k-steps split between them) without a k split -- a partial last block,
+# m < 32, a single 256-k chunk, and both output formats.
+@pytest.mark.parametrize("m,n_out,k", [(32, 24576 + 67, 512), (7, 24700, 256), (32, 24576, 768)])
+@pytest.mark.parametrize("ofmt", [wsl.WSL_OUT_F32, wsl.WSL_OUT_BF16])
+def test_gemm_nf4_tall_m32(m, n_out, k, ofmt):
+    import torch
+    say(f"gemm nf4 tall m={m} n={n_out} k={k} ofmt={ofmt}")
+    assert wsl.linear_gemm_workspace_bytes(wsl.WSL_W_NF4, n_out, k, m) == 0
+    wb = synth.weight_bits(98, n_out, n_out, k)
+    xb = synth.act_bits(98, 1000 + m, (m, k))
+    packed = wsl.nf4_pack(to_dev_bf16(wb))
+    y = wsl.linear_gemm(packed, to_dev_bf16(xb), wfmt=wsl.WSL_W_NF4, n_out=n_out, k=k, ofmt=ofmt)
+    torch.cuda.synchronize()
+    y_ref, s_ref = oracle.gemm_ref(f64(xb), _tile_f64(wb))
+    ok, worst, i = _check(y, y_ref, s_ref, ofmt)
+    assert ok, f"elem {i}: worst ratio {worst}"
+
+
 @pytest.mark.parametrize("m,n_out,k", [(5, 100, 192), (130, 200, 320), (128, 128, 64), (257, 129, 576), (1, 8, 64)])
 @pytest.mark.parametrize("ofmt", [wsl.WSL_OUT_F32, wsl.WSL_OUT_BF16])
 def test_gemm_bf16_small(m, n_out, k, ofmt):

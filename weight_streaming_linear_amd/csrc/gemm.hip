@@ -362,43 +362,52 @@ __global__ __launch_bounds__(256) void gemm_nf4_kernel(const uint8_t *__restrict
 
 // ---------------------------------------------------------------- NF4, shared X, M <= 32
 // The prefill kernel for up to 32 positions and k a multiple of 256.  A
-// workgroup of 8 waves owns 256 weight rows (wave w: rows 32w .. 32w+31, lane l
-// row l % 32) and the k range of its split.  Per 256-k chunk:
+// workgroup of 8 waves owns 256 / KH weight rows: waves w and w + 8 / KH share
+// rows 32 (w % (8 / KH)) .. + 31 (lane l row l % 32), and with KH = 2 each of the
+// two takes half of every chunk's k-steps.  It covers the k range of its split.
+// Per 256-k chunk:
 //   * the workgroup stages X[32 positions][256 k] (16 KB) once in LDS (two
 //     buffers; row i at i * 512, 16-byte chunk c at c ^ (i % 32) so that the
 //     fragment reads of a 32-lane half are free of bank conflicts), instead of
 //     every wave reading its own copy;
-//   * lane (n, h) holds the 64 bytes of codes of row n for k in
-//     [kc + 128h, kc + 128h + 128) -- 16 MFMA k-steps of 8 codes -- and the two
-//     scales of those groups, loaded one chunk ahead.  Each load instruction
-//     touches 32 rows; the four that cover a 128-byte line of a row are issued
-//     back to back as ordinary (L1-allocating) loads, so the line is fetched
-//     from L2 once;
+//   * lane (n, h) owns the codes of row n for k in [kc + 128h, kc + 128h + 128)
+//     -- 16 MFMA k-steps of 8 codes, 64 bytes -- of which its wave takes steps
+//     [16 kh / KH, 16 (kh + 1) / KH), loaded one chunk ahead with the scales of
+//     those groups as ordinary (L1-allocating) loads;
 //   * each k-step restores 8 codes through the replicated pair table into a
 //     bf16 B fragment t = bf16(fp32(level * s)) and issues one
-//     v_mfma_f32_32x32x16_bf16 against the A fragment X[i][same 8 k] from LDS.
+//     v_mfma_f32_32x32x16_bf16 against the A fragment X[i][same 8 k] from LDS;
+//     the table and X reads of step t + 1 are issued before step t's math.
 // The barrier that publishes a staged chunk is an asm statement with a memory
 // clobber and no vmcnt wait, so the next chunk's loads stay in flight across it
-// and the compiler cannot move LDS accesses over it.  The wave writes its
-// 32 x 32 result to Y, or to the split workspace.
+// and the compiler cannot move LDS accesses over it.  With KH = 2 the second
+// half's accumulators meet the first's in LDS (a fixed order), then the 32 x 32
+// result goes to Y, or to the split workspace.
+// KH = 2 (128 rows per workgroup) lets tall matrices fill the CUs without
+// splitting k, so they need no workspace and no reduction pass.
 constexpr int kX32Chunk = 256;
 constexpr int kX32Stage = 32 * kX32Chunk * 2;
-constexpr int kX32Rows = 256;
 
+template <int KH>
 __global__ __launch_bounds__(512) void gemm_nf4_x32_kernel(const uint8_t *__restrict__ packed, int64_t n_out,
                                                            int64_t k, const uint16_t *__restrict__ x, int64_t m,
                                                            int64_t ldx, void *__restrict__ y, int ofmt, int64_t ldy,
                                                            float *__restrict__ ws, int64_t k_per_split) {
+    constexpr int RG = 8 / KH;        // row groups of 32 per workgroup
+    constexpr int NQ = 4 / KH;        // 16-byte code loads per lane per chunk
+    constexpr int NS = 16 / KH;       // k-steps per wave per chunk
+    constexpr int NG = 2 / KH;        // scales per lane per chunk
     __shared__ __align__(16) char tab[kPairTableBytes];
     __shared__ __align__(16) char xst[2][kX32Stage];
     fill_pair_table(tab);
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
+    const int rg = wave % RG, kh = wave / RG;
     const int half = lane >> 5, l32 = lane & 31;
     const int64_t groups = k >> 6;
     const int64_t rowbytes = k >> 1;
     const uint16_t *scales = reinterpret_cast<const uint16_t *>(packed + n_out * rowbytes);
-    const int64_t rowt = static_cast<int64_t>(blockIdx.x) * kX32Rows + wave * 32 + l32;
+    const int64_t rowt = static_cast<int64_t>(blockIdx.x) * (32 * RG) + rg * 32 + l32;
     const int64_t row = rowt < n_out ? rowt : n_out - 1;
     const int64_t kbeg = static_cast<int64_t>(blockIdx.y) * k_per_split;
     const int64_t kend = (kbeg + k_per_split < k) ? kbeg + k_per_split : k;
@@ -406,7 +415,7 @@ __global__ __launch_bounds__(512) void gemm_nf4_x32_kernel(const uint8_t *__rest
     uint32_t ad[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) ad[i] = static_cast<uint32_t>(lane & 31) << 3;
-    const uint8_t *crow = packed + row * rowbytes + 64 * half;
+    const uint8_t *crow = packed + row * rowbytes + 64 * half + (64 / KH) * kh;
     const int64_t srem = n_out - ((row >> 4) << 4);
     const int64_t srb = srem < 16 ? srem : 16;
     const uint16_t *srow = scales + (row >> 4) * 16 * groups + (row & 15);   // scale (row, g) at srow[g * srb]
@@ -417,16 +426,16 @@ __global__ __launch_bounds__(512) void gemm_nf4_x32_kernel(const uint8_t *__rest
     const int xoff0 = xi0 * 512 + ((xcc ^ xi0) << 4);
     const int xoff1 = xi1 * 512 + ((xcc ^ xi1) << 4);
 
-    auto fetch = [&](int c, uint4 (&q)[4], uint32_t (&sr)[2], uint4 &xv0, uint4 &xv1) {
+    auto fetch = [&](int c, uint4 (&q)[NQ], uint32_t (&sr)[NG], uint4 &xv0, uint4 &xv1) {
         const int64_t kc = kbeg + static_cast<int64_t>(c) * kX32Chunk;
         xv0 = *reinterpret_cast<const uint4 *>(xrow0 + kc);
         xv1 = *reinterpret_cast<const uint4 *>(xrow1 + kc);
         const uint8_t *src = crow + (kc >> 1);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) q[j] = *reinterpret_cast<const uint4 *>(src + 16 * j);
-        const int64_t g0 = (kc >> 6) + 2 * half;
-        sr[0] = srow[g0 * srb];
-        sr[1] = srow[(g0 + 1) * srb];
+        for (int j = 0; j < NQ; ++j) q[j] = *reinterpret_cast<const uint4 *>(src + 16 * j);
+        const int64_t g0 = (kc >> 6) + 2 * half + (KH == 2 ? kh : 0);
+#pragma unroll
+        for (int j = 0; j < NG; ++j) sr[j] = srow[(g0 + j) * srb];
         __builtin_amdgcn_sched_barrier(0);
     };
     auto stage_x = [&](char *st, const uint4 &xv0, const uint4 &xv1) {
@@ -442,8 +451,10 @@ __global__ __launch_bounds__(512) void gemm_nf4_x32_kernel(const uint8_t *__rest
     uint32_t adb[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) adb[i] = ad[i];
-    auto compute = [&](const char *st, const uint4 (&q)[4], const uint32_t (&sr)[2]) {
-        const float s0 = f16_to_f32(sr[0]), s1 = f16_to_f32(sr[1]);
+    auto compute = [&](const char *st, const uint4 (&q)[NQ], const uint32_t (&sr)[NG]) {
+        float sv[NG];
+#pragma unroll
+        for (int j = 0; j < NG; ++j) sv[j] = f16_to_f32(sr[j]);
         float2 la[4], lb[4];
         uint4 ava, avb;
         auto issue = [&](int t, uint32_t (&a4)[4], float2 (&l)[4], uint4 &av) {
@@ -455,23 +466,23 @@ __global__ __launch_bounds__(512) void gemm_nf4_x32_kernel(const uint8_t *__rest
             pair_addr<3>(a4[3], wn);
 #pragma unroll
             for (int i = 0; i < 4; ++i) l[i] = *reinterpret_cast<const float2 *>(tab + a4[i]);
-            const int c = 16 * half + t;   // 16-byte chunk of k = kc + 128h + 8t
+            const int c = 16 * half + NS * kh + t;   // 16-byte chunk of k = kc + 128h + 8 (NS kh + t)
             av = *reinterpret_cast<const uint4 *>(st + l32 * 512 + ((c ^ l32) << 4));
         };
         auto finish = [&](int t, const float2 (&l)[4], const uint4 &av) {
-            const float sc = t < 8 ? s0 : s1;
+            const float sc = sv[t >> 3];
             const uint4 bv = make_uint4(pack_bf16x2(l[0].x * sc, l[0].y * sc), pack_bf16x2(l[1].x * sc, l[1].y * sc),
                                         pack_bf16x2(l[2].x * sc, l[2].y * sc), pack_bf16x2(l[3].x * sc, l[3].y * sc));
             acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(bv), acc, 0, 0, 0);
         };
         issue(0, ad, la, ava);
 #pragma unroll
-        for (int t = 0; t < 16; t += 2) {
+        for (int t = 0; t < NS; t += 2) {
             issue(t + 1, adb, lb, avb);
             __builtin_amdgcn_sched_barrier(0);
             finish(t, la, ava);
             __builtin_amdgcn_sched_barrier(0);
-            if (t + 2 < 16) issue(t + 2, ad, la, ava);
+            if (t + 2 < NS) issue(t + 2, ad, la, ava);
             __builtin_amdgcn_sched_barrier(0);
             finish(t + 1, lb, avb);
             __builtin_amdgcn_sched_barrier(0);
@@ -479,8 +490,8 @@ __global__ __launch_bounds__(512) void gemm_nf4_x32_kernel(const uint8_t *__rest
     };
     auto sync = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
 
-    uint4 qa[4], qb[4], xa0, xa1, xb0, xb1;
-    uint32_t sa[2], sb[2];
+    uint4 qa[NQ], qb[NQ], xa0, xa1, xb0, xb1;
+    uint32_t sa[NG], sb[NG];
     __syncthreads();   // pair table complete
     // Chunk c lives in buffer A and LDS stage 0 when c is even, in B and stage 1 when odd.
     // Inside the loop the prefetch of the next chunk is unconditional (the last chunk is
@@ -508,6 +519,20 @@ __global__ __launch_bounds__(512) void gemm_nf4_x32_kernel(const uint8_t *__rest
             sync();
             compute(xst[1], qb, sb);
         }
+    }
+    if constexpr (KH == 2) {
+        // The second half parks its accumulators in the X stages (4 row groups x
+        // 64 lanes x 16 floats = 16 KB); the first half adds them.
+        __syncthreads();
+        float *park = reinterpret_cast<float *>(&xst[0][0]);
+        if (kh == 1) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) park[(rg * 16 + e) * 64 + lane] = acc[e];
+        }
+        __syncthreads();
+        if (kh == 1) return;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[e] += park[(rg * 16 + e) * 64 + lane];
     }
     // Output element e of lane l: position 8*(e/4) + 4*h + e%4, column rowt.
     if (rowt < n_out) {
@@ -747,11 +772,15 @@ constexpr int64_t kNf4RowsPerWg = 4 * 32 * kNf4Nb;
 
 static bool use_x32(int64_t k, int64_t m) { return m <= 32 && (k % kX32Chunk) == 0; }
 static bool use_tiled(int64_t m) { return m > 32; }
+// Matrices with at least 192 blocks of 128 rows fill the CUs with the KH = 2
+// form and no k split.
+static bool x32_tall(int64_t n_out) { return n_out >= 192 * 128; }
 
 static int nf4_splits(int64_t n_out, int64_t k, int64_t m) {
     if (use_tiled(m)) return 1;
     if (use_x32(k, m)) {
-        const int64_t blocks = (n_out + kX32Rows - 1) / kX32Rows;
+        if (x32_tall(n_out)) return 1;
+        const int64_t blocks = (n_out + 255) / 256;
         const int64_t chunks = k / kX32Chunk;
         int64_t splits = 256 / blocks;
         if (splits < 1) splits = 1;
@@ -807,10 +836,15 @@ int launch_gemm_nf4(const void *w, int64_t n_out, int64_t k, const void *x, int6
     const auto *wp = static_cast<const uint8_t *>(w);
     const auto *xp = static_cast<const uint16_t *>(x);
     if (use_x32(k, m)) {
-        const int64_t gx = (n_out + kX32Rows - 1) / kX32Rows;
+        const bool tall = x32_tall(n_out);
+        const int64_t rows = tall ? 128 : 256;
+        const int64_t gx = (n_out + rows - 1) / rows;
         if (gx > 0x7fffffff) return WSL_E_SHAPE;
-        hipLaunchKernelGGL(gemm_nf4_x32_kernel, dim3(static_cast<unsigned>(gx), static_cast<unsigned>(splits)),
-                           dim3(512), 0, s, wp, n_out, k, xp, m, ldx, y, ofmt, ldy, wsp, kps);
+        const dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(splits));
+        if (tall) hipLaunchKernelGGL(gemm_nf4_x32_kernel<2>, grid, dim3(512), 0, s, wp, n_out, k, xp, m, ldx, y, ofmt,
+                                     ldy, wsp, kps);
+        else hipLaunchKernelGGL(gemm_nf4_x32_kernel<1>, grid, dim3(512), 0, s, wp, n_out, k, xp, m, ldx, y, ofmt, ldy,
+                                wsp, kps);
     } else {
         const int64_t gx = (n_out + kNf4RowsPerWg - 1) / kNf4RowsPerWg;
         const int64_t gz = (m + 31) / 32;
