@@ -636,7 +636,8 @@ def source_sha():
 def traffic_probe():
     """The launches that a counter run of this script sees: 3 elementwise copies of CALIB_BYTES
     (torch.neg into a second buffer: a kernel that reads and writes exactly CALIB_BYTES), then
-    4 eager steps of the headline layer.  No timing, no oracle."""
+    4 eager launches of the headline layer's gate_up GEMV (the only GEMV dispatches of the
+    run).  No timing, no oracle."""
     import torch
     src = torch.empty(CALIB_BYTES // 2, dtype=torch.bfloat16, device="cuda").normal_()
     dst = torch.empty_like(src)
@@ -647,7 +648,8 @@ def traffic_probe():
     _, _, _, steps = setup_layer_5120(copies=2)
     for i in range(4):
         for l in steps[i % 2]:
-            l.fn()
+            if l.name == "gate_up":
+                l.fn()
     torch.cuda.synchronize()
     print("traffic probe done", flush=True)
 
@@ -676,7 +678,7 @@ def traffic_summarize(fetch_dir, write_dir, commands):
     """Per-launch HBM bytes of the dominant kernel from two counter runs of --traffic-probe."""
     # calibration: the elementwise negation of CALIB_BYTES (reads and writes CALIB_BYTES)
     is_calib = lambda n: "neg_kernel" in n
-    is_dom = lambda n: "gemv_bf16_kernel" in n and ("<8>" in n or "ILi8E" in n)
+    is_dom = lambda n: "gemv_bf16_kernel" in n
     out = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = _counter_rows(d, counter)
@@ -689,7 +691,7 @@ def traffic_summarize(fetch_dir, write_dir, commands):
                         "calibration_copy_kib": float(np.mean(calib)), "factor": float(factor),
                         "bytes_per_launch": float(np.mean(dom) * 1024 / factor)}
     algo = 2 * 34816 * 5120
-    res = {"kernel": "gemv_bf16_kernel<8> (gate_up 34816x5120)", "kernel_source_sha256": source_sha(),
+    res = {"kernel": "gemv_bf16_kernel<2> (gate_up 34816x5120)", "kernel_source_sha256": source_sha(),
            "algorithmic_bytes_per_launch": algo, "counters": out,
            "bytes_per_launch": out["FETCH_SIZE"]["bytes_per_launch"] + out["WRITE_SIZE"]["bytes_per_launch"],
            "commands": commands}
@@ -709,6 +711,38 @@ def traffic_from_file():
         return None
 
 
+def trace_summarize(run_dir, title, command):
+    """Markdown summary of a rocprofv3 --kernel-trace --output-format csv run: the library's
+    dispatches grouped by kernel and grid size (one template instance serves several
+    matrix shapes, which differ in grid size), durations in microseconds."""
+    import csv
+    groups = {}
+    for path in glob.glob(os.path.join(run_dir, "**", "*kernel_trace.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                name = r.get("Kernel_Name", "")
+                if "wsl::" not in name:
+                    continue
+                short = name.split("(")[0].replace("void ", "")
+                us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                dims = lambda pre: "x".join(r.get(f"{pre}_{a}", "1") for a in "XYZ").replace("x1x1", "").replace(
+                    "x1", "") if f"{pre}_X" in r else r.get(pre, "?")
+                key = (short, dims("Grid_Size"), dims("Workgroup_Size"))
+                groups.setdefault(key, []).append(us)
+    total = sum(sum(v) for v in groups.values())
+    lines = [f"# {title}", "", "Command (run from the repository root on one MI355X, ROCm 7.2, rocprofv3):", "",
+             "```", command, "```", "",
+             "Library dispatches of the run, grouped by kernel and grid size (work-items); durations "
+             "in microseconds from the kernel trace.  Summary written by "
+             "`python bench.py --trace-summarize <run dir> <title> <command>`.", "",
+             "| kernel | grid | workgroup | calls | total (us) | average (us) | min (us) | max (us) | % of library time |",
+             "|---|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    for (short, grid, wg), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| `{short}` | {grid} | {wg} | {len(v)} | {sum(v):.1f} | {np.mean(v):.3f} | {min(v):.3f} | "
+                     f"{max(v):.3f} | {100 * sum(v) / total:.2f} |")
+    print("\n".join(lines))
+
+
 # ---------------------------------------------------------------- main
 def main():
     ap = argparse.ArgumentParser()
@@ -721,7 +755,12 @@ def main():
     ap.add_argument("--traffic-probe", action="store_true", help="launch sequence for rocprofv3 counter runs")
     ap.add_argument("--traffic-summarize", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--traffic-commands", default="", help="the counter commands, recorded with the summary")
+    ap.add_argument("--trace-summarize", nargs=3, metavar=("RUN_DIR", "TITLE", "COMMAND"),
+                    help="markdown summary of a rocprofv3 kernel-trace CSV run")
     args = ap.parse_args()
+    if args.trace_summarize:
+        trace_summarize(*args.trace_summarize)
+        return
     if args.traffic_summarize:
         traffic_summarize(*args.traffic_summarize, args.traffic_commands)
         return
@@ -785,7 +824,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic_from_file(),
-            "kernel": "gemv_bf16_kernel<8> (gate_up 34816x5120)",
+            "kernel": "gemv_bf16_kernel<2> (gate_up 34816x5120)",
             "bytes_per_launch": head["dominant_bytes"],
             "avg_launch_us": round(head["dominant_avg_us"], 3),
         },

