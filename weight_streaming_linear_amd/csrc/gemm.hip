@@ -681,13 +681,30 @@ __global__ __launch_bounds__(512) void gemm_nf4_tiled_kernel(const uint16_t *__r
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f[i]),
                                                                     __builtin_bit_cast(bf16x8, f[4 + j]), acc[i][j], 0, 0, 0);
     };
-    auto compute_stage = [&](uint32_t abase, uint32_t bbase) {
+    // The restoration of the next weight stage runs between the two halves of the
+    // stage's MFMAs, so its table reads and multiplies overlap the matrix pipe
+    // instead of delaying the first MFMA after the barrier.
+    auto mfmas_half = [&](const u32x4 (&f)[6], int i0) {
+#pragma unroll
+        for (int i = i0; i < i0 + 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f[i]),
+                                                                    __builtin_bit_cast(bf16x8, f[4 + j]), acc[i][j], 0, 0, 0);
+    };
+    auto compute_stage = [&](uint32_t abase, uint32_t bbase, auto &&restore0, auto &&restore1) {
         u32x4 f0[6], f1[6];
         issue(abase + offa[0], bbase + offb[0], f0);
         landed(f0);
         issue(abase + offa[1], bbase + offb[1], f1);
         __builtin_amdgcn_sched_barrier(0);
-        mfmas(f0);
+        mfmas_half(f0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        restore0();
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas_half(f0, 2);
+        __builtin_amdgcn_sched_barrier(0);
+        restore1();
         __builtin_amdgcn_sched_barrier(0);
         landed(f1);
         mfmas(f1);
@@ -698,7 +715,7 @@ __global__ __launch_bounds__(512) void gemm_nf4_tiled_kernel(const uint16_t *__r
     uint2 q0, q1, q2, q3;
     uint32_t r0, r1, r2, r3;
     // step kt: wait (A(kt) and the codes of kt+1 landed), barrier, issue codes(kt+3) then A(kt+3),
-    // restore B(kt+1), multiply stage kt.
+    // multiply stage kt with the restoration of B(kt+1) between its two MFMA halves.
     auto step = [&](int64_t kt, uint32_t acur, uint32_t bcur, char *arefill, uint2 &qload, uint32_t &rload,
                     char *bnext, const uint2 &qnext, const uint32_t &rnext) {
         const int64_t ahead = ktiles - 1 - kt;
@@ -710,8 +727,17 @@ __global__ __launch_bounds__(512) void gemm_nf4_tiled_kernel(const uint16_t *__r
             load_codes(kt + 3, qload, rload);
             copy_a(kt + 3, arefill);
         }
-        if (kt + 1 < ktiles) put_b(bnext, qnext, rnext);
-        compute_stage(acur, bcur);
+        const bool more = kt + 1 < ktiles;
+        uint4 v0;
+        compute_stage(acur, bcur, [&]() {
+            if (more) v0 = dequant8(qnext.x, f16_to_f32(rnext), lutp);
+        }, [&]() {
+            if (more) {
+                const uint4 v1 = dequant8(qnext.y, f16_to_f32(rnext), lutp);
+                *reinterpret_cast<uint4 *>(bnext + boff0) = v0;
+                *reinterpret_cast<uint4 *>(bnext + boff1) = v1;
+            }
+        });
     };
     __syncthreads();   // lut
     // prologue: codes and A for stages 0, 1, 2; restore B(0)
