@@ -53,8 +53,10 @@ def _sample_rows(n, rng, count):
 
 
 # Decode sweep with hidden size 6144: gate/up 6144 -> 32768 and down 16384 -> 6144; plus ragged
-# large shapes (odd row count, k not a multiple of 2048).  These take the pair-table kernel.
-@pytest.mark.parametrize("n_out,k,tid", [(32768, 6144, 0), (6144, 16384, 1), (8195, 6208, 2), (20000, 2112, 3)])
+# large shapes (odd row count, k not a multiple of 2048).  The two sweep shapes and 12291x6208
+# take the pair-table kernel (>= 64 Mi weights), the others the 16-entry table.
+@pytest.mark.parametrize("n_out,k,tid", [(32768, 6144, 0), (6144, 16384, 1), (12291, 6208, 4), (8195, 6208, 2),
+                                         (20000, 2112, 3)])
 def test_gemv_nf4_large_sampled(n_out, k, tid):
     import torch
     say(f"gemv nf4 large {n_out}x{k}")

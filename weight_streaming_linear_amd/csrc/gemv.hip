@@ -561,11 +561,15 @@ int launch_gemv_bf16(const void *w, int64_t n_out, int64_t k, const void *x, flo
 }
 
 // NF4 plan.  k <= 32768: the team kernel with S = ceil(k / 2048) waves per team.
-// Large matrices (>= 40 Mi weights) take the pair table, 2 rows per row group and
+// Large matrices (>= 64 Mi weights) take the pair table, 2 rows per row group and
 // 16 / S teams in one workgroup per CU (the 64 KB table leaves room for one); the
-// others the 16-entry table, 4 rows (2 below 4096 rows), at most 2 teams and two
-// workgroups per CU.  The grid is a multiple of 8 (one share per XCD) and never
-// larger than needed.  k > 32768: the wide kernel.
+// others the 16-entry table (no 64 KB table to build per launch), 4 rows (2 up to
+// 4096 rows), at most 2 teams, and two workgroups per CU -- three below 32 Mi
+// weights when that stays within 16 waves per CU.  The grid is a multiple of 8
+// (one share per XCD) and never larger than needed.  k > 32768: the wide kernel.
+// (Measured on the decode shapes: 8192x6144 runs 10.5 us with the pair table and
+// 9.8 us with the 16-entry table; 4096x4096 5.55 us with 4 rows and two workgroups
+// per CU, 5.2 us with 2 rows and three.)
 struct Nf4GemvPlan {
     bool wide, pair;
     int rows, S, T;
@@ -587,16 +591,17 @@ static Nf4GemvPlan plan_gemv_nf4(int64_t n_out, int64_t k) {
     p.wide = false;
     p.S = static_cast<int>(slices);
     int64_t per_cu;
-    if (n_out * k >= (static_cast<int64_t>(40) << 20)) {
+    const int64_t weights = n_out * k;
+    if (weights >= (static_cast<int64_t>(64) << 20)) {
         p.pair = true;
         p.rows = 2;
         p.T = 16 / p.S;
         per_cu = 1;
     } else {
         p.pair = false;
-        p.rows = n_out >= 4096 ? 4 : 2;
+        p.rows = n_out > 4096 ? 4 : 2;
         p.T = 16 / p.S < 2 ? 1 : 2;
-        per_cu = 2;
+        per_cu = (weights < (static_cast<int64_t>(32) << 20) && 3 * p.S * p.T <= 16) ? 3 : 2;
     }
     const int64_t rg = (n_out + p.rows - 1) / p.rows;
     const int64_t full = (n_out % p.rows == 0) ? rg : ((n_out >> 4) << 4) / p.rows;
