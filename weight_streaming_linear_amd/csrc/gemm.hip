@@ -383,8 +383,9 @@ __global__ __launch_bounds__(256) void gemm_nf4_kernel(const uint8_t *__restrict
 // and the compiler cannot move LDS accesses over it.  With KH = 2 the second
 // half's accumulators meet the first's in LDS (a fixed order), then the 32 x 32
 // result goes to Y, or to the split workspace.
-// KH = 2 (128 rows per workgroup) lets tall matrices fill the CUs without
-// splitting k, so they need no workspace and no reduction pass.
+// The library launches KH = 2 (128 rows per workgroup): tall matrices then fill the
+// CUs without splitting k (no workspace, no reduction pass), and short ones need
+// half the k splits of the 256-row form.
 constexpr int kX32Chunk = 256;
 constexpr int kX32Stage = 32 * kX32Chunk * 2;
 
@@ -798,15 +799,17 @@ constexpr int64_t kNf4RowsPerWg = 4 * 32 * kNf4Nb;
 
 static bool use_x32(int64_t k, int64_t m) { return m <= 32 && (k % kX32Chunk) == 0; }
 static bool use_tiled(int64_t m) { return m > 32; }
-// Matrices with at least 192 blocks of 128 rows fill the CUs with the KH = 2
-// form and no k split.
-static bool x32_tall(int64_t n_out) { return n_out >= 192 * 128; }
+// The shared-X kernel always runs its 128-row form (KH = 2), k split into as many
+// ranges as keep the grid within one pass over the 256 CUs.  Measured at M = 32:
+// 27648x5120 32.6 us unsplit against 38.7 us for the 256-row form with 2 splits;
+// 5120x27648 32.9 us with 6 splits against 38.2 us for the 256-row form with 12.
+constexpr int kX32Kh = 2;
+constexpr int64_t kX32BlockRows = 256 / kX32Kh;
 
 static int nf4_splits(int64_t n_out, int64_t k, int64_t m) {
     if (use_tiled(m)) return 1;
     if (use_x32(k, m)) {
-        if (x32_tall(n_out)) return 1;
-        const int64_t blocks = (n_out + 255) / 256;
+        const int64_t blocks = (n_out + kX32BlockRows - 1) / kX32BlockRows;
         const int64_t chunks = k / kX32Chunk;
         int64_t splits = 256 / blocks;
         if (splits < 1) splits = 1;
@@ -862,15 +865,11 @@ int launch_gemm_nf4(const void *w, int64_t n_out, int64_t k, const void *x, int6
     const auto *wp = static_cast<const uint8_t *>(w);
     const auto *xp = static_cast<const uint16_t *>(x);
     if (use_x32(k, m)) {
-        const bool tall = x32_tall(n_out);
-        const int64_t rows = tall ? 128 : 256;
-        const int64_t gx = (n_out + rows - 1) / rows;
+        const int64_t gx = (n_out + kX32BlockRows - 1) / kX32BlockRows;
         if (gx > 0x7fffffff) return WSL_E_SHAPE;
         const dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(splits));
-        if (tall) hipLaunchKernelGGL(gemm_nf4_x32_kernel<2>, grid, dim3(512), 0, s, wp, n_out, k, xp, m, ldx, y, ofmt,
-                                     ldy, wsp, kps);
-        else hipLaunchKernelGGL(gemm_nf4_x32_kernel<1>, grid, dim3(512), 0, s, wp, n_out, k, xp, m, ldx, y, ofmt, ldy,
-                                wsp, kps);
+        hipLaunchKernelGGL(gemm_nf4_x32_kernel<kX32Kh>, grid, dim3(512), 0, s, wp, n_out, k, xp, m, ldx, y, ofmt, ldy,
+                           wsp, kps);
     } else {
         const int64_t gx = (n_out + kNf4RowsPerWg - 1) / kNf4RowsPerWg;
         const int64_t gz = (m + 31) / 32;
