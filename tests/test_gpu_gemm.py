@@ -205,7 +205,29 @@ def test_gemm_nf4_verify_m8192_full_shape_sampled(n_out, k, tid):
     assert ok, f"elem {i}: worst ratio {worst}"
 
 
-@pytest.mark.parametrize("m,n_out,k", [(64, 300, 512), (200, 1000, 1024), (257, 130, 2048), (513, 260, 64)])
+# 32 < M <= 256 with k % 256 == 0: the shared-X kernel with two 32-position groups per
+# workgroup and position blocks on grid z -- M not a multiple of 32 or 64, ragged row
+# counts, tall matrices without a k split, one to four position blocks.
+@pytest.mark.parametrize("m,n_out,k", [(33, 257, 512), (48, 1000, 768), (130, 4109, 2304), (256, 24700, 256),
+                                       (200, 160, 5120)])
+@pytest.mark.parametrize("ofmt", [wsl.WSL_OUT_F32, wsl.WSL_OUT_BF16])
+def test_gemm_nf4_mid_m_shared_x(m, n_out, k, ofmt):
+    import torch
+    say(f"gemm nf4 mid m={m} n={n_out} k={k} ofmt={ofmt}")
+    wb = synth.weight_bits(99, n_out, n_out, k)
+    xb = synth.act_bits(99, 1000 + m, (m, k))
+    packed = wsl.nf4_pack(to_dev_bf16(wb))
+    nb = wsl.linear_gemm_workspace_bytes(wsl.WSL_W_NF4, n_out, k, m)
+    ws = torch.full((max(nb, 16) // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    y = wsl.linear_gemm(packed, to_dev_bf16(xb), wfmt=wsl.WSL_W_NF4, n_out=n_out, k=k, ofmt=ofmt, workspace=ws)
+    torch.cuda.synchronize()
+    y_ref, s_ref = oracle.gemm_ref(f64(xb), _tile_f64(wb))
+    ok, worst, i = _check(y, y_ref, s_ref, ofmt)
+    assert ok, f"elem {i}: worst ratio {worst}"
+
+
+# M > 256, or M > 32 with k % 256 != 0: the tiled kernel.
+@pytest.mark.parametrize("m,n_out,k", [(64, 300, 448), (257, 130, 2048), (513, 260, 64), (300, 1000, 1024)])
 @pytest.mark.parametrize("ofmt", [wsl.WSL_OUT_F32, wsl.WSL_OUT_BF16])
 def test_gemm_nf4_tiled_mid_m(m, n_out, k, ofmt):
     import torch

@@ -389,7 +389,7 @@ __global__ __launch_bounds__(256) void gemm_nf4_kernel(const uint8_t *__restrict
 constexpr int kX32Chunk = 256;
 constexpr int kX32Stage = 32 * kX32Chunk * 2;
 
-template <int KH>
+template <int KH, int MB>
 __global__ __launch_bounds__(512) void gemm_nf4_x32_kernel(const uint8_t *__restrict__ packed, int64_t n_out,
                                                            int64_t k, const uint16_t *__restrict__ x, int64_t m,
                                                            int64_t ldx, void *__restrict__ y, int ofmt, int64_t ldy,
@@ -399,7 +399,7 @@ __global__ __launch_bounds__(512) void gemm_nf4_x32_kernel(const uint8_t *__rest
     constexpr int NS = 16 / KH;       // k-steps per wave per chunk
     constexpr int NG = 2 / KH;        // scales per lane per chunk
     __shared__ __align__(16) char tab[kPairTableBytes];
-    __shared__ __align__(16) char xst[2][kX32Stage];
+    __shared__ __align__(16) char xst[2][MB * kX32Stage];   // position group g at g * kX32Stage
     fill_pair_table(tab);
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -420,17 +420,28 @@ __global__ __launch_bounds__(512) void gemm_nf4_x32_kernel(const uint8_t *__rest
     const int64_t srem = n_out - ((row >> 4) << 4);
     const int64_t srb = srem < 16 ? srem : 16;
     const uint16_t *srow = scales + (row >> 4) * 16 * groups + (row & 15);   // scale (row, g) at srow[g * srb]
-    // X staging: thread t moves the 16-byte chunks (row t / 32, chunk t % 32) and (row t / 32 + 16, same chunk).
+    // Positions of this workgroup: p0 .. p0 + 32 MB - 1 (blockIdx.z), in MB groups of 32.
+    // X staging: for each group g, thread t moves the 16-byte chunks (row t / 32, chunk
+    // t % 32) and (row t / 32 + 16, same chunk); rows past m repeat row m - 1.
+    const int64_t p0 = static_cast<int64_t>(blockIdx.z) * 32 * MB;
     const int xi0 = tid >> 5, xi1 = xi0 + 16, xcc = tid & 31;
-    const uint16_t *xrow0 = x + (xi0 < m ? xi0 : m - 1) * ldx + xcc * 8;
-    const uint16_t *xrow1 = x + (xi1 < m ? xi1 : m - 1) * ldx + xcc * 8;
+    const uint16_t *xrow0[MB], *xrow1[MB];
+#pragma unroll
+    for (int g = 0; g < MB; ++g) {
+        const int64_t r0 = p0 + 32 * g + xi0, r1 = p0 + 32 * g + xi1;
+        xrow0[g] = x + (r0 < m ? r0 : m - 1) * ldx + xcc * 8;
+        xrow1[g] = x + (r1 < m ? r1 : m - 1) * ldx + xcc * 8;
+    }
     const int xoff0 = xi0 * 512 + ((xcc ^ xi0) << 4);
     const int xoff1 = xi1 * 512 + ((xcc ^ xi1) << 4);
 
-    auto fetch = [&](int c, uint4 (&q)[NQ], uint32_t (&sr)[NG], uint4 &xv0, uint4 &xv1) {
+    auto fetch = [&](int c, uint4 (&q)[NQ], uint32_t (&sr)[NG], uint4 (&xv0)[MB], uint4 (&xv1)[MB]) {
         const int64_t kc = kbeg + static_cast<int64_t>(c) * kX32Chunk;
-        xv0 = *reinterpret_cast<const uint4 *>(xrow0 + kc);
-        xv1 = *reinterpret_cast<const uint4 *>(xrow1 + kc);
+#pragma unroll
+        for (int g = 0; g < MB; ++g) {
+            xv0[g] = *reinterpret_cast<const uint4 *>(xrow0[g] + kc);
+            xv1[g] = *reinterpret_cast<const uint4 *>(xrow1[g] + kc);
+        }
         const uint8_t *src = crow + (kc >> 1);
 #pragma unroll
         for (int j = 0; j < NQ; ++j) q[j] = *reinterpret_cast<const uint4 *>(src + 16 * j);
@@ -439,13 +450,18 @@ __global__ __launch_bounds__(512) void gemm_nf4_x32_kernel(const uint8_t *__rest
         for (int j = 0; j < NG; ++j) sr[j] = srow[(g0 + j) * srb];
         __builtin_amdgcn_sched_barrier(0);
     };
-    auto stage_x = [&](char *st, const uint4 &xv0, const uint4 &xv1) {
-        *reinterpret_cast<uint4 *>(st + xoff0) = xv0;
-        *reinterpret_cast<uint4 *>(st + xoff1) = xv1;
-    };
-    f32x16 acc;
+    auto stage_x = [&](char *st, const uint4 (&xv0)[MB], const uint4 (&xv1)[MB]) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+        for (int g = 0; g < MB; ++g) {
+            *reinterpret_cast<uint4 *>(st + g * kX32Stage + xoff0) = xv0[g];
+            *reinterpret_cast<uint4 *>(st + g * kX32Stage + xoff1) = xv1[g];
+        }
+    };
+    f32x16 acc[MB];
+#pragma unroll
+    for (int g = 0; g < MB; ++g)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[g][e] = 0.f;
     // Each k-step: the four pair-table reads of its code word and the X fragment
     // read are issued one step ahead (two register sets), so the LDS latency of a
     // step is covered by the previous step's multiplies and MFMA.
@@ -457,8 +473,8 @@ __global__ __launch_bounds__(512) void gemm_nf4_x32_kernel(const uint8_t *__rest
 #pragma unroll
         for (int j = 0; j < NG; ++j) sv[j] = f16_to_f32(sr[j]);
         float2 la[4], lb[4];
-        uint4 ava, avb;
-        auto issue = [&](int t, uint32_t (&a4)[4], float2 (&l)[4], uint4 &av) {
+        uint4 ava[MB], avb[MB];
+        auto issue = [&](int t, uint32_t (&a4)[4], float2 (&l)[4], uint4 (&av)[MB]) {
             const uint4 qq = q[t >> 2];
             const uint32_t wn = rotr32((t & 3) == 0 ? qq.x : (t & 3) == 1 ? qq.y : (t & 3) == 2 ? qq.z : qq.w, 2);
             pair_addr<0>(a4[0], wn);
@@ -468,13 +484,18 @@ __global__ __launch_bounds__(512) void gemm_nf4_x32_kernel(const uint8_t *__rest
 #pragma unroll
             for (int i = 0; i < 4; ++i) l[i] = *reinterpret_cast<const float2 *>(tab + a4[i]);
             const int c = 16 * half + NS * kh + t;   // 16-byte chunk of k = kc + 128h + 8 (NS kh + t)
-            av = *reinterpret_cast<const uint4 *>(st + l32 * 512 + ((c ^ l32) << 4));
+#pragma unroll
+            for (int g = 0; g < MB; ++g)
+                av[g] = *reinterpret_cast<const uint4 *>(st + g * kX32Stage + l32 * 512 + ((c ^ l32) << 4));
         };
-        auto finish = [&](int t, const float2 (&l)[4], const uint4 &av) {
+        // One restored B fragment feeds the MFMAs of all MB position groups.
+        auto finish = [&](int t, const float2 (&l)[4], const uint4 (&av)[MB]) {
             const float sc = sv[t >> 3];
             const uint4 bv = make_uint4(pack_bf16x2(l[0].x * sc, l[0].y * sc), pack_bf16x2(l[1].x * sc, l[1].y * sc),
                                         pack_bf16x2(l[2].x * sc, l[2].y * sc), pack_bf16x2(l[3].x * sc, l[3].y * sc));
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(bv), acc, 0, 0, 0);
+#pragma unroll
+            for (int g = 0; g < MB; ++g)
+                acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av[g]), as_bf16x8(bv), acc[g], 0, 0, 0);
         };
         issue(0, ad, la, ava);
 #pragma unroll
@@ -491,7 +512,7 @@ __global__ __launch_bounds__(512) void gemm_nf4_x32_kernel(const uint8_t *__rest
     };
     auto sync = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
 
-    uint4 qa[NQ], qb[NQ], xa0, xa1, xb0, xb1;
+    uint4 qa[NQ], qb[NQ], xa0[MB], xa1[MB], xb0[MB], xb1[MB];
     uint32_t sa[NG], sb[NG];
     __syncthreads();   // pair table complete
     // Chunk c lives in buffer A and LDS stage 0 when c is even, in B and stage 1 when odd.
@@ -522,26 +543,32 @@ __global__ __launch_bounds__(512) void gemm_nf4_x32_kernel(const uint8_t *__rest
         }
     }
     if constexpr (KH == 2) {
-        // The second half parks its accumulators in the X stages (4 row groups x
-        // 64 lanes x 16 floats = 16 KB); the first half adds them.
+        // The second half parks its accumulators in the X stages (4 row groups x MB
+        // groups x 64 lanes x 16 floats = 16 KB per group); the first half adds them.
         __syncthreads();
         float *park = reinterpret_cast<float *>(&xst[0][0]);
         if (kh == 1) {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) park[(rg * 16 + e) * 64 + lane] = acc[e];
+            for (int g = 0; g < MB; ++g)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) park[((rg * MB + g) * 16 + e) * 64 + lane] = acc[g][e];
         }
         __syncthreads();
         if (kh == 1) return;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[e] += park[(rg * 16 + e) * 64 + lane];
+        for (int g = 0; g < MB; ++g)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[g][e] += park[((rg * MB + g) * 16 + e) * 64 + lane];
     }
-    // Output element e of lane l: position 8*(e/4) + 4*h + e%4, column rowt.
+    // Output element e of lane l, group g: position p0 + 32 g + 8*(e/4) + 4*h + e%4, column rowt.
     if (rowt < n_out) {
 #pragma unroll
+        for (int g = 0; g < MB; ++g)
+#pragma unroll
         for (int e = 0; e < 16; ++e) {
-            const int64_t p = 8 * (e >> 2) + 4 * half + (e & 3);
+            const int64_t p = p0 + 32 * g + 8 * (e >> 2) + 4 * half + (e & 3);
             if (p >= m) continue;
-            const float v = acc[e];
+            const float v = acc[g][e];
             if (ws != nullptr) {
                 ws[(static_cast<int64_t>(blockIdx.y) * m + p) * n_out + rowt] = v;
             } else if (ofmt == WSL_OUT_F32) {
@@ -797,19 +824,26 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float *__restri
 constexpr int kNf4Nb = 1;
 constexpr int64_t kNf4RowsPerWg = 4 * 32 * kNf4Nb;
 
-static bool use_x32(int64_t k, int64_t m) { return m <= 32 && (k % kX32Chunk) == 0; }
-static bool use_tiled(int64_t m) { return m > 32; }
-// The shared-X kernel always runs its 128-row form (KH = 2), k split into as many
-// ranges as keep the grid within one pass over the 256 CUs.  Measured at M = 32:
-// 27648x5120 32.6 us unsplit against 38.7 us for the 256-row form with 2 splits;
-// 5120x27648 32.9 us with 6 splits against 38.2 us for the 256-row form with 12.
+// Shared-X kernel: M <= 256 with k a multiple of 256; the tiled kernel above 256 (or for
+// M > 32 with other k); the general kernel for M <= 32 with other k.
+constexpr int64_t kX32MaxM = 256;
+static bool use_x32(int64_t k, int64_t m) { return m <= kX32MaxM && (k % kX32Chunk) == 0; }
+static bool use_tiled(int64_t k, int64_t m) { return m > 32 && !use_x32(k, m); }
+// The shared-X kernel always runs its 128-row form (KH = 2), with MB = 2 groups of 32
+// positions per workgroup when M > 32 (one restored weight fragment feeds both groups'
+// MFMAs) and further position blocks on grid z; k is split into as many ranges as keep
+// the grid within one pass over the 256 CUs.  Measured at M = 32: 27648x5120 32.6 us
+// unsplit against 38.7 us for the 256-row form with 2 splits; 5120x27648 32.9 us with
+// 6 splits against 38.2 us for the 256-row form with 12.
 constexpr int kX32Kh = 2;
 constexpr int64_t kX32BlockRows = 256 / kX32Kh;
+static int x32_mb(int64_t m) { return m > 32 ? 2 : 1; }
+static int64_t x32_zblocks(int64_t m) { return (m + 32 * x32_mb(m) - 1) / (32 * x32_mb(m)); }
 
 static int nf4_splits(int64_t n_out, int64_t k, int64_t m) {
-    if (use_tiled(m)) return 1;
+    if (use_tiled(k, m)) return 1;
     if (use_x32(k, m)) {
-        const int64_t blocks = (n_out + kX32BlockRows - 1) / kX32BlockRows;
+        const int64_t blocks = (n_out + kX32BlockRows - 1) / kX32BlockRows * x32_zblocks(m);
         const int64_t chunks = k / kX32Chunk;
         int64_t splits = 256 / blocks;
         if (splits < 1) splits = 1;
@@ -849,7 +883,7 @@ int launch_gemm_bf16(const void *w, int64_t n_out, int64_t k, const void *x, int
 
 int launch_gemm_nf4(const void *w, int64_t n_out, int64_t k, const void *x, int64_t m, int64_t ldx, void *y,
                     int ofmt, int64_t ldy, void *ws, size_t ws_bytes, hipStream_t s) {
-    if (use_tiled(m)) {
+    if (use_tiled(k, m)) {
         const int64_t tn = (n_out + kBN - 1) / kBN, tm = (m + kBM - 1) / kBM;
         if (tn * tm > 0x7fffffff / 2) return WSL_E_SHAPE;
         hipLaunchKernelGGL(gemm_nf4_tiled_kernel, dim3(static_cast<unsigned>(tn * tm)), dim3(512), 0, s,
@@ -867,9 +901,13 @@ int launch_gemm_nf4(const void *w, int64_t n_out, int64_t k, const void *x, int6
     if (use_x32(k, m)) {
         const int64_t gx = (n_out + kX32BlockRows - 1) / kX32BlockRows;
         if (gx > 0x7fffffff) return WSL_E_SHAPE;
-        const dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(splits));
-        hipLaunchKernelGGL(gemm_nf4_x32_kernel<kX32Kh>, grid, dim3(512), 0, s, wp, n_out, k, xp, m, ldx, y, ofmt, ldy,
-                           wsp, kps);
+        const dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(splits), static_cast<unsigned>(x32_zblocks(m)));
+        if (x32_mb(m) == 2)
+            hipLaunchKernelGGL((gemm_nf4_x32_kernel<kX32Kh, 2>), grid, dim3(512), 0, s, wp, n_out, k, xp, m, ldx, y,
+                               ofmt, ldy, wsp, kps);
+        else
+            hipLaunchKernelGGL((gemm_nf4_x32_kernel<kX32Kh, 1>), grid, dim3(512), 0, s, wp, n_out, k, xp, m, ldx, y,
+                               ofmt, ldy, wsp, kps);
     } else {
         const int64_t gx = (n_out + kNf4RowsPerWg - 1) / kNf4RowsPerWg;
         const int64_t gz = (m + 31) / 32;
