@@ -85,6 +85,30 @@ def test_gemm_bf16_small(m, n_out, k, ofmt):
     assert ok, f"elem {i}: worst ratio {worst}"
 
 
+# bf16 with M <= 64 and k % 256 == 0: the shared-X kernel (weights loaded straight into
+# MFMA B fragments) -- m < 32, one and two position groups, ragged row counts, a tall
+# matrix without a k split, many k splits with and without a workspace; M = 65 and 130
+# just past it take the tiled kernel.
+@pytest.mark.parametrize("m,n_out,k", [(1, 16, 256), (7, 4109, 2304), (32, 1000, 512), (48, 300, 768),
+                                       (64, 24700, 256), (33, 160, 5120), (65, 257, 1024), (130, 257, 1024)])
+@pytest.mark.parametrize("ofmt", [wsl.WSL_OUT_F32, wsl.WSL_OUT_BF16])
+@pytest.mark.parametrize("use_ws", [False, True])
+def test_gemm_bf16_shared_x(m, n_out, k, ofmt, use_ws):
+    import torch
+    say(f"gemm bf16 shared-x m={m} n={n_out} k={k} ofmt={ofmt} ws={use_ws}")
+    wb = synth.weight_bits(96, n_out, n_out, k)
+    xb = synth.act_bits(96, 1000 + m, (m, k))
+    ws = None
+    if use_ws:
+        nb = wsl.linear_gemm_workspace_bytes(wsl.WSL_W_BF16, n_out, k, m)
+        ws = torch.full((max(nb, 16) // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    y = wsl.linear_gemm(to_dev_bf16(wb), to_dev_bf16(xb), wfmt=wsl.WSL_W_BF16, ofmt=ofmt, workspace=ws)
+    torch.cuda.synchronize()
+    y_ref, s_ref = oracle.gemm_ref(f64(xb), f64(wb))
+    ok, worst, i = _check(y, y_ref, s_ref, ofmt)
+    assert ok, f"elem {i}: worst ratio {worst}"
+
+
 @pytest.mark.parametrize("m,k", [(40, 192), (20, 512)])
 def test_gemm_strided_x_and_y(m, k):
     """Leading dimensions larger than the logical widths."""

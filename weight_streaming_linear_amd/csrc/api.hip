@@ -13,7 +13,7 @@ int launch_dequant_tile(const void *packed, int64_t n_out, int64_t k, int64_t ro
 int launch_gemv_bf16(const void *w, int64_t n_out, int64_t k, const void *x, float *y, hipStream_t s);
 int launch_gemv_nf4(const void *w, int64_t n_out, int64_t k, const void *x, float *y, hipStream_t s);
 int launch_gemm_bf16(const void *w, int64_t n_out, int64_t k, const void *x, int64_t m, int64_t ldx, void *y,
-                     int ofmt, int64_t ldy, hipStream_t s);
+                     int ofmt, int64_t ldy, void *ws, size_t ws_bytes, hipStream_t s);
 int launch_gemm_nf4(const void *w, int64_t n_out, int64_t k, const void *x, int64_t m, int64_t ldx, void *y,
                     int ofmt, int64_t ldy, void *ws, size_t ws_bytes, hipStream_t s);
 size_t gemm_ws_bytes(int wfmt, int64_t n_out, int64_t k, int64_t m);
@@ -106,7 +106,8 @@ int linear_gemm(int wfmt, const void *d_w, int64_t n_out, int64_t k, const void 
     if (wfmt == WSL_W_NF4)
         return wsl::after_launch(
             wsl::launch_gemm_nf4(d_w, n_out, k, d_x, m, ldx, d_y, ofmt, ldy, d_ws, ws_bytes, wsl::as_stream(stream)));
-    return wsl::after_launch(wsl::launch_gemm_bf16(d_w, n_out, k, d_x, m, ldx, d_y, ofmt, ldy, wsl::as_stream(stream)));
+    return wsl::after_launch(
+        wsl::launch_gemm_bf16(d_w, n_out, k, d_x, m, ldx, d_y, ofmt, ldy, d_ws, ws_bytes, wsl::as_stream(stream)));
 }
 
 int nf4_embed_rows(const void *d_packed, int64_t n_rows, int64_t k, const int64_t *d_ids, int64_t count,

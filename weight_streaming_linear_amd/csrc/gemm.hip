@@ -580,6 +580,152 @@ __global__ __launch_bounds__(512) void gemm_nf4_x32_kernel(const uint8_t *__rest
     }
 }
 
+// ---------------------------------------------------------------- bf16, shared X, M <= 64
+// The bf16 counterpart of the shared-X kernel for up to 64 positions and k a multiple
+// of 256: the weights need no restoring, so a lane's 16-byte weight load is an MFMA B
+// fragment as it stands.  Same organization: 8 waves, 4 groups of 32 rows x 2 halves of
+// each chunk's k-steps (128 rows per workgroup), MB groups of 32 positions sharing each
+// B fragment, X staged per 256-k chunk in LDS (XOR-swizzled rows, two buffers), the
+// lane's 128 bytes of weights per chunk loaded one chunk ahead, the two halves'
+// accumulators summed in LDS at the end.
+template <int MB>
+__global__ __launch_bounds__(512) void gemm_bf16_x32_kernel(const uint16_t *__restrict__ w, int64_t n_out, int64_t k,
+                                                            const uint16_t *__restrict__ x, int64_t m, int64_t ldx,
+                                                            void *__restrict__ y, int ofmt, int64_t ldy,
+                                                            float *__restrict__ ws, int64_t k_per_split) {
+    constexpr int NQ = 8;   // 16-byte weight loads per lane per chunk (8 k-steps of 8 k)
+    __shared__ __align__(16) char xst[2][MB * kX32Stage];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int rg = wave & 3, kh = wave >> 2;
+    const int half = lane >> 5, l32 = lane & 31;
+    const int64_t rowt = static_cast<int64_t>(blockIdx.x) * 128 + rg * 32 + l32;
+    const int64_t row = rowt < n_out ? rowt : n_out - 1;
+    const int64_t kbeg = static_cast<int64_t>(blockIdx.y) * k_per_split;
+    const int64_t kend = (kbeg + k_per_split < k) ? kbeg + k_per_split : k;
+    const int nch = kend > kbeg ? static_cast<int>((kend - kbeg) / kX32Chunk) : 0;
+    // Lane (n, h) of wave half kh: k [kc + 128 h + 64 kh, + 64) of row n, 8 k per step.
+    const uint16_t *wrow = w + row * k + 128 * half + 64 * kh;
+    const int64_t p0 = static_cast<int64_t>(blockIdx.z) * 32 * MB;
+    const int xi0 = tid >> 5, xi1 = xi0 + 16, xcc = tid & 31;
+    const uint16_t *xrow0[MB], *xrow1[MB];
+#pragma unroll
+    for (int g = 0; g < MB; ++g) {
+        const int64_t r0 = p0 + 32 * g + xi0, r1 = p0 + 32 * g + xi1;
+        xrow0[g] = x + (r0 < m ? r0 : m - 1) * ldx + xcc * 8;
+        xrow1[g] = x + (r1 < m ? r1 : m - 1) * ldx + xcc * 8;
+    }
+    const int xoff0 = xi0 * 512 + ((xcc ^ xi0) << 4);
+    const int xoff1 = xi1 * 512 + ((xcc ^ xi1) << 4);
+
+    auto fetch = [&](int c, uint4 (&q)[NQ], uint4 (&xv0)[MB], uint4 (&xv1)[MB]) {
+        const int64_t kc = kbeg + static_cast<int64_t>(c) * kX32Chunk;
+#pragma unroll
+        for (int g = 0; g < MB; ++g) {
+            xv0[g] = *reinterpret_cast<const uint4 *>(xrow0[g] + kc);
+            xv1[g] = *reinterpret_cast<const uint4 *>(xrow1[g] + kc);
+        }
+        // Ordinary (L1-allocating) loads: each load instruction touches 32 rows, and the
+        // instructions that share a 128-byte line of a row are served by one fetch.
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) q[j] = *reinterpret_cast<const uint4 *>(wrow + kc + 8 * j);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto stage_x = [&](char *st, const uint4 (&xv0)[MB], const uint4 (&xv1)[MB]) {
+#pragma unroll
+        for (int g = 0; g < MB; ++g) {
+            *reinterpret_cast<uint4 *>(st + g * kX32Stage + xoff0) = xv0[g];
+            *reinterpret_cast<uint4 *>(st + g * kX32Stage + xoff1) = xv1[g];
+        }
+    };
+    f32x16 acc[MB];
+#pragma unroll
+    for (int g = 0; g < MB; ++g)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[g][e] = 0.f;
+    // Step t: X chunk c = 16 h + 8 kh + t (k = kc + 128 h + 64 kh + 8 t) against weight load t;
+    // the X reads of step t + 1 are issued before step t's MFMAs.
+    auto compute = [&](const char *st, const uint4 (&q)[NQ]) {
+        uint4 ava[MB], avb[MB];
+        auto issue = [&](int t, uint4 (&av)[MB]) {
+            const int c = 16 * half + 8 * kh + t;
+#pragma unroll
+            for (int g = 0; g < MB; ++g)
+                av[g] = *reinterpret_cast<const uint4 *>(st + g * kX32Stage + l32 * 512 + ((c ^ l32) << 4));
+        };
+        auto finish = [&](int t, const uint4 (&av)[MB]) {
+#pragma unroll
+            for (int g = 0; g < MB; ++g)
+                acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av[g]), as_bf16x8(q[t]), acc[g], 0, 0, 0);
+        };
+        issue(0, ava);
+#pragma unroll
+        for (int t = 0; t < NQ; t += 2) {
+            issue(t + 1, avb);
+            __builtin_amdgcn_sched_barrier(0);
+            finish(t, ava);
+            __builtin_amdgcn_sched_barrier(0);
+            if (t + 2 < NQ) issue(t + 2, ava);
+            __builtin_amdgcn_sched_barrier(0);
+            finish(t + 1, avb);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    auto sync = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+
+    uint4 qa[NQ], qb[NQ], xa0[MB], xa1[MB], xb0[MB], xb1[MB];
+    if (nch > 0) {
+        fetch(0, qa, xa0, xa1);
+        for (int c = 0;; c += 2) {
+            stage_x(xst[0], xa0, xa1);
+            if (c + 1 >= nch) {
+                sync();
+                compute(xst[0], qa);
+                break;
+            }
+            fetch(c + 1, qb, xb0, xb1);
+            sync();
+            compute(xst[0], qa);
+            stage_x(xst[1], xb0, xb1);
+            if (c + 2 >= nch) {
+                sync();
+                compute(xst[1], qb);
+                break;
+            }
+            fetch(c + 2, qa, xa0, xa1);
+            sync();
+            compute(xst[1], qb);
+        }
+    }
+    __syncthreads();
+    float *park = reinterpret_cast<float *>(&xst[0][0]);
+    if (kh == 1) {
+#pragma unroll
+        for (int g = 0; g < MB; ++g)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) park[((rg * MB + g) * 16 + e) * 64 + lane] = acc[g][e];
+    }
+    __syncthreads();
+    if (kh == 1) return;
+    if (rowt < n_out) {
+#pragma unroll
+        for (int g = 0; g < MB; ++g)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int64_t p = p0 + 32 * g + 8 * (e >> 2) + 4 * half + (e & 3);
+                if (p >= m) continue;
+                const float v = acc[g][e] + park[((rg * MB + g) * 16 + e) * 64 + lane];
+                if (ws != nullptr) {
+                    ws[(static_cast<int64_t>(blockIdx.y) * m + p) * n_out + rowt] = v;
+                } else if (ofmt == WSL_OUT_F32) {
+                    static_cast<float *>(y)[p * ldy + rowt] = v;
+                } else {
+                    static_cast<uint16_t *>(y)[p * ldy + rowt] = static_cast<uint16_t>(pack_bf16x2(v, 0.f) & 0xffffu);
+                }
+            }
+    }
+}
+
 // ---------------------------------------------------------------- NF4, tiled, M > 32
 // NF4 GEMM over many positions (batch verification, long prefill): the bf16
 // kernel's 256 x 256 tiles, 8 waves of 128 x 64 and 4-stage ring, but the weight
@@ -864,20 +1010,54 @@ static int64_t nf4_k_per_split(int64_t k, int64_t m, int splits) {
     return ((chunks + splits - 1) / splits) * unit;
 }
 
+// bf16: the shared-X kernel for M <= 64 with k % 256 == 0 (one position block: further
+// blocks would re-read the 2-byte weights; same splitting rule as the NF4 one), the
+// tiled kernel otherwise.
+constexpr int64_t kBf16X32MaxM = 64;
+static bool use_bf16_x32(int64_t k, int64_t m) { return m <= kBf16X32MaxM && (k % kX32Chunk) == 0; }
+static int bf16_splits(int64_t n_out, int64_t k, int64_t m) {
+    return use_bf16_x32(k, m) ? nf4_splits(n_out, k, m) : 1;
+}
+
 size_t gemm_ws_bytes(int wfmt, int64_t n_out, int64_t k, int64_t m) {
-    if (wfmt != WSL_W_NF4) return 0;
-    const int splits = nf4_splits(n_out, k, m);
+    const int splits = wfmt == WSL_W_NF4 ? nf4_splits(n_out, k, m) : bf16_splits(n_out, k, m);
     if (splits <= 1) return 0;
     return static_cast<size_t>(splits) * static_cast<size_t>(m) * static_cast<size_t>(n_out) * sizeof(float);
 }
 
 int launch_gemm_bf16(const void *w, int64_t n_out, int64_t k, const void *x, int64_t m, int64_t ldx, void *y,
-                     int ofmt, int64_t ldy, hipStream_t s) {
-    const int64_t tn = (n_out + kBN - 1) / kBN, tm = (m + kBM - 1) / kBM;
-    if (tn * tm > 0x7fffffff / 2) return WSL_E_SHAPE;
-    hipLaunchKernelGGL(gemm_bf16_kernel, dim3(static_cast<unsigned>(tn * tm)), dim3(512), 0, s,
-                       static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(w), m, n_out, k, ldx, y, ofmt,
-                       ldy, static_cast<int>(tm), static_cast<int>(tn));
+                     int ofmt, int64_t ldy, void *ws, size_t ws_bytes, hipStream_t s) {
+    const auto *wp = static_cast<const uint16_t *>(w);
+    const auto *xp = static_cast<const uint16_t *>(x);
+    if (!use_bf16_x32(k, m)) {
+        const int64_t tn = (n_out + kBN - 1) / kBN, tm = (m + kBM - 1) / kBM;
+        if (tn * tm > 0x7fffffff / 2) return WSL_E_SHAPE;
+        hipLaunchKernelGGL(gemm_bf16_kernel, dim3(static_cast<unsigned>(tn * tm)), dim3(512), 0, s, xp, wp, m, n_out, k,
+                           ldx, y, ofmt, ldy, static_cast<int>(tm), static_cast<int>(tn));
+        return WSL_OK;
+    }
+    int splits = bf16_splits(n_out, k, m);
+    if (splits > 1 && (ws == nullptr || ws_bytes < gemm_ws_bytes(WSL_W_BF16, n_out, k, m))) splits = 1;
+    const int64_t chunks = k / kX32Chunk;
+    const int64_t kps = ((chunks + splits - 1) / splits) * kX32Chunk;
+    splits = static_cast<int>((k + kps - 1) / kps);   // no empty trailing split
+    float *wsp = splits > 1 ? static_cast<float *>(ws) : nullptr;
+    const int64_t gx = (n_out + kX32BlockRows - 1) / kX32BlockRows;
+    if (gx > 0x7fffffff) return WSL_E_SHAPE;
+    const dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(splits), static_cast<unsigned>(x32_zblocks(m)));
+    if (x32_mb(m) == 2)
+        hipLaunchKernelGGL((gemm_bf16_x32_kernel<2>), grid, dim3(512), 0, s, wp, n_out, k, xp, m, ldx, y, ofmt, ldy,
+                           wsp, kps);
+    else
+        hipLaunchKernelGGL((gemm_bf16_x32_kernel<1>), grid, dim3(512), 0, s, wp, n_out, k, xp, m, ldx, y, ofmt, ldy,
+                           wsp, kps);
+    if (splits > 1) {
+        const int64_t total = m * n_out;
+        int64_t blocks = (total + 255) / 256;
+        if (blocks > 4096) blocks = 4096;
+        hipLaunchKernelGGL(split_reduce_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, wsp, splits, m,
+                           n_out, y, ofmt, ldy);
+    }
     return WSL_OK;
 }
 

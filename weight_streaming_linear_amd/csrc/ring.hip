@@ -13,7 +13,7 @@ namespace wsl {
 int launch_gemv_bf16(const void *w, int64_t n_out, int64_t k, const void *x, float *y, hipStream_t s);
 int launch_gemv_nf4(const void *w, int64_t n_out, int64_t k, const void *x, float *y, hipStream_t s);
 int launch_gemm_bf16(const void *w, int64_t n_out, int64_t k, const void *x, int64_t m, int64_t ldx, void *y,
-                     int ofmt, int64_t ldy, hipStream_t s);
+                     int ofmt, int64_t ldy, void *ws, size_t ws_bytes, hipStream_t s);
 int launch_gemm_nf4(const void *w, int64_t n_out, int64_t k, const void *x, int64_t m, int64_t ldx, void *y,
                     int ofmt, int64_t ldy, void *ws, size_t ws_bytes, hipStream_t s);
 
@@ -71,7 +71,7 @@ int ring_gemm(int wfmt, int64_t count, const void *const *h_w, const int64_t *n_
                     [&](int64_t i, void *w, hipStream_t s) {
                         return wfmt == WSL_W_NF4
                                    ? launch_gemm_nf4(w, n_out[i], k[i], x[i], m, ldx, y[i], ofmt, ldy, ws, ws_bytes, s)
-                                   : launch_gemm_bf16(w, n_out[i], k[i], x[i], m, ldx, y[i], ofmt, ldy, s);
+                                   : launch_gemm_bf16(w, n_out[i], k[i], x[i], m, ldx, y[i], ofmt, ldy, ws, ws_bytes, s);
                     });
 }
 
