@@ -93,10 +93,22 @@ __device__ __forceinline__ void write_levels(float *lut) {
     }
 }
 
+// Entry i = b * 32 + copy, so a wave's 64 consecutive entries hold two byte values
+// b0 (lanes 0..31) and b0 + 1 (lanes 32..63), both wave-uniform: the four levels come
+// from scalar loads of the constant table and each lane selects its half's pair.
+// (A per-lane index would make every level a vector memory load, each followed by a
+// wait, in the prologue of every workgroup.)  blockDim.x must be a multiple of 64.
 __device__ __forceinline__ void fill_pair_table(char *tab) {
-    for (int i = threadIdx.x; i < kPairTableBytes / 8; i += blockDim.x) {
-        const int b = i >> 5;
-        reinterpret_cast<float2 *>(tab)[i] = make_float2(level(b & 15), level(b >> 4));
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const int nw = static_cast<int>(blockDim.x >> 6);
+    const bool upper = (threadIdx.x & 32) != 0;
+    float2 *t2 = reinterpret_cast<float2 *>(tab) + (threadIdx.x & 63);
+    for (int b0 = 2 * wave; b0 < 256; b0 += 2 * nw) {
+        float lo0 = level(b0 & 15), lo1 = level((b0 + 1) & 15), hi = level(b0 >> 4);   // b0 is even
+        // pinned as scalar values, so the select below is not turned back into a
+        // per-lane table address
+        asm volatile("" : "+s"(lo0), "+s"(lo1), "+s"(hi));
+        t2[b0 * 32] = make_float2(upper ? lo1 : lo0, hi);
     }
 }
 

@@ -276,11 +276,15 @@ __device__ __forceinline__ float nf4_dot32_pair(const uint4 q, const float (&xf)
     return p0 + p1;
 }
 
-__device__ __forceinline__ void load_x32(const uint16_t *__restrict__ x, int64_t kk, bool active, float (&xf)[32]) {
-    uint4 xv[4];
+// 32 bf16 x values from x + kk (zeros when !active), raw and then widened to fp32:
+// issue_x32 lets a prologue start the load before work that does not need x.
+__device__ __forceinline__ void issue_x32(const uint16_t *__restrict__ x, int64_t kk, bool active, uint4 (&xv)[4]) {
     const uint4 *xp = reinterpret_cast<const uint4 *>(x + kk);
 #pragma unroll
     for (int i = 0; i < 4; ++i) xv[i] = active ? xp[i] : make_uint4(0, 0, 0, 0);
+}
+
+__device__ __forceinline__ void widen_x32(const uint4 (&xv)[4], float (&xf)[32]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         xf[8 * i + 0] = bf16_lo(xv[i].x);
@@ -292,6 +296,12 @@ __device__ __forceinline__ void load_x32(const uint16_t *__restrict__ x, int64_t
         xf[8 * i + 6] = bf16_lo(xv[i].w);
         xf[8 * i + 7] = bf16_hi(xv[i].w);
     }
+}
+
+__device__ __forceinline__ void load_x32(const uint16_t *__restrict__ x, int64_t kk, bool active, float (&xf)[32]) {
+    uint4 xv[4];
+    issue_x32(x, kk, active, xv);
+    widen_x32(xv, xf);
 }
 
 // Contiguous chunk of `total` work items owned by XCD `xcd` (of 8).
@@ -330,12 +340,6 @@ __global__ __launch_bounds__(1024) void gemv_nf4_team_kernel(const uint8_t *__re
     __shared__ __align__(16) char tab[TAB == 0 ? 64 : kPairTableBytes];
     __shared__ float red[2][16][R];
     __shared__ float yl[kRowSumCap];
-    if constexpr (TAB == 0) {
-        if (threadIdx.x < 16) reinterpret_cast<float *>(tab)[threadIdx.x] = level(threadIdx.x);
-    } else {
-        fill_pair_table(tab);
-    }
-    __syncthreads();
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int T = (blockDim.x >> 6) / S;
@@ -360,7 +364,6 @@ __global__ __launch_bounds__(1024) void gemv_nf4_team_kernel(const uint8_t *__re
     const uint32_t coff = static_cast<uint32_t>(kkl >> 1);
     const uint32_t gl = static_cast<uint32_t>(kkl >> 6);
     float xf[32];
-    load_x32(x, kkl, active, xf);
 
     auto dot = [&](const uint4 &q) -> float {
         if constexpr (TAB == 0) return nf4_dot32(q, xf, tab, m60);
@@ -412,22 +415,37 @@ __global__ __launch_bounds__(1024) void gemv_nf4_team_kernel(const uint8_t *__re
 
     uint4 qa[R], qb[R];
     SB sa, sb;
+    // The first super-group's loads and the x loads are in flight while the table is
+    // built (x last: the first multiply needs both, so one wait for all is no loss).
+    if (n > 0) fetch(0, qa, sa);
+    uint4 xv[4];
+    issue_x32(x, kkl, active, xv);
+    if constexpr (TAB == 0) {
+        write_levels(reinterpret_cast<float *>(tab));
+    } else {
+        fill_pair_table(tab);
+    }
+    __syncthreads();
+    widen_x32(xv, xf);
     for (jbeg = 0; jbeg < n; jbeg += cap) {
         jend = (jbeg + cap < n) ? jbeg + cap : n;
-        fetch(jbeg, qa, sa);
-        for (int64_t j = jbeg;; j += 2) {   // unrolled by two so that the two buffers swap without copies
-            if (j + 1 >= jend) {
-                consume(j, qa, sa);
-                break;
-            }
+        if (jbeg > 0) fetch(jbeg, qa, sa);
+        int64_t j = jbeg;
+        // Unrolled by two so that the two buffers swap without copies; the loop has its
+        // only exit at the top, so no path reaches the next iteration with a buffer's
+        // loads still pending and the next prefetch is issued without waiting for them.
+        for (; j + 2 < jend; j += 2) {
             fetch(j + 1, qb, sb);
             consume(j, qa, sa);
-            if (j + 2 >= jend) {
-                consume(j + 1, qb, sb);
-                break;
-            }
             fetch(j + 2, qa, sa);
             consume(j + 1, qb, sb);
+        }
+        if (j + 1 < jend) {
+            fetch(j + 1, qb, sb);
+            consume(j, qa, sa);
+            consume(j + 1, qb, sb);
+        } else {
+            consume(j, qa, sa);
         }
         if (park) {
             __syncthreads();
@@ -561,15 +579,18 @@ int launch_gemv_bf16(const void *w, int64_t n_out, int64_t k, const void *x, flo
 }
 
 // NF4 plan.  k <= 32768: the team kernel with S = ceil(k / 2048) waves per team.
-// Large matrices (>= 64 Mi weights) take the pair table, 2 rows per row group and
-// 16 / S teams in one workgroup per CU (the 64 KB table leaves room for one); the
-// others the 16-entry table (no 64 KB table to build per launch), 4 rows (2 up to
-// 4096 rows), at most 2 teams, and two workgroups per CU -- three below 32 Mi
-// weights when that stays within 16 waves per CU.  The grid is a multiple of 8
-// (one share per XCD) and never larger than needed.  k > 32768: the wide kernel.
-// (Measured on the decode shapes: 8192x6144 runs 10.5 us with the pair table and
-// 9.8 us with the 16-entry table; 4096x4096 5.55 us with 4 rows and two workgroups
-// per CU, 5.2 us with 2 rows and three.)
+// Large matrices (>= 32 Mi weights; >= 96 Mi when k <= 4096, where the 64 KB table
+// is built for few steps) take the pair table, 2 rows per row group and up to 16 / S
+// teams in one workgroup per CU, one team fewer when that makes the waves a multiple
+// of 4 (k = 6144: 4 teams of 3 waves, 3 per SIMD, instead of 5 teams); the others
+// the 16-entry table, 4 rows (2 up to 4096 rows), at most 2 teams, and two
+// workgroups per CU -- three below 32 Mi weights when that stays within 16 waves per
+// CU.  The grid is a multiple of 8 (one share per XCD) and never larger than
+// needed.  k > 32768: the wide kernel.
+// (Measured per launch on the decode shapes: 8192x6144 8.8 us with the pair table
+// and 4 teams, 9.9 us with the 16-entry table; 32768x6144 21.7 us with 4 teams,
+// 22.4 us with 5; 4096x4096 5.3 us with the 16-entry table, 2 rows and three
+// workgroups per CU, 5.6-5.8 us with the pair table.)
 struct Nf4GemvPlan {
     bool wide, pair;
     int rows, S, T;
@@ -592,10 +613,12 @@ static Nf4GemvPlan plan_gemv_nf4(int64_t n_out, int64_t k) {
     p.S = static_cast<int>(slices);
     int64_t per_cu;
     const int64_t weights = n_out * k;
-    if (weights >= (static_cast<int64_t>(64) << 20)) {
+    if (weights >= (static_cast<int64_t>(p.S <= 2 ? 96 : 32) << 20)) {
         p.pair = true;
         p.rows = 2;
         p.T = 16 / p.S;
+        // a multiple of 4 waves when one team fewer gives it: equal waves per SIMD
+        if ((p.S * p.T) % 4 != 0 && p.T > 1 && (p.S * (p.T - 1)) % 4 == 0) --p.T;
         per_cu = 1;
     } else {
         p.pair = false;
