@@ -373,7 +373,12 @@ __global__ __launch_bounds__(256) void gemm_nf4_kernel(const uint8_t *__restrict
 //   * lane (n, h) owns the codes of row n for k in [kc + 128h, kc + 128h + 128)
 //     -- 16 MFMA k-steps of 8 codes, 64 bytes -- of which its wave takes steps
 //     [16 kh / KH, 16 (kh + 1) / KH), loaded one chunk ahead with the scales of
-//     those groups as ordinary (L1-allocating) loads;
+//     those groups.  When the workgroup is the matrix's only position block (CS),
+//     the chunk's codes are instead copied with whole-line streaming loads into an
+//     LDS stage and each lane reads its pieces from there: on 27648x5120 at M = 32
+//     this runs 28.5 us against 32.7 us for per-lane cached loads, whose lines are
+//     split over four instructions.  With several position blocks the per-lane
+//     cached loads stay (the blocks share the lines through the caches);
 //   * each k-step restores 8 codes through the replicated pair table into a
 //     bf16 B fragment t = bf16(fp32(level * s)) and issues one
 //     v_mfma_f32_32x32x16_bf16 against the A fragment X[i][same 8 k] from LDS;
@@ -389,7 +394,7 @@ __global__ __launch_bounds__(256) void gemm_nf4_kernel(const uint8_t *__restrict
 constexpr int kX32Chunk = 256;
 constexpr int kX32Stage = 32 * kX32Chunk * 2;
 
-template <int KH, int MB>
+template <int KH, int MB, int CS>
 __global__ __launch_bounds__(512) void gemm_nf4_x32_kernel(const uint8_t *__restrict__ packed, int64_t n_out,
                                                            int64_t k, const uint16_t *__restrict__ x, int64_t m,
                                                            int64_t ldx, void *__restrict__ y, int ofmt, int64_t ldy,
@@ -400,6 +405,7 @@ __global__ __launch_bounds__(512) void gemm_nf4_x32_kernel(const uint8_t *__rest
     constexpr int NG = 2 / KH;        // scales per lane per chunk
     __shared__ __align__(16) char tab[kPairTableBytes];
     __shared__ __align__(16) char xst[2][MB * kX32Stage];   // position group g at g * kX32Stage
+    __shared__ __align__(16) char cst[CS ? 2 : 1][CS ? 32 * RG * (kX32Chunk / 2) : 16];   // CS: the chunk's codes
     fill_pair_table(tab);
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -416,7 +422,26 @@ __global__ __launch_bounds__(512) void gemm_nf4_x32_kernel(const uint8_t *__rest
     uint32_t ad[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) ad[i] = static_cast<uint32_t>(lane & 31) << 3;
+    // Codes.  CS = 0: lane (n, h) loads its own 16-byte pieces of row n (ordinary
+    // loads: 4 lanes share each 128-byte line, and the line serves the other
+    // position blocks of the matrix too).  CS = 1 (the only position block): copy j
+    // of thread t moves 16-byte segment t % 8 of row 64 j + t / 8 of the chunk -- 8
+    // threads per 128-byte row, whole lines per wave instruction -- with loads that
+    // bypass the caches, into LDS at row * 128 + 16 (segment ^ (row % 8)); the lane
+    // reads its pieces back from there (conflict-free: 8 consecutive rows of one
+    // segment fall in distinct bank groups).
     const uint8_t *crow = packed + row * rowbytes + 64 * half + (64 / KH) * kh;
+    const uint8_t *ccp[NQ];
+    int coff[NQ], lcoff[NQ];
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+        const int r = 64 * j + (tid >> 3), sg = tid & 7;
+        const int64_t rt = static_cast<int64_t>(blockIdx.x) * (32 * RG) + r;
+        ccp[j] = packed + (rt < n_out ? rt : n_out - 1) * rowbytes + 16 * sg;
+        coff[j] = r * 128 + ((sg ^ (r & 7)) << 4);
+        const int lr = rg * 32 + l32, lsg = 4 * half + NQ * kh + j;
+        lcoff[j] = lr * 128 + ((lsg ^ (lr & 7)) << 4);
+    }
     const int64_t srem = n_out - ((row >> 4) << 4);
     const int64_t srb = srem < 16 ? srem : 16;
     const uint16_t *srow = scales + (row >> 4) * 16 * groups + (row & 15);   // scale (row, g) at srow[g * srb]
@@ -442,19 +467,25 @@ __global__ __launch_bounds__(512) void gemm_nf4_x32_kernel(const uint8_t *__rest
             xv0[g] = *reinterpret_cast<const uint4 *>(xrow0[g] + kc);
             xv1[g] = *reinterpret_cast<const uint4 *>(xrow1[g] + kc);
         }
-        const uint8_t *src = crow + (kc >> 1);
 #pragma unroll
-        for (int j = 0; j < NQ; ++j) q[j] = *reinterpret_cast<const uint4 *>(src + 16 * j);
+        for (int j = 0; j < NQ; ++j) {
+            if constexpr (CS) q[j] = load_stream16(ccp[j] + (kc >> 1));
+            else q[j] = *reinterpret_cast<const uint4 *>(crow + (kc >> 1) + 16 * j);
+        }
         const int64_t g0 = (kc >> 6) + 2 * half + (KH == 2 ? kh : 0);
 #pragma unroll
         for (int j = 0; j < NG; ++j) sr[j] = srow[(g0 + j) * srb];
         __builtin_amdgcn_sched_barrier(0);
     };
-    auto stage_x = [&](char *st, const uint4 (&xv0)[MB], const uint4 (&xv1)[MB]) {
+    auto stage_x = [&](char *st, char *cs, const uint4 (&q)[NQ], const uint4 (&xv0)[MB], const uint4 (&xv1)[MB]) {
 #pragma unroll
         for (int g = 0; g < MB; ++g) {
             *reinterpret_cast<uint4 *>(st + g * kX32Stage + xoff0) = xv0[g];
             *reinterpret_cast<uint4 *>(st + g * kX32Stage + xoff1) = xv1[g];
+        }
+        if constexpr (CS) {
+#pragma unroll
+            for (int j = 0; j < NQ; ++j) *reinterpret_cast<uint4 *>(cs + coff[j]) = q[j];
         }
     };
     f32x16 acc[MB];
@@ -468,7 +499,13 @@ __global__ __launch_bounds__(512) void gemm_nf4_x32_kernel(const uint8_t *__rest
     uint32_t adb[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) adb[i] = ad[i];
-    auto compute = [&](const char *st, const uint4 (&q)[NQ], const uint32_t (&sr)[NG]) {
+    auto compute = [&](const char *st, const char *cs, const uint4 (&qr)[NQ], const uint32_t (&sr)[NG]) {
+        uint4 q[NQ];
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) {
+            if constexpr (CS) q[j] = *reinterpret_cast<const uint4 *>(cs + lcoff[j]);
+            else q[j] = qr[j];
+        }
         float sv[NG];
 #pragma unroll
         for (int j = 0; j < NG; ++j) sv[j] = f16_to_f32(sr[j]);
@@ -522,24 +559,24 @@ __global__ __launch_bounds__(512) void gemm_nf4_x32_kernel(const uint8_t *__rest
     if (nch > 0) {
         fetch(0, qa, sa, xa0, xa1);
         for (int c = 0;; c += 2) {
-            stage_x(xst[0], xa0, xa1);
+            stage_x(xst[0], cst[0], qa, xa0, xa1);
             if (c + 1 >= nch) {
                 sync();
-                compute(xst[0], qa, sa);
+                compute(xst[0], cst[0], qa, sa);
                 break;
             }
             fetch(c + 1, qb, sb, xb0, xb1);
             sync();
-            compute(xst[0], qa, sa);
-            stage_x(xst[1], xb0, xb1);
+            compute(xst[0], cst[0], qa, sa);
+            stage_x(xst[1], cst[CS], qb, xb0, xb1);
             if (c + 2 >= nch) {
                 sync();
-                compute(xst[1], qb, sb);
+                compute(xst[1], cst[CS], qb, sb);
                 break;
             }
             fetch(c + 2, qa, sa, xa0, xa1);
             sync();
-            compute(xst[1], qb, sb);
+            compute(xst[1], cst[CS], qb, sb);
         }
     }
     if constexpr (KH == 2) {
@@ -1082,12 +1119,18 @@ int launch_gemm_nf4(const void *w, int64_t n_out, int64_t k, const void *x, int6
         const int64_t gx = (n_out + kX32BlockRows - 1) / kX32BlockRows;
         if (gx > 0x7fffffff) return WSL_E_SHAPE;
         const dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(splits), static_cast<unsigned>(x32_zblocks(m)));
-        if (x32_mb(m) == 2)
-            hipLaunchKernelGGL((gemm_nf4_x32_kernel<kX32Kh, 2>), grid, dim3(512), 0, s, wp, n_out, k, xp, m, ldx, y,
+        // one position block: codes staged through LDS from streaming loads
+        if (x32_zblocks(m) == 1) {
+            if (x32_mb(m) == 2)
+                hipLaunchKernelGGL((gemm_nf4_x32_kernel<kX32Kh, 2, 1>), grid, dim3(512), 0, s, wp, n_out, k, xp, m, ldx,
+                                   y, ofmt, ldy, wsp, kps);
+            else
+                hipLaunchKernelGGL((gemm_nf4_x32_kernel<kX32Kh, 1, 1>), grid, dim3(512), 0, s, wp, n_out, k, xp, m, ldx,
+                                   y, ofmt, ldy, wsp, kps);
+        } else {
+            hipLaunchKernelGGL((gemm_nf4_x32_kernel<kX32Kh, 2, 0>), grid, dim3(512), 0, s, wp, n_out, k, xp, m, ldx, y,
                                ofmt, ldy, wsp, kps);
-        else
-            hipLaunchKernelGGL((gemm_nf4_x32_kernel<kX32Kh, 1>), grid, dim3(512), 0, s, wp, n_out, k, xp, m, ldx, y,
-                               ofmt, ldy, wsp, kps);
+        }
     } else {
         const int64_t gx = (n_out + kNf4RowsPerWg - 1) / kNf4RowsPerWg;
         const int64_t gz = (m + 31) / 32;
