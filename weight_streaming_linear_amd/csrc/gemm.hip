@@ -982,17 +982,60 @@ __global__ __launch_bounds__(512) void gemm_nf4_tiled_kernel(const uint16_t *__r
         }
 }
 
-// Sum split partials in split order (fixed, so the result is deterministic).
+// Sum split partials in split order (fixed, so the result is deterministic).  A
+// thread takes 4 consecutive outputs of one row (n_out % 4 == 0; one output
+// otherwise) and issues the loads of up to 8 splits before adding them, so their
+// latencies overlap instead of adding up.
+__device__ __forceinline__ void store_out(void *y, int ofmt, int64_t idx, float v) {
+    if (ofmt == WSL_OUT_F32) static_cast<float *>(y)[idx] = v;
+    else static_cast<uint16_t *>(y)[idx] = static_cast<uint16_t>(pack_bf16x2(v, 0.f) & 0xffffu);
+}
+
 __global__ __launch_bounds__(256) void split_reduce_kernel(const float *__restrict__ ws, int splits, int64_t m,
                                                            int64_t n_out, void *__restrict__ y, int ofmt, int64_t ldy) {
     const int64_t total = m * n_out;
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
-         i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    if ((n_out & 3) == 0) {
+        const float4 *w4 = reinterpret_cast<const float4 *>(ws);
+        const int64_t t4 = total >> 2;
+        for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < t4; i += stride) {
+            float4 v = w4[i];
+            for (int s0 = 1; s0 < splits; s0 += 8) {
+                float4 t[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    if (s0 + j < splits) t[j] = w4[static_cast<int64_t>(s0 + j) * t4 + i];
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    if (s0 + j < splits) {
+                        v.x += t[j].x;
+                        v.y += t[j].y;
+                        v.z += t[j].z;
+                        v.w += t[j].w;
+                    }
+            }
+            const int64_t e = i << 2, row = e / n_out, col = e - row * n_out;
+            const int64_t o = row * ldy + col;
+            store_out(y, ofmt, o, v.x);
+            store_out(y, ofmt, o + 1, v.y);
+            store_out(y, ofmt, o + 2, v.z);
+            store_out(y, ofmt, o + 3, v.w);
+        }
+        return;
+    }
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += stride) {
         float v = ws[i];
-        for (int sidx = 1; sidx < splits; ++sidx) v += ws[static_cast<int64_t>(sidx) * total + i];
+        for (int s0 = 1; s0 < splits; s0 += 8) {
+            float t[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (s0 + j < splits) t[j] = ws[static_cast<int64_t>(s0 + j) * total + i];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (s0 + j < splits) v += t[j];
+        }
         const int64_t row = i / n_out, col = i - row * n_out;
-        if (ofmt == WSL_OUT_F32) static_cast<float *>(y)[row * ldy + col] = v;
-        else static_cast<uint16_t *>(y)[row * ldy + col] = static_cast<uint16_t>(pack_bf16x2(v, 0.f) & 0xffffu);
+        store_out(y, ofmt, row * ldy + col, v);
     }
 }
 
@@ -1089,8 +1132,8 @@ int launch_gemm_bf16(const void *w, int64_t n_out, int64_t k, const void *x, int
         hipLaunchKernelGGL((gemm_bf16_x32_kernel<1>), grid, dim3(512), 0, s, wp, n_out, k, xp, m, ldx, y, ofmt, ldy,
                            wsp, kps);
     if (splits > 1) {
-        const int64_t total = m * n_out;
-        int64_t blocks = (total + 255) / 256;
+        const int64_t items = (n_out % 4 == 0) ? m * n_out / 4 : m * n_out;
+        int64_t blocks = (items + 255) / 256;
         if (blocks > 4096) blocks = 4096;
         hipLaunchKernelGGL(split_reduce_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, wsp, splits, m,
                            n_out, y, ofmt, ldy);
@@ -1140,8 +1183,8 @@ int launch_gemm_nf4(const void *w, int64_t n_out, int64_t k, const void *x, int6
                            wsp, kps);
     }
     if (splits > 1) {
-        const int64_t total = m * n_out;
-        int64_t blocks = (total + 255) / 256;
+        const int64_t items = (n_out % 4 == 0) ? m * n_out / 4 : m * n_out;
+        int64_t blocks = (items + 255) / 256;
         if (blocks > 4096) blocks = 4096;
         hipLaunchKernelGGL(split_reduce_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, wsp, splits, m,
                            n_out, y, ofmt, ldy);
