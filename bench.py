@@ -25,9 +25,15 @@ the NF4 GEMV 4096x4096, the 48-layer NF4 decode sweep (hidden 6144), the NF4
 prefill GEMM at 32 positions (5120 <-> 27648) and the bf16 batch-verification
 GEMM at 8192 positions (5120 <-> 17408).
 
+GEMV figures are also given against ``read_ceiling``, the rate of a read-only
+streaming kernel (``wsl_stream_read``) over 2 GiB on the same box.
+
 Protocol (IPE page, "How it is benchmarked"; deep-fold README, lab-plate
 rules): a failed correctness check stops the run before timing; warm-up and
-graph capture are outside every timer.
+graph capture are outside every timer.  By default the whole run is repeated in
+three fresh processes, one after another: the line is the first run's with the
+headline value and ms_per_step replaced by the medians, and ``repeats`` holds
+every run's figures with their median, interquartile range and A/A spread.
 """
 
 import argparse
@@ -136,6 +142,27 @@ def capture(launches):
             l.fn()
     torch.cuda.synchronize()
     return g
+
+
+READ_CEILING = {}
+
+
+def measure_read_ceiling(reps=10, nbytes=2 << 30):
+    """Streaming-read ceiling of the box: wsl_stream_read (16-byte loads that bypass the
+    caches, 4 KB of consecutive bytes per wave and iteration) over a 2 GiB buffer, 8x the
+    MALL, timed as one block of launches between HIP events."""
+    import torch
+    import weight_streaming_linear_amd as wsl
+    if "gbs" not in READ_CEILING:
+        buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+        sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+        us = time_block([Launch(lambda: wsl.stream_read(buf, sink))], reps, 3)
+        READ_CEILING.update({"gbs": round(nbytes / 1e3 / us, 1), "buffer_bytes": nbytes, "avg_launch_us": round(us, 2),
+                             "frac_hbm": round(nbytes / 1e3 / us / HBM_PEAK_GBS, 4),
+                             "what": "wsl_stream_read over a 2 GiB buffer (read-only streaming kernel)"})
+        del buf
+        torch.cuda.empty_cache()
+    return READ_CEILING
 
 
 def time_graphs(graphs, k_steps, warmup):
@@ -294,7 +321,8 @@ def run_nf4_gemv_4096(k_steps, warmup, copies=128):
                      flops=2 * n * k, name="nf4_gemv_4096")] for p in packs]
     out = summarize(time_step_launches(steps, k_steps, warmup))
     out.update({"workload": "NF4 GEMV 4096x4096, fp32 out", "rotation_copies": copies, "sanity_worst_ratio": worst,
-                "frac_hbm": out["kernel_gbs"] / HBM_PEAK_GBS})
+                "frac_hbm": out["kernel_gbs"] / HBM_PEAK_GBS,
+                "frac_read_ceiling": out["kernel_gbs"] / measure_read_ceiling()["gbs"]})
     del packs
     torch.cuda.empty_cache()
     return out
@@ -353,6 +381,7 @@ def run_nf4_decode_sweep(k_steps, warmup, layers=48):
         "graph_ms_per_token": graph_ms, "graph_tokens_per_s": 1e3 / graph_ms,
         "graph_gbs": out["bytes_per_step"] / 1e9 / (graph_ms / 1e3),
         "frac_hbm_graph": out["bytes_per_step"] / 1e9 / (graph_ms / 1e3) / HBM_PEAK_GBS,
+        "frac_read_ceiling_graph": out["bytes_per_step"] / 1e9 / (graph_ms / 1e3) / measure_read_ceiling()["gbs"],
         "launch_gap_us_per_launch": 1e3 * (graph_ms - out["kernel_ms_per_step"]) / out["launches_per_step"],
         "decode_step_graph": {"ms_per_token": step_ms, "tokens_per_s": 1e3 / step_ms,
                               "what": "embedding gather (device-resident token id) + 192 GEMVs + id advance, one graph",
@@ -788,6 +817,70 @@ def trace_summarize(run_dir, title, command):
 
 
 # ---------------------------------------------------------------- main
+# Figures summarised across repeats: (label, path of keys into the JSON line).
+REPEAT_FIGURES = [
+    ("value_gbs", ("value",)),
+    ("ms_per_step", ("ms_per_step",)),
+    ("dominant_kernel_gbs", ("roofline", "achieved")),
+    ("read_ceiling_gbs", ("read_ceiling", "gbs")),
+    ("nf4_sweep_graph_ms_per_token", ("paths", "nf4_decode_sweep_48x6144", "graph_ms_per_token")),
+    ("nf4_gemv_4096_us", ("paths", "nf4_gemv_4096", "launches", "nf4_gemv_4096", "avg_us")),
+    ("nf4_gemm_m32_tflops", ("paths", "nf4_prefill_gemm_m32", "kernel_tflops")),
+    ("bf16_gemm_m8192_tflops", ("paths", "bf16_verify_gemm_m8192", "kernel_tflops")),
+    ("nf4_gemm_m8192_tflops", ("paths", "nf4_verify_gemm_m8192", "kernel_tflops")),
+]
+
+
+def _dig(d, keys):
+    for k in keys:
+        if not isinstance(d, dict) or k not in d:
+            return None
+        d = d[k]
+    return d if isinstance(d, (int, float)) else None
+
+
+def run_repeats(args):
+    """The same run in args.repeats fresh processes, one at a time (this process never
+    touches the GPU).  The printed line is the first run's, with value and ms_per_step
+    replaced by the medians over the runs, plus a `repeats` record: for the headline and
+    the main path figures every run's value, the median, the interquartile range and the
+    A/A spread (max - min over the median: the runs are identical, so this is the noise
+    floor the differences between versions have to exceed).  Only the first run times the
+    CPU oracle."""
+    import subprocess
+    lines = []
+    for r in range(args.repeats):
+        cmd = [sys.executable, os.path.abspath(__file__), "--repeats", "1", "--steps", str(args.steps),
+               "--warmup", str(args.warmup)]
+        if args.no_paths:
+            cmd.append("--no-paths")
+        if args.only:
+            cmd += ["--only", args.only]
+        if args.no_cpu_baseline or r > 0:
+            cmd.append("--no-cpu-baseline")
+        log(f"repeat {r + 1}/{args.repeats} in a fresh process")
+        p = subprocess.run(cmd, stdout=subprocess.PIPE, text=True)
+        if p.returncode != 0:
+            log(f"repeat {r + 1} ended with status {p.returncode}")
+            return p.returncode
+        lines.append(json.loads(p.stdout.strip().splitlines()[-1]))
+    rec = {"processes": len(lines), "figures": {}}
+    for label, keys in REPEAT_FIGURES:
+        vals = [_dig(l, keys) for l in lines]
+        if any(v is None for v in vals):
+            continue
+        med = float(np.median(vals))
+        q75, q25 = np.percentile(vals, [75, 25])
+        rec["figures"][label] = {"runs": vals, "median": med, "iqr": float(q75 - q25),
+                                 "aa_spread": float((max(vals) - min(vals)) / med) if med else None}
+    out = lines[0]
+    out["value"] = round(rec["figures"]["value_gbs"]["median"], 2)
+    out["ms_per_step"] = round(rec["figures"]["ms_per_step"]["median"], 6)
+    out["repeats"] = rec
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -795,6 +888,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-paths", action="store_true", help="only the headline workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--repeats", type=int, default=3,
+                    help="fresh processes to run (one after another); the line reports medians, IQR and the "
+                         "A/A spread over them (1: a single run in this process)")
     ap.add_argument("--only", default="", help="comma list of paths: " + ",".join(n for n, _ in PATHS))
     ap.add_argument("--traffic-probe", action="store_true", help="launch sequence for rocprofv3 counter runs")
     ap.add_argument("--traffic-summarize", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -813,6 +909,9 @@ def main():
               "single MI355X and has no multi-GPU path. Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
+    if args.repeats > 1 and not args.traffic_probe:
+        sys.exit(run_repeats(args))
+
     import torch
     import weight_streaming_linear_amd as wsl
     wsl.lib()
@@ -828,6 +927,9 @@ def main():
     achieved = head["dominant_bytes"] / 1e3 / head["dominant_avg_us"]
     log(f"bf16 decode layer: {head['ms_per_step'] * 1e3:.1f} us/step (graph), {value:.0f} GB/s; "
         f"kernels {per_launch['kernel_ms_per_step'] * 1e3:.1f} us/step; gate_up kernel {achieved:.0f} GB/s")
+
+    ceiling = measure_read_ceiling()
+    log(f"streaming-read ceiling: {ceiling['gbs']:.0f} GB/s")
 
     paths = {}
     if not args.no_paths:
@@ -872,7 +974,10 @@ def main():
             "bytes_per_launch": head["dominant_bytes"],
             "avg_launch_us": round(head["dominant_avg_us"], 3),
         },
+        "read_ceiling": ceiling,
         "headline_detail": {
+            "frac_read_ceiling": round(value / ceiling["gbs"], 4),
+            "dominant_frac_read_ceiling": round(achieved / ceiling["gbs"], 4),
             "sanity_worst_ratio": head["sanity_worst_ratio"],
             "kernel_ms_per_step": round(per_launch["kernel_ms_per_step"], 6),
             "launches": per_launch["launches"],

@@ -240,6 +240,24 @@ int linear_gemm_streamed(int wfmt, int64_t count, const void *const *h_w, const 
                          void *d_ws, size_t ws_bytes, void *const *d_slot, size_t slot_bytes,
                          void *copy_stream, void *compute_stream, void *const *events);
 
+/*
+ * wsl_stream_read -- measurement aid, not part of the linear path: a read-only
+ * kernel that reads bytes bytes at d_buf once, with the access form of the GEMV
+ * weight stream (16-byte loads that bypass the caches, 1 KB of consecutive bytes
+ * per wave instruction, 4 KB per wave in flight), so that its rate over a
+ * buffer much larger than the caches is the streaming-read ceiling the GB/s
+ * figures are compared with (a figure the pages do not give: measured on the box).
+ * d_buf    device, 16-byte aligned; bytes a multiple of 16.  bytes == 0 enqueues
+ *          nothing and returns 0.
+ * d_sink   device uint32 [1], 4-byte aligned: each lane XOR-combines the words it
+ *          reads and writes the result to d_sink[0] only if it equals 0x9e3779b9,
+ *          so the kernel writes nothing in practice (a test plants that value to
+ *          check that every word is read).
+ * Returns WSL_E_NULL, WSL_E_SHAPE (bytes % 16 != 0), WSL_E_ALIGN, WSL_E_DEVICE or
+ * WSL_E_LAUNCH as the other entry points do; asynchronous on stream.
+ */
+int wsl_stream_read(const void *d_buf, size_t bytes, uint32_t *d_sink, void *stream);
+
 /* wsl_strerror -- static description of a status code (never NULL). */
 const char *wsl_strerror(int code);
 

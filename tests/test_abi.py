@@ -73,6 +73,10 @@ def test_argument_errors_return_before_any_launch():
     assert L.linear_gemv_streamed(wsl.WSL_W_NF4, 1, one, shp, shp, one, one, two, 100, None, None, four) == 7
     assert L.linear_gemm_streamed(wsl.WSL_W_NF4, 1, one, shp, shp, one, 0, 64, one, 0, 64, None, 0, two, 4096,
                                   None, None, four) == 2
+    assert L.wsl_stream_read(a, 0, None, None) == 0
+    assert L.wsl_stream_read(None, 16, a, None) == 1
+    assert L.wsl_stream_read(a, 24, a, None) == 2
+    assert L.wsl_stream_read(odd, 16, a, None) == 3
     assert wsl.wsl_strerror(7).startswith("tile")
     assert L.nf4_codebook(None) == 1
 

@@ -29,7 +29,7 @@ WSL_STATUS_OVERFLOW = 2
 EXPORTED = [
     "nf4_packed_bytes", "nf4_codebook", "nf4_pack", "nf4_dequant_tile", "linear_gemv",
     "linear_gemm_workspace_bytes", "linear_gemm", "nf4_embed_rows", "linear_gemv_streamed",
-    "linear_gemm_streamed", "wsl_strerror",
+    "linear_gemm_streamed", "wsl_stream_read", "wsl_strerror",
 ]
 
 
@@ -73,6 +73,8 @@ def lib():
     L.linear_gemm_streamed.argtypes = [ctypes.c_int, i64, vp, vp, vp, vp, i64, i64, vp, ctypes.c_int, i64, vp, sz, vp,
                                        sz, vp, vp, vp]
     L.linear_gemm_streamed.restype = ctypes.c_int
+    L.wsl_stream_read.argtypes = [vp, sz, vp, vp]
+    L.wsl_stream_read.restype = ctypes.c_int
     L.wsl_strerror.argtypes = [ctypes.c_int]
     L.wsl_strerror.restype = ctypes.c_char_p
     _lib = L
@@ -184,6 +186,14 @@ def linear_gemm(w, x, y=None, wfmt=None, n_out=None, k=None, ofmt=WSL_OUT_F32, w
                            _ptr(workspace), ws_bytes, _stream(stream))
     _check(rc, "linear_gemm")
     return y
+
+
+def stream_read(buf, sink, stream=None):
+    """Read every byte of the device tensor ``buf`` once (wsl_stream_read): the
+    streaming-read ceiling probe.  ``sink`` is a device int32/uint32 tensor of one
+    element, written only if a lane's words XOR to 0x9e3779b9."""
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib().wsl_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(stream)), "wsl_stream_read")
 
 
 # ---------------------------------------------------------------- copy ring

@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libwsl.so")
 
-HIP_SOURCES = ["api.hip", "pack.hip", "gemv.hip", "gemm.hip", "embed.hip", "ring.hip"]
+HIP_SOURCES = ["api.hip", "pack.hip", "gemv.hip", "gemm.hip", "embed.hip", "ring.hip", "probe.hip"]
 CXX_SOURCES = ["validate.cpp"]
 
 HIP_FLAGS = [

@@ -24,6 +24,7 @@ int ring_gemv(int wfmt, int64_t count, const void *const *h_w, const int64_t *n_
 int ring_gemm(int wfmt, int64_t count, const void *const *h_w, const int64_t *n_out, const int64_t *k,
               const void *const *x, int64_t m, int64_t ldx, void *const *y, int ofmt, int64_t ldy, void *ws,
               size_t ws_bytes, void *const *slot, hipStream_t copy, hipStream_t compute, void *const *events);
+int launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t s);
 int launch_embed_rows(const void *packed, int64_t n_rows, int64_t k, const int64_t *ids, int64_t count, void *out,
                       int ofmt, int64_t ld_out, uint32_t *status, hipStream_t s);
 
@@ -143,6 +144,17 @@ int linear_gemm_streamed(int wfmt, int64_t count, const void *const *h_w, const 
     if ((rc = wsl::check_pinned(count, h_w)) != WSL_OK) return rc;
     return wsl::ring_gemm(wfmt, count, h_w, n_out, k, d_x, m, ldx, d_y, ofmt, ldy, d_ws, ws_bytes, d_slot,
                           wsl::as_stream(copy_stream), wsl::as_stream(compute_stream), events);
+}
+
+int wsl_stream_read(const void *d_buf, size_t bytes, uint32_t *d_sink, void *stream) {
+    if (bytes == 0) return WSL_OK;
+    if (!d_buf || !d_sink) return WSL_E_NULL;
+    if ((bytes % 16) != 0) return WSL_E_SHAPE;
+    if ((reinterpret_cast<uintptr_t>(d_buf) % 16) != 0 || (reinterpret_cast<uintptr_t>(d_sink) % 4) != 0)
+        return WSL_E_ALIGN;
+    int rc;
+    if ((rc = wsl::device_ok()) != WSL_OK) return rc;
+    return wsl::after_launch(wsl::launch_stream_read(d_buf, bytes, d_sink, wsl::as_stream(stream)));
 }
 
 const char *wsl_strerror(int code) {
