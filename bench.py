@@ -165,6 +165,22 @@ def measure_read_ceiling(reps=10, nbytes=2 << 30):
     return READ_CEILING
 
 
+LAUNCH_FLOOR = {}
+
+
+def measure_launch_floor(reps=200):
+    """t0: the block-timed duration of a launch that does almost nothing (wsl_stream_read of
+    16 bytes: one workgroup), the fixed cost every kernel of the path pays on this machine."""
+    import torch
+    import weight_streaming_linear_amd as wsl
+    if "us" not in LAUNCH_FLOOR:
+        buf = torch.zeros(16, dtype=torch.uint8, device="cuda")
+        sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+        LAUNCH_FLOOR["us"] = round(time_block([Launch(lambda: wsl.stream_read(buf, sink))], reps, 10), 3)
+        LAUNCH_FLOOR["what"] = "block-timed wsl_stream_read of 16 bytes (one workgroup)"
+    return LAUNCH_FLOOR
+
+
 def time_graphs(graphs, k_steps, warmup):
     """Replay graphs[i % len] for `warmup` untimed and k_steps timed steps; wall ms."""
     import torch
@@ -320,6 +336,12 @@ def run_nf4_gemv_4096(k_steps, warmup, copies=128):
     steps = [[Launch(lambda p=p: wsl.linear_gemv(p, x, y=y, wfmt=wsl.WSL_W_NF4, n_out=n, k=k), nbytes=nb,
                      flops=2 * n * k, name="nf4_gemv_4096")] for p in packs]
     out = summarize(time_step_launches(steps, k_steps, warmup))
+    t0 = measure_launch_floor()["us"]
+    us = out["launches"]["nf4_gemv_4096"]["avg_us"]
+    out["launch_floor"] = {"t0_us": t0, "ideal_us_at_8tbs": round(nb / 8e12 * 1e6, 3),
+                           "us_above_t0": round(us - t0, 3),
+                           "gbs_above_t0": round(nb / 1e3 / (us - t0), 1) if us > t0 else None,
+                           "bytes_for_75pct_at_this_t0": round(3 * t0 * 1e-6 * HBM_PEAK_GBS * 1e9)}
     out.update({"workload": "NF4 GEMV 4096x4096, fp32 out", "rotation_copies": copies, "sanity_worst_ratio": worst,
                 "frac_hbm": out["kernel_gbs"] / HBM_PEAK_GBS,
                 "frac_read_ceiling": out["kernel_gbs"] / measure_read_ceiling()["gbs"]})
@@ -382,6 +404,7 @@ def run_nf4_decode_sweep(k_steps, warmup, layers=48):
         "graph_gbs": out["bytes_per_step"] / 1e9 / (graph_ms / 1e3),
         "frac_hbm_graph": out["bytes_per_step"] / 1e9 / (graph_ms / 1e3) / HBM_PEAK_GBS,
         "frac_read_ceiling_graph": out["bytes_per_step"] / 1e9 / (graph_ms / 1e3) / measure_read_ceiling()["gbs"],
+        "launch_floor_ms_per_token": round(out["launches_per_step"] * measure_launch_floor()["us"] / 1e3, 4),
         "launch_gap_us_per_launch": 1e3 * (graph_ms - out["kernel_ms_per_step"]) / out["launches_per_step"],
         "decode_step_graph": {"ms_per_token": step_ms, "tokens_per_s": 1e3 / step_ms,
                               "what": "embedding gather (device-resident token id) + 192 GEMVs + id advance, one graph",
