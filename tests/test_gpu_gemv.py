@@ -52,11 +52,12 @@ def _sample_rows(n, rng, count):
     return np.unique(np.clip(np.concatenate([np.array(edges), rng.integers(0, n, count)]), 0, n - 1))
 
 
-# Decode sweep with hidden size 6144: gate/up 6144 -> 32768 and down 16384 -> 6144; plus ragged
-# large shapes (odd row count, k not a multiple of 2048).  The two sweep shapes and 12291x6208
-# take the pair-table kernel (>= 64 Mi weights), the others the 16-entry table.
+# Decode sweep with hidden size 6144: gate/up 6144 -> 32768, down 16384 -> 6144, qkv 6144 -> 8192,
+# o 6144 -> 6144; plus ragged large shapes (odd row count, k not a multiple of 2048).  Matrices
+# from 32 Mi weights take the pair-table kernel (from 96 Mi when k <= 4096: 28672x4096 does,
+# 20000x2112 takes the 16-entry table).
 @pytest.mark.parametrize("n_out,k,tid", [(32768, 6144, 0), (6144, 16384, 1), (12291, 6208, 4), (8195, 6208, 2),
-                                         (20000, 2112, 3)])
+                                         (20000, 2112, 3), (8192, 6144, 5), (6144, 6144, 6), (28672, 4096, 7)])
 def test_gemv_nf4_large_sampled(n_out, k, tid):
     import torch
     say(f"gemv nf4 large {n_out}x{k}")
