@@ -148,7 +148,7 @@ READ_CEILING = {}
 
 
 def measure_read_ceiling(reps=10, nbytes=2 << 30):
-    """Streaming-read ceiling of the box: wsl_stream_read (16-byte loads that bypass the
+    """Streaming-read ceiling of the GPU: wsl_stream_read (16-byte loads that bypass the
     caches, 4 KB of consecutive bytes per wave and iteration) over a 2 GiB buffer, 8x the
     MALL, timed as one block of launches between HIP events."""
     import torch
@@ -928,7 +928,7 @@ def main():
         traffic_summarize(*args.traffic_summarize, args.traffic_commands)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build measures the kernels on a "
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): it measures the kernels on a "
               "single MI355X and has no multi-GPU path. Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 

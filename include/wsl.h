@@ -246,7 +246,7 @@ int linear_gemm_streamed(int wfmt, int64_t count, const void *const *h_w, const 
  * weight stream (16-byte loads that bypass the caches, 1 KB of consecutive bytes
  * per wave instruction, 4 KB per wave in flight), so that its rate over a
  * buffer much larger than the caches is the streaming-read ceiling the GB/s
- * figures are compared with (a figure the pages do not give: measured on the box).
+ * figures are compared with (a figure the pages do not give: measured on the GPU at hand).
  * d_buf    device, 16-byte aligned; bytes a multiple of 16.  bytes == 0 enqueues
  *          nothing and returns 0.
  * d_sink   device uint32 [1], 4-byte aligned: each lane XOR-combines the words it

@@ -11,7 +11,7 @@ constexpr uint32_t kStreamReadMagic = 0x9e3779b9u;
 // do), waves striding over the buffer by the number of waves; a tail shorter than
 // 4 KB is read word by word.  The words a lane reads are XOR-combined; the lane
 // writes the result to sink[0] only if it equals kStreamReadMagic, so the kernel's
-// traffic is the read.  (Measured on the box against lane-strided forms and 8 or
+// traffic is the read.  (Measured on MI355X against lane-strided forms and 8 or
 // 16 KB per wave: this form reached 6.9-7.0 TB/s at every launch shape tried.)
 __global__ __launch_bounds__(512) void stream_read_kernel(const uint8_t *__restrict__ p, int64_t n16,
                                                           uint32_t *__restrict__ sink) {
