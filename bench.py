@@ -4,11 +4,13 @@
 Headline workload (``value``): batch-1 bf16 decode GEMV over one dense decoder
 layer with hidden size 5120 -- q/k/v fused into one 7168x5120 matrix, o
 5120x5120, gate/up fused into one 34816x5120 matrix, down 5120x17408 -- four
-launches per step in decoder order, each step replayed as one captured HIP
-graph.  ``value`` is the effective weight stream: weight bytes read per step /
-wall time per step (GB/s, 1e9 B/s), every input resident in HBM before the
-timed region starts.  Steps alternate between two distinct copies of the layer
-(1.32 GB) so that the 256 MB last-level cache cannot serve the weights.
+launches per step in decoder order.  The W warm-up steps and then the K timed
+steps are each captured as one HIP graph, the way a decode step's graph holds
+every layer of a model (the time with one graph launch per step is reported
+beside it).  ``value`` is the effective weight stream: weight bytes read per
+step / wall time per step (GB/s, 1e9 B/s), every input resident in HBM before
+the timed region starts.  Steps alternate between two distinct copies of the
+layer (1.32 GB) so that the 256 MB last-level cache cannot serve the weights.
 
 ``roofline`` describes the dominant kernel, the gate/up GEMV (34816x5120, the
 largest matrix of the step): its algorithmic bytes per launch divided by its
@@ -298,15 +300,34 @@ def gate_layer_5120(layers, xs, ys):
 
 
 def measure_headline(k_steps, warmup):
+    """The W warm-up steps and then exactly K timed steps, each step one pass over the layer's
+    four matrices (alternating the two copies), the K steps captured as one graph -- as a
+    decode step's graph holds every layer of the model, so no graph launch sits between
+    layers.  Also: the same steps with one graph per step (a graph launch per layer), and
+    block-timed kernel durations."""
     import torch
     layers, xs, ys, steps = setup_layer_5120(copies=2)
     worst = gate_layer_5120(layers, xs, ys)
     log(f"bf16 decode layer parity ok (worst ratio {worst:.3g})")
+    seq = lambda n, start: [l for i in range(n) for l in steps[(start + i) % len(steps)]]
+    warm = capture(seq(max(warmup, 1), 0))
+    timed = capture(seq(k_steps, max(warmup, 1)))
+    warm.replay()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    timed.replay()
+    b.record()
+    torch.cuda.synchronize()
+    gwall = a.elapsed_time(b)
+    del warm, timed
     graphs = [capture(st) for st in steps]
-    gwall = time_graphs(graphs, k_steps, warmup)
+    gwall1 = time_graphs(graphs, k_steps, warmup)
     per_kind = time_step_launches(steps, k_steps, warmup)
     per_launch = summarize(per_kind)
-    out = {"ms_per_step": gwall / k_steps, "sanity_worst_ratio": worst, "per_launch": per_launch,
+    out = {"ms_per_step": gwall / k_steps, "ms_per_step_one_graph_per_step": gwall1 / k_steps,
+           "sanity_worst_ratio": worst, "per_launch": per_launch,
            "dominant_avg_us": per_kind[DOMINANT][0], "dominant_bytes": per_kind[DOMINANT][1].nbytes}
     del graphs, steps, layers
     torch.cuda.empty_cache()
@@ -979,8 +1000,8 @@ def main():
         "data": "synthetic (seeded N(0,0.02) weights, N(0,1) activations; drawn on the device)",
         "config": {
             "workload": "bf16 decode GEMV, batch 1, one dense decoder layer, hidden 5120: "
-                        "qkv 7168x5120, o 5120x5120, gate_up 34816x5120, down 5120x17408 (4 launches/step, "
-                        "one graph replay per step)",
+                        "qkv 7168x5120, o 5120x5120, gate_up 34816x5120, down 5120x17408 (4 launches per "
+                        "step; the K timed steps replayed as one captured graph, two layer copies alternating)",
             "weight_bytes_per_step": per_launch["bytes_per_step"],
             "rotation_bytes": 2 * per_launch["bytes_per_step"],
             "parallelism": "single GPU",
@@ -999,6 +1020,9 @@ def main():
         },
         "read_ceiling": ceiling,
         "headline_detail": {
+            "ms_per_step_one_graph_per_step": round(head["ms_per_step_one_graph_per_step"], 6),
+            "gbs_one_graph_per_step": round(per_launch["bytes_per_step"] / 1e9
+                                            / (head["ms_per_step_one_graph_per_step"] / 1e3), 2),
             "frac_read_ceiling": round(value / ceiling["gbs"], 4),
             "dominant_frac_read_ceiling": round(achieved / ceiling["gbs"], 4),
             "sanity_worst_ratio": head["sanity_worst_ratio"],
