@@ -50,6 +50,12 @@ def build(verbose=False):
         objs.append(obj)
     tmp = LIB + ".tmp"
     _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+    # an unresolved symbol (e.g. a kernel's host launch stub that was not emitted) only
+    # shows when the library is loaded: load it here, in a child process, before installing
+    r = subprocess.run([sys.executable, "-c", "import ctypes, sys; ctypes.CDLL(sys.argv[1])", tmp],
+                       stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("built library does not load: " + r.stdout.strip()[-2000:])
     os.replace(tmp, LIB)
     return LIB
 

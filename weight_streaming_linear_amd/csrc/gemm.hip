@@ -45,6 +45,13 @@ __device__ __forceinline__ int swz(int row, int chunk) { return row * 64 + (chun
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// One 16-byte-per-lane direct global -> LDS copy (lane L writes lds_dst + 16 L).  A plain
+// function: called straight from a kernel template, the builtin left that template's
+// host-side launch stub unemitted.
+__device__ __forceinline__ void lds_copy16(const void *src, char *lds_dst) {
+    __builtin_amdgcn_global_load_lds(src, (lds_void *)lds_dst, 16, 0, 0);
+}
+
 // s_waitcnt with vmcnt <= N and the other counters left alone (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -403,8 +410,16 @@ __global__ __launch_bounds__(512) void gemm_nf4_x32_kernel(const uint8_t *__rest
     constexpr int NQ = 4 / KH;        // 16-byte code loads per lane per chunk
     constexpr int NS = 16 / KH;       // k-steps per wave per chunk
     constexpr int NG = 2 / KH;        // scales per lane per chunk
+    // X goes global -> LDS directly for two position groups (M 33..64: 57.5 -> 38.4 us on
+    // 27648x5120, where the register staging's loads were moved by the compiler to just
+    // before their use); with one group the register staging, whose loads are issued
+    // before the barrier, is faster (29.4 against 31.7 us at M = 32).
+    constexpr bool XD = MB == 2;
     __shared__ __align__(16) char tab[kPairTableBytes];
-    __shared__ __align__(16) char xst[2][MB * kX32Stage];   // position group g at g * kX32Stage
+    // X stages (position group g at g * kX32Stage), two separate objects so that the
+    // compiler can tell reads of one from direct copies still in flight into the other
+    __shared__ __attribute__((aligned(1024))) char xs0[MB * kX32Stage];
+    __shared__ __attribute__((aligned(1024))) char xs1[MB * kX32Stage];
     __shared__ __align__(16) char cst[CS ? 2 : 1][CS ? 32 * RG * (kX32Chunk / 2) : 16];   // CS: the chunk's codes
     fill_pair_table(tab);
     const int tid = threadIdx.x;
@@ -459,13 +474,34 @@ __global__ __launch_bounds__(512) void gemm_nf4_x32_kernel(const uint8_t *__rest
     }
     const int xoff0 = xi0 * 512 + ((xcc ^ xi0) << 4);
     const int xoff1 = xi1 * 512 + ((xcc ^ xi1) << 4);
-
-    auto fetch = [&](int c, uint4 (&q)[NQ], uint32_t (&sr)[NG], uint4 (&xv0)[MB], uint4 (&xv1)[MB]) {
-        const int64_t kc = kbeg + static_cast<int64_t>(c) * kX32Chunk;
+    // XD: X goes global -> LDS directly.  Copy i of wave w (i < 2) fills 1 KB of a
+    // group's stage: rows r = 2 (2w + i) + (lane / 32), slot lane % 32; since a lane's LDS
+    // slot is fixed, the swizzle is applied by copying chunk slot ^ (r % 32) of row r.
+    const uint16_t *xdsrc[MB][2];
 #pragma unroll
-        for (int g = 0; g < MB; ++g) {
-            xv0[g] = *reinterpret_cast<const uint4 *>(xrow0[g] + kc);
-            xv1[g] = *reinterpret_cast<const uint4 *>(xrow1[g] + kc);
+    for (int g = 0; g < MB; ++g)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int r = 2 * (2 * wave + i) + (lane >> 5);
+            const int64_t pr = p0 + 32 * g + r;
+            xdsrc[g][i] = x + (pr < m ? pr : m - 1) * ldx + ((l32 ^ r) << 3);
+        }
+
+    auto fetch = [&](int c, uint4 (&q)[NQ], uint32_t (&sr)[NG], uint4 (&xv0)[MB], uint4 (&xv1)[MB], char *xdst) {
+        const int64_t kc = kbeg + static_cast<int64_t>(c) * kX32Chunk;
+        if constexpr (XD) {
+            // first, so that the wait for this chunk's code loads covers the X copies too
+#pragma unroll
+            for (int g = 0; g < MB; ++g)
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    lds_copy16(xdsrc[g][i] + kc, xdst + g * kX32Stage + (2 * wave + i) * 1024);
+        } else {
+#pragma unroll
+            for (int g = 0; g < MB; ++g) {
+                xv0[g] = *reinterpret_cast<const uint4 *>(xrow0[g] + kc);
+                xv1[g] = *reinterpret_cast<const uint4 *>(xrow1[g] + kc);
+            }
         }
 #pragma unroll
         for (int j = 0; j < NQ; ++j) {
@@ -478,10 +514,12 @@ __global__ __launch_bounds__(512) void gemm_nf4_x32_kernel(const uint8_t *__rest
         __builtin_amdgcn_sched_barrier(0);
     };
     auto stage_x = [&](char *st, char *cs, const uint4 (&q)[NQ], const uint4 (&xv0)[MB], const uint4 (&xv1)[MB]) {
+        if constexpr (!XD) {
 #pragma unroll
-        for (int g = 0; g < MB; ++g) {
-            *reinterpret_cast<uint4 *>(st + g * kX32Stage + xoff0) = xv0[g];
-            *reinterpret_cast<uint4 *>(st + g * kX32Stage + xoff1) = xv1[g];
+            for (int g = 0; g < MB; ++g) {
+                *reinterpret_cast<uint4 *>(st + g * kX32Stage + xoff0) = xv0[g];
+                *reinterpret_cast<uint4 *>(st + g * kX32Stage + xoff1) = xv1[g];
+            }
         }
         if constexpr (CS) {
 #pragma unroll
@@ -548,6 +586,12 @@ __global__ __launch_bounds__(512) void gemm_nf4_x32_kernel(const uint8_t *__rest
         }
     };
     auto sync = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+    // XD without code staging: before the barrier that publishes a chunk, this wave's X
+    // copies of it must be complete; they were issued first in the chunk's fetch, so
+    // waiting until only its code and scale loads remain is enough.
+    auto xd_ready = [&]() {
+        if constexpr (XD && !CS) wait_vmcnt<NQ + NG>();
+    };
 
     uint4 qa[NQ], qb[NQ], xa0[MB], xa1[MB], xb0[MB], xb1[MB];
     uint32_t sa[NG], sb[NG];
@@ -556,34 +600,49 @@ __global__ __launch_bounds__(512) void gemm_nf4_x32_kernel(const uint8_t *__rest
     // Inside the loop the prefetch of the next chunk is unconditional (the last chunk is
     // peeled), so the compiler waits for exactly the loads of the chunk being used.  A
     // stage is rewritten only after the barrier that follows every wave's use of it.
+    // With XD the next chunk's X copies go straight into the stage the previous chunk
+    // used, so they are issued only after the barrier at which every wave is done with
+    // that chunk; otherwise the next chunk is loaded into registers before the barrier.
     if (nch > 0) {
-        fetch(0, qa, sa, xa0, xa1);
+        fetch(0, qa, sa, xa0, xa1, xs0);
         for (int c = 0;; c += 2) {
-            stage_x(xst[0], cst[0], qa, xa0, xa1);
+            stage_x(xs0, cst[0], qa, xa0, xa1);
+            xd_ready();
             if (c + 1 >= nch) {
                 sync();
-                compute(xst[0], cst[0], qa, sa);
+                compute(xs0, cst[0], qa, sa);
                 break;
             }
-            fetch(c + 1, qb, sb, xb0, xb1);
-            sync();
-            compute(xst[0], cst[0], qa, sa);
-            stage_x(xst[1], cst[CS], qb, xb0, xb1);
+            if constexpr (XD) {
+                sync();
+                fetch(c + 1, qb, sb, xb0, xb1, xs1);
+            } else {
+                fetch(c + 1, qb, sb, xb0, xb1, xs1);
+                sync();
+            }
+            compute(xs0, cst[0], qa, sa);
+            stage_x(xs1, cst[CS ? 1 : 0], qb, xb0, xb1);
+            xd_ready();
             if (c + 2 >= nch) {
                 sync();
-                compute(xst[1], cst[CS], qb, sb);
+                compute(xs1, cst[CS ? 1 : 0], qb, sb);
                 break;
             }
-            fetch(c + 2, qa, sa, xa0, xa1);
-            sync();
-            compute(xst[1], cst[CS], qb, sb);
+            if constexpr (XD) {
+                sync();
+                fetch(c + 2, qa, sa, xa0, xa1, xs0);
+            } else {
+                fetch(c + 2, qa, sa, xa0, xa1, xs0);
+                sync();
+            }
+            compute(xs1, cst[CS ? 1 : 0], qb, sb);
         }
     }
     if constexpr (KH == 2) {
         // The second half parks its accumulators in the X stages (4 row groups x MB
         // groups x 64 lanes x 16 floats = 16 KB per group); the first half adds them.
         __syncthreads();
-        float *park = reinterpret_cast<float *>(&xst[0][0]);
+        float *park = reinterpret_cast<float *>(xs0);
         if (kh == 1) {
 #pragma unroll
             for (int g = 0; g < MB; ++g)
