@@ -690,7 +690,11 @@ __global__ __launch_bounds__(512) void gemm_bf16_x32_kernel(const uint16_t *__re
                                                             void *__restrict__ y, int ofmt, int64_t ldy,
                                                             float *__restrict__ ws, int64_t k_per_split) {
     constexpr int NQ = 8;   // 16-byte weight loads per lane per chunk (8 k-steps of 8 k)
-    __shared__ __align__(16) char xst[2][MB * kX32Stage];
+    // Two position groups: X goes global -> LDS directly (as in the NF4 kernel), into two
+    // separate stage objects; one group keeps the register staging.
+    constexpr bool XD = MB == 2;
+    __shared__ __attribute__((aligned(1024))) char xs0[MB * kX32Stage];
+    __shared__ __attribute__((aligned(1024))) char xs1[MB * kX32Stage];
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int rg = wave & 3, kh = wave >> 2;
@@ -713,13 +717,32 @@ __global__ __launch_bounds__(512) void gemm_bf16_x32_kernel(const uint16_t *__re
     }
     const int xoff0 = xi0 * 512 + ((xcc ^ xi0) << 4);
     const int xoff1 = xi1 * 512 + ((xcc ^ xi1) << 4);
-
-    auto fetch = [&](int c, uint4 (&q)[NQ], uint4 (&xv0)[MB], uint4 (&xv1)[MB]) {
-        const int64_t kc = kbeg + static_cast<int64_t>(c) * kX32Chunk;
+    // XD copies: copy i of wave w fills rows 2 (2w + i) + lane / 32 of a group's stage,
+    // slot lane % 32 holding chunk slot ^ row.
+    const uint16_t *xdsrc[MB][2];
 #pragma unroll
-        for (int g = 0; g < MB; ++g) {
-            xv0[g] = *reinterpret_cast<const uint4 *>(xrow0[g] + kc);
-            xv1[g] = *reinterpret_cast<const uint4 *>(xrow1[g] + kc);
+    for (int g = 0; g < MB; ++g)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int r = 2 * (2 * wave + i) + (lane >> 5);
+            const int64_t pr = p0 + 32 * g + r;
+            xdsrc[g][i] = x + (pr < m ? pr : m - 1) * ldx + ((l32 ^ r) << 3);
+        }
+
+    auto fetch = [&](int c, uint4 (&q)[NQ], uint4 (&xv0)[MB], uint4 (&xv1)[MB], char *xdst) {
+        const int64_t kc = kbeg + static_cast<int64_t>(c) * kX32Chunk;
+        if constexpr (XD) {
+#pragma unroll
+            for (int g = 0; g < MB; ++g)
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    lds_copy16(xdsrc[g][i] + kc, xdst + g * kX32Stage + (2 * wave + i) * 1024);
+        } else {
+#pragma unroll
+            for (int g = 0; g < MB; ++g) {
+                xv0[g] = *reinterpret_cast<const uint4 *>(xrow0[g] + kc);
+                xv1[g] = *reinterpret_cast<const uint4 *>(xrow1[g] + kc);
+            }
         }
         // Ordinary (L1-allocating) loads: each load instruction touches 32 rows, and the
         // instructions that share a 128-byte line of a row are served by one fetch.
@@ -728,10 +751,16 @@ __global__ __launch_bounds__(512) void gemm_bf16_x32_kernel(const uint16_t *__re
         __builtin_amdgcn_sched_barrier(0);
     };
     auto stage_x = [&](char *st, const uint4 (&xv0)[MB], const uint4 (&xv1)[MB]) {
+        if constexpr (XD) {
+            // this wave's copies of the chunk were issued before its NQ weight loads:
+            // once at most NQ loads are outstanding they are complete
+            wait_vmcnt<NQ>();
+        } else {
 #pragma unroll
-        for (int g = 0; g < MB; ++g) {
-            *reinterpret_cast<uint4 *>(st + g * kX32Stage + xoff0) = xv0[g];
-            *reinterpret_cast<uint4 *>(st + g * kX32Stage + xoff1) = xv1[g];
+            for (int g = 0; g < MB; ++g) {
+                *reinterpret_cast<uint4 *>(st + g * kX32Stage + xoff0) = xv0[g];
+                *reinterpret_cast<uint4 *>(st + g * kX32Stage + xoff1) = xv1[g];
+            }
         }
     };
     f32x16 acc[MB];
@@ -769,32 +798,44 @@ __global__ __launch_bounds__(512) void gemm_bf16_x32_kernel(const uint16_t *__re
     };
     auto sync = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
 
+    // With XD the next chunk's copies go into the stage of the previous chunk, so they are
+    // issued after the barrier at which every wave is done with it.
     uint4 qa[NQ], qb[NQ], xa0[MB], xa1[MB], xb0[MB], xb1[MB];
     if (nch > 0) {
-        fetch(0, qa, xa0, xa1);
+        fetch(0, qa, xa0, xa1, xs0);
         for (int c = 0;; c += 2) {
-            stage_x(xst[0], xa0, xa1);
+            stage_x(xs0, xa0, xa1);
             if (c + 1 >= nch) {
                 sync();
-                compute(xst[0], qa);
+                compute(xs0, qa);
                 break;
             }
-            fetch(c + 1, qb, xb0, xb1);
-            sync();
-            compute(xst[0], qa);
-            stage_x(xst[1], xb0, xb1);
+            if constexpr (XD) {
+                sync();
+                fetch(c + 1, qb, xb0, xb1, xs1);
+            } else {
+                fetch(c + 1, qb, xb0, xb1, xs1);
+                sync();
+            }
+            compute(xs0, qa);
+            stage_x(xs1, xb0, xb1);
             if (c + 2 >= nch) {
                 sync();
-                compute(xst[1], qb);
+                compute(xs1, qb);
                 break;
             }
-            fetch(c + 2, qa, xa0, xa1);
-            sync();
-            compute(xst[1], qb);
+            if constexpr (XD) {
+                sync();
+                fetch(c + 2, qa, xa0, xa1, xs0);
+            } else {
+                fetch(c + 2, qa, xa0, xa1, xs0);
+                sync();
+            }
+            compute(xs1, qb);
         }
     }
     __syncthreads();
-    float *park = reinterpret_cast<float *>(&xst[0][0]);
+    float *park = reinterpret_cast<float *>(xs0);
     if (kh == 1) {
 #pragma unroll
         for (int g = 0; g < MB; ++g)
