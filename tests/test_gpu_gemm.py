@@ -189,6 +189,40 @@ def test_gemm_nf4_prefill_m32_full_shape_sampled(n_out, k, tid):
     assert ok, f"elem {i}: worst ratio {worst}"
 
 
+# The tiled bf16 kernel runs one workgroup per CU; an XCD whose last round would leave at
+# least half its 32 CUs idle runs those tiles as two 128-row halves.  264 tiles of 256 x 256
+# give each XCD 33: 32 whole tiles and one split; 36 tiles split every one (every output
+# element checked).
+@pytest.mark.parametrize("m,n_out,k", [(2048, 8448, 64), (1536, 1536, 128), (2000, 8400, 192)])
+def test_gemm_bf16_tiled_tail_halves(m, n_out, k):
+    import torch
+    say(f"gemm bf16 tiled tail m={m} n={n_out} k={k}")
+    wb = synth.weight_bits(93, 0, n_out, k)
+    xb = synth.act_bits(93, 1, (m, k))
+    y = wsl.linear_gemm(to_dev_bf16(wb), to_dev_bf16(xb), ofmt=wsl.WSL_OUT_BF16)
+    torch.cuda.synchronize()
+    y_ref, s_ref = oracle.gemm_ref(f64(xb), f64(wb))
+    ok, worst, i = oracle.check_bf16(bits_of(y), y_ref, s_ref)
+    assert ok, f"elem {i}: worst ratio {worst}"
+
+
+# The tiled NF4 kernel splits the tiles of a short last round the same way (k = 64, 192: not
+# multiples of 256, so M > 32 takes the tiled kernel; 2048 x 8448 and 2000 x 8400 mix whole
+# tiles with halves, 1536 x 1536 runs halves only).
+@pytest.mark.parametrize("m,n_out,k", [(2048, 8448, 64), (1536, 1536, 128), (2000, 8400, 192)])
+def test_gemm_nf4_tiled_tail_halves(m, n_out, k):
+    import torch
+    say(f"gemm nf4 tiled tail m={m} n={n_out} k={k}")
+    wb = synth.weight_bits(92, 0, n_out, k)
+    xb = synth.act_bits(92, 1, (m, k))
+    packed = wsl.nf4_pack(to_dev_bf16(wb))
+    y = wsl.linear_gemm(packed, to_dev_bf16(xb), wfmt=wsl.WSL_W_NF4, n_out=n_out, k=k, ofmt=wsl.WSL_OUT_F32)
+    torch.cuda.synchronize()
+    y_ref, s_ref = oracle.gemm_ref(f64(xb), _tile_f64(wb))
+    ok, worst, i = _check(y, y_ref, s_ref, wsl.WSL_OUT_F32)
+    assert ok, f"elem {i}: worst ratio {worst}"
+
+
 # bf16 batch verification, M = 8192 positions, gate (5120 -> 17408) and down (17408 -> 5120).
 @pytest.mark.parametrize("n_out,k,tid", [(17408, 5120, 0), (5120, 17408, 1)])
 def test_gemm_bf16_verify_m8192_full_shape_sampled(n_out, k, tid):

@@ -12,6 +12,8 @@
 // element) works as long as A and B use the same one; the NF4 kernel uses
 // that freedom so a lane's four MFMA k-steps read one contiguous 16-byte run
 // of codes.
+#include <atomic>
+
 #include "device_common.h"
 
 namespace wsl {
@@ -58,67 +60,59 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// One workgroup tile: TM = 256 rows of X (each wave 128 x 64 of the output, 4 x 2
+// MFMA tiles) or TM = 128 (each wave 64 x 64, 2 x 2 tiles: the half tiles that
+// shorten the last, partly filled round of a launch).
 // The four ring stages are separate LDS objects and the k loop is unrolled by
 // four, so every copy and every fragment read names its stage at compile time;
 // the compiler can then tell that reading stage s does not alias the copies
 // still in flight into the other stages, and does not drain them.
-__global__ __launch_bounds__(512) void gemm_bf16_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
-                                                        int64_t m, int64_t n_out, int64_t k, int64_t ldx,
-                                                        void *__restrict__ y, int ofmt, int64_t ldy,
-                                                        int tiles_m, int tiles_n) {
-    __shared__ __attribute__((aligned(1024))) char st0[kStageBytes];
-    __shared__ __attribute__((aligned(1024))) char st1[kStageBytes];
-    __shared__ __attribute__((aligned(1024))) char st2[kStageBytes];
-    __shared__ __attribute__((aligned(1024))) char st3[kStageBytes];
+template <int TM>
+__device__ __forceinline__ void bf16_tile(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, int64_t m,
+                                          int64_t n_out, int64_t k, int64_t ldx, void *__restrict__ y, int ofmt,
+                                          int64_t ldy, int64_t m0, int64_t n0, char *st0, char *st1, char *st2,
+                                          char *st3) {
+    constexpr int MI = TM / 64;         // 32-row MFMA tiles per wave along m
+    constexpr int NA = TM / 128;        // A wave-loads per wave per stage
+    constexpr int NV = NA + 2;          // copies per wave per stage
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wm = wave >> 2, wn = wave & 3;
 
-    // XCD-aware tile order (a bijection of [0, tiles)): XCD x = bid % 8 gets
-    // tiles [start(x), start(x) + count(x)) in its dispatch order bid / 8.
-    const int ntiles = tiles_m * tiles_n;
-    const int bid = blockIdx.x;
-    const int per_xcd = ntiles >> 3, rem = ntiles & 7;
-    const int xcd = bid & 7, slot = bid >> 3;
-    const int t = xcd * per_xcd + (xcd < rem ? xcd : rem) + slot;
-    const int band = 8;
-    const int band_tiles = band * tiles_n;
-    const int b_idx = t / band_tiles, in_band = t - b_idx * band_tiles;
-    const int band_rows = (tiles_m - b_idx * band) < band ? (tiles_m - b_idx * band) : band;
-    const int tm = b_idx * band + in_band % band_rows;
-    const int tn = in_band / band_rows;
-    const int64_t m0 = static_cast<int64_t>(tm) * kBM;
-    const int64_t n0 = static_cast<int64_t>(tn) * kBN;
-
-    // Copies: wave w issues wave-loads g = 2w, 2w+1 of each operand; load g
-    // covers tile rows 16g .. 16g+15, lane L row 16g + L/4, LDS slot L % 4.
-    // Rows outside the matrix are clamped (they only feed discarded outputs).
-    const uint16_t *asrc[2];
+    // Copies: A wave-load g (g = NA*wave + i) and B wave-loads g = 2*wave + i each
+    // cover 16 tile rows, lane L row 16g + L/4, LDS slot L % 4.  Rows outside the
+    // matrix are clamped (they only feed discarded outputs).
+    const uint16_t *asrc[NA];
     const uint16_t *bsrc[2];
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+        const int row = 16 * (NA * wave + i) + (lane >> 2);
+        const int c = chunk_swz(row, lane & 3);                 // global chunk landing in slot lane % 4
+        const int64_t gm = (m0 + row < m) ? m0 + row : m - 1;
+        asrc[i] = x + gm * ldx + c * 8;
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int row = 16 * (2 * wave + i) + (lane >> 2);
-        const int c = chunk_swz(row, lane & 3);                 // global chunk landing in slot lane % 4
-        const int64_t gm = (m0 + row < m) ? m0 + row : m - 1;
+        const int c = chunk_swz(row, lane & 3);
         const int64_t gn = (n0 + row < n_out) ? n0 + row : n_out - 1;
-        asrc[i] = x + gm * ldx + c * 8;
         bsrc[i] = w + gn * k + c * 8;
     }
     auto copy_stage = [&](int64_t kt, char *sa) {
         char *sb = sa + kBM * kBK * 2;
         const int64_t k0 = kt * kBK;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int g = 2 * wave + i;
-            __builtin_amdgcn_global_load_lds(asrc[i] + k0, (lds_void *)(sa + g * 1024), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(bsrc[i] + k0, (lds_void *)(sb + g * 1024), 16, 0, 0);
-        }
+        for (int i = 0; i < NA; ++i)
+            __builtin_amdgcn_global_load_lds(asrc[i] + k0, (lds_void *)(sa + (NA * wave + i) * 1024), 16, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            __builtin_amdgcn_global_load_lds(bsrc[i] + k0, (lds_void *)(sb + (2 * wave + i) * 1024), 16, 0, 0);
     };
 
-    f32x16 acc[4][2];
+    f32x16 acc[MI][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -126,48 +120,63 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(const uint16_t *__restri
 
     const int half = lane >> 5, l32 = lane & 31;
     const int64_t ktiles = k / kBK;
-    // Fragment reads: the lane's 4 A rows (and 2 B rows) are 32 rows apart and
+    // Fragment reads: the lane's MI A rows (and 2 B rows) are 32 rows apart and
     // share their swizzled chunk, so one base address plus immediate offsets
-    // (2048 B apart) covers the six 16-byte reads of a 16-k step.  They are
-    // issued from inline asm with their own lgkmcnt wait: the compiler then
-    // has no LDS read of its own there to order against the copies still in
-    // flight into the other stages (it cannot prove those disjoint across the
-    // loop back-edge and would drain every copy).
+    // (2048 B apart) covers the reads of a 16-k step.  They are issued from
+    // inline asm with their own lgkmcnt wait: the compiler then has no LDS read
+    // of its own there to order against the copies still in flight into the
+    // other stages (it cannot prove those disjoint across the loop back-edge and
+    // would drain every copy).
     uint32_t offa[2], offb[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-        offa[ks] = static_cast<uint32_t>(swz(wm * 128 + l32, ks * 2 + half));
+        offa[ks] = static_cast<uint32_t>(swz(wm * (TM / 2) + l32, ks * 2 + half));
         offb[ks] = static_cast<uint32_t>(kBM * kBK * 2 + swz(wn * 64 + l32, ks * 2 + half));
     }
     // Per stage: issue the reads of step 0, wait; issue the reads of step 1,
-    // run the 8 MFMAs of step 0 while they are in flight, wait; run step 1.
+    // run the MFMAs of step 0 while they are in flight, wait; run step 1.
     // The wait is a separate asm statement that takes the fragments as in/out
     // operands, so no MFMA can use them before it.
-    auto issue = [&](uint32_t a_addr, uint32_t b_addr, u32x4 (&f)[6]) {
-        asm volatile(
-            "ds_read_b128 %0, %6\n\t"
-            "ds_read_b128 %1, %6 offset:2048\n\t"
-            "ds_read_b128 %2, %6 offset:4096\n\t"
-            "ds_read_b128 %3, %6 offset:6144\n\t"
-            "ds_read_b128 %4, %7\n\t"
-            "ds_read_b128 %5, %7 offset:2048"
-            : "=&v"(f[0]), "=&v"(f[1]), "=&v"(f[2]), "=&v"(f[3]), "=&v"(f[4]), "=&v"(f[5])
-            : "v"(a_addr), "v"(b_addr));
+    using frags = u32x4[MI + 2];
+    auto issue = [&](uint32_t a_addr, uint32_t b_addr, frags &f) {
+        if constexpr (MI == 4) {
+            asm volatile(
+                "ds_read_b128 %0, %6\n\t"
+                "ds_read_b128 %1, %6 offset:2048\n\t"
+                "ds_read_b128 %2, %6 offset:4096\n\t"
+                "ds_read_b128 %3, %6 offset:6144\n\t"
+                "ds_read_b128 %4, %7\n\t"
+                "ds_read_b128 %5, %7 offset:2048"
+                : "=&v"(f[0]), "=&v"(f[1]), "=&v"(f[2]), "=&v"(f[3]), "=&v"(f[4]), "=&v"(f[5])
+                : "v"(a_addr), "v"(b_addr));
+        } else {
+            asm volatile(
+                "ds_read_b128 %0, %4\n\t"
+                "ds_read_b128 %1, %4 offset:2048\n\t"
+                "ds_read_b128 %2, %5\n\t"
+                "ds_read_b128 %3, %5 offset:2048"
+                : "=&v"(f[0]), "=&v"(f[1]), "=&v"(f[2]), "=&v"(f[3])
+                : "v"(a_addr), "v"(b_addr));
+        }
     };
-    auto landed = [&](u32x4 (&f)[6]) {
-        asm volatile("s_waitcnt lgkmcnt(0)"
-                     : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]), "+v"(f[4]), "+v"(f[5]));
+    auto landed = [&](frags &f) {
+        if constexpr (MI == 4) {
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]), "+v"(f[4]), "+v"(f[5]));
+        } else {
+            asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]));
+        }
     };
-    auto mfmas = [&](const u32x4 (&f)[6]) {
+    auto mfmas = [&](const frags &f) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int j = 0; j < 2; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f[i]),
-                                                                    __builtin_bit_cast(bf16x8, f[4 + j]), acc[i][j], 0, 0, 0);
+                                                                    __builtin_bit_cast(bf16x8, f[MI + j]), acc[i][j], 0, 0, 0);
     };
     auto compute_stage = [&](uint32_t base) {
-        u32x4 f0[6], f1[6];
+        frags f0, f1;
         issue(base + offa[0], base + offb[0], f0);
         landed(f0);
         issue(base + offa[1], base + offb[1], f1);
@@ -178,15 +187,15 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(const uint16_t *__restri
         mfmas(f1);
     };
     // One k-stage: wait for this wave's copies of stage kt (copies of kt+1 and
-    // kt+2, 4 wave-loads each, may stay in flight), a bare barrier (no memory
-    // fence, which would also wait for those), refill the stage freed by the
-    // previous iteration with k-tile kt+3, multiply stage kt.
+    // kt+2 may stay in flight), a bare barrier (no memory fence, which would also
+    // wait for those), refill the stage freed by the previous iteration with
+    // k-tile kt+3, multiply stage kt.
     auto lds_addr = [](char *p) { return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void *)p)); };
     const uint32_t a0 = lds_addr(st0), a1 = lds_addr(st1), a2 = lds_addr(st2), a3 = lds_addr(st3);
     auto step = [&](int64_t kt, uint32_t cur, char *refill) {
         const int64_t ahead = ktiles - 1 - kt;
-        if (ahead >= 2) wait_vmcnt<8>();
-        else if (ahead == 1) wait_vmcnt<4>();
+        if (ahead >= 2) wait_vmcnt<2 * NV>();
+        else if (ahead == 1) wait_vmcnt<NV>();
         else wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();
         if (kt + 3 < ktiles) copy_stage(kt + 3, refill);
@@ -208,14 +217,14 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(const uint16_t *__restri
 
     // 32x32 accumulator layout: element e of lane l is row 8*(e/4) + 4*(l/32) + e%4, column l%32.
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int64_t col = n0 + wn * 64 + j * 32 + l32;
             if (col >= n_out) continue;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int64_t row = m0 + wm * 128 + i * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
+                const int64_t row = m0 + wm * (TM / 2) + i * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
                 if (row >= m) continue;
                 if (ofmt == WSL_OUT_F32) {
                     static_cast<float *>(y)[row * ldy + col] = acc[i][j][e];
@@ -225,6 +234,63 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(const uint16_t *__restri
                 }
             }
         }
+}
+
+// Work item -> tile, XCD-aware: XCD x = blockIdx % 8 takes the contiguous tile
+// range [start(x), start(x) + count(x)) in its dispatch order blockIdx / 8.  When
+// the XCD's last round (count mod its CU count, one workgroup per CU) would
+// leave at least half of its CUs idle, those tiles run as two 128-row halves
+// each, so that round takes about half as long.  Tiles are ordered in bands of 8
+// m-tiles, so tiles sharing rows of X or of W run on the same XCD (one L2) at
+// about the same time.  Returns false for a work item past the XCD's end.
+struct TileItem {
+    int64_t m0, n0;
+    int half;   // -1: the whole 256-row tile; 0 / 1: its first / second 128 rows
+};
+__device__ __forceinline__ bool tile_item(int tiles_m, int tiles_n, int xcd_cus, TileItem &it) {
+    const int ntiles = tiles_m * tiles_n;
+    const int per_xcd = ntiles >> 3, rem = ntiles & 7;
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int count = per_xcd + (xcd < rem ? 1 : 0);
+    const int start = xcd * per_xcd + (xcd < rem ? xcd : rem);
+    const int r = count % xcd_cus;
+    const int split = (r > 0 && 2 * r <= xcd_cus) ? r : 0;
+    const int full = count - split;
+    int t;
+    it.half = -1;
+    if (slot < full) {
+        t = start + slot;
+    } else {
+        const int h = slot - full;
+        if (h >= 2 * split) return false;
+        t = start + full + (h >> 1);
+        it.half = h & 1;
+    }
+    const int band = 8;
+    const int band_tiles = band * tiles_n;
+    const int b_idx = t / band_tiles, in_band = t - b_idx * band_tiles;
+    const int band_rows = (tiles_m - b_idx * band) < band ? (tiles_m - b_idx * band) : band;
+    const int tm = b_idx * band + in_band % band_rows;
+    const int tn = in_band / band_rows;
+    it.m0 = static_cast<int64_t>(tm) * kBM + (it.half > 0 ? kBM / 2 : 0);
+    it.n0 = static_cast<int64_t>(tn) * kBN;
+    return true;
+}
+
+__global__ __launch_bounds__(512) void gemm_bf16_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
+                                                        int64_t m, int64_t n_out, int64_t k, int64_t ldx,
+                                                        void *__restrict__ y, int ofmt, int64_t ldy,
+                                                        int tiles_m, int tiles_n, int xcd_cus) {
+    __shared__ __attribute__((aligned(1024))) char st0[kStageBytes];
+    __shared__ __attribute__((aligned(1024))) char st1[kStageBytes];
+    __shared__ __attribute__((aligned(1024))) char st2[kStageBytes];
+    __shared__ __attribute__((aligned(1024))) char st3[kStageBytes];
+    TileItem it;
+    if (!tile_item(tiles_m, tiles_n, xcd_cus, it) || it.m0 >= m) return;
+    if (it.half < 0)
+        bf16_tile<256>(x, w, m, n_out, k, ldx, y, ofmt, ldy, it.m0, it.n0, st0, st1, st2, st3);
+    else
+        bf16_tile<128>(x, w, m, n_out, k, ldx, y, ofmt, ldy, it.m0, it.n0, st0, st1, st2, st3);
 }
 
 // ---------------------------------------------------------------- NF4, weight-stationary
@@ -879,42 +945,25 @@ __global__ __launch_bounds__(512) void gemm_bf16_x32_kernel(const uint16_t *__re
 // remain), one barrier (an asm statement with a memory clobber, so no LDS access
 // moves across it), issue the codes and X copy of stage kt + 3, restore stage
 // kt + 1, multiply stage kt.  Each weight tile is restored once per 256 positions.
-__global__ __launch_bounds__(512) void gemm_nf4_tiled_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ packed,
-                                                      int64_t m, int64_t n_out, int64_t k, int64_t ldx,
-                                                      void *__restrict__ y, int ofmt, int64_t ldy, int tiles_m, int tiles_n) {
-    constexpr int kHalf = kBM * kBK * 2;   // 16 KB per operand per stage
-    __shared__ __attribute__((aligned(1024))) char sa0[kHalf];
-    __shared__ __attribute__((aligned(1024))) char sa1[kHalf];
-    __shared__ __attribute__((aligned(1024))) char sa2[kHalf];
-    __shared__ __attribute__((aligned(1024))) char sa3[kHalf];
-    __shared__ __attribute__((aligned(1024))) char sb0[kHalf];
-    __shared__ __attribute__((aligned(1024))) char sb1[kHalf];
-    __shared__ __attribute__((aligned(1024))) char sb2[kHalf];
-    __shared__ __attribute__((aligned(1024))) char sb3[kHalf];
-    __shared__ float lut[16];
+// One workgroup tile of the NF4 GEMM: TM = 256 rows of X (each wave 128 x 64 of
+// the output) or TM = 128 (each wave 64 x 64: the half tiles of a short last
+// round); the restored weight tile is 256 rows either way.
+template <int TM>
+__device__ __forceinline__ void nf4_tile(const uint16_t *__restrict__ x, const uint8_t *__restrict__ packed, int64_t m,
+                                         int64_t n_out, int64_t k, int64_t ldx, void *__restrict__ y, int ofmt,
+                                         int64_t ldy, int64_t m0, int64_t n0, char *sa0, char *sa1, char *sa2,
+                                         char *sa3, char *sb0, char *sb1, char *sb2, char *sb3, const float *lut) {
+    constexpr int MI = TM / 64;         // 32-row MFMA tiles per wave along m
+    constexpr int NA = TM / 128;        // A wave-loads per wave per stage
     const int tid = threadIdx.x;
-    write_levels(lut);
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wm = wave >> 2, wn = wave & 3;
-    const int ntiles = tiles_m * tiles_n;
-    const int bid = blockIdx.x;
-    const int per_xcd = ntiles >> 3, rem = ntiles & 7;
-    const int xcd = bid & 7, slot = bid >> 3;
-    const int t = xcd * per_xcd + (xcd < rem ? xcd : rem) + slot;
-    const int band = 8;
-    const int band_tiles = band * tiles_n;
-    const int b_idx = t / band_tiles, in_band = t - b_idx * band_tiles;
-    const int band_rows = (tiles_m - b_idx * band) < band ? (tiles_m - b_idx * band) : band;
-    const int tm = b_idx * band + in_band % band_rows;
-    const int tn = in_band / band_rows;
-    const int64_t m0 = static_cast<int64_t>(tm) * kBM;
-    const int64_t n0 = static_cast<int64_t>(tn) * kBN;
 
-    const uint16_t *asrc[2];
+    const uint16_t *asrc[NA];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int row = 16 * (2 * wave + i) + (lane >> 2);
+    for (int i = 0; i < NA; ++i) {
+        const int row = 16 * (NA * wave + i) + (lane >> 2);
         const int c = chunk_swz(row, lane & 3);
         const int64_t gm = (m0 + row < m) ? m0 + row : m - 1;
         asrc[i] = x + gm * ldx + c * 8;
@@ -935,10 +984,8 @@ __global__ __launch_bounds__(512) void gemm_nf4_tiled_kernel(const uint16_t *__r
     auto copy_a = [&](int64_t kt, char *sa) {
         const int64_t k0 = kt * kBK;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int g = 2 * wave + i;
-            __builtin_amdgcn_global_load_lds(asrc[i] + k0, (lds_void *)(sa + g * 1024), 16, 0, 0);
-        }
+        for (int i = 0; i < NA; ++i)
+            __builtin_amdgcn_global_load_lds(asrc[i] + k0, (lds_void *)(sa + (NA * wave + i) * 1024), 16, 0, 0);
     };
     auto load_codes = [&](int64_t kt, uint2 &q, uint32_t &sraw) {
         const int64_t k0 = kt * kBK;
@@ -953,9 +1000,9 @@ __global__ __launch_bounds__(512) void gemm_nf4_tiled_kernel(const uint16_t *__r
         *reinterpret_cast<uint4 *>(sb + boff1) = v1;
     };
 
-    f32x16 acc[4][2];
+    f32x16 acc[MI][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -966,45 +1013,60 @@ __global__ __launch_bounds__(512) void gemm_nf4_tiled_kernel(const uint16_t *__r
     uint32_t offa[2], offb[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-        offa[ks] = static_cast<uint32_t>(swz(wm * 128 + l32, ks * 2 + half));
+        offa[ks] = static_cast<uint32_t>(swz(wm * (TM / 2) + l32, ks * 2 + half));
         offb[ks] = static_cast<uint32_t>(swz(wn * 64 + l32, ks * 2 + half));
     }
-    auto issue = [&](uint32_t a_addr, uint32_t b_addr, u32x4 (&f)[6]) {
-        asm volatile(
-            "ds_read_b128 %0, %6\n\t"
-            "ds_read_b128 %1, %6 offset:2048\n\t"
-            "ds_read_b128 %2, %6 offset:4096\n\t"
-            "ds_read_b128 %3, %6 offset:6144\n\t"
-            "ds_read_b128 %4, %7\n\t"
-            "ds_read_b128 %5, %7 offset:2048"
-            : "=&v"(f[0]), "=&v"(f[1]), "=&v"(f[2]), "=&v"(f[3]), "=&v"(f[4]), "=&v"(f[5])
-            : "v"(a_addr), "v"(b_addr));
+    using frags = u32x4[MI + 2];
+    auto issue = [&](uint32_t a_addr, uint32_t b_addr, frags &f) {
+        if constexpr (MI == 4) {
+            asm volatile(
+                "ds_read_b128 %0, %6\n\t"
+                "ds_read_b128 %1, %6 offset:2048\n\t"
+                "ds_read_b128 %2, %6 offset:4096\n\t"
+                "ds_read_b128 %3, %6 offset:6144\n\t"
+                "ds_read_b128 %4, %7\n\t"
+                "ds_read_b128 %5, %7 offset:2048"
+                : "=&v"(f[0]), "=&v"(f[1]), "=&v"(f[2]), "=&v"(f[3]), "=&v"(f[4]), "=&v"(f[5])
+                : "v"(a_addr), "v"(b_addr));
+        } else {
+            asm volatile(
+                "ds_read_b128 %0, %4\n\t"
+                "ds_read_b128 %1, %4 offset:2048\n\t"
+                "ds_read_b128 %2, %5\n\t"
+                "ds_read_b128 %3, %5 offset:2048"
+                : "=&v"(f[0]), "=&v"(f[1]), "=&v"(f[2]), "=&v"(f[3])
+                : "v"(a_addr), "v"(b_addr));
+        }
     };
-    auto landed = [&](u32x4 (&f)[6]) {
-        asm volatile("s_waitcnt lgkmcnt(0)"
-                     : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]), "+v"(f[4]), "+v"(f[5]));
+    auto landed = [&](frags &f) {
+        if constexpr (MI == 4) {
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]), "+v"(f[4]), "+v"(f[5]));
+        } else {
+            asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]));
+        }
     };
-    auto mfmas = [&](const u32x4 (&f)[6]) {
+    auto mfmas = [&](const frags &f) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int j = 0; j < 2; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f[i]),
-                                                                    __builtin_bit_cast(bf16x8, f[4 + j]), acc[i][j], 0, 0, 0);
+                                                                    __builtin_bit_cast(bf16x8, f[MI + j]), acc[i][j], 0, 0, 0);
     };
     // The restoration of the next weight stage runs between the two halves of the
     // stage's MFMAs, so its table reads and multiplies overlap the matrix pipe
     // instead of delaying the first MFMA after the barrier.
-    auto mfmas_half = [&](const u32x4 (&f)[6], int i0) {
+    auto mfmas_half = [&](const frags &f, int i0) {
 #pragma unroll
-        for (int i = i0; i < i0 + 2; ++i)
+        for (int i = i0; i < i0 + MI / 2; ++i)
 #pragma unroll
             for (int j = 0; j < 2; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f[i]),
-                                                                    __builtin_bit_cast(bf16x8, f[4 + j]), acc[i][j], 0, 0, 0);
+                                                                    __builtin_bit_cast(bf16x8, f[MI + j]), acc[i][j], 0, 0, 0);
     };
     auto compute_stage = [&](uint32_t abase, uint32_t bbase, auto &&restore0, auto &&restore1) {
-        u32x4 f0[6], f1[6];
+        frags f0, f1;
         issue(abase + offa[0], bbase + offb[0], f0);
         landed(f0);
         issue(abase + offa[1], bbase + offb[1], f1);
@@ -1013,7 +1075,7 @@ __global__ __launch_bounds__(512) void gemm_nf4_tiled_kernel(const uint16_t *__r
         __builtin_amdgcn_sched_barrier(0);
         restore0();
         __builtin_amdgcn_sched_barrier(0);
-        mfmas_half(f0, 2);
+        mfmas_half(f0, MI / 2);
         __builtin_amdgcn_sched_barrier(0);
         restore1();
         __builtin_amdgcn_sched_barrier(0);
@@ -1030,8 +1092,8 @@ __global__ __launch_bounds__(512) void gemm_nf4_tiled_kernel(const uint16_t *__r
     auto step = [&](int64_t kt, uint32_t acur, uint32_t bcur, char *arefill, uint2 &qload, uint32_t &rload,
                     char *bnext, const uint2 &qnext, const uint32_t &rnext) {
         const int64_t ahead = ktiles - 1 - kt;
-        if (ahead >= 2) wait_vmcnt<6>();
-        else if (ahead == 1) wait_vmcnt<2>();
+        if (ahead >= 2) wait_vmcnt<2 * NA + 2>();
+        else if (ahead == 1) wait_vmcnt<NA>();
         else wait_vmcnt<0>();
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         if (kt + 3 < ktiles) {
@@ -1067,19 +1129,42 @@ __global__ __launch_bounds__(512) void gemm_nf4_tiled_kernel(const uint16_t *__r
     if (kt + 1 < ktiles) step(kt + 1, A1, B1, sa0, q0, r0, sb2, q2, r2);
     if (kt + 2 < ktiles) step(kt + 2, A2, B2, sa1, q1, r1, sb3, q3, r3);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int64_t col = n0 + wn * 64 + j * 32 + l32;
             if (col >= n_out) continue;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int64_t row = m0 + wm * 128 + i * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
+                const int64_t row = m0 + wm * (TM / 2) + i * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
                 if (row >= m) continue;
                 if (ofmt == WSL_OUT_F32) static_cast<float *>(y)[row * ldy + col] = acc[i][j][e];
                 else static_cast<uint16_t *>(y)[row * ldy + col] = static_cast<uint16_t>(pack_bf16x2(acc[i][j][e], 0.f) & 0xffffu);
             }
         }
+}
+
+__global__ __launch_bounds__(512) void gemm_nf4_tiled_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ packed,
+                                                      int64_t m, int64_t n_out, int64_t k, int64_t ldx,
+                                                      void *__restrict__ y, int ofmt, int64_t ldy, int tiles_m, int tiles_n,
+                                                      int xcd_cus) {
+    constexpr int kHalf = kBM * kBK * 2;   // 16 KB per operand per stage
+    __shared__ __attribute__((aligned(1024))) char sa0[kHalf];
+    __shared__ __attribute__((aligned(1024))) char sa1[kHalf];
+    __shared__ __attribute__((aligned(1024))) char sa2[kHalf];
+    __shared__ __attribute__((aligned(1024))) char sa3[kHalf];
+    __shared__ __attribute__((aligned(1024))) char sb0[kHalf];
+    __shared__ __attribute__((aligned(1024))) char sb1[kHalf];
+    __shared__ __attribute__((aligned(1024))) char sb2[kHalf];
+    __shared__ __attribute__((aligned(1024))) char sb3[kHalf];
+    __shared__ float lut[16];
+    TileItem it;
+    if (!tile_item(tiles_m, tiles_n, xcd_cus, it) || it.m0 >= m) return;
+    write_levels(lut);
+    if (it.half < 0)
+        nf4_tile<256>(x, packed, m, n_out, k, ldx, y, ofmt, ldy, it.m0, it.n0, sa0, sa1, sa2, sa3, sb0, sb1, sb2, sb3, lut);
+    else
+        nf4_tile<128>(x, packed, m, n_out, k, ldx, y, ofmt, ldy, it.m0, it.n0, sa0, sa1, sa2, sa3, sb0, sb1, sb2, sb3, lut);
 }
 
 // Sum split partials in split order (fixed, so the result is deterministic).  A
@@ -1205,15 +1290,46 @@ size_t gemm_ws_bytes(int wfmt, int64_t n_out, int64_t k, int64_t m) {
     return static_cast<size_t>(splits) * static_cast<size_t>(m) * static_cast<size_t>(n_out) * sizeof(float);
 }
 
+// CUs per XCD of the current device (one workgroup of the tiled kernels per CU),
+// cached per device; 32 on MI355X (256 CUs in 8 XCDs).
+static int xcd_cus() {
+    constexpr int kDevs = 64;
+    static std::atomic<int> cache[kDevs];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevs) return 32;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8) cus = 256;
+        v = cus / 8;
+        cache[dev].store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
+// Grid of the tiled kernels: 8 XCDs times the largest per-XCD item count (whole
+// tiles plus the half tiles of a short last round), as tile_item() assigns them.
+static unsigned tile_grid(int64_t ntiles, int cus) {
+    int64_t most = 0;
+    for (int x = 0; x < 8; ++x) {
+        const int64_t count = ntiles / 8 + (x < ntiles % 8 ? 1 : 0);
+        const int64_t r = count % cus;
+        const int64_t items = count + ((r > 0 && 2 * r <= cus) ? r : 0);
+        if (items > most) most = items;
+    }
+    return static_cast<unsigned>(8 * most);
+}
+
 int launch_gemm_bf16(const void *w, int64_t n_out, int64_t k, const void *x, int64_t m, int64_t ldx, void *y,
                      int ofmt, int64_t ldy, void *ws, size_t ws_bytes, hipStream_t s) {
     const auto *wp = static_cast<const uint16_t *>(w);
     const auto *xp = static_cast<const uint16_t *>(x);
     if (!use_bf16_x32(k, m)) {
         const int64_t tn = (n_out + kBN - 1) / kBN, tm = (m + kBM - 1) / kBM;
-        if (tn * tm > 0x7fffffff / 2) return WSL_E_SHAPE;
-        hipLaunchKernelGGL(gemm_bf16_kernel, dim3(static_cast<unsigned>(tn * tm)), dim3(512), 0, s, xp, wp, m, n_out, k,
-                           ldx, y, ofmt, ldy, static_cast<int>(tm), static_cast<int>(tn));
+        if (tn * tm > 0x7fffffff / 4) return WSL_E_SHAPE;
+        const int cus = xcd_cus();
+        hipLaunchKernelGGL(gemm_bf16_kernel, dim3(tile_grid(tm * tn, cus)), dim3(512), 0, s, xp, wp, m, n_out, k,
+                           ldx, y, ofmt, ldy, static_cast<int>(tm), static_cast<int>(tn), cus);
         return WSL_OK;
     }
     int splits = bf16_splits(n_out, k, m);
@@ -1245,10 +1361,11 @@ int launch_gemm_nf4(const void *w, int64_t n_out, int64_t k, const void *x, int6
                     int ofmt, int64_t ldy, void *ws, size_t ws_bytes, hipStream_t s) {
     if (use_tiled(k, m)) {
         const int64_t tn = (n_out + kBN - 1) / kBN, tm = (m + kBM - 1) / kBM;
-        if (tn * tm > 0x7fffffff / 2) return WSL_E_SHAPE;
-        hipLaunchKernelGGL(gemm_nf4_tiled_kernel, dim3(static_cast<unsigned>(tn * tm)), dim3(512), 0, s,
+        if (tn * tm > 0x7fffffff / 4) return WSL_E_SHAPE;
+        const int cus = xcd_cus();
+        hipLaunchKernelGGL(gemm_nf4_tiled_kernel, dim3(tile_grid(tm * tn, cus)), dim3(512), 0, s,
                            static_cast<const uint16_t *>(x), static_cast<const uint8_t *>(w), m, n_out, k, ldx, y,
-                           ofmt, ldy, static_cast<int>(tm), static_cast<int>(tn));
+                           ofmt, ldy, static_cast<int>(tm), static_cast<int>(tn), cus);
         return WSL_OK;
     }
     int splits = nf4_splits(n_out, k, m);
