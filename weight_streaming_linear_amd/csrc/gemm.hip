@@ -30,7 +30,8 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast
 // staging and three stages (96 KB per CU) stay in flight: enough bytes in
 // flight to cover the L2/MALL latency at the operand rate a 256 x 256 tile
 // needs.  Per stage: wait for the oldest copies (s_waitcnt vmcnt), one
-// barrier, refill the stage freed by the previous iteration, then 2 x 8 MFMAs.
+// barrier, then 2 x 8 MFMAs with the refill of the stage freed by the previous
+// iteration issued among them.
 // LDS rows are 32 bf16 = 64 B = 4 chunks of 16 B; chunk c of row r sits at
 // c ^ ((r >> 1) & 3) ^ ((r >> 3) & 1): the fragment reads (32 rows, one chunk
 // column) are free of bank conflicts for 32 and for 64 banks.  Because a
@@ -104,10 +105,10 @@ __device__ __forceinline__ void bf16_tile(const uint16_t *__restrict__ x, const 
         const int64_t k0 = kt * kBK;
 #pragma unroll
         for (int i = 0; i < NA; ++i)
-            __builtin_amdgcn_global_load_lds(asrc[i] + k0, (lds_void *)(sa + (NA * wave + i) * 1024), 16, 0, 0);
+            lds_copy16(asrc[i] + k0, sa + (NA * wave + i) * 1024);
 #pragma unroll
         for (int i = 0; i < 2; ++i)
-            __builtin_amdgcn_global_load_lds(bsrc[i] + k0, (lds_void *)(sb + (2 * wave + i) * 1024), 16, 0, 0);
+            lds_copy16(bsrc[i] + k0, sb + (2 * wave + i) * 1024);
     };
 
     f32x16 acc[MI][2];
@@ -136,7 +137,11 @@ __device__ __forceinline__ void bf16_tile(const uint16_t *__restrict__ x, const 
     // Per stage: issue the reads of step 0, wait; issue the reads of step 1,
     // run the MFMAs of step 0 while they are in flight, wait; run step 1.
     // The wait is a separate asm statement that takes the fragments as in/out
-    // operands, so no MFMA can use them before it.
+    // operands, so no MFMA can use them before it (each fragment is named once,
+    // so the compiler has no reason to copy one before the wait).
+    // The refill's NV copies are spread among the stage's MFMAs: issued together
+    // right after the barrier they stalled the wave at issue (the vector memory
+    // queue fills) ahead of its fragment reads and MFMAs.
     using frags = u32x4[MI + 2];
     auto issue = [&](uint32_t a_addr, uint32_t b_addr, frags &f) {
         if constexpr (MI == 4) {
@@ -167,29 +172,43 @@ __device__ __forceinline__ void bf16_tile(const uint16_t *__restrict__ x, const 
             asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]));
         }
     };
-    auto mfmas = [&](const frags &f) {
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f[i]),
-                                                                    __builtin_bit_cast(bf16x8, f[MI + j]), acc[i][j], 0, 0, 0);
+    // One operand copy of the refill, piece q < NV (NA A-loads, then 2 B-loads).
+    auto copy_piece = [&](int q, int64_t kt, char *sa) {
+        const int64_t k0 = kt * kBK;
+        if (q < NA)
+            lds_copy16(asrc[q] + k0, sa + (NA * wave + q) * 1024);
+        else
+            lds_copy16(bsrc[q - NA] + k0, sa + kBM * kBK * 2 + (2 * wave + q - NA) * 1024);
     };
-    auto compute_stage = [&](uint32_t base) {
+    auto compute_stage = [&](uint32_t base, bool refill, int64_t kn, char *dst) {
         frags f0, f1;
         issue(base + offa[0], base + offb[0], f0);
         landed(f0);
         issue(base + offa[1], base + offb[1], f1);
         __builtin_amdgcn_sched_barrier(0);
-        mfmas(f0);
-        __builtin_amdgcn_sched_barrier(0);
-        landed(f1);
-        mfmas(f1);
+        constexpr int MF = 2 * MI;   // MFMAs per 16-k step
+        int q = 0;
+#pragma unroll
+        for (int t = 0; t < 2 * MF; ++t) {
+            if (t == MF) {
+                landed(f1);
+            }
+            frags &f = t < MF ? f0 : f1;
+            const int i = (t % MF) >> 1, j = t & 1;
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f[i]),
+                                                                __builtin_bit_cast(bf16x8, f[MI + j]), acc[i][j], 0, 0, 0);
+            if ((t + 1) == (q + 1) * 2 * MF / (NV + 1) && q < NV) {
+                __builtin_amdgcn_sched_barrier(0);
+                if (refill) copy_piece(q, kn, dst);
+                __builtin_amdgcn_sched_barrier(0);
+                ++q;
+            }
+        }
     };
     // One k-stage: wait for this wave's copies of stage kt (copies of kt+1 and
     // kt+2 may stay in flight), a bare barrier (no memory fence, which would also
-    // wait for those), refill the stage freed by the previous iteration with
-    // k-tile kt+3, multiply stage kt.
+    // wait for those), multiply stage kt while refilling the stage freed by the
+    // previous iteration with k-tile kt+3.
     auto lds_addr = [](char *p) { return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void *)p)); };
     const uint32_t a0 = lds_addr(st0), a1 = lds_addr(st1), a2 = lds_addr(st2), a3 = lds_addr(st3);
     auto step = [&](int64_t kt, uint32_t cur, char *refill) {
@@ -198,8 +217,7 @@ __device__ __forceinline__ void bf16_tile(const uint16_t *__restrict__ x, const 
         else if (ahead == 1) wait_vmcnt<NV>();
         else wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();
-        if (kt + 3 < ktiles) copy_stage(kt + 3, refill);
-        compute_stage(cur);
+        compute_stage(cur, kt + 3 < ktiles, kt + 3, refill);
     };
     if (0 < ktiles) copy_stage(0, st0);
     if (1 < ktiles) copy_stage(1, st1);
@@ -945,6 +963,41 @@ __global__ __launch_bounds__(512) void gemm_bf16_x32_kernel(const uint16_t *__re
 // remain), one barrier (an asm statement with a memory clobber, so no LDS access
 // moves across it), issue the codes and X copy of stage kt + 3, restore stage
 // kt + 1, multiply stage kt.  Each weight tile is restored once per 256 positions.
+// dequant8 with the table reads issued from inline asm (and waited for inside it): the
+// compiler then has no LDS access of its own to order against direct global -> LDS
+// copies in flight, which it would otherwise drain first.  lut_addr is the table's LDS
+// byte address.
+__device__ __forceinline__ uint4 dequant8_asm(uint32_t w, float s, uint32_t lut_addr) {
+    const uint32_t wo = rotr32(w, 4);
+    float l0, l1, l2, l3, l4, l5, l6, l7;
+    asm volatile(
+        "ds_read_b32 %0, %8\n\t"
+        "ds_read_b32 %1, %9\n\t"
+        "ds_read_b32 %2, %10\n\t"
+        "ds_read_b32 %3, %11\n\t"
+        "ds_read_b32 %4, %12\n\t"
+        "ds_read_b32 %5, %13\n\t"
+        "ds_read_b32 %6, %14\n\t"
+        "ds_read_b32 %7, %15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(l0), "=&v"(l1), "=&v"(l2), "=&v"(l3), "=&v"(l4), "=&v"(l5), "=&v"(l6), "=&v"(l7)
+        : "v"(lut_addr + (w & 0x3cu)), "v"(lut_addr + (wo & 0x3cu)), "v"(lut_addr + ((w >> 8) & 0x3cu)),
+          "v"(lut_addr + ((wo >> 8) & 0x3cu)), "v"(lut_addr + ((w >> 16) & 0x3cu)), "v"(lut_addr + ((wo >> 16) & 0x3cu)),
+          "v"(lut_addr + ((w >> 24) & 0x3cu)), "v"(lut_addr + ((wo >> 24) & 0x3cu)));
+    uint4 r;
+    r.x = pack_bf16x2(l0 * s, l1 * s);
+    r.y = pack_bf16x2(l2 * s, l3 * s);
+    r.z = pack_bf16x2(l4 * s, l5 * s);
+    r.w = pack_bf16x2(l6 * s, l7 * s);
+    return r;
+}
+
+// 16-byte LDS store from inline asm (see dequant8_asm).
+__device__ __forceinline__ void lds_store16(uint32_t addr, uint4 v) {
+    const u32x4 vv = __builtin_bit_cast(u32x4, v);
+    asm volatile("ds_write_b128 %0, %1" : : "v"(addr), "v"(vv));
+}
+
 // One workgroup tile of the NF4 GEMM: TM = 256 rows of X (each wave 128 x 64 of
 // the output) or TM = 128 (each wave 64 x 64: the half tiles of a short last
 // round); the restored weight tile is 256 rows either way.
@@ -979,13 +1032,13 @@ __device__ __forceinline__ void nf4_tile(const uint16_t *__restrict__ x, const u
     const uint16_t *srow = scales + (gn >> 4) * 16 * groups + (gn & 15);
     const uint32_t boff0 = static_cast<uint32_t>(swz(brow, 2 * bhp));
     const uint32_t boff1 = static_cast<uint32_t>(swz(brow, 2 * bhp + 1));
-    const char *lutp = reinterpret_cast<const char *>(lut);
+    const uint32_t lut_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void *)lut));
 
     auto copy_a = [&](int64_t kt, char *sa) {
         const int64_t k0 = kt * kBK;
 #pragma unroll
         for (int i = 0; i < NA; ++i)
-            __builtin_amdgcn_global_load_lds(asrc[i] + k0, (lds_void *)(sa + (NA * wave + i) * 1024), 16, 0, 0);
+            lds_copy16(asrc[i] + k0, sa + (NA * wave + i) * 1024);
     };
     auto load_codes = [&](int64_t kt, uint2 &q, uint32_t &sraw) {
         const int64_t k0 = kt * kBK;
@@ -994,10 +1047,11 @@ __device__ __forceinline__ void nf4_tile(const uint16_t *__restrict__ x, const u
     };
     auto put_b = [&](char *sb, const uint2 &q, uint32_t sraw) {
         const float s = f16_to_f32(sraw);
-        const uint4 v0 = dequant8(q.x, s, lutp);
-        const uint4 v1 = dequant8(q.y, s, lutp);
-        *reinterpret_cast<uint4 *>(sb + boff0) = v0;
-        *reinterpret_cast<uint4 *>(sb + boff1) = v1;
+        const uint4 v0 = dequant8_asm(q.x, s, lut_addr);
+        const uint4 v1 = dequant8_asm(q.y, s, lut_addr);
+        const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void *)sb));
+        lds_store16(base + boff0, v0);
+        lds_store16(base + boff1, v1);
     };
 
     f32x16 acc[MI][2];
@@ -1046,49 +1100,45 @@ __device__ __forceinline__ void nf4_tile(const uint16_t *__restrict__ x, const u
             asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]));
         }
     };
-    auto mfmas = [&](const frags &f) {
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f[i]),
-                                                                    __builtin_bit_cast(bf16x8, f[MI + j]), acc[i][j], 0, 0, 0);
-    };
-    // The restoration of the next weight stage runs between the two halves of the
-    // stage's MFMAs, so its table reads and multiplies overlap the matrix pipe
-    // instead of delaying the first MFMA after the barrier.
-    auto mfmas_half = [&](const frags &f, int i0) {
-#pragma unroll
-        for (int i = i0; i < i0 + MI / 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f[i]),
-                                                                    __builtin_bit_cast(bf16x8, f[MI + j]), acc[i][j], 0, 0, 0);
-    };
-    auto compute_stage = [&](uint32_t abase, uint32_t bbase, auto &&restore0, auto &&restore1) {
+    // The restoration of the next weight stage runs between the two quarters of the
+    // stage's first 16-k step, so its table reads and multiplies overlap the matrix
+    // pipe instead of delaying the first MFMA after the barrier.
+    // The stage's loads for k-tile kt+3 (piece 0: this thread's codes and scale; pieces
+    // 1..NA: the wave's A copies) are spread among its MFMAs rather than issued together
+    // after the barrier, where a full vector memory queue stalled the wave at issue.
+    auto compute_stage = [&](uint32_t abase, uint32_t bbase, auto &&restore0, auto &&restore1, auto &&piece) {
         frags f0, f1;
         issue(abase + offa[0], bbase + offb[0], f0);
         landed(f0);
         issue(abase + offa[1], bbase + offb[1], f1);
         __builtin_amdgcn_sched_barrier(0);
-        mfmas_half(f0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        restore0();
-        __builtin_amdgcn_sched_barrier(0);
-        mfmas_half(f0, MI / 2);
-        __builtin_amdgcn_sched_barrier(0);
-        restore1();
-        __builtin_amdgcn_sched_barrier(0);
-        landed(f1);
-        mfmas(f1);
+        constexpr int MF = 2 * MI;   // MFMAs per 16-k step
+        constexpr int NP = NA + 1;   // load pieces
+        int q = 0;
+#pragma unroll
+        for (int t = 0; t < 2 * MF; ++t) {
+            if (t == MF) landed(f1);
+            frags &f = t < MF ? f0 : f1;
+            const int i = (t % MF) >> 1, j = t & 1;
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f[i]),
+                                                                __builtin_bit_cast(bf16x8, f[MI + j]), acc[i][j], 0, 0, 0);
+            const bool at_piece = q < NP && t + 1 == (q + 1) * 2 * MF / (NP + 1);
+            if (at_piece || t + 1 == MF / 2 || t + 1 == MF) {
+                __builtin_amdgcn_sched_barrier(0);
+                if (at_piece) piece(q++);
+                if (t + 1 == MF / 2) restore0();
+                if (t + 1 == MF) restore1();
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
     };
     auto lds_addr = [](char *p) { return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void *)p)); };
     const uint32_t A0 = lds_addr(sa0), A1 = lds_addr(sa1), A2 = lds_addr(sa2), A3 = lds_addr(sa3);
     const uint32_t B0 = lds_addr(sb0), B1 = lds_addr(sb1), B2 = lds_addr(sb2), B3 = lds_addr(sb3);
     uint2 q0, q1, q2, q3;
     uint32_t r0, r1, r2, r3;
-    // step kt: wait (A(kt) and the codes of kt+1 landed), barrier, issue codes(kt+3) then A(kt+3),
-    // multiply stage kt with the restoration of B(kt+1) between its two MFMA halves.
+    // step kt: wait (A(kt) and the codes of kt+1 landed), barrier, multiply stage kt with the
+    // restoration of B(kt+1) and the loads of codes(kt+3), then A(kt+3), among its MFMAs.
     auto step = [&](int64_t kt, uint32_t acur, uint32_t bcur, char *arefill, uint2 &qload, uint32_t &rload,
                     char *bnext, const uint2 &qnext, const uint32_t &rnext) {
         const int64_t ahead = ktiles - 1 - kt;
@@ -1096,20 +1146,22 @@ __device__ __forceinline__ void nf4_tile(const uint16_t *__restrict__ x, const u
         else if (ahead == 1) wait_vmcnt<NA>();
         else wait_vmcnt<0>();
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        if (kt + 3 < ktiles) {
-            load_codes(kt + 3, qload, rload);
-            copy_a(kt + 3, arefill);
-        }
+        const bool refill = kt + 3 < ktiles;
         const bool more = kt + 1 < ktiles;
         uint4 v0;
         compute_stage(acur, bcur, [&]() {
-            if (more) v0 = dequant8(qnext.x, f16_to_f32(rnext), lutp);
+            if (more) v0 = dequant8_asm(qnext.x, f16_to_f32(rnext), lut_addr);
         }, [&]() {
             if (more) {
-                const uint4 v1 = dequant8(qnext.y, f16_to_f32(rnext), lutp);
-                *reinterpret_cast<uint4 *>(bnext + boff0) = v0;
-                *reinterpret_cast<uint4 *>(bnext + boff1) = v1;
+                const uint4 v1 = dequant8_asm(qnext.y, f16_to_f32(rnext), lut_addr);
+                const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void *)bnext));
+                lds_store16(base + boff0, v0);
+                lds_store16(base + boff1, v1);
             }
+        }, [&](int q) {
+            if (!refill) return;
+            if (q == 0) load_codes(kt + 3, qload, rload);
+            else lds_copy16(asrc[q - 1] + (kt + 3) * kBK, arefill + (NA * (threadIdx.x >> 6) + q - 1) * 1024);
         });
     };
     __syncthreads();   // lut
