@@ -263,11 +263,14 @@ def test_gemm_nf4_verify_m8192_full_shape_sampled(n_out, k, tid):
     assert ok, f"elem {i}: worst ratio {worst}"
 
 
-# 32 < M <= 256 with k % 256 == 0: the shared-X kernel with two 32-position groups per
-# workgroup and position blocks on grid z -- M not a multiple of 32 or 64, ragged row
-# counts, tall matrices without a k split, one to four position blocks.
-@pytest.mark.parametrize("m,n_out,k", [(33, 257, 512), (48, 1000, 768), (130, 4109, 2304), (256, 24700, 256),
-                                       (200, 160, 5120)])
+# M > 32 with k % 256 == 0 where the shared-X kernel is the faster one (the launch compares
+# a time model of both kernels): two 32-position groups per workgroup and position blocks
+# on grid z -- M not a multiple of 32 or 64, ragged row counts, tall matrices without a k
+# split, one to sixteen position blocks (M up to 1000 on matrices with few rows, where the
+# 256 x 256 tiles would leave most CUs idle).
+@pytest.mark.parametrize("m,n_out,k", [(33, 257, 512), (48, 1000, 768), (130, 4109, 2304), (200, 160, 5120),
+                                       (257, 130, 2048), (300, 1000, 1024), (333, 300, 2048), (320, 512, 8192),
+                                       (1000, 256, 4096)])
 @pytest.mark.parametrize("ofmt", [wsl.WSL_OUT_F32, wsl.WSL_OUT_BF16])
 def test_gemm_nf4_mid_m_shared_x(m, n_out, k, ofmt):
     import torch
@@ -284,8 +287,9 @@ def test_gemm_nf4_mid_m_shared_x(m, n_out, k, ofmt):
     assert ok, f"elem {i}: worst ratio {worst}"
 
 
-# M > 256, or M > 32 with k % 256 != 0: the tiled kernel.
-@pytest.mark.parametrize("m,n_out,k", [(64, 300, 448), (257, 130, 2048), (513, 260, 64), (300, 1000, 1024)])
+# M > 32 with k % 256 != 0, or where the time model prefers 256 x 256 tiles (many rows and
+# positions, short k): the tiled kernel.
+@pytest.mark.parametrize("m,n_out,k", [(64, 300, 448), (513, 260, 64), (256, 24700, 256), (1024, 8192, 512)])
 @pytest.mark.parametrize("ofmt", [wsl.WSL_OUT_F32, wsl.WSL_OUT_BF16])
 def test_gemm_nf4_tiled_mid_m(m, n_out, k, ofmt):
     import torch

@@ -1287,11 +1287,28 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float *__restri
 constexpr int kNf4Nb = 1;
 constexpr int64_t kNf4RowsPerWg = 4 * 32 * kNf4Nb;
 
-// Shared-X kernel: M <= 256 with k a multiple of 256; the tiled kernel above 256 (or for
-// M > 32 with other k); the general kernel for M <= 32 with other k.
-constexpr int64_t kX32MaxM = 256;
-static bool use_x32(int64_t k, int64_t m) { return m <= kX32MaxM && (k % kX32Chunk) == 0; }
-static bool use_tiled(int64_t k, int64_t m) { return m > 32 && !use_x32(k, m); }
+// k a multiple of 256: the shared-X kernel for M <= 32; above that, the shared-X or the
+// tiled kernel, whichever a time model fitted to MI355X measurements puts first.  The
+// shared-X kernel streams the packed weights once per 64 positions at about 2 TB/s; a
+// round of 256 x 256 tiles (one workgroup per CU) takes about 33 ns per unit of k, and a
+// last round of at most 128 tiles, which runs as half tiles, about 23.5 ns.  Measured
+// (us, tiled / shared-X): 27648x5120 M = 64 127 / 42, M = 256 121 / 158; 5120x27648
+// M = 256 608 / 197; at M = 320, where a fixed cut at 256 took the tiled kernel,
+// 5120x27648 608 and 6144x16384 368.  Other k: the tiled kernel for M > 32, the general
+// kernel for M <= 32.
+static bool x32_faster(int64_t n_out, int64_t k, int64_t m) {
+    const double packed = static_cast<double>(n_out) * static_cast<double>(k / 2 + (k / 64) * 2);
+    const double t_x32 = static_cast<double>((m + 63) / 64) * packed / 2.0e12;
+    const int64_t tiles = ((m + kBM - 1) / kBM) * ((n_out + kBN - 1) / kBN);
+    const int64_t full = tiles / 256, tail = tiles % 256;
+    double per_k = static_cast<double>(full) * 33e-9;
+    if (tail > 0) per_k += tail <= 128 ? 23.5e-9 : 33e-9;
+    return t_x32 <= per_k * static_cast<double>(k);
+}
+static bool use_x32(int64_t n_out, int64_t k, int64_t m) {
+    return (k % kX32Chunk) == 0 && (m <= 32 || x32_faster(n_out, k, m));
+}
+static bool use_tiled(int64_t n_out, int64_t k, int64_t m) { return m > 32 && !use_x32(n_out, k, m); }
 // The shared-X kernel always runs its 128-row form (KH = 2), with MB = 2 groups of 32
 // positions per workgroup when M > 32 (one restored weight fragment feeds both groups'
 // MFMAs) and further position blocks on grid z; k is split into as many ranges as keep
@@ -1304,8 +1321,8 @@ static int x32_mb(int64_t m) { return m > 32 ? 2 : 1; }
 static int64_t x32_zblocks(int64_t m) { return (m + 32 * x32_mb(m) - 1) / (32 * x32_mb(m)); }
 
 static int nf4_splits(int64_t n_out, int64_t k, int64_t m) {
-    if (use_tiled(k, m)) return 1;
-    if (use_x32(k, m)) {
+    if (use_tiled(n_out, k, m)) return 1;
+    if (use_x32(n_out, k, m)) {
         const int64_t blocks = (n_out + kX32BlockRows - 1) / kX32BlockRows * x32_zblocks(m);
         const int64_t chunks = k / kX32Chunk;
         int64_t splits = 256 / blocks;
@@ -1321,8 +1338,8 @@ static int nf4_splits(int64_t n_out, int64_t k, int64_t m) {
     return static_cast<int>(splits);
 }
 
-static int64_t nf4_k_per_split(int64_t k, int64_t m, int splits) {
-    const int64_t unit = use_x32(k, m) ? kX32Chunk : 128;
+static int64_t nf4_k_per_split(int64_t n_out, int64_t k, int64_t m, int splits) {
+    const int64_t unit = use_x32(n_out, k, m) ? kX32Chunk : 128;
     const int64_t chunks = (k + unit - 1) / unit;
     return ((chunks + splits - 1) / splits) * unit;
 }
@@ -1411,7 +1428,7 @@ int launch_gemm_bf16(const void *w, int64_t n_out, int64_t k, const void *x, int
 
 int launch_gemm_nf4(const void *w, int64_t n_out, int64_t k, const void *x, int64_t m, int64_t ldx, void *y,
                     int ofmt, int64_t ldy, void *ws, size_t ws_bytes, hipStream_t s) {
-    if (use_tiled(k, m)) {
+    if (use_tiled(n_out, k, m)) {
         const int64_t tn = (n_out + kBN - 1) / kBN, tm = (m + kBM - 1) / kBM;
         if (tn * tm > 0x7fffffff / 4) return WSL_E_SHAPE;
         const int cus = xcd_cus();
@@ -1422,12 +1439,12 @@ int launch_gemm_nf4(const void *w, int64_t n_out, int64_t k, const void *x, int6
     }
     int splits = nf4_splits(n_out, k, m);
     if (splits > 1 && (ws == nullptr || ws_bytes < gemm_ws_bytes(WSL_W_NF4, n_out, k, m))) splits = 1;
-    int64_t kps = nf4_k_per_split(k, m, splits);
+    int64_t kps = nf4_k_per_split(n_out, k, m, splits);
     splits = static_cast<int>((k + kps - 1) / kps);   // no empty trailing split
     float *wsp = splits > 1 ? static_cast<float *>(ws) : nullptr;
     const auto *wp = static_cast<const uint8_t *>(w);
     const auto *xp = static_cast<const uint16_t *>(x);
-    if (use_x32(k, m)) {
+    if (use_x32(n_out, k, m)) {
         const int64_t gx = (n_out + kX32BlockRows - 1) / kX32BlockRows;
         if (gx > 0x7fffffff) return WSL_E_SHAPE;
         const dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(splits), static_cast<unsigned>(x32_zblocks(m)));
