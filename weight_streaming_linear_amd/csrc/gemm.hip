@@ -1320,17 +1320,21 @@ constexpr int64_t kX32BlockRows = 256 / kX32Kh;
 static int x32_mb(int64_t m) { return m > 32 ? 2 : 1; }
 static int64_t x32_zblocks(int64_t m) { return (m + 32 * x32_mb(m) - 1) / (32 * x32_mb(m)); }
 
+// k split of the shared-X kernels (NF4 and bf16): as many ranges of whole 256-k chunks as
+// keep the grid within one pass over the 256 CUs.
+static int x32_splits(int64_t n_out, int64_t k, int64_t m) {
+    const int64_t blocks = (n_out + kX32BlockRows - 1) / kX32BlockRows * x32_zblocks(m);
+    const int64_t chunks = k / kX32Chunk;
+    int64_t splits = 256 / blocks;
+    if (splits < 1) splits = 1;
+    if (splits > chunks) splits = chunks;
+    if (splits > 64) splits = 64;
+    return static_cast<int>(splits);
+}
+
 static int nf4_splits(int64_t n_out, int64_t k, int64_t m) {
     if (use_tiled(n_out, k, m)) return 1;
-    if (use_x32(n_out, k, m)) {
-        const int64_t blocks = (n_out + kX32BlockRows - 1) / kX32BlockRows * x32_zblocks(m);
-        const int64_t chunks = k / kX32Chunk;
-        int64_t splits = 256 / blocks;
-        if (splits < 1) splits = 1;
-        if (splits > chunks) splits = chunks;
-        if (splits > 64) splits = 64;
-        return static_cast<int>(splits);
-    }
+    if (use_x32(n_out, k, m)) return x32_splits(n_out, k, m);
     const int64_t waves = ((n_out + 32 * kNf4Nb - 1) / (32 * kNf4Nb)) * ((m + 31) / 32);
     const int64_t chunks = (k + 127) / 128;
     int64_t splits = 1;
@@ -1350,7 +1354,7 @@ static int64_t nf4_k_per_split(int64_t n_out, int64_t k, int64_t m, int splits) 
 constexpr int64_t kBf16X32MaxM = 64;
 static bool use_bf16_x32(int64_t k, int64_t m) { return m <= kBf16X32MaxM && (k % kX32Chunk) == 0; }
 static int bf16_splits(int64_t n_out, int64_t k, int64_t m) {
-    return use_bf16_x32(k, m) ? nf4_splits(n_out, k, m) : 1;
+    return use_bf16_x32(k, m) ? x32_splits(n_out, k, m) : 1;
 }
 
 size_t gemm_ws_bytes(int wfmt, int64_t n_out, int64_t k, int64_t m) {
