@@ -85,12 +85,15 @@ def test_gemm_bf16_small(m, n_out, k, ofmt):
     assert ok, f"elem {i}: worst ratio {worst}"
 
 
-# bf16 with M <= 64 and k % 256 == 0: the shared-X kernel (weights loaded straight into
-# MFMA B fragments) -- m < 32, one and two position groups, ragged row counts, a tall
-# matrix without a k split, many k splits with and without a workspace; M = 65 and 130
-# just past it take the tiled kernel.
+# bf16 with k % 256 == 0 where the shared-X kernel runs (M <= 32, and larger M where the
+# launch's time model prefers it to the tiles; weights loaded straight into MFMA B
+# fragments) -- m < 32, one and two position groups, ragged row counts, a tall matrix
+# without a k split, many k splits with and without a workspace, and several position
+# blocks on matrices with few rows (M = 65 to 300).  The last two cases (tall matrices,
+# M = 96 and 160) are where the model picks the tiled kernel.
 @pytest.mark.parametrize("m,n_out,k", [(1, 16, 256), (7, 4109, 2304), (32, 1000, 512), (48, 300, 768),
-                                       (64, 24700, 256), (33, 160, 5120), (65, 257, 1024), (130, 257, 1024)])
+                                       (64, 24700, 256), (33, 160, 5120), (65, 257, 1024), (130, 257, 1024),
+                                       (200, 333, 2048), (300, 512, 4096), (96, 27648, 256), (160, 17500, 512)])
 @pytest.mark.parametrize("ofmt", [wsl.WSL_OUT_F32, wsl.WSL_OUT_BF16])
 @pytest.mark.parametrize("use_ws", [False, True])
 def test_gemm_bf16_shared_x(m, n_out, k, ofmt, use_ws):

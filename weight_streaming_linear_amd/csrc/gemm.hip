@@ -1348,13 +1348,26 @@ static int64_t nf4_k_per_split(int64_t n_out, int64_t k, int64_t m, int splits) 
     return ((chunks + splits - 1) / splits) * unit;
 }
 
-// bf16: the shared-X kernel for M <= 64 with k % 256 == 0 (one position block: further
-// blocks would re-read the 2-byte weights; same splitting rule as the NF4 one), the
-// tiled kernel otherwise.
-constexpr int64_t kBf16X32MaxM = 64;
-static bool use_bf16_x32(int64_t k, int64_t m) { return m <= kBf16X32MaxM && (k % kX32Chunk) == 0; }
+// bf16, k a multiple of 256: the shared-X kernel for M <= 32; above that, the same kind of
+// time model as for NF4, fitted to bf16 measurements: every 64 positions re-stream the
+// 2-byte weights at about 3.2 TB/s; a round of 256 x 256 tiles takes about 30 ns per unit
+// of k, a last round of at most 128 (half) tiles about 21 ns.  Measured (us, tiled /
+// shared-X): 27648x5120 M = 64 106 / 78, M = 96 108 / 135; 5120x27648 M = 128 474 / 118,
+// M = 256 443 / 296, M = 512 446 / 600; 5120x17408 M = 256 281 / 189.  Other k: tiled.
+static bool bf16_x32_faster(int64_t n_out, int64_t k, int64_t m) {
+    const double bytes = 2.0 * static_cast<double>(n_out) * static_cast<double>(k);
+    const double t_x32 = static_cast<double>((m + 63) / 64) * bytes / 3.2e12;
+    const int64_t tiles = ((m + kBM - 1) / kBM) * ((n_out + kBN - 1) / kBN);
+    const int64_t full = tiles / 256, tail = tiles % 256;
+    double per_k = static_cast<double>(full) * 30e-9;
+    if (tail > 0) per_k += tail <= 128 ? 21e-9 : 30e-9;
+    return t_x32 <= per_k * static_cast<double>(k);
+}
+static bool use_bf16_x32(int64_t n_out, int64_t k, int64_t m) {
+    return (k % kX32Chunk) == 0 && (m <= 32 || bf16_x32_faster(n_out, k, m));
+}
 static int bf16_splits(int64_t n_out, int64_t k, int64_t m) {
-    return use_bf16_x32(k, m) ? x32_splits(n_out, k, m) : 1;
+    return use_bf16_x32(n_out, k, m) ? x32_splits(n_out, k, m) : 1;
 }
 
 size_t gemm_ws_bytes(int wfmt, int64_t n_out, int64_t k, int64_t m) {
@@ -1397,7 +1410,7 @@ int launch_gemm_bf16(const void *w, int64_t n_out, int64_t k, const void *x, int
                      int ofmt, int64_t ldy, void *ws, size_t ws_bytes, hipStream_t s) {
     const auto *wp = static_cast<const uint16_t *>(w);
     const auto *xp = static_cast<const uint16_t *>(x);
-    if (!use_bf16_x32(k, m)) {
+    if (!use_bf16_x32(n_out, k, m)) {
         const int64_t tn = (n_out + kBN - 1) / kBN, tm = (m + kBM - 1) / kBM;
         if (tn * tm > 0x7fffffff / 4) return WSL_E_SHAPE;
         const int cus = xcd_cus();
