@@ -9,7 +9,9 @@ built, every call raises.
 
 Entry points (same names as the C ABI):
   nf4_packed_bytes, nf4_codebook, nf4_pack, nf4_dequant_tile,
-  linear_gemv, linear_gemm, linear_gemm_workspace_bytes, wsl_strerror
+  linear_gemv, linear_gemm, linear_gemm_workspace_bytes, nf4_embed_rows, wsl_strerror;
+  stream_read (wsl_stream_read); CopyRing.gemv / CopyRing.gemm (linear_gemv_streamed /
+  linear_gemm_streamed, weights streamed from page-locked host memory, see to_pinned).
 """
 
 import ctypes
