@@ -322,3 +322,43 @@ def test_gemm_deterministic():
     d = wsl.linear_gemm(to_dev_bf16(wb), x)
     torch.cuda.synchronize()
     assert torch.equal(a, b) and torch.equal(c, d)
+
+
+# A captured linear_gemm replays to the eager result: the shared-X kernels with a k split
+# (workspace + reduction kernel) and the tiled kernels.  Each replay follows eager work of
+# the program's own and a synchronization, with the output poisoned first.
+@pytest.mark.parametrize("wfmt,m,n_out,k", [(wsl.WSL_W_NF4, 32, 640, 16384), (wsl.WSL_W_NF4, 300, 1000, 448),
+                                            (wsl.WSL_W_BF16, 200, 700, 1024), (wsl.WSL_W_BF16, 200, 700, 1088)])
+def test_gemm_graph_replays_match_eager(wfmt, m, n_out, k):
+    import torch
+    say(f"gemm graph wfmt={wfmt} m={m} n={n_out} k={k}")
+    wb = synth.weight_bits(91, n_out, n_out, k)
+    xb = synth.act_bits(91, 1000 + m, (m, k))
+    w = wsl.nf4_pack(to_dev_bf16(wb)) if wfmt == wsl.WSL_W_NF4 else to_dev_bf16(wb)
+    x = to_dev_bf16(xb)
+    nb = wsl.linear_gemm_workspace_bytes(wfmt, n_out, k, m)
+    ws = torch.zeros((max(nb, 16) // 4,), dtype=torch.float32, device="cuda")
+    y_eager = wsl.linear_gemm(w, x, wfmt=wfmt, n_out=n_out, k=k, workspace=ws)
+    yg = torch.empty_like(y_eager)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        wsl.linear_gemm(w, x, y=yg, wfmt=wfmt, n_out=n_out, k=k, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        wsl.linear_gemm(w, x, y=yg, wfmt=wfmt, n_out=n_out, k=k, workspace=ws)
+    torch.cuda.synchronize()
+    for r in range(3):
+        yg.fill_(float("nan"))
+        ws.fill_(float("nan"))
+        scratch = torch.randn(4096, device="cuda").sum()   # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(yg, y_eager), f"replay {r}"
+    assert torch.isfinite(scratch)
+    y_ref, s_ref = oracle.gemm_ref(f64(xb), _tile_f64(wb) if wfmt == wsl.WSL_W_NF4 else f64(wb))
+    ok, worst, i = _check(y_eager, y_ref, s_ref, wsl.WSL_OUT_F32)
+    assert ok, f"elem {i}: worst ratio {worst}"
