@@ -828,6 +828,102 @@ def traffic_from_file():
         return None
 
 
+# ---------------------------------------------------------------- MFMA work from rocprofv3 counters
+MFMA_CASES = [("bf16", 8192, 17408, 5120), ("bf16", 8192, 5120, 17408), ("nf4", 8192, 17408, 5120),
+              ("nf4", 8192, 5120, 17408), ("nf4", 32, 27648, 5120), ("nf4", 32, 5120, 27648)]
+
+
+def mfma_probe():
+    """The launches that an MFMA counter run of this script sees: for each GEMM case, in
+    order, two launches of linear_gemm (bf16 out for M = 8192, fp32 for M = 32; the
+    workspace the library asks for).  No timing, no oracle."""
+    import torch
+    import synth
+    import weight_streaming_linear_amd as wsl
+    for i, (fmt, m, n, k) in enumerate(MFMA_CASES):
+        w = synth.device_weight(4, 50 + i, n, k)
+        if fmt == "nf4":
+            w = wsl.nf4_pack(w)
+        wfmt = wsl.WSL_W_NF4 if fmt == "nf4" else wsl.WSL_W_BF16
+        ofmt = wsl.WSL_OUT_BF16 if m > 32 else wsl.WSL_OUT_F32
+        x = synth.device_normal_bf16(4, 60 + i, (m, k))
+        nb = wsl.linear_gemm_workspace_bytes(wfmt, n, k, m)
+        ws = torch.empty(max(nb, 16), dtype=torch.uint8, device="cuda")
+        for _ in range(2):
+            wsl.linear_gemm(w, x, wfmt=wfmt, n_out=n, k=k, ofmt=ofmt, workspace=ws)
+        torch.cuda.synchronize()
+        del w, x, ws
+        torch.cuda.empty_cache()
+    print("mfma probe done", flush=True)
+
+
+def mfma_summarize(run_dir, command):
+    """Markdown summary of a counter run of --mfma-probe: per GEMM case, the MFMA flops the
+    hardware counted (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512) against 2 M N K, and the matrix
+    pipes' busy cycles against the GPU-active cycles.  rocprofv3 writes one value per
+    counter and dispatch, summed over the XCDs (GRBM_GUI_ACTIVE too, so it is divided by
+    the agent's XCD count)."""
+    import csv
+    simds, xccs = 1024, 8
+    for path in glob.glob(os.path.join(run_dir, "**", "*agent_info.csv"), recursive=True):
+        with open(path) as f:
+            for a in csv.DictReader(f):
+                if a.get("Name", "").startswith("gfx"):
+                    simds, xccs = int(a["Simd_Count"]), int(a["Num_Xcc"])
+    disp = {}
+    for path in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                name = r.get("Kernel_Name", "")
+                if "wsl::gemm_" not in name and "wsl::split_reduce" not in name:
+                    continue
+                d = disp.setdefault(r["Dispatch_Id"], {"name": name.split("(")[0].replace("void ", ""),
+                                                       "t": (int(r["Start_Timestamp"]), int(r["End_Timestamp"])),
+                                                       "vals": {}})
+                d["vals"][r["Counter_Name"]] = d["vals"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    # the probe's GEMM launches in order, two per case; a split reduction (no MFMA work) is
+    # listed with the case whose launch it follows
+    cases, idx = [], -1
+    for key in sorted(disp, key=int):
+        d = disp[key]
+        if "split_reduce" in d["name"]:
+            if cases:
+                cases[-1]["reduce"] = True
+            continue
+        idx += 1
+        if idx // 2 >= len(MFMA_CASES):
+            break
+        if idx % 2 == 0:
+            cases.append({"case": MFMA_CASES[idx // 2], "kernel": d["name"], "launches": [], "reduce": False})
+        cases[-1]["launches"].append(d)
+    lines = ["# MFMA work of the GEMM kernels from hardware counters", "",
+             "Command (run from the repository root on one MI355X, ROCm 7.2, rocprofv3):", "", "```", command, "```", "",
+             "Per launch: counted = SQ_INSTS_VALU_MFMA_MOPS_BF16 × 512 (the counter's own flop unit), "
+             f"against 2·M·N·K; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES (all {simds} SIMDs) over {simds} × the "
+             f"GPU-active cycles of one XCD (GRBM_GUI_ACTIVE / {xccs}); clock = those cycles over the launch's "
+             "duration in the counter run; TFLOP/s = counted flops over that duration (launches under a "
+             "counter run are serialized, so these run slightly slower than in the benchmark; for launches "
+             "of a few tens of µs the active-cycle count also takes in dispatch overhead, so the clock "
+             "column over-reads there).  Summary "
+             "written by `python bench.py --mfma-summarize <run dir> <command>`.", "",
+             "| case (M × N × K) | kernel | launches | counted MFMA flop / launch | 2·M·N·K | ratio | MFMA busy | clock (GHz) | TFLOP/s |",
+             "|---|---|---:|---:|---:|---:|---:|---:|---:|"]
+    for c in cases:
+        fmt, m, n, k = c["case"]
+        algo = 2.0 * m * n * k
+        ls = c["launches"]
+        flops = [d["vals"].get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512 for d in ls]
+        cyc = [d["vals"].get("GRBM_GUI_ACTIVE", 0.0) / xccs for d in ls]
+        busy = [d["vals"].get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (simds * max(g, 1.0)) for d, g in zip(ls, cyc)]
+        dur = [max(d["t"][1] - d["t"][0], 1) * 1e-9 for d in ls]
+        kern = c["kernel"] + (" (+ split_reduce_kernel)" if c["reduce"] else "")
+        lines.append(f"| {fmt} {m} × {n} × {k} | `{kern}` | {len(ls)} | {np.mean(flops):.4e} | {algo:.4e} | "
+                     f"{np.mean(flops) / algo:.4f} | {100 * np.mean(busy):.1f} % | "
+                     f"{np.mean([g / t / 1e9 for g, t in zip(cyc, dur)]):.2f} | "
+                     f"{np.mean([f / t / 1e12 for f, t in zip(flops, dur)]):.0f} |")
+    print("\n".join(lines))
+
+
 def trace_summarize(run_dir, title, command):
     """Markdown summary of a rocprofv3 --kernel-trace --output-format csv run: the library's
     dispatches grouped by kernel and grid size (one template instance serves several
@@ -938,6 +1034,8 @@ def main():
     ap.add_argument("--only", default="", help="comma list of paths: " + ",".join(n for n, _ in PATHS))
     ap.add_argument("--traffic-probe", action="store_true", help="launch sequence for rocprofv3 counter runs")
     ap.add_argument("--traffic-summarize", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--mfma-probe", action="store_true", help="GEMM launch sequence for rocprofv3 MFMA counter runs")
+    ap.add_argument("--mfma-summarize", nargs=2, metavar=("RUN_DIR", "COMMAND"))
     ap.add_argument("--traffic-commands", default="", help="the counter commands, recorded with the summary")
     ap.add_argument("--trace-summarize", nargs=3, metavar=("RUN_DIR", "TITLE", "COMMAND"),
                     help="markdown summary of a rocprofv3 kernel-trace CSV run")
@@ -948,12 +1046,15 @@ def main():
     if args.traffic_summarize:
         traffic_summarize(*args.traffic_summarize, args.traffic_commands)
         return
+    if args.mfma_summarize:
+        mfma_summarize(*args.mfma_summarize)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): it measures the kernels on a "
               "single MI355X and has no multi-GPU path. Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
-    if args.repeats > 1 and not args.traffic_probe:
+    if args.repeats > 1 and not args.traffic_probe and not args.mfma_probe:
         sys.exit(run_repeats(args))
 
     import torch
@@ -961,6 +1062,9 @@ def main():
     wsl.lib()
     if args.traffic_probe:
         traffic_probe()
+        return
+    if args.mfma_probe:
+        mfma_probe()
         return
     props = torch.cuda.get_device_properties(0)
     log(f"device {props.name} ({getattr(props, 'gcnArchName', '?')}), {props.multi_processor_count} CUs")
