@@ -37,10 +37,14 @@ def test_gemv_nf4_tolerance(n_out, k):
     assert ok, f"row {i}: worst ratio {worst}"
 
 
-@pytest.mark.parametrize("n_out,k", [(4099, 2112), (37, 32832), (130, 40960), (20, 2048), (16, 64)])
+@pytest.mark.parametrize("n_out,k", [(4099, 2112), (37, 32832), (130, 40960), (20, 2048), (16, 64), (3073, 16384),
+                                     (1029, 16384)])
 def test_gemv_nf4_plan_edges(n_out, k):
     """Row counts that leave a partial 16-row block and row groups outside the pipelined
-    loop; k > 32768 (several slices per wave); k = 2048 (one full slice)."""
+    loop; k > 32768 (several slices per wave); k = 2048 (one full slice).  3073x16384 and
+    1029x16384: every workgroup runs an odd number of pipelined row groups without the
+    parking flush, then a leftover round in which one team has no row (its partials must
+    not overwrite those wave 0 is still summing)."""
     say(f"gemv nf4 {n_out}x{k}")
     y, y_ref, s_ref = _nf4_case(n_out, k, 97, 0, 1)
     ok, worst, i = oracle.check_rows_f32(y, y_ref, s_ref)

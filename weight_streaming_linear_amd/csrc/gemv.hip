@@ -461,9 +461,12 @@ __global__ __launch_bounds__(1024) void gemv_nf4_team_kernel(const uint8_t *__re
     // rows clamped to the matrix and scales read one row at a time.  They go to the
     // last workgroups, which own one super-group fewer than the first ones when the
     // super-groups do not divide evenly, so the leftovers do not lengthen the kernel.
+    // The first leftover round uses the reduction buffer the last consume() did not:
+    // without the flush's barriers (n < 4) a team of this round may write its partials
+    // while wave 0 still reads that consume()'s partials from the other buffer.
     const int64_t left0 = supers * T;
     const int64_t nleft = row_groups - left0;
-    int it = 0;
+    int it = ph;
     for (int64_t b = gridDim.x - 1 - blockIdx.x; b * T < nleft; b += gridDim.x) {
         const int64_t rg = left0 + b * T + team;
         float acc[R];
