@@ -96,6 +96,42 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _require(t, name, dtypes, device=None, contiguous=False, ndim=None):
+    """Raise ValueError unless t is a device tensor of one of ``dtypes`` whose last
+    dimension is unit-stride (whole tensor contiguous if ``contiguous``), on ``device``.
+    The C ABI reads raw row-major memory, so a transposed or sliced view, or a tensor of
+    another element type, must be refused here rather than misread."""
+    if not t.is_cuda:
+        raise ValueError(f"{name}: expected a GPU tensor, got one on {t.device}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name}: dtype {t.dtype} not in {[str(d) for d in dtypes]}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name}: expected {ndim} dimensions, got shape {tuple(t.shape)}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if t.dim() > 0 and t.numel() > 1 and t.stride(-1) != 1:
+        raise ValueError(f"{name}: last dimension must have stride 1 (got strides {t.stride()})")
+
+
+def _weight(w, wfmt, n_out, k, name="w"):
+    """Check a weight tensor against its format and shape: bf16 [n_out][k] contiguous, or a
+    contiguous uint8 buffer of at least nf4_packed_bytes(n_out, k) bytes."""
+    import torch
+    if wfmt == WSL_W_NF4:
+        _require(w, name, (torch.uint8,), contiguous=True)
+        need = nf4_packed_bytes(n_out, k)
+        if need and w.numel() < need:
+            raise ValueError(f"{name}: {w.numel()} bytes, a packed {n_out}x{k} matrix needs {need}")
+    elif wfmt == WSL_W_BF16:
+        _require(w, name, (torch.bfloat16,), contiguous=True)
+        if w.numel() < n_out * k:
+            raise ValueError(f"{name}: {w.numel()} elements, a {n_out}x{k} bf16 matrix needs {n_out * k}")
+    else:
+        raise ValueError(f"{name}: unknown weight format {wfmt}")
+
+
 def _stream(stream):
     import torch
     if stream is None:
@@ -119,8 +155,15 @@ def nf4_codebook():
 def nf4_pack(w, packed=None, status=None, stream=None):
     """Encode a bf16 [n_out][k] device tensor into a packed NF4 uint8 device tensor."""
     import torch
+    _require(w, "w", (torch.bfloat16,), contiguous=True, ndim=2)
     n_out, k = w.shape
     nbytes = nf4_packed_bytes(n_out, k)
+    if packed is not None:
+        _require(packed, "packed", (torch.uint8,), device=w.device, contiguous=True)
+        if packed.numel() < nbytes:
+            raise ValueError(f"packed: {packed.numel()} bytes, {n_out}x{k} needs {nbytes}")
+    if status is not None:
+        _require(status, "status", (torch.int32, torch.uint32), device=w.device)
     if packed is None:
         packed = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=w.device)
     rc = lib().nf4_pack(_ptr(w), n_out, k, _ptr(packed), _ptr(status), _stream(stream))
@@ -131,9 +174,11 @@ def nf4_pack(w, packed=None, status=None, stream=None):
 def nf4_dequant_tile(packed, n_out, k, row0, k0, rows, cols, tile=None, ld_tile=None, stream=None):
     """Restore the bf16 tile [rows][cols] at (row0, k0) of a packed NF4 matrix."""
     import torch
+    _weight(packed, WSL_W_NF4, n_out, k, "packed")
     if tile is None:
         tile = torch.empty((rows, cols), dtype=torch.bfloat16, device=packed.device)
         ld_tile = cols
+    _require(tile, "tile", (torch.bfloat16,), device=packed.device)
     if ld_tile is None:
         ld_tile = tile.stride(0)
     rc = lib().nf4_dequant_tile(_ptr(packed), n_out, k, row0, k0, rows, cols, _ptr(tile), ld_tile, _stream(stream))
@@ -144,10 +189,15 @@ def nf4_dequant_tile(packed, n_out, k, row0, k0, rows, cols, tile=None, ld_tile=
 def nf4_embed_rows(packed, n_rows, k, ids, out=None, ofmt=WSL_OUT_BF16, status=None, stream=None):
     """Restore rows ids (int64 device tensor) of a packed NF4 [n_rows][k] matrix into out [count][>= k]."""
     import torch
+    _weight(packed, WSL_W_NF4, n_rows, k, "packed")
+    _require(ids, "ids", (torch.int64,), device=packed.device, contiguous=True)
     count = int(ids.numel())
+    dt = torch.bfloat16 if ofmt == WSL_OUT_BF16 else torch.float32
     if out is None:
-        dt = torch.bfloat16 if ofmt == WSL_OUT_BF16 else torch.float32
         out = torch.empty((count, k), dtype=dt, device=packed.device)
+    _require(out, "out", (dt,), device=packed.device, ndim=2)
+    if status is not None:
+        _require(status, "status", (torch.int32, torch.uint32), device=packed.device)
     rc = lib().nf4_embed_rows(_ptr(packed), n_rows, k, _ptr(ids), count, _ptr(out), int(ofmt), out.stride(0),
                               _ptr(status), _stream(stream))
     _check(rc, "nf4_embed_rows")
@@ -161,8 +211,15 @@ def linear_gemv(w, x, y=None, wfmt=None, n_out=None, k=None, stream=None):
         wfmt = WSL_W_NF4 if w.dtype == torch.uint8 else WSL_W_BF16
     if n_out is None or k is None:
         n_out, k = w.shape
+    _weight(w, wfmt, n_out, k)
+    _require(x, "x", (torch.bfloat16,), device=w.device, contiguous=True)
+    if x.numel() < k:
+        raise ValueError(f"x: {x.numel()} elements, k = {k}")
     if y is None:
         y = torch.empty(n_out, dtype=torch.float32, device=x.device)
+    _require(y, "y", (torch.float32,), device=w.device, contiguous=True)
+    if y.numel() < n_out:
+        raise ValueError(f"y: {y.numel()} elements, n_out = {n_out}")
     rc = lib().linear_gemv(int(wfmt), _ptr(w), n_out, k, _ptr(x), _ptr(y), _stream(stream))
     _check(rc, "linear_gemv")
     return y
@@ -179,10 +236,19 @@ def linear_gemm(w, x, y=None, wfmt=None, n_out=None, k=None, ofmt=WSL_OUT_F32, w
         wfmt = WSL_W_NF4 if w.dtype == torch.uint8 else WSL_W_BF16
     if n_out is None or k is None:
         n_out, k = w.shape
+    _weight(w, wfmt, n_out, k)
+    _require(x, "x", (torch.bfloat16,), device=w.device, ndim=2)
+    if x.shape[1] < k:
+        raise ValueError(f"x: shape {tuple(x.shape)}, k = {k}")
     m = x.shape[0]
+    dt = torch.float32 if ofmt == WSL_OUT_F32 else torch.bfloat16
     if y is None:
-        dt = torch.float32 if ofmt == WSL_OUT_F32 else torch.bfloat16
         y = torch.empty((m, n_out), dtype=dt, device=x.device)
+    _require(y, "y", (dt,), device=w.device, ndim=2)
+    if y.shape[0] < m or y.shape[1] < n_out:
+        raise ValueError(f"y: shape {tuple(y.shape)}, need at least ({m}, {n_out})")
+    if workspace is not None:
+        _require(workspace, "workspace", (workspace.dtype,), device=w.device, contiguous=True)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = lib().linear_gemm(int(wfmt), _ptr(w), n_out, k, _ptr(x), m, x.stride(0), _ptr(y), int(ofmt), y.stride(0),
                            _ptr(workspace), ws_bytes, _stream(stream))
@@ -238,7 +304,16 @@ class CopyRing:
         for e in self.events:
             e.record()          # creates the events; a recorded, completed event is a no-op to wait on
 
-    def _common(self, mats):
+    def _common(self, mats, xs, ys, x_dtype, y_dtypes):
+        import torch
+        if not (len(mats) == len(xs) == len(ys)):
+            raise ValueError(f"{len(mats)} matrices, {len(xs)} inputs, {len(ys)} outputs")
+        dev = self.slots[0].device
+        for i, ((h, _, _), x, y) in enumerate(zip(mats, xs, ys)):
+            if h.is_cuda or not h.is_contiguous():
+                raise ValueError(f"matrix {i}: expected a contiguous host tensor (see to_pinned)")
+            _require(x, f"x[{i}]", (x_dtype,), device=dev)
+            _require(y, f"y[{i}]", y_dtypes, device=dev)
         hs = _ptr_array([h for h, _, _ in mats])
         ns = _i64_array([n for _, n, _ in mats])
         ks = _i64_array([k for _, _, k in mats])
@@ -248,7 +323,8 @@ class CopyRing:
 
     def gemv(self, mats, xs, ys, wfmt=WSL_W_NF4, stream=None):
         """mats: [(pinned host tensor, n_out, k)]; xs: bf16 [k] device tensors; ys: fp32 [n_out]."""
-        hs, ns, ks, slots, evs = self._common(mats)
+        import torch
+        hs, ns, ks, slots, evs = self._common(mats, xs, ys, torch.bfloat16, (torch.float32,))
         rc = lib().linear_gemv_streamed(int(wfmt), len(mats), hs, ns, ks, _ptr_array(xs), _ptr_array(ys), slots,
                                         self.slot_bytes, ctypes.c_void_p(self.copy_stream.cuda_stream),
                                         _stream(stream), evs)
@@ -256,7 +332,9 @@ class CopyRing:
         return ys
 
     def gemm(self, mats, xs, ys, m, ldx, ldy, wfmt=WSL_W_NF4, ofmt=WSL_OUT_F32, workspace=None, stream=None):
-        hs, ns, ks, slots, evs = self._common(mats)
+        import torch
+        ydt = torch.float32 if ofmt == WSL_OUT_F32 else torch.bfloat16
+        hs, ns, ks, slots, evs = self._common(mats, xs, ys, torch.bfloat16, (ydt,))
         nb = 0 if workspace is None else workspace.numel() * workspace.element_size()
         rc = lib().linear_gemm_streamed(int(wfmt), len(mats), hs, ns, ks, _ptr_array(xs), int(m), int(ldx),
                                         _ptr_array(ys), int(ofmt), int(ldy), _ptr(workspace), nb, slots,
