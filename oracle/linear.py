@@ -57,11 +57,16 @@ def check_rows_f32(y, y_ref, s, rel=REL_TOL):
 
 
 def ulp_bf16(v):
-    """Spacing of bf16 values at |v| (2^(e-7) for |v| in [2^e, 2^(e+1)); min normal spacing below)."""
+    """Spacing of bf16 values in the binade that holds |v|: 2^(e-7) for |v| in [2^e, 2^(e+1)),
+    and the subnormal spacing 2^-133 for |v| < 2^-126 (0 included).
+
+    The binade e is read exactly from the binary exponent (frexp gives |v| = f * 2^x with
+    f in [0.5, 1), so e = x - 1); a logarithm would round values just below a power of two
+    up into the next binade."""
     v = np.abs(np.asarray(v, dtype=np.float64))
-    e = np.floor(np.log2(np.where(v > 0, v, 1.0)))
-    e = np.maximum(e, -126.0)
-    return np.where(v > 0, np.exp2(e - 7.0), np.exp2(-133.0))
+    _, x = np.frexp(v)
+    e = np.maximum(x.astype(np.int64) - 1, -126)
+    return np.where(v > 0, np.ldexp(1.0, e - 7), np.ldexp(1.0, -133))
 
 
 def check_bf16(y_bits, y_ref, s, rel=REL_TOL):

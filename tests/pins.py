@@ -189,6 +189,35 @@ def brute_code(w, s, levels):
     return bi
 
 
+_FIX = 200   # every bf16, fp16 and binary32 value and every product c*s is an integer multiple of 2^-200
+
+
+def _fixed(v):
+    """v * 2^_FIX as an exact Python integer (v a float whose lowest bit is >= 2^-200)."""
+    n, d = float(v).as_integer_ratio()
+    q, r = divmod(n << _FIX, d)
+    assert r == 0
+    return q
+
+
+def brute_codes_exact(ws, s, levels):
+    """Exact nearest-level codes for many w at one scale s > 0: argmin_i |w - c_i s| (the
+    same order as |w/s - c_i|, s being positive) over all 16 levels, ties to the lower index,
+    in integer arithmetic on multiples of 2^-200.  Plain brute force, no midpoints."""
+    ts = [_fixed(float(c)) * _fixed(s) >> _FIX for c in levels]
+    assert all(_fixed(float(c)) * _fixed(s) % (1 << _FIX) == 0 for c in levels)
+    out = []
+    for w in ws:
+        wi = _fixed(w)
+        best, bi = None, 0
+        for i, t in enumerate(ts):
+            d = abs(wi - t)
+            if best is None or d < best:
+                best, bi = d, i
+        out.append(bi)
+    return out
+
+
 def _groups_for(anchor, ws):
     """One 64-wide group per candidate w: [anchor, w, 0, ...]; anchor fixes the absmax."""
     m = np.zeros((len(ws), 64), dtype=np.float64)
@@ -197,23 +226,28 @@ def _groups_for(anchor, ws):
     return m
 
 
-def pin_code_rule_bruteforce():
-    """For several scales (normal, fp16-subnormal, and s < absmax from rounding), every bf16
-    w in [-absmax, absmax] and every midpoint * s (+- one binary32 ulp): oracle code ==
-    exact argmin with ties to the lower index."""
+# Group absmax values a (the anchor of every test group) and the stored scale s = fp16(a)
+# they give: s == a (1.0, 0.0234375), s < a by fp16 rounding (1 + 2^-12 and 3 - 2^-12 round
+# down), fp16-subnormal scales where s < a by up to half a subnormal step (1.46875 * 2^-24
+# stores s = 2^-24, so |w| / s reaches 1.47 and the grid covers [-1.1 s, 1.1 s] and beyond),
+# and s > a (3 * 2^-25 rounds up to 2^-23; 2^-20 * 1.0078125 is exact).
+CODE_RULE_ANCHORS = [1.0, 0.0234375, 2.0 ** -20 * 1.0078125, 1.0 + 2.0 ** -12, 3.0 - 2.0 ** -12, 6e-8,
+                     1.46875 * 2.0 ** -24, 3.0 * 2.0 ** -25]
+
+
+def pin_code_rule_bruteforce(anchors=None):
+    """For each anchor absmax a: EVERY bf16 value w with |w| <= a (both signs, +-0, the
+    subnormals) and every midpoint * s (+- one binary32 ulp) in that range: oracle code ==
+    exact argmin over the 16 levels with ties to the lower index (integer arithmetic)."""
     levels = ocb.nf4_levels_f32()
     mids = (levels[:-1].astype(np.float64) + levels[1:].astype(np.float64)) / 2.0
-    # (anchor value, stride over the bf16 grid) -- anchors chosen to exercise s == a,
-    # s < a (fp16 rounds down: fp16-subnormal and binary32 anchors) and s > a.
-    anchors = [1.0, 0.0234375, 2.0 ** -20 * 1.0078125, 1.0 + 2.0 ** -12, 3.0 - 2.0 ** -12, 6e-8]
-    for a in anchors:
+    all_bits = np.arange(0, 0x7F80, dtype=np.uint16)
+    all_vals = onum.f32_from_bf16_bits(all_bits).astype(np.float64)
+    for a in (CODE_RULE_ANCHORS if anchors is None else anchors):
         s = float(np.float64(a).astype(np.float16))
         if s == 0.0:
             continue
-        bits = np.arange(0, 0x7F80, dtype=np.uint16)
-        vals = onum.f32_from_bf16_bits(bits).astype(np.float64)
-        vals = vals[vals <= a]
-        vals = vals[np.linspace(0, vals.size - 1, min(vals.size, 6000)).astype(np.int64)]
+        vals = all_vals[all_vals <= a]
         cand = np.concatenate([vals, -vals])
         ex = mids * s
         near = np.concatenate([ex, np.nextafter(ex.astype(np.float32), np.float32(np.inf)).astype(np.float64),
@@ -223,10 +257,21 @@ def pin_code_rule_bruteforce():
         codes, scales = onf4.pack_codes(_groups_for(a, cand))
         if np.any(scales[:, 0].astype(np.float64) != s):
             return False
-        for w, code in zip(cand.tolist(), codes[:, 1].tolist()):
-            if code != brute_code(w, s, levels):
-                return False
+        if codes[:, 1].tolist() != brute_codes_exact(cand.tolist(), s, levels):
+            return False
         if np.any(codes[:, 2:] != 7):
+            return False
+    return True
+
+
+def pin_code_rule_fraction_spotcheck():
+    """The integer brute force itself against Fraction argmin on a few hundred values."""
+    levels = ocb.nf4_levels_f32()
+    rng = np.random.default_rng(41)
+    for a in (1.0, 6e-8, 3.0 - 2.0 ** -12):
+        s = float(np.float64(a).astype(np.float16))
+        ws = (rng.uniform(-1.0, 1.0, 300) * a).astype(np.float32).astype(np.float64).tolist()
+        if brute_codes_exact(ws, s, levels) != [brute_code(w, s, levels) for w in ws]:
             return False
     return True
 
@@ -457,10 +502,71 @@ def pin_tolerance_checker():
     return ok1 and (not ok2) and i2 == 1 and (not ok3) and (not ok4)
 
 
+def _exact_bf16_spacing(q):
+    """Spacing of the bf16 grid in the binade of a non-negative rational q: 2^(e-7) for q in
+    [2^e, 2^(e+1)), e >= -126; 2^-133 below 2^-126 (subnormals) and at 0."""
+    if q == 0:
+        return Fraction(1, 2 ** 133)
+    return Fraction(2) ** (max(_floor_log2(q), -126) - 7)
+
+
+def pin_ulp_bf16_exact(seed=43):
+    """ulp_bf16 against exact rational spacing: at every positive finite bf16 value (where it
+    must also equal the gap to the next bf16 value up), the binary64 value just below and just
+    above each of them, every power of two from 2^-140 to 2^127 and its neighbours, zero, the
+    subnormal range, negative arguments, and a log-uniform binary64 sample."""
+    bits = all_positive_finite_bf16_bits()
+    vals = onum.f32_from_bf16_bits(bits).astype(np.float64)
+    nxt = onum.f32_from_bf16_bits(bits + np.uint16(1)).astype(np.float64)
+    gap_ok = bits < 0x7F7F                                   # the next pattern up is finite
+    got = olin.ulp_bf16(vals)
+    if not np.array_equal(got[gap_ok], (nxt - vals)[gap_ok]):
+        return False
+    pw = np.ldexp(1.0, np.arange(-140, 128))
+    rng = np.random.default_rng(seed)
+    sample = np.ldexp(rng.uniform(1.0, 2.0, 4000), rng.integers(-150, 128, 4000))
+    probes = np.concatenate([vals, np.nextafter(vals, 0.0), np.nextafter(vals, np.inf), pw,
+                             np.nextafter(pw, 0.0), np.nextafter(pw, np.inf), sample, [0.0, 5e-324, 1e-40]])
+    probes = probes[np.isfinite(probes)]
+    got = olin.ulp_bf16(probes)
+    want = [_exact_bf16_spacing(Fraction(float(v))) for v in probes.tolist()]
+    if any(Fraction(float(g)) != w for g, w in zip(got.tolist(), want)):
+        return False
+    neg = olin.ulp_bf16(-probes)
+    return bool(np.array_equal(neg, got)) and np.ndim(olin.ulp_bf16(1.0)) == 0
+
+
+def pin_check_bf16_boundary():
+    """check_bf16 accepts an error of exactly 1e-4*S + ulp(|y_ref|) and rejects one bf16 step
+    beyond it, and rejects a binary64 hair beyond it.  Built so every quantity is exact in
+    binary64: S = 10000 (fl(1e-4) * 10000 rounds to exactly 1), y_ref in [1024, 2048) where the
+    bf16 spacing is 8, so the allowed error is 9; the bf16 values are multiples of 8 there."""
+    b = lambda v: onum.bf16_bits_from_f32(np.array([v], np.float32))
+    S = np.array([10000.0])
+    if float(np.float64(olin.REL_TOL) * 10000.0) != 1.0:
+        return False
+    cases = [  # (bf16 output, y_ref, accepted?)
+        (1040.0, 1031.0, True), (1048.0, 1031.0, False), (1040.0, float(np.nextafter(1031.0, 0.0)), False),
+        (-1040.0, -1031.0, True), (-1048.0, -1031.0, False), (1024.0, 1033.0, True), (1016.0, 1025.0, True),
+        (1016.0, float(np.nextafter(1025.0, 0.0)), True), (1008.0, 1025.0, False),
+    ]
+    for yv, r, want in cases:
+        ok, _, _ = olin.check_bf16(b(yv), np.array([r]), S)
+        if ok != want:
+            return False
+    # S = 0: the bound is one ulp of |y_ref|; just below a power of two the ulp is the lower binade's
+    ok_lo, _, _ = olin.check_bf16(b(1.0), np.array([1.0 - 2.0 ** -8]), np.array([0.0]))
+    bad_lo, _, _ = olin.check_bf16(b(1.0), np.array([float(np.nextafter(1.0 - 2.0 ** -8, 0.0))]), np.array([0.0]))
+    nan_out, _, _ = olin.check_bf16(np.array([0x7FC0], np.uint16), np.array([1.0]), np.array([1.0]))
+    return ok_lo and not bad_lo and not nan_out
+
+
 ALL_PINS = [
     pin_fp16_rounding_exhaustive, pin_fp16_rounding_f32_sample, pin_bf16_rounding,
     pin_codebook_invariants, pin_codebook_recomputed, pin_code_rule_bruteforce,
+    pin_code_rule_fraction_spotcheck,
     pin_pack_invariants, pin_tile_rounding_exhaustive, pin_byte_fixtures,
     pin_layout_roundtrip, pin_roundtrip_idempotent, pin_gemv_bruteforce,
     pin_gemm_bruteforce, pin_exact_integer_cases, pin_tolerance_checker,
+    pin_ulp_bf16_exact, pin_check_bf16_boundary,
 ]

@@ -96,6 +96,34 @@ def _dev_rot4(code_bytes, scales):
     return base
 
 
+_orig_ulp = olin.ulp_bf16
+
+
+def _ulp_doubled(v):
+    return 2.0 * _orig_ulp(v)
+
+
+def _ulp_binade_low(v):
+    """The binade taken one too low: half the spacing everywhere."""
+    return 0.5 * _orig_ulp(v)
+
+
+def _ulp_binade_high_near_powers(v):
+    """The binade read with a rounded logarithm: values just below a power of two land in the
+    binade above (the defect an inexact log2 makes)."""
+    v = np.abs(np.asarray(v, dtype=np.float64))
+    e = np.maximum(np.floor(np.log2(np.where(v > 0, v, 1.0))), -126.0)
+    return np.where(v > 0, np.exp2(e - 7.0), np.exp2(-133.0))
+
+
+def _check_bf16_no_ulp(y_bits, y_ref, s, rel=olin.REL_TOL):
+    y = onum.f32_from_bf16_bits(y_bits).astype(np.float64)
+    err = np.abs(y - np.asarray(y_ref, np.float64))
+    ratio = err / np.maximum(rel * np.asarray(s, np.float64), 1e-300)
+    i = int(np.argmax(ratio))
+    return bool(ratio[i] <= 1.0), float(ratio[i]), i
+
+
 DEFECTS = [
     ("swapped nibble order", onf4, "codes_to_bytes", _swap_nibbles, [pins.pin_byte_fixtures]),
     ("scale of the wrong group", onf4, "dequant_exact", _wrong_group_dequant, [pins.pin_pack_invariants]),
@@ -109,6 +137,12 @@ DEFECTS = [
     ("GEMM reversed reduction index", olin, "gemm_ref", _gemm_reversed_k, [pins.pin_gemm_bruteforce]),
     ("midpoints replaced by upper levels", onf4, "nf4_midpoints", _mids_upper, [pins.pin_code_rule_bruteforce]),
     ("device word rotated by 4", onf4, "device_from_canonical", _dev_rot4, [pins.pin_byte_fixtures]),
+    ("bf16 ulp doubled", olin, "ulp_bf16", _ulp_doubled, [pins.pin_ulp_bf16_exact, pins.pin_check_bf16_boundary]),
+    ("bf16 ulp binade one too low", olin, "ulp_bf16", _ulp_binade_low,
+     [pins.pin_ulp_bf16_exact, pins.pin_check_bf16_boundary]),
+    ("bf16 ulp binade from a rounded log2", olin, "ulp_bf16", _ulp_binade_high_near_powers,
+     [pins.pin_ulp_bf16_exact]),
+    ("bf16 checker without the rounding ulp", olin, "check_bf16", _check_bf16_no_ulp, [pins.pin_check_bf16_boundary]),
 ]
 
 
