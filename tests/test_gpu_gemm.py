@@ -192,6 +192,54 @@ def test_gemm_nf4_prefill_m32_full_shape_sampled(n_out, k, tid):
     assert ok, f"elem {i}: worst ratio {worst}"
 
 
+# NF4 prefill chunks of more than 32 positions on the 32B-class up projection (5120 -> 27648):
+# M = 64 and 128 take the shared-X kernel (two position groups per workgroup, 1 and 2 position
+# blocks), M = 256 the tiled kernel, as the launch's time model decides for this shape.
+@pytest.mark.parametrize("m", [64, 128, 256])
+def test_gemm_nf4_up_27648x5120_mid_m_sampled(m):
+    import torch
+    say(f"gemm nf4 up 27648x5120 m={m}")
+    n_out, k = 27648, 5120
+    wb = synth.weight_bits(3, 700, n_out, k)
+    xb = synth.act_bits(3, 40 + m, (m, k))
+    w_dev = to_dev_bf16(wb)
+    packed = wsl.nf4_pack(w_dev)
+    del w_dev
+    nb = wsl.linear_gemm_workspace_bytes(wsl.WSL_W_NF4, n_out, k, m)
+    ws = torch.empty(max(nb, 16), dtype=torch.uint8, device="cuda")
+    y = wsl.linear_gemm(packed, to_dev_bf16(xb), wfmt=wsl.WSL_W_NF4, n_out=n_out, k=k, workspace=ws)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(71 + m)
+    cols = _sample_idx(n_out, 128, rng, 160)
+    y_ref, s_ref = oracle.gemm_ref(f64(xb), _tile_f64(wb[cols]))
+    ok, worst, i = oracle.check_rows_f32(y.cpu().numpy()[:, cols], y_ref, s_ref)
+    assert ok, f"elem {i}: worst ratio {worst}"
+
+
+def test_binding_refuses_misread_tensors():
+    """The binding refuses what the C ABI would read as something else: a transposed X, an
+    fp32 X, a non-contiguous bf16 weight, an output of the wrong type, a short packed buffer."""
+    import torch
+    n_out, k, m = 64, 256, 8
+    w = to_dev_bf16(synth.weight_bits(110, 0, n_out, k))
+    packed = wsl.nf4_pack(w)
+    x = to_dev_bf16(synth.act_bits(110, 1, (m, k)))
+    bad = [
+        lambda: wsl.linear_gemm(w, x.t().contiguous().t()),                        # column-major view
+        lambda: wsl.linear_gemm(w, x.float()),                                     # fp32 activations
+        lambda: wsl.linear_gemm(torch.cat([w, w], 1)[:, ::2], x),                  # strided weight
+        lambda: wsl.linear_gemm(w, x, y=torch.empty((m, n_out), dtype=torch.float16, device="cuda")),
+        lambda: wsl.linear_gemv(packed[:-1], x[0], wfmt=wsl.WSL_W_NF4, n_out=n_out, k=k),
+        lambda: wsl.linear_gemv(w, x[0].float()),
+        lambda: wsl.linear_gemv(w, x[:, 0]),                                       # strided vector
+        lambda: wsl.nf4_pack(w.t()),
+    ]
+    for i, f in enumerate(bad):
+        with pytest.raises(ValueError):
+            f()
+    torch.cuda.synchronize()
+
+
 # The tiled bf16 kernel runs one workgroup per CU; an XCD whose last round would leave at
 # least half its 32 CUs idle runs those tiles as two 128-row halves.  264 tiles of 256 x 256
 # give each XCD 33: 32 whole tiles and one split; 36 tiles split every one (every output

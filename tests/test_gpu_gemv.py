@@ -89,9 +89,11 @@ def _bf16_case(n_out, k, stream, tid_w, tid_x):
     return y.cpu().numpy(), y_ref, s_ref
 
 
-# One dense decoder layer with hidden size 5120: k/v 1024 rows, gate/up 17408 rows, down k = 17408.
+# One dense decoder layer with hidden size 5120: k/v 1024 rows, gate/up 17408 rows, down k = 17408;
+# fused q/k/v 7168 rows and fused gate/up 34816 rows (every row of every shape is checked).
 @pytest.mark.parametrize("n_out,k,tid", [(5120, 5120, 0), (1024, 5120, 1), (17408, 5120, 4), (5120, 17408, 6),
-                                         (7168, 5120, 10), (3, 8, 11), (5, 520, 12), (1, 4104, 13), (333, 1000, 14)])
+                                         (7168, 5120, 10), (34816, 5120, 15), (3, 8, 11), (5, 520, 12),
+                                         (1, 4104, 13), (333, 1000, 14)])
 def test_gemv_bf16_tolerance(n_out, k, tid):
     say(f"gemv bf16 {n_out}x{k}")
     y, y_ref, s_ref = _bf16_case(n_out, k, 1, tid, 100 + tid)

@@ -1,14 +1,17 @@
 """Copy ring (linear_gemv_streamed / linear_gemm_streamed): matrices held in page-locked
-host memory, streamed through two device slots, give the same bits as the resident calls."""
+host memory, streamed through two device slots.  Every streamed output is checked against
+the fp64 oracle (deep-fold README, "Метод" table and Figure 1: the same kernels read the
+matrices from the slots), and must also equal the resident call bit for bit."""
 
 import ctypes
 
 import numpy as np
 import pytest
 
+import oracle
 import synth
 import weight_streaming_linear_amd as wsl
-from gpu_common import say
+from gpu_common import to_dev_bf16, f64, say
 
 pytestmark = pytest.mark.gpu
 
@@ -16,55 +19,82 @@ SHAPES = [(1000, 512), (257, 2048), (4096, 320), (64, 6144), (3000, 1024), (17, 
 
 
 def _stack(wfmt):
-    import torch
-    mats, dev = [], []
+    """Seeded host weights (bf16 bits), their device form, pinned host copies, and the slot size."""
+    mats, dev, bits = [], [], []
     for i, (n, k) in enumerate(SHAPES):
-        w = synth.device_weight(105, i, n, k)
+        wb = synth.weight_bits(105, i, n, k)
+        w = to_dev_bf16(wb)
         d = wsl.nf4_pack(w) if wfmt == wsl.WSL_W_NF4 else w
+        bits.append(wb)
         dev.append(d)
         mats.append((wsl.to_pinned(d), n, k))
     nbytes = max((wsl.nf4_packed_bytes(n, k) if wfmt == wsl.WSL_W_NF4 else 2 * n * k) for n, k in SHAPES)
-    return mats, dev, nbytes
+    return mats, dev, bits, nbytes
+
+
+def _gemv_ref(wfmt, wb, xb):
+    if wfmt == wsl.WSL_W_NF4:
+        codes, scales = oracle.pack_codes(f64(wb))
+        return oracle.gemv_ref(oracle.dequant_exact(codes, scales), f64(xb))
+    return oracle.gemv_ref(f64(wb), f64(xb))
 
 
 @pytest.mark.parametrize("wfmt", [wsl.WSL_W_NF4, wsl.WSL_W_BF16])
-def test_gemv_streamed_matches_resident(wfmt):
+def test_gemv_streamed_against_oracle(wfmt):
     import torch
     say(f"ring gemv wfmt={wfmt}")
-    mats, dev, nbytes = _stack(wfmt)
-    xs = [synth.device_normal_bf16(105, 100 + i, (k,)) for i, (_, k) in enumerate(SHAPES)]
+    mats, dev, bits, nbytes = _stack(wfmt)
+    xbs = [synth.act_bits(105, 100 + i, (k,)) for i, (_, k) in enumerate(SHAPES)]
+    xs = [to_dev_bf16(b) for b in xbs]
+    refs = [_gemv_ref(wfmt, wb, xb) for wb, xb in zip(bits, xbs)]
     want = [wsl.linear_gemv(d, x, wfmt=wfmt, n_out=n, k=k) for d, x, (n, k) in zip(dev, xs, SHAPES)]
     ring = wsl.CopyRing(nbytes)
     for rep in range(3):               # the slots and events carry over between calls
         ys = [torch.full((n,), float("nan"), dtype=torch.float32, device="cuda") for n, _ in SHAPES]
         ring.gemv(mats, xs, ys, wfmt=wfmt)
         torch.cuda.synchronize()
-        for i, (y, w) in enumerate(zip(ys, want)):
-            assert torch.equal(y, w), f"matrix {i} differs on call {rep}"
+        for i, (y, w, (y_ref, s_ref)) in enumerate(zip(ys, want, refs)):
+            ok, worst, r = oracle.check_rows_f32(y.cpu().numpy(), y_ref, s_ref)
+            assert ok, f"matrix {i} {SHAPES[i]} call {rep}: row {r} worst ratio {worst}"
+            assert torch.equal(y, w), f"matrix {i} differs from the resident call on call {rep}"
 
 
-def test_gemm_streamed_matches_resident():
+@pytest.mark.parametrize("ofmt", [wsl.WSL_OUT_F32, wsl.WSL_OUT_BF16])
+def test_gemm_streamed_against_oracle(ofmt):
     import torch
-    say("ring gemm")
-    mats, dev, nbytes = _stack(wsl.WSL_W_NF4)
+    say(f"ring gemm ofmt={ofmt}")
+    mats, dev, bits, nbytes = _stack(wsl.WSL_W_NF4)
     m = 32
     kmax = max(k for _, k in SHAPES)
-    xs = [synth.device_normal_bf16(106, 100 + i, (m, k)) for i, (_, k) in enumerate(SHAPES)]
+    xbs = [synth.act_bits(106, 100 + i, (m, k)) for i, (_, k) in enumerate(SHAPES)]
     # one shared leading dimension: X rows padded to kmax, Y rows to the largest n_out
     nmax = max(n for n, _ in SHAPES)
     xp = [torch.zeros((m, kmax), dtype=torch.bfloat16, device="cuda") for _ in SHAPES]
-    for a, b in zip(xp, xs):
-        a[:, :b.shape[1]] = b
+    for a, b in zip(xp, xbs):
+        a[:, :b.shape[1]] = to_dev_bf16(b)
     ws_bytes = max(wsl.linear_gemm_workspace_bytes(wsl.WSL_W_NF4, n, k, m) for n, k in SHAPES)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
-    want = [wsl.linear_gemm(d, a[:, :k], wfmt=wsl.WSL_W_NF4, n_out=n, k=k, workspace=ws)
+    want = [wsl.linear_gemm(d, a[:, :k], wfmt=wsl.WSL_W_NF4, n_out=n, k=k, ofmt=ofmt, workspace=ws)
             for d, a, (n, k) in zip(dev, xp, SHAPES)]
-    ys = [torch.full((m, nmax), float("nan"), dtype=torch.float32, device="cuda") for _ in SHAPES]
+    ydt = torch.float32 if ofmt == wsl.WSL_OUT_F32 else torch.bfloat16
+    ys = [torch.full((m, nmax), float("nan"), dtype=ydt, device="cuda") for _ in SHAPES]
     ring = wsl.CopyRing(nbytes)
-    ring.gemm(mats, xp, ys, m, kmax, nmax, workspace=ws)
+    ring.gemm(mats, xp, ys, m, kmax, nmax, ofmt=ofmt, workspace=ws)
     torch.cuda.synchronize()
-    for i, ((n, k), y, w) in enumerate(zip(SHAPES, ys, want)):
-        assert torch.equal(y[:, :n], w), f"matrix {i} differs"
+    for i, ((n, k), y, w, wb, xb) in enumerate(zip(SHAPES, ys, want, bits, xbs)):
+        codes, scales = oracle.pack_codes(f64(wb))
+        t = oracle.f32_from_bf16_bits(oracle.dequant_tile_bits(codes, scales)).astype(np.float64)
+        y_ref, s_ref = oracle.gemm_ref(f64(xb), t)
+        if ofmt == wsl.WSL_OUT_F32:
+            ok, worst, r = oracle.check_rows_f32(y[:, :n].cpu().numpy(), y_ref, s_ref)
+        else:
+            yb = y[:, :n].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+            ok, worst, r = oracle.check_bf16(yb, y_ref, s_ref)
+        assert ok, f"matrix {i} {(n, k)}: element {r} worst ratio {worst}"
+        assert torch.equal(y[:, :n], w), f"matrix {i} differs from the resident call"
+    # columns past each matrix's n_out are not written
+    for (n, _), y in zip(SHAPES, ys):
+        assert bool(torch.isnan(y[:, n:].float()).all())
 
 
 def test_streamed_rejects_pageable_host_memory():
