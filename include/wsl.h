@@ -60,7 +60,8 @@ enum {
     WSL_E_DEVICE = 5,  /* current device is not gfx950, or the device query failed */
     WSL_E_LAUNCH = 6,  /* a kernel launch failed */
     WSL_E_RANGE = 7,   /* a tile or workspace lies outside its matrix or buffer */
-    WSL_E_MEMORY = 8   /* a host buffer of a streamed call is not pinned (page-locked) host memory */
+    WSL_E_MEMORY = 8,  /* a host buffer of a streamed call is not pinned (page-locked) host memory */
+    WSL_E_SCRATCH = 9  /* linear_gemm_noalloc: the shape needs more split workspace than its scratch holds */
 };
 
 /* Weight formats. */
@@ -174,6 +175,27 @@ int linear_gemm(int wfmt, const void *d_w, int64_t n_out, int64_t k,
                 const void *d_x, int64_t m, int64_t ldx,
                 void *d_y, int ofmt, int64_t ldy,
                 void *d_ws, size_t ws_bytes, void *stream);
+
+/*
+ * linear_gemm_noalloc -- linear_gemm for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, kernels and results (bit for bit) as linear_gemm given a workspace of
+ * linear_gemm_workspace_bytes(); instead of a caller workspace, the split-reduction
+ * partials go to a scratch array of WSL_NOALLOC_SCRATCH_BYTES that the library holds in
+ * device memory of every GPU it runs on, from the first call on that GPU until the process
+ * ends.  The call itself allocates nothing: on its first call on a device it looks up that
+ * device's copy of the array (hipGetSymbolAddress), afterwards it only enqueues kernels.
+ * Returns WSL_E_SCRATCH, launching nothing, for a shape whose split workspace
+ * (linear_gemm_workspace_bytes) exceeds WSL_NOALLOC_SCRATCH_BYTES (4 MiB: enough for
+ * every shape at up to 32 positions with k % 256 == 0, the prefill width; more positions
+ * or other k may need more); linear_gemm with a caller workspace serves those.  Every call on one GPU shares that GPU's scratch: calls
+ * that overlap on one device (different streams, or different host threads without
+ * ordering) race and may return wrong results; calls ordered on one stream do not.
+ */
+#define WSL_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+int linear_gemm_noalloc(int wfmt, const void *d_w, int64_t n_out, int64_t k,
+                        const void *d_x, int64_t m, int64_t ldx,
+                        void *d_y, int ofmt, int64_t ldy, void *stream);
 
 /*
  * nf4_embed_rows -- restore only the requested rows of a packed NF4 matrix (a

@@ -56,6 +56,8 @@ def test_argument_errors_return_before_any_launch():
     assert L.linear_gemv(5, a, 4, 64, a, a, None) == 4
     assert L.linear_gemm(wsl.WSL_W_BF16, a, 4, 64, a, 3, 64, a, 7, 8, None, 0, None) == 4
     assert L.linear_gemm(wsl.WSL_W_BF16, a, 4, 64, a, 3, 32, a, 0, 8, None, 0, None) == 2
+    assert L.linear_gemm_noalloc(wsl.WSL_W_BF16, a, 4, 64, a, 3, 64, a, 7, 8, None) == 4
+    assert L.linear_gemm_noalloc(wsl.WSL_W_NF4, a, 4, 96, a, 3, 96, a, 0, 8, None) == 2
     assert L.nf4_pack(a, 4, 100, a, None, None) == 2
     assert L.nf4_dequant_tile(a, 4, 64, 4, 0, 1, 1, a, 1, None) == 7
     assert L.nf4_embed_rows(a, 4, 64, None, 2, a, wsl.WSL_OUT_BF16, 64, None, None) == 1

@@ -31,8 +31,10 @@ WSL_STATUS_OVERFLOW = 2
 EXPORTED = [
     "nf4_packed_bytes", "nf4_codebook", "nf4_pack", "nf4_dequant_tile", "linear_gemv",
     "linear_gemm_workspace_bytes", "linear_gemm", "nf4_embed_rows", "linear_gemv_streamed",
-    "linear_gemm_streamed", "wsl_stream_read", "wsl_strerror",
+    "linear_gemm_streamed", "wsl_stream_read", "wsl_strerror", "linear_gemm_noalloc",
 ]
+WSL_E_SCRATCH = 9
+NOALLOC_SCRATCH_BYTES = 4 << 20
 
 
 class WSLError(RuntimeError):
@@ -68,6 +70,8 @@ def lib():
     L.linear_gemm_workspace_bytes.restype = sz
     L.linear_gemm.argtypes = [ctypes.c_int, vp, i64, i64, vp, i64, i64, vp, ctypes.c_int, i64, vp, sz, vp]
     L.linear_gemm.restype = ctypes.c_int
+    L.linear_gemm_noalloc.argtypes = [ctypes.c_int, vp, i64, i64, vp, i64, i64, vp, ctypes.c_int, i64, vp]
+    L.linear_gemm_noalloc.restype = ctypes.c_int
     L.nf4_embed_rows.argtypes = [vp, i64, i64, vp, i64, vp, ctypes.c_int, i64, vp, vp]
     L.nf4_embed_rows.restype = ctypes.c_int
     L.linear_gemv_streamed.argtypes = [ctypes.c_int, i64, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
@@ -253,6 +257,30 @@ def linear_gemm(w, x, y=None, wfmt=None, n_out=None, k=None, ofmt=WSL_OUT_F32, w
     rc = lib().linear_gemm(int(wfmt), _ptr(w), n_out, k, _ptr(x), m, x.stride(0), _ptr(y), int(ofmt), y.stride(0),
                            _ptr(workspace), ws_bytes, _stream(stream))
     _check(rc, "linear_gemm")
+    return y
+
+
+def linear_gemm_noalloc(w, x, y, wfmt=None, n_out=None, k=None, ofmt=WSL_OUT_F32, stream=None):
+    """linear_gemm without a workspace argument and without allocating: the split partials use
+    the library's per-device scratch (linear_gemm_noalloc).  y must be given (nothing is
+    allocated here either)."""
+    import torch
+    if wfmt is None:
+        wfmt = WSL_W_NF4 if w.dtype == torch.uint8 else WSL_W_BF16
+    if n_out is None or k is None:
+        n_out, k = w.shape
+    _weight(w, wfmt, n_out, k)
+    _require(x, "x", (torch.bfloat16,), device=w.device, ndim=2)
+    if x.shape[1] < k:
+        raise ValueError(f"x: shape {tuple(x.shape)}, k = {k}")
+    m = x.shape[0]
+    dt = torch.float32 if ofmt == WSL_OUT_F32 else torch.bfloat16
+    _require(y, "y", (dt,), device=w.device, ndim=2)
+    if y.shape[0] < m or y.shape[1] < n_out:
+        raise ValueError(f"y: shape {tuple(y.shape)}, need at least ({m}, {n_out})")
+    rc = lib().linear_gemm_noalloc(int(wfmt), _ptr(w), n_out, k, _ptr(x), m, x.stride(0), _ptr(y), int(ofmt),
+                                   y.stride(0), _stream(stream))
+    _check(rc, "linear_gemm_noalloc")
     return y
 
 

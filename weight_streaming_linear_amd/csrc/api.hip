@@ -17,6 +17,8 @@ int launch_gemm_bf16(const void *w, int64_t n_out, int64_t k, const void *x, int
 int launch_gemm_nf4(const void *w, int64_t n_out, int64_t k, const void *x, int64_t m, int64_t ldx, void *y,
                     int ofmt, int64_t ldy, void *ws, size_t ws_bytes, hipStream_t s);
 size_t gemm_ws_bytes(int wfmt, int64_t n_out, int64_t k, int64_t m);
+int launch_gemm_noalloc(int wfmt, const void *w, int64_t n_out, int64_t k, const void *x, int64_t m, int64_t ldx,
+                        void *y, int ofmt, int64_t ldy, hipStream_t s);
 int check_pinned(int64_t count, const void *const *h_w);
 int ring_gemv(int wfmt, int64_t count, const void *const *h_w, const int64_t *n_out, const int64_t *k,
               const void *const *x, float *const *y, void *const *slot, hipStream_t copy, hipStream_t compute,
@@ -111,6 +113,15 @@ int linear_gemm(int wfmt, const void *d_w, int64_t n_out, int64_t k, const void 
         wsl::launch_gemm_bf16(d_w, n_out, k, d_x, m, ldx, d_y, ofmt, ldy, d_ws, ws_bytes, wsl::as_stream(stream)));
 }
 
+int linear_gemm_noalloc(int wfmt, const void *d_w, int64_t n_out, int64_t k, const void *d_x, int64_t m,
+                        int64_t ldx, void *d_y, int ofmt, int64_t ldy, void *stream) {
+    int rc = wsl::check_gemm(wfmt, d_w, n_out, k, d_x, m, ldx, d_y, ofmt, ldy, nullptr, 0);
+    if (rc != WSL_OK) return rc;
+    if ((rc = wsl::device_ok()) != WSL_OK) return rc;
+    return wsl::after_launch(
+        wsl::launch_gemm_noalloc(wfmt, d_w, n_out, k, d_x, m, ldx, d_y, ofmt, ldy, wsl::as_stream(stream)));
+}
+
 int nf4_embed_rows(const void *d_packed, int64_t n_rows, int64_t k, const int64_t *d_ids, int64_t count,
                    void *d_out, int ofmt, int64_t ld_out, uint32_t *d_status, void *stream) {
     int rc = wsl::check_embed(d_packed, n_rows, k, d_ids, count, d_out, ofmt, ld_out);
@@ -168,6 +179,9 @@ const char *wsl_strerror(int code) {
         case WSL_E_LAUNCH: return "kernel launch failed";
         case WSL_E_RANGE: return "tile or workspace outside its matrix or buffer";
         case WSL_E_MEMORY: return "host buffer is not pinned (page-locked) host memory";
+        case WSL_E_SCRATCH:
+            return "linear_gemm_noalloc: the shape's split workspace exceeds WSL_NOALLOC_SCRATCH_BYTES "
+                   "(use linear_gemm with a caller workspace)";
         default: return "unknown status code";
     }
 }

@@ -13,6 +13,7 @@
 // that freedom so a lane's four MFMA k-steps read one contiguous 16-byte run
 // of codes.
 #include <atomic>
+#include <mutex>
 
 #include "device_common.h"
 
@@ -1493,6 +1494,49 @@ int launch_gemm_nf4(const void *w, int64_t n_out, int64_t k, const void *x, int6
                            n_out, y, ofmt, ldy);
     }
     return WSL_OK;
+}
+
+// ---------------------------------------------------------------- no-allocation variant
+// Split partials of linear_gemm_noalloc live in this array: one copy per device, created
+// with the code object when the library is first used on that device.  In host code its
+// name stands for a host-side shadow, not a device address, so kernels only ever receive
+// the address hipGetSymbolAddress returns for the current device.
+namespace {
+constexpr size_t kScratchBytes = WSL_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kScratchDevs = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kScratchDevs];
+}  // namespace
+
+// Device address of this device's scratch, looked up once per device (with that device
+// current) and kept.
+static int scratch_ptr(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevs) return WSL_E_DEVICE;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return WSL_E_DEVICE;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return WSL_OK;
+}
+
+// linear_gemm with the split partials in the scratch array.  The split kernels write
+// every partial before split_reduce_kernel reads it, so nothing needs clearing.
+int launch_gemm_noalloc(int wfmt, const void *w, int64_t n_out, int64_t k, const void *x, int64_t m, int64_t ldx,
+                        void *y, int ofmt, int64_t ldy, hipStream_t s) {
+    const size_t need = gemm_ws_bytes(wfmt, n_out, k, m);
+    if (need > kScratchBytes) return WSL_E_SCRATCH;
+    void *ws = nullptr;
+    if (need > 0) {
+        const int rc = scratch_ptr(&ws);
+        if (rc != WSL_OK) return rc;
+    }
+    if (wfmt == WSL_W_NF4) return launch_gemm_nf4(w, n_out, k, x, m, ldx, y, ofmt, ldy, ws, need, s);
+    return launch_gemm_bf16(w, n_out, k, x, m, ldx, y, ofmt, ldy, ws, need, s);
 }
 
 }  // namespace wsl
