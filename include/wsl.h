@@ -73,6 +73,8 @@ enum { WSL_OUT_F32 = 0, WSL_OUT_BF16 = 1 };
 #define WSL_STATUS_NONFINITE 1u   /* a group held a NaN or an infinity */
 #define WSL_STATUS_OVERFLOW  2u   /* a group's absmax rounds to +inf in fp16 (>= 65520) */
 #define WSL_STATUS_INDEX     4u   /* nf4_embed_rows: a requested row index was outside the matrix */
+#define WSL_STATUS_SWEEP_TIMEOUT 8u   /* linear_gemv_sweep: a stage barrier waited past its bound */
+#define WSL_STATUS_DESCRIPTOR    16u  /* linear_gemv_sweep: a device stage descriptor was invalid (skipped) */
 
 /*
  * nf4_packed_bytes -- size in bytes of one packed NF4 matrix.
@@ -147,6 +149,54 @@ int nf4_dequant_tile(const void *d_packed, int64_t n_out, int64_t k,
  */
 int linear_gemv(int wfmt, const void *d_w, int64_t n_out, int64_t k,
                 const void *d_x, float *d_y, void *stream);
+
+/* One stage of linear_gemv_sweep: y = W x with W a packed NF4 [n_out][k] matrix. */
+typedef struct wsl_gemv_stage {
+    const void *w;   /* device, packed NF4 (nf4_pack layout), 16-byte aligned */
+    const void *x;   /* device, bf16 [k], 16-byte aligned */
+    float *y;        /* device, fp32 [n_out], 4-byte aligned */
+    int64_t n_out;   /* >= 1 */
+    int64_t k;       /* 64 <= k <= 32768, k % 64 == 0 */
+} wsl_gemv_stage;
+
+/*
+ * linear_gemv_sweep_workspace_bytes -- size of the synchronization workspace that
+ * linear_gemv_sweep needs (a few KB of counters).
+ */
+size_t linear_gemv_sweep_workspace_bytes(void);
+
+/*
+ * linear_gemv_sweep -- a decode sweep: `count` NF4 GEMVs (the linear stages of every
+ * layer of a decoder, in decoder order) in one launch.
+ *   (deep-fold README, "Метод" table: decode runs N=1 NF4 GEMVs inside one graph of
+ *   the whole greedy step; a token's step sweeps every layer's weights once.)
+ * Computes, for i = 0 .. count-1, what linear_gemv(WSL_W_NF4, ...) of stage i computes
+ * (same per-row tolerance: |y - y_exact| <= 1e-4 * sum_k |w_hat x|).  The stages run in
+ * order: no part of stage i + 1 starts (nor reads its x) before every part of stage i
+ * has finished (a device-wide barrier between stages); the loads of its weights may
+ * begin earlier.  No stage may read another stage's output: every y must be disjoint
+ * from every w and x of the call.  Every y is written when the call completes.
+ * wfmt       WSL_W_NF4 (bf16 weights return WSL_E_FORMAT).
+ * count      number of stages, 0 <= count <= 2^24 (0 enqueues nothing).
+ * h_stages   host array of count descriptors: every argument is validated from it
+ *            before anything is enqueued (as linear_gemv validates; k <= 32768).
+ * d_stages   device array holding the same count descriptors (8-byte aligned), which
+ *            the kernel reads.  If the two differ the results are undefined; a device
+ *            descriptor that is invalid is skipped and WSL_STATUS_DESCRIPTOR is ORed
+ *            into the status word.
+ * d_ws       device workspace of at least linear_gemv_sweep_workspace_bytes() bytes,
+ *            128-byte aligned, all zero before the first call; every call leaves it
+ *            zero again except the status word, its uint32 at byte offset 1280, into
+ *            which WSL_STATUS_SWEEP_TIMEOUT / WSL_STATUS_DESCRIPTOR bits are ORed (a
+ *            caller that sees a nonzero status zeroes the workspace before reuse).
+ *            Calls that share a workspace must not overlap.
+ * The call launches one workgroup per compute unit and needs all of them resident at
+ * once (nothing else occupying the GPU's compute units); a barrier that is not reached
+ * within about a second is abandoned with WSL_STATUS_SWEEP_TIMEOUT so the kernel always
+ * ends.  Deterministic: the same inputs give the same bits.
+ */
+int linear_gemv_sweep(int wfmt, int64_t count, const wsl_gemv_stage *h_stages,
+                      const wsl_gemv_stage *d_stages, void *d_ws, size_t ws_bytes, void *stream);
 
 /*
  * linear_gemm_workspace_bytes -- workspace linear_gemm can use for a shape

@@ -59,6 +59,21 @@ def test_argument_errors_return_before_any_launch():
     assert L.linear_gemm_noalloc(wsl.WSL_W_BF16, a, 4, 64, a, 3, 64, a, 7, 8, None) == 4
     assert L.linear_gemm_noalloc(wsl.WSL_W_NF4, a, 4, 96, a, 3, 96, a, 0, 8, None) == 2
     assert L.nf4_pack(a, 4, 100, a, None, None) == 2
+    st = (wsl.WslGemvStage * 2)(wsl.WslGemvStage(4096, 4096, 4096, 4, 64), wsl.WslGemvStage(4096, 4096, 4096, 4, 64))
+    ws = wsl.lib().linear_gemv_sweep_workspace_bytes()
+    assert ws >= 1284
+    assert L.linear_gemv_sweep(wsl.WSL_W_NF4, 0, None, None, None, 0, None) == 0          # nothing to do
+    assert L.linear_gemv_sweep(wsl.WSL_W_BF16, 2, st, a, a, ws, None) == 4
+    assert L.linear_gemv_sweep(wsl.WSL_W_NF4, 2, None, a, a, ws, None) == 1
+    assert L.linear_gemv_sweep(wsl.WSL_W_NF4, 2, st, a, ctypes.c_void_p(4096 + 64), ws, None) == 3
+    assert L.linear_gemv_sweep(wsl.WSL_W_NF4, 2, st, a, a, ws - 1, None) == 7
+    st[1].k = 96
+    assert L.linear_gemv_sweep(wsl.WSL_W_NF4, 2, st, a, a, ws, None) == 2
+    st[1].k = 32768 + 64
+    assert L.linear_gemv_sweep(wsl.WSL_W_NF4, 2, st, a, a, ws, None) == 2
+    st[1].k = 64
+    st[1].w = 4098
+    assert L.linear_gemv_sweep(wsl.WSL_W_NF4, 2, st, a, a, ws, None) == 3
     assert L.nf4_dequant_tile(a, 4, 64, 4, 0, 1, 1, a, 1, None) == 7
     assert L.nf4_embed_rows(a, 4, 64, None, 2, a, wsl.WSL_OUT_BF16, 64, None, None) == 1
     assert L.nf4_embed_rows(a, 4, 64, a, 2, a, 9, 64, None, None) == 4

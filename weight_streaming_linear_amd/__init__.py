@@ -10,6 +10,7 @@ built, every call raises.
 Entry points (same names as the C ABI):
   nf4_packed_bytes, nf4_codebook, nf4_pack, nf4_dequant_tile,
   linear_gemv, linear_gemm, linear_gemm_workspace_bytes, nf4_embed_rows, wsl_strerror;
+  linear_gemm_noalloc; GemvSweep (linear_gemv_sweep, linear_gemv_sweep_workspace_bytes);
   stream_read (wsl_stream_read); CopyRing.gemv / CopyRing.gemm (linear_gemv_streamed /
   linear_gemm_streamed, weights streamed from page-locked host memory, see to_pinned).
 """
@@ -32,7 +33,11 @@ EXPORTED = [
     "nf4_packed_bytes", "nf4_codebook", "nf4_pack", "nf4_dequant_tile", "linear_gemv",
     "linear_gemm_workspace_bytes", "linear_gemm", "nf4_embed_rows", "linear_gemv_streamed",
     "linear_gemm_streamed", "wsl_stream_read", "wsl_strerror", "linear_gemm_noalloc",
+    "linear_gemv_sweep_workspace_bytes", "linear_gemv_sweep",
 ]
+WSL_STATUS_SWEEP_TIMEOUT = 8
+WSL_STATUS_DESCRIPTOR = 16
+SWEEP_STATUS_OFFSET = 1280      # byte offset of the status word in the sweep workspace
 WSL_E_SCRATCH = 9
 NOALLOC_SCRATCH_BYTES = 4 << 20
 
@@ -70,6 +75,10 @@ def lib():
     L.linear_gemm_workspace_bytes.restype = sz
     L.linear_gemm.argtypes = [ctypes.c_int, vp, i64, i64, vp, i64, i64, vp, ctypes.c_int, i64, vp, sz, vp]
     L.linear_gemm.restype = ctypes.c_int
+    L.linear_gemv_sweep_workspace_bytes.argtypes = []
+    L.linear_gemv_sweep_workspace_bytes.restype = sz
+    L.linear_gemv_sweep.argtypes = [ctypes.c_int, i64, vp, vp, vp, sz, vp]
+    L.linear_gemv_sweep.restype = ctypes.c_int
     L.linear_gemm_noalloc.argtypes = [ctypes.c_int, vp, i64, i64, vp, i64, i64, vp, ctypes.c_int, i64, vp]
     L.linear_gemm_noalloc.restype = ctypes.c_int
     L.nf4_embed_rows.argtypes = [vp, i64, i64, vp, i64, vp, ctypes.c_int, i64, vp, vp]
@@ -282,6 +291,49 @@ def linear_gemm_noalloc(w, x, y, wfmt=None, n_out=None, k=None, ofmt=WSL_OUT_F32
                                    y.stride(0), _stream(stream))
     _check(rc, "linear_gemm_noalloc")
     return y
+
+
+class WslGemvStage(ctypes.Structure):
+    """struct wsl_gemv_stage of the C ABI."""
+    _fields_ = [("w", ctypes.c_void_p), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("n_out", ctypes.c_int64), ("k", ctypes.c_int64)]
+
+
+class GemvSweep:
+    """A decode sweep for linear_gemv_sweep: NF4 GEMVs run in order in one launch.
+
+    stages: [(packed NF4 uint8 tensor, x bf16 [k], y fp32 [n_out], n_out, k)].  The host and
+    device descriptor arrays and the zeroed synchronization workspace are built once here;
+    each call enqueues the one launch on the current (or given) stream."""
+
+    def __init__(self, stages):
+        import torch
+        if not stages:
+            raise ValueError("a sweep needs at least one stage")
+        dev = stages[0][0].device
+        self.h = (WslGemvStage * len(stages))()
+        for i, (w, x, y, n_out, k) in enumerate(stages):
+            _weight(w, WSL_W_NF4, n_out, k, f"w[{i}]")
+            _require(x, f"x[{i}]", (torch.bfloat16,), device=dev, contiguous=True)
+            _require(y, f"y[{i}]", (torch.float32,), device=dev, contiguous=True)
+            if x.numel() < k or y.numel() < n_out:
+                raise ValueError(f"stage {i}: x has {x.numel()} of {k}, y {y.numel()} of {n_out} elements")
+            self.h[i] = WslGemvStage(w.data_ptr(), x.data_ptr(), y.data_ptr(), int(n_out), int(k))
+        self.count = len(stages)
+        self.tensors = [t for st in stages for t in st[:3]]      # keep the buffers alive
+        raw = bytes(self.h)
+        self.d = torch.frombuffer(bytearray(raw), dtype=torch.uint8).to(dev)
+        self.ws_bytes = int(lib().linear_gemv_sweep_workspace_bytes())
+        self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=dev)
+
+    def __call__(self, stream=None):
+        rc = lib().linear_gemv_sweep(WSL_W_NF4, self.count, ctypes.byref(self.h), _ptr(self.d), _ptr(self.ws),
+                                     self.ws_bytes, _stream(stream))
+        _check(rc, "linear_gemv_sweep")
+
+    def status(self):
+        """The workspace's status word (reads the device: for tests and diagnostics)."""
+        return int(self.ws[SWEEP_STATUS_OFFSET:SWEEP_STATUS_OFFSET + 4].view(__import__("torch").int32).item())
 
 
 def stream_read(buf, sink, stream=None):

@@ -314,7 +314,7 @@ __device__ __forceinline__ void xcd_chunk(int64_t total, int xcd, int64_t &first
 // NF4 GEMV for k <= 32768.  A lane owns 32 consecutive codes (16 B, half a group) of
 // a row; a wave covers a 2048-code k-slice.  A workgroup holds T teams of S waves,
 // S = ceil(k / 2048): the S waves of a team split the row into slices and keep their
-// 32 x values in registers for the whole kernel; team t works on row group
+// 32 x values in registers for the whole matrix; team t works on row group
 // sg * T + t of super-group sg (R rows per row group).
 // Super-groups of full row groups (every row present, scales of the R rows
 // contiguous) are split into 8 contiguous chunks, one per XCD (workgroup b runs on
@@ -330,60 +330,83 @@ __device__ __forceinline__ void xcd_chunk(int64_t total, int xcd, int64_t &first
 // store sits between the loads of its loop.  Rows of a last partial 16-row block whose size is not a
 // multiple of R, and super-groups left incomplete, are done at the end with per-row
 // loads.  TAB selects the 16-entry table (0) or the replicated pair table (1).
+// Waves of the workgroup beyond the T teams (the decode sweep runs every matrix in
+// 16-wave workgroups) take part in the barriers only.
 constexpr int kRowSumCap = 2048;   // finished row sums parked per round
 
+// LDS of the team GEMV: the level table, the cross-wave row sums (double-buffered)
+// and the parked row sums of a round.
 template <int R, int TAB>
-__global__ __launch_bounds__(1024) void gemv_nf4_team_kernel(const uint8_t *__restrict__ packed, int64_t n_out,
-                                                             int64_t k, const uint16_t *__restrict__ x,
-                                                             float *__restrict__ y, int S) {
+struct TeamLds {
+    __align__(16) char tab[TAB == 0 ? 64 : kPairTableBytes];
+    float red[2][16][R];
+    float yl[kRowSumCap];
+};
+
+// One matrix as seen by one workgroup: geometry, this wave's slice and this
+// workgroup's super-groups first + i0 + j * nloc, j = 0 .. n - 1.  WIDE: the workgroup
+// may hold more waves than the T teams need (idle waves: they run the barrier-only form
+// of team_run); the wave index is then made wave-uniform.
+template <int R, bool WIDE>
+struct TeamStage {
     typedef typename ScaleBits<R>::T SB;
-    __shared__ __align__(16) char tab[TAB == 0 ? 64 : kPairTableBytes];
-    __shared__ float red[2][16][R];
-    __shared__ float yl[kRowSumCap];
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int T = (blockDim.x >> 6) / S;
-    const int team = wave / S;
-    const int slice = wave - team * S;
-    const int64_t groups = k >> 6;
-    const int64_t rowbytes = k >> 1;
-    const int64_t row_groups = (n_out + R - 1) / R;
-    const int64_t full_rg = (n_out % R == 0) ? row_groups : ((n_out >> 4) << 4) / R;
-    const int64_t supers = full_rg / T;
-    const uint16_t *scales = reinterpret_cast<const uint16_t *>(packed + n_out * rowbytes);
-    const uint32_t m60 = 0x3c;
-    uint32_t ad[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ad[i] = static_cast<uint32_t>(lane & 31) << 3;
-    constexpr int span = 64 / R;
+    const uint8_t *packed;
+    const uint16_t *scales;
+    const uint16_t *x;
+    float *y;
+    int64_t n_out, groups, rowbytes, row_groups, supers, first, i0, nloc, n, cap;
+    int S, T, team, fteam;
+    bool idle, active, park;
+    int64_t kkl;
+    uint32_t coff, gl;
 
-    // Lanes past k read valid codes of the row's last group and multiply them by x = 0.
-    const int64_t kk0 = static_cast<int64_t>(slice) * 2048 + lane * 32;
-    const bool active = kk0 < k;
-    const int64_t kkl = active ? kk0 : k - 32;
-    const uint32_t coff = static_cast<uint32_t>(kkl >> 1);
-    const uint32_t gl = static_cast<uint32_t>(kkl >> 6);
-    float xf[32];
+    __device__ __forceinline__ void init(const uint8_t *p, int64_t n_out_, int64_t k, const uint16_t *x_, float *y_,
+                                         int S_, int T_, int wave, int lane) {
+        packed = p;
+        x = x_;
+        y = y_;
+        n_out = n_out_;
+        S = S_;
+        T = T_;
+        groups = k >> 6;
+        rowbytes = k >> 1;
+        row_groups = (n_out + R - 1) / R;
+        const int64_t full_rg = (n_out % R == 0) ? row_groups : ((n_out >> 4) << 4) / R;
+        supers = full_rg / T;
+        scales = reinterpret_cast<const uint16_t *>(packed + n_out * rowbytes);
+        // In 16-wave workgroups the wave index is made wave-uniform, so that rows, row
+        // addresses and the idle test are scalar: the per-lane 64-bit address arithmetic
+        // otherwise takes the registers the prefetch needs (the sweep kernel runs at the
+        // 128-register limit of 16 waves per CU).
+        const int wv = WIDE ? __builtin_amdgcn_readfirstlane(wave) : wave;
+        team = wv / S;
+        idle = WIDE && team >= T;
+        fteam = idle ? T - 1 : team;
+        const int slice = wv - team * S;
+        // Lanes past k read valid codes of the row's last group and multiply them by x = 0.
+        const int64_t kk0 = static_cast<int64_t>(slice) * 2048 + lane * 32;
+        active = kk0 < k;
+        kkl = active ? kk0 : k - 32;
+        coff = static_cast<uint32_t>(kkl >> 1);
+        gl = static_cast<uint32_t>(kkl >> 6);
+        const int xcd = blockIdx.x & 7;
+        nloc = gridDim.x >> 3;   // the grid is a multiple of 8
+        int64_t count;
+        xcd_chunk(supers, xcd, first, count);
+        i0 = blockIdx.x >> 3;
+        n = i0 < count ? (count - i0 + nloc - 1) / nloc : 0;
+        cap = kRowSumCap / (T * R);
+        // Parking pays off once a workgroup owns several super-groups; with one or two
+        // the two extra barriers of the flush cost more than the stores they move.
+        park = n >= 4;
+    }
 
-    auto dot = [&](const uint4 &q) -> float {
-        if constexpr (TAB == 0) return nf4_dot32(q, xf, tab, m60);
-        else return nf4_dot32_pair(q, xf, tab, ad);
-    };
-    // This workgroup's super-groups: first + i0 + j * nloc, j = 0 .. n - 1.
-    const int xcd = blockIdx.x & 7;
-    const int64_t nloc = gridDim.x >> 3;   // the grid is a multiple of 8
-    int64_t first, count;
-    xcd_chunk(supers, xcd, first, count);
-    const int64_t i0 = blockIdx.x >> 3;
-    const int64_t n = i0 < count ? (count - i0 + nloc - 1) / nloc : 0;
-    const int64_t cap = kRowSumCap / (T * R);
-    // Parking pays off once a workgroup owns several super-groups; with one or two
-    // the two extra barriers of the flush cost more than the stores they move.
-    const bool park = n >= 4;
-
-    int64_t jend = 0;   // end of the current round
-    auto fetch = [&](int64_t j, uint4 (&q)[R], SB &sb) {
-        const int64_t row0 = ((first + i0 + j * nloc) * T + team) * R;
+    // Loads of super-group j of this wave's team.  An idle wave loads what the last team
+    // loads (in bounds, and never used): with no branch around the loads, every path has
+    // the same loads in flight, and the compiler's waits before the first multiply stay
+    // exact (a branch that issues no loads makes it wait for every load in flight).
+    __device__ __forceinline__ void fetch(int64_t j, uint4 (&q)[R], SB &sb) const {
+        const int64_t row0 = ((first + i0 + j * nloc) * T + fteam) * R;
         const uint8_t *rowp = packed + row0 * rowbytes;
 #pragma unroll
         for (int r = 0; r < R; ++r) q[r] = load_stream16(rowp + r * rowbytes + coff);
@@ -393,42 +416,59 @@ __global__ __launch_bounds__(1024) void gemv_nf4_team_kernel(const uint8_t *__re
         const uint16_t *sp = scales + blk * 16 * groups + (row0 & 15);
         sb = *reinterpret_cast<const SB *>(reinterpret_cast<const char *>(sp) + gl * rb * 2u);
         __builtin_amdgcn_sched_barrier(0);   // the whole prefetch is issued before the math below
-    };
+    }
+
+    __device__ __forceinline__ void issue_x(uint4 (&xv)[4]) const { issue_x32(x, kkl, active, xv); }
+};
+
+template <int TAB>
+__device__ __forceinline__ float team_dot(const uint4 &q, const float (&xf)[32], const char *tab, uint32_t (&ad)[4]) {
+    if constexpr (TAB == 0) return nf4_dot32(q, xf, tab, 0x3cu);
+    else return nf4_dot32_pair(q, xf, tab, ad);
+}
+
+// Multiply this workgroup's share of the matrix: the pipelined super-groups, the
+// parked-sum flushes and the leftover row groups.  On entry qa/sa hold the loads of
+// super-group 0 (when st.n > 0), xf this wave's x slice and the table is built.
+// SKIP: the form an idle wave runs -- no loads and no math, the same barriers and the
+// same share of the parked-sum stores as the other waves.
+template <int R, int TAB, bool SKIP, bool WIDE>
+__device__ __forceinline__ void team_run(const TeamStage<R, WIDE> &st, TeamLds<R, TAB> &lds, const float (&xf)[32],
+                                         uint32_t (&ad)[4], uint4 (&qa)[R], typename ScaleBits<R>::T &sa) {
+    typedef typename ScaleBits<R>::T SB;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    constexpr int span = 64 / R;
+    const int T = st.T, S = st.S;
     int ph = 0;
     int64_t jbeg = 0;
     auto consume = [&](int64_t j, const uint4 (&q)[R], const SB &sb) {
-        float acc[R];
+        if constexpr (!SKIP) {
+            float acc[R];
 #pragma unroll
-        for (int r = 0; r < R; ++r) acc[r] = scale_at<R>(sb, r) * dot(q[r]);
-        const float v = reduce_rows<R>(acc, lane);
-        if ((lane % span) == 0) red[ph][wave][lane / span] = v;
+            for (int r = 0; r < R; ++r) acc[r] = scale_at<R>(sb, r) * team_dot<TAB>(q[r], xf, lds.tab, ad);
+            const float v = reduce_rows<R>(acc, lane);
+            if ((lane % span) == 0) lds.red[ph][wave][lane / span] = v;
+        }
         lds_barrier();
         if (threadIdx.x < T * R) {
             const int tm = threadIdx.x / R, r = threadIdx.x - tm * R;
-            float t = red[ph][tm * S][r];
-            for (int s = 1; s < S; ++s) t += red[ph][tm * S + s][r];
-            if (park) yl[(j - jbeg) * T * R + threadIdx.x] = t;
-            else y[(first + i0 + j * nloc) * T * R + threadIdx.x] = t;
+            float t = lds.red[ph][tm * S][r];
+            for (int s = 1; s < S; ++s) t += lds.red[ph][tm * S + s][r];
+            if (st.park) lds.yl[(j - jbeg) * T * R + threadIdx.x] = t;
+            else st.y[(st.first + st.i0 + j * st.nloc) * T * R + threadIdx.x] = t;
         }
         ph ^= 1;
     };
 
-    uint4 qa[R], qb[R];
-    SB sa, sb;
-    // The first super-group's loads and the x loads are in flight while the table is
-    // built (x last: the first multiply needs both, so one wait for all is no loss).
-    if (n > 0) fetch(0, qa, sa);
-    uint4 xv[4];
-    issue_x32(x, kkl, active, xv);
-    if constexpr (TAB == 0) {
-        write_levels(reinterpret_cast<float *>(tab));
-    } else {
-        fill_pair_table(tab);
-    }
-    __syncthreads();
-    widen_x32(xv, xf);
-    for (jbeg = 0; jbeg < n; jbeg += cap) {
-        jend = (jbeg + cap < n) ? jbeg + cap : n;
+    auto fetch = [&](int64_t j, uint4 (&q)[R], SB &s_) {
+        if constexpr (!SKIP) st.fetch(j, q, s_);
+    };
+    uint4 qb[R];
+    SB sb;
+    const int64_t n = st.n;
+    for (jbeg = 0; jbeg < n; jbeg += st.cap) {
+        const int64_t jend = (jbeg + st.cap < n) ? jbeg + st.cap : n;
         if (jbeg > 0) fetch(jbeg, qa, sa);
         int64_t j = jbeg;
         // Unrolled by two so that the two buffers swap without copies; the loop has its
@@ -447,12 +487,12 @@ __global__ __launch_bounds__(1024) void gemv_nf4_team_kernel(const uint8_t *__re
         } else {
             consume(j, qa, sa);
         }
-        if (park) {
+        if (st.park) {
             __syncthreads();
             for (int64_t e = threadIdx.x; e < (jend - jbeg) * T * R; e += blockDim.x) {
                 const int64_t jj = jbeg + e / (T * R);
                 const int64_t rest = e - (e / (T * R)) * (T * R);
-                y[(first + i0 + jj * nloc) * T * R + rest] = yl[e];
+                st.y[(st.first + st.i0 + jj * st.nloc) * T * R + rest] = lds.yl[e];
             }
             __syncthreads();
         }
@@ -464,38 +504,209 @@ __global__ __launch_bounds__(1024) void gemv_nf4_team_kernel(const uint8_t *__re
     // The first leftover round uses the reduction buffer the last consume() did not:
     // without the flush's barriers (n < 4) a team of this round may write its partials
     // while wave 0 still reads that consume()'s partials from the other buffer.
-    const int64_t left0 = supers * T;
-    const int64_t nleft = row_groups - left0;
+    const int64_t left0 = st.supers * T;
+    const int64_t nleft = st.row_groups - left0;
     int it = ph;
     for (int64_t b = gridDim.x - 1 - blockIdx.x; b * T < nleft; b += gridDim.x) {
-        const int64_t rg = left0 + b * T + team;
+        const int64_t rg = left0 + b * T + st.team;
         float acc[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[r] = 0.f;
-        if (rg < row_groups) {
+        if (!SKIP && rg < st.row_groups) {
             const int64_t row0 = rg * R;
             uint4 q[R];
             float s[R];
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                const int64_t row = (row0 + r < n_out) ? row0 + r : n_out - 1;
-                q[r] = load_stream16(packed + row * rowbytes + coff);
-                s[r] = f16_to_f32(scales[scale_index(row, gl, groups, n_out)]);
+                const int64_t row = (row0 + r < st.n_out) ? row0 + r : st.n_out - 1;
+                q[r] = load_stream16(st.packed + row * st.rowbytes + st.coff);
+                s[r] = f16_to_f32(st.scales[scale_index(row, st.gl, st.groups, st.n_out)]);
             }
 #pragma unroll
-            for (int r = 0; r < R; ++r) acc[r] = s[r] * dot(q[r]);
+            for (int r = 0; r < R; ++r) acc[r] = s[r] * team_dot<TAB>(q[r], xf, lds.tab, ad);
         }
         const float v = reduce_rows<R>(acc, lane);
-        if ((lane % span) == 0) red[it & 1][wave][lane / span] = v;
+        if ((lane % span) == 0) lds.red[it & 1][wave][lane / span] = v;
         __syncthreads();
         if (threadIdx.x < T * R) {
             const int tm = threadIdx.x / R, r = threadIdx.x - tm * R;
-            float t = red[it & 1][tm * S][r];
-            for (int s = 1; s < S; ++s) t += red[it & 1][tm * S + s][r];
+            float t = lds.red[it & 1][tm * S][r];
+            for (int s = 1; s < S; ++s) t += lds.red[it & 1][tm * S + s][r];
             const int64_t row = (left0 + b * T) * R + tm * R + r;
-            if (row < n_out) y[row] = t;
+            if (row < st.n_out) st.y[row] = t;
         }
         ++it;
+    }
+}
+
+template <int R, int TAB>
+__global__ __launch_bounds__(1024) void gemv_nf4_team_kernel(const uint8_t *__restrict__ packed, int64_t n_out,
+                                                             int64_t k, const uint16_t *__restrict__ x,
+                                                             float *__restrict__ y, int S) {
+    __shared__ TeamLds<R, TAB> lds;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    TeamStage<R, false> st;
+    st.init(packed, n_out, k, x, y, S, (blockDim.x >> 6) / S, wave, lane);
+    uint32_t ad[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ad[i] = static_cast<uint32_t>(lane & 31) << 3;
+    uint4 qa[R];
+    typename ScaleBits<R>::T sa;
+    // The first super-group's loads and the x loads are in flight while the table is
+    // built (x last: the first multiply needs both, so one wait for all is no loss).
+    if (st.n > 0) st.fetch(0, qa, sa);
+    uint4 xv[4];
+    st.issue_x(xv);
+    if constexpr (TAB == 0) {
+        write_levels(reinterpret_cast<float *>(lds.tab));
+    } else {
+        fill_pair_table(lds.tab);
+    }
+    __syncthreads();
+    float xf[32];
+    widen_x32(xv, xf);
+    team_run<R, TAB, false, false>(st, lds, xf, ad, qa, sa);
+}
+
+// ---------------------------------------------------------------- decode sweep
+// Teams per workgroup for a k of S slices in a 16-wave workgroup: 16 / S, one team fewer
+// when that makes the busy waves a multiple of 4 (equal waves per SIMD; k = 6144: 4
+// teams of 3 waves rather than 5).
+__host__ __device__ __forceinline__ int sweep_teams(int S) {
+    int T = 16 / S;
+    if ((S * T) % 4 != 0 && T > 1 && (S * (T - 1)) % 4 == 0) --T;
+    return T;
+}
+
+// Words of the sweep's synchronization workspace (each counter in its own 128-byte line).
+constexpr int kSyncGroupWord = 0;      // + 32 * g, g = 0..7: arrivals of workgroup group g
+constexpr int kSyncAllWord = 8 * 32;   // groups complete
+constexpr int kSyncExitWord = 9 * 32;  // workgroups finished
+constexpr int kSyncStatusWord = 10 * 32;
+
+// A stage descriptor as the kernel reads it: wsl_gemv_stage with its pointers typed in the
+// global address space.  A pointer read from memory as a plain pointer is generic to the
+// compiler, which then emits flat loads and stores -- counted by lgkmcnt as well, so
+// every LDS-only wait would also wait for the weight loads in flight.
+#define WSL_GLOBAL __attribute__((address_space(1)))
+struct SweepStage {
+    const WSL_GLOBAL uint8_t *w;
+    const WSL_GLOBAL uint16_t *x;
+    WSL_GLOBAL float *y;
+    int64_t n_out, k;
+};
+static_assert(sizeof(SweepStage) == sizeof(wsl_gemv_stage), "descriptor layouts differ");
+
+__device__ __forceinline__ bool sweep_stage_ok(const SweepStage &d) {
+    const uintptr_t a = (uintptr_t)d.w | (uintptr_t)d.x;
+    return d.w != nullptr && d.x != nullptr && d.y != nullptr && (a & 15) == 0 && ((uintptr_t)d.y & 3) == 0 && d.n_out >= 1 && d.k >= 64 && d.k <= 32768 &&
+           (d.k & 63) == 0;
+}
+
+// Device-wide barrier between two stages, the b-th of the call.  Workgroups arrive per
+// group (workgroup % 8, one group per XCD): the last arrival of a group counts the
+// group as complete, and every workgroup waits until all 8 groups are.  It orders
+// execution only: no stage reads another stage's output, so no cache write-back or
+// invalidation is made here (device-scope release/acquire fences cost about 6 us per
+// barrier on this GPU, against about 0.7 us for the relaxed counters); every output is
+// visible when the kernel ends, as for any launch.  The wait is bounded: past
+// `spin_limit` polls it sets WSL_STATUS_SWEEP_TIMEOUT and goes on, so the kernel always
+// ends.  Called by one thread per workgroup.
+__device__ __forceinline__ void sweep_arrive(uint32_t *sync, uint32_t b) {
+    const uint32_t g = blockIdx.x & 7;
+    const uint32_t per = gridDim.x >> 3;
+    const uint32_t old = __hip_atomic_fetch_add(sync + kSyncGroupWord + 32 * g, 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+    if (old + 1 == (b + 1) * per)
+        __hip_atomic_fetch_add(sync + kSyncAllWord, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// `gave_up` is set once this workgroup has abandoned a barrier; it then waits at no
+// later barrier, so a call whose workgroups are not all resident ends after one bound.
+__device__ __forceinline__ void sweep_wait(uint32_t *sync, uint32_t b, uint32_t spin_limit, bool &gave_up) {
+    const uint32_t target = 8 * (b + 1);
+    uint32_t polls = 0;
+    while (!gave_up && __hip_atomic_load(sync + kSyncAllWord, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++polls > spin_limit) {
+            __hip_atomic_fetch_or(sync + kSyncStatusWord, WSL_STATUS_SWEEP_TIMEOUT, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+            gave_up = true;
+        }
+    }
+}
+
+// The decode sweep: `count` NF4 GEMVs (stages) in order in one launch, one 16-wave
+// workgroup per CU for the whole call.  Each stage runs exactly as the team kernel with
+// the pair table (R = 2, T = sweep_teams(S)).  Between stages every workgroup meets a
+// device-wide barrier, so no workgroup starts a stage (nor reads its x) before every
+// workgroup has finished the previous one, as in a decode step where each stage's input
+// depends on the stage before.  The weights do not depend on earlier stages, so a
+// workgroup issues the loads of its first super-group of the next stage as soon as it
+// has arrived, and those loads are in flight while it waits.  The 64 KB pair table is built once per call instead of once
+// per stage.  On exit the last workgroup to finish returns the counters to zero.
+__global__ __launch_bounds__(1024) void gemv_nf4_sweep_kernel(const wsl_gemv_stage *__restrict__ stages, int count,
+                                                              uint32_t *__restrict__ sync, uint32_t spin_limit) {
+    constexpr int R = 2;
+    __shared__ TeamLds<R, 1> lds;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    uint32_t ad[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ad[i] = static_cast<uint32_t>(lane & 31) << 3;
+    TeamStage<R, true> st;
+    uint4 qa[R];
+    ScaleBits<R>::T sa;
+    bool ok = false, gave_up = false;
+    auto setup = [&](int s) {
+        const SweepStage d = reinterpret_cast<const SweepStage *>(stages)[s];
+        ok = sweep_stage_ok(d);
+        const int S = ok ? static_cast<int>((d.k + 2047) / 2048) : 1;
+        st.init((const uint8_t *)d.w, ok ? d.n_out : 0, ok ? d.k : 64, (const uint16_t *)d.x, (float *)d.y, S,
+                sweep_teams(S), wave, lane);
+        if (!ok) {
+            st.n = 0;
+            st.row_groups = 0;
+            st.supers = 0;
+        }
+        if (st.n > 0) st.fetch(0, qa, sa);
+    };
+    setup(0);
+    for (int s = 0; s < count; ++s) {
+        uint4 xv[4];
+        if (ok) st.issue_x(xv);
+        if (s == 0) {   // the table is built while the first loads are in flight
+            fill_pair_table(lds.tab);
+            __syncthreads();
+        }
+        if (ok) {
+            float xf[32];
+            widen_x32(xv, xf);
+            if (st.idle) team_run<R, 1, true, true>(st, lds, xf, ad, qa, sa);   // wave-uniform branch
+            else team_run<R, 1, false, true>(st, lds, xf, ad, qa, sa);
+        } else if (threadIdx.x == 0 && blockIdx.x == 0) {
+            __hip_atomic_fetch_or(sync + kSyncStatusWord, WSL_STATUS_DESCRIPTOR, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (s + 1 < count) {
+            lds_barrier();     // this stage's LDS reads are done (its y stores may still drain)
+            if (threadIdx.x == 0) sweep_arrive(sync, static_cast<uint32_t>(s));
+            setup(s + 1);      // next stage's first loads, in flight during the wait
+            if (threadIdx.x == 0) sweep_wait(sync, static_cast<uint32_t>(s), spin_limit, gave_up);
+            lds_barrier();     // every wave waits for the wait (not for its own loads)
+        }
+    }
+    lds_barrier();
+    if (threadIdx.x == 0) {
+        const uint32_t done = __hip_atomic_fetch_add(sync + kSyncExitWord, 1u, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        if (done + 1 == gridDim.x) {   // every workgroup is past its last wait
+            for (int g = 0; g < 8; ++g)
+                __hip_atomic_store(sync + kSyncGroupWord + 32 * g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(sync + kSyncAllWord, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(sync + kSyncExitWord, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
 }
 
@@ -651,6 +862,28 @@ int launch_gemv_nf4(const void *w, int64_t n_out, int64_t k, const void *x, floa
         if (p.rows == 4) hipLaunchKernelGGL((gemv_nf4_team_kernel<4, 0>), g, b, 0, s, wp, n_out, k, xp, y, p.S);
         else hipLaunchKernelGGL((gemv_nf4_team_kernel<2, 0>), g, b, 0, s, wp, n_out, k, xp, y, p.S);
     }
+    return WSL_OK;
+}
+
+// Decode sweep: one 16-wave workgroup per compute unit (a multiple of 8, one share per
+// XCD), all resident at once for the device-wide stage barriers.
+constexpr size_t kSweepWsBytes = 2048;
+constexpr uint32_t kSweepSpinLimit = 1u << 20;   // polls of a stage barrier (about a second)
+
+size_t sweep_ws_bytes() { return kSweepWsBytes; }
+
+int launch_gemv_nf4_sweep(const wsl_gemv_stage *d_stages, int64_t count, void *ws, hipStream_t s) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8)
+        return WSL_E_DEVICE;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(gemv_nf4_sweep_kernel),
+                                                     1024, 0) != hipSuccess ||
+        per_cu < 1)
+        return WSL_E_LAUNCH;
+    const unsigned grid = static_cast<unsigned>(cus / 8 * 8);
+    hipLaunchKernelGGL(gemv_nf4_sweep_kernel, dim3(grid), dim3(1024), 0, s, d_stages, static_cast<int>(count),
+                       static_cast<uint32_t *>(ws), kSweepSpinLimit);
     return WSL_OK;
 }
 

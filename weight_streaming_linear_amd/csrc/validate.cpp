@@ -124,4 +124,21 @@ int check_embed(const void *packed, int64_t n_rows, int64_t k, const void *ids, 
     return WSL_OK;
 }
 
+int check_sweep(int wfmt, int64_t count, const void *h_stages, const void *d_stages, const void *ws,
+                size_t ws_bytes, size_t ws_need) {
+    if (wfmt != WSL_W_NF4) return WSL_E_FORMAT;
+    if (count < 0 || count > (int64_t(1) << 24)) return WSL_E_SHAPE;
+    if (count == 0) return WSL_OK;
+    if (!h_stages || !d_stages || !ws) return WSL_E_NULL;
+    if (!aligned(d_stages, 8) || !aligned(ws, 128)) return WSL_E_ALIGN;
+    if (ws_bytes < ws_need) return WSL_E_RANGE;
+    const wsl_gemv_stage *st = static_cast<const wsl_gemv_stage *>(h_stages);
+    for (int64_t i = 0; i < count; ++i) {
+        const int rc = check_gemv(WSL_W_NF4, st[i].w, st[i].n_out, st[i].k, st[i].x, st[i].y);
+        if (rc != WSL_OK) return rc;
+        if (st[i].k > 32768) return WSL_E_SHAPE;
+    }
+    return WSL_OK;
+}
+
 }  // namespace wsl

@@ -29,6 +29,10 @@ int check_gemm(int wfmt, const void *w, int64_t n_out, int64_t k, const void *x,
 int check_ring(int wfmt, int64_t count, const void *const *h_w, const int64_t *n_out, const int64_t *k,
                const void *const *x, int64_t m, int64_t ldx, const void *const *y, int ofmt, int64_t ldy,
                const void *ws, size_t ws_bytes, const void *const *slot, size_t slot_bytes, const void *const *events);
+// Decode sweep: count in [0, 2^24], the host descriptors (each as check_gemv for NF4,
+// plus k <= 32768), the device descriptor array and the workspace.
+int check_sweep(int wfmt, int64_t count, const void *h_stages, const void *d_stages, const void *ws,
+                size_t ws_bytes, size_t ws_need);
 int check_embed(const void *packed, int64_t n_rows, int64_t k, const void *ids, int64_t count, const void *out,
                 int ofmt, int64_t ld_out);
 
