@@ -1,41 +1,37 @@
 #!/usr/bin/env python3
 """Benchmark of the weight-streaming linear layers on one MI355X.
 
-Headline workload (``value``): batch-1 bf16 decode GEMV over one dense decoder
-layer with hidden size 5120 -- q/k/v fused into one 7168x5120 matrix, o
-5120x5120, gate/up fused into one 34816x5120 matrix, down 5120x17408 -- four
-launches per step in decoder order.  The W warm-up steps and then the K timed
-steps are each captured as one HIP graph, the way a decode step's graph holds
-every layer of a model (the time with one graph launch per step is reported
-beside it).  ``value`` is the effective weight stream: weight bytes read per
-step / wall time per step (GB/s, 1e9 B/s), every input resident in HBM before
-the timed region starts.  Steps alternate between two distinct copies of the
-layer (1.32 GB) so that the 256 MB last-level cache cannot serve the weights.
+Headline workload (``value``): the batch-1 NF4 decode sweep over a 48-layer stack of
+hidden size 6144 (20B class): per layer qkv 8192x6144, o 6144x6144, gate_up 32768x6144
+and down 6144x16384, packed NF4 (group 64, fp16 scales), 192 GEMV launches per token in
+decoder order on one stream, captured as one HIP graph per token (deep-fold README,
+"Метод" table: decode is an N=1 NF4 GEMV inside a graph of the whole step).  A "step"
+is one token: the W warm-up tokens and then exactly K timed tokens are replayed between
+HIP events; ``value`` = packed weight bytes per token (9,946,791,936 B, every byte read
+once) / wall time per token, in GB/s (1e9 B/s), every input resident in HBM before the
+timed region starts.  The 9.9 GB stack is 39x the 256 MB last-level cache, so no
+rotation copies are needed.
 
-``roofline`` describes the dominant kernel, the gate/up GEMV (34816x5120, the
-largest matrix of the step): its algorithmic bytes per launch divided by its
-average launch duration, measured as a block of K back-to-back launches
-(alternating the two copies) between one pair of HIP events on the launch
-stream.  ``traffic`` is the
-HBM bytes per launch read from rocprofv3 FETCH_SIZE/WRITE_SIZE counter runs of
-this script (``--traffic-probe``), scaled by what the same counters read for a
-plain copy of known size; it is null when the kernel source changed since the
-counters were taken.
+``roofline`` describes the dominant kernel, the gate_up GEMV (gemv_nf4_team_kernel<2,1>
+on 32768x6144, 54 % of the bytes): its algorithmic bytes per launch (packed bytes)
+divided by its average duration, measured as one block of launches over the 48 layers'
+gate_up matrices between HIP events on the launch stream.  ``traffic`` is the HBM bytes
+per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE counter runs of ``--traffic-probe``,
+scaled by what the same counters read for a plain copy of known size; null when the
+kernel source changed since the counters were taken.
 
-The same run measures the other workloads of the hot path (under ``paths``):
-the NF4 GEMV 4096x4096, the 48-layer NF4 decode sweep (hidden 6144), the NF4
-prefill GEMM at 32 positions (5120 <-> 27648) and the bf16 batch-verification
-GEMM at 8192 positions (5120 <-> 17408).
+``paths`` holds the other workloads of the hot path measured in the same run: the sweep
+as one linear_gemv_sweep launch per token, the bf16 decode layer of hidden 5120 (fused
+q/k/v and gate/up: 4 launches; unfused: 7), the NF4 GEMV 4096x4096, the NF4 prefill GEMM
+at 32 positions, the NF4 GEMM at 64/128/256 positions, the bf16 and NF4 verification
+GEMMs at 8192 positions, the packed-embedding gather and the copy ring.
 
-GEMV figures are also given against ``read_ceiling``, the rate of a read-only
-streaming kernel (``wsl_stream_read``) over 2 GiB on the same box.
-
-Protocol (IPE page, "How it is benchmarked"; deep-fold README, lab-plate
-rules): a failed correctness check stops the run before timing; warm-up and
-graph capture are outside every timer.  By default the whole run is repeated in
-three fresh processes, one after another: the line is the first run's with the
-headline value and ms_per_step replaced by the medians, and ``repeats`` holds
-every run's figures with their median, interquartile range and A/A spread.
+Protocol (IPE page, "How it is benchmarked"): a failed sanity gate stops the run before
+timing; warm-up and graph capture are outside every timer; by default the whole run is
+repeated in three fresh processes, one after another -- the line is the first run's with
+the headline value and ms_per_step replaced by the medians, ``repeats`` holds every run's
+figures with median, interquartile range and A/A spread, and the SHA-256 of every
+workload's outputs must agree across the processes (``determinism``).
 """
 
 import argparse
@@ -56,8 +52,9 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, 8 TB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, 2.5 PFLOP/s
 METRIC = "GEMV effective weight GB/s (% of HBM peak); GEMM TFLOP/s (% of MFMA peak)"
 GEMV_SRC = os.path.join(ROOT, "weight_streaming_linear_amd", "csrc", "gemv.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_bf16_gate_up_34816x5120.json")
-DOMINANT = "gate_up"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_nf4_gate_up_32768x6144.json")
+DOMINANT = "nf4_gemv_gate_up"
+DOMINANT_KERNEL = "gemv_nf4_team_kernel<2,1> (gate_up 32768x6144)"
 CALIB_BYTES = 1 << 30            # plain copy used to calibrate the byte counters
 
 
@@ -69,8 +66,8 @@ def log(msg):
 class Launch:
     """One kernel launch of a step: a closure plus its algorithmic work."""
 
-    def __init__(self, fn, nbytes=0, flops=0, name=""):
-        self.fn, self.nbytes, self.flops, self.name = fn, nbytes, flops, name
+    def __init__(self, fn, nbytes=0, flops=0, name="", dispatches=1):
+        self.fn, self.nbytes, self.flops, self.name, self.dispatches = fn, nbytes, flops, name, dispatches
 
 
 _SPIN = {}
@@ -91,7 +88,14 @@ def spin_cycles_per_ms():
     return _SPIN["rate"]
 
 
-def time_block(launches, reps, warmup):
+# Every timed block, in order: (label, launches timed, dispatches per launch).  With
+# --block-log the list is written to a file, so that a rocprofv3 kernel trace of the same
+# command can be cut into these blocks (each follows one spin kernel) and summarized per
+# workload and shape (--trace-summarize).
+BLOCK_LOG = []
+
+
+def time_block(launches, reps, warmup, label=None, dispatches=1):
     """Average duration of one launch: `warmup` untimed launches, then `reps` launches back to
     back (cycling through `launches`) between one pair of HIP events on the current stream,
     the one the launches use.  A spin kernel queued first keeps the GPU busy while the host
@@ -107,6 +111,7 @@ def time_block(launches, reps, warmup):
     torch.cuda.synchronize()
     host_ms = 1e3 * (time.perf_counter() - t0)
     torch.cuda._sleep(int((2.0 * host_ms * reps + 2.0) * spin_cycles_per_ms()))
+    BLOCK_LOG.append((label or launches[0].name or "block", reps, dispatches))
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
     a.record()
@@ -125,7 +130,8 @@ def time_step_launches(steps, k_steps, warmup):
     for st in steps:
         for l in st:
             kinds.setdefault(l.name, []).append(l)
-    return {name: (time_block(ls, k_steps, warmup), ls[0]) for name, ls in kinds.items()}
+    return {name: (time_block(ls, k_steps, warmup, label=name, dispatches=ls[0].dispatches), ls[0])
+            for name, ls in kinds.items()}
 
 
 def capture(launches):
@@ -150,15 +156,16 @@ READ_CEILING = {}
 
 
 def measure_read_ceiling(reps=10, nbytes=2 << 30):
-    """Streaming-read ceiling of the GPU: wsl_stream_read (16-byte loads that bypass the
-    caches, 4 KB of consecutive bytes per wave and iteration) over a 2 GiB buffer, 8x the
-    MALL, timed as one block of launches between HIP events."""
+    """A reference streaming read on the same GPU: wsl_stream_read (16-byte loads that
+    bypass the caches, 4 KB of consecutive bytes per wave and iteration) over a 2 GiB
+    buffer, 8x the MALL, timed as one block of launches between HIP events.  A plain read
+    kernel, not a bound: a kernel with a better access pattern can exceed it."""
     import torch
     import weight_streaming_linear_amd as wsl
     if "gbs" not in READ_CEILING:
         buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
         sink = torch.zeros(1, dtype=torch.int32, device="cuda")
-        us = time_block([Launch(lambda: wsl.stream_read(buf, sink))], reps, 3)
+        us = time_block([Launch(lambda: wsl.stream_read(buf, sink))], reps, 3, label="stream_read_probe_2GiB")
         READ_CEILING.update({"gbs": round(nbytes / 1e3 / us, 1), "buffer_bytes": nbytes, "avg_launch_us": round(us, 2),
                              "frac_hbm": round(nbytes / 1e3 / us / HBM_PEAK_GBS, 4),
                              "what": "wsl_stream_read over a 2 GiB buffer (read-only streaming kernel)"})
@@ -178,7 +185,8 @@ def measure_launch_floor(reps=200):
     if "us" not in LAUNCH_FLOOR:
         buf = torch.zeros(16, dtype=torch.uint8, device="cuda")
         sink = torch.zeros(1, dtype=torch.int32, device="cuda")
-        LAUNCH_FLOOR["us"] = round(time_block([Launch(lambda: wsl.stream_read(buf, sink))], reps, 10), 3)
+        LAUNCH_FLOOR["us"] = round(time_block([Launch(lambda: wsl.stream_read(buf, sink))], reps, 10,
+                                              label="launch_floor_t0"), 3)
         LAUNCH_FLOOR["what"] = "block-timed wsl_stream_read of 16 bytes (one workgroup)"
     return LAUNCH_FLOOR
 
@@ -250,6 +258,35 @@ def check_close(name, got, ref, scale, rel, ulp_rel=0.0):
     return ratio
 
 
+def nf4_rows_f32(packed, n_out, k, rows):
+    """fp32(level * s) of the given rows of a packed matrix, restored by the library's row
+    gather (nf4_embed_rows): within 2^-24 relative of the exact level * s."""
+    import torch
+    import weight_streaming_linear_amd as wsl
+    ids = torch.as_tensor(np.asarray(rows), dtype=torch.int64, device="cuda")
+    return wsl.nf4_embed_rows(packed, n_out, k, ids, ofmt=wsl.WSL_OUT_F32)
+
+
+def gate_gemv_nf4(name, y, packed, n_out, k, rows, x):
+    """NF4 GEMV rows against fp64 sums of fp32(level * s) * x, at the 1e-4 * sum|w x| bound
+    (the restored fp32 weights differ from level * s by at most 2^-24 relative)."""
+    import torch
+    w = nf4_rows_f32(packed, n_out, k, rows).double()
+    xf = x.double()
+    return check_close(name, y[torch.as_tensor(np.asarray(rows), device="cuda")], w @ xf, w.abs() @ xf.abs(), 1e-4)
+
+
+def sha256_of(tensors):
+    """SHA-256 of the bytes of device tensors, in order (the determinism record)."""
+    h = hashlib.sha256()
+    for t in tensors:
+        h.update(t.detach().contiguous().view(-1).view(__import__("torch").uint8).cpu().numpy().tobytes())
+    return h.hexdigest()
+
+
+OUTPUT_SHA = {}
+
+
 def nf4_rows_tile(packed, n_out, k, rows):
     """bf16 tiles of the given rows, restored by the library (one nf4_dequant_tile per row)."""
     import torch
@@ -267,70 +304,185 @@ def gate_gemv(name, y, w_rows, x, rel):
     return check_close(name, y, wf @ xf, wf.abs() @ xf.abs(), rel)
 
 
-# ---------------------------------------------------------------- headline: bf16 decode layer
-LAYER_5120 = [("qkv", 7168, 5120), ("o", 5120, 5120), ("gate_up", 34816, 5120), ("down", 5120, 17408)]
+# ---------------------------------------------------------------- headline: NF4 decode sweep
+SWEEP_6144 = [("qkv", 8192, 6144), ("o", 6144, 6144), ("gate_up", 32768, 6144), ("down", 6144, 16384)]
+SWEEP_LAYERS = 48
 
 
-def setup_layer_5120(copies=2):
-    """One dense decoder layer (hidden 5120) in bf16, `copies` distinct copies."""
+def setup_sweep(layers=SWEEP_LAYERS):
+    """The 48-layer stack, packed on the device (seeded weights drawn on the device, stage j
+    of layer l with tensor id 16 l + j); one x per stage kind; one y per (layer, stage)."""
     import torch
     import synth
     import weight_streaming_linear_amd as wsl
-    layers = [[synth.device_weight(1, 10 * c + j, n, k) for j, (_, n, k) in enumerate(LAYER_5120)]
-              for c in range(copies)]
-    xs = [synth.device_normal_bf16(1, 100 + j, (k,)) for j, (_, n, k) in enumerate(LAYER_5120)]
-    ys = [torch.empty(n, dtype=torch.float32, device="cuda") for (_, n, _) in LAYER_5120]
-    steps = [[Launch(lambda w=mats[j], x=xs[j], y=ys[j]: wsl.linear_gemv(w, x, y=y), nbytes=2 * n * k,
-                     flops=2 * n * k, name=name) for j, (name, n, k) in enumerate(LAYER_5120)] for mats in layers]
-    return layers, xs, ys, steps
-
-
-def gate_layer_5120(layers, xs, ys):
-    import torch
-    import weight_streaming_linear_amd as wsl
-    worst = 0.0
-    for c, mats in enumerate(layers):
-        for j, (name, n, k) in enumerate(LAYER_5120):
-            wsl.linear_gemv(mats[j], xs[j], y=ys[j])
-            rows = torch.as_tensor(sample_rows(n, 48, 7 + j + 10 * c), device="cuda")
-            worst = max(worst, gate_gemv(f"bf16 decode layer copy {c} {name}", ys[j][rows], mats[j][rows], xs[j],
-                                         1e-4))
+    xs = [synth.device_normal_bf16(2, 1000 + j, (k,)) for j, (_, n, k) in enumerate(SWEEP_6144)]
+    packs, ys = [], []
+    t0 = time.time()
+    for l in range(layers):
+        for j, (name, n, k) in enumerate(SWEEP_6144):
+            w = synth.device_weight(2, 16 * l + j, n, k)
+            packs.append((wsl.nf4_pack(w), n, k, j))
+            ys.append(torch.empty(n, dtype=torch.float32, device="cuda"))
+            del w
     torch.cuda.synchronize()
+    log(f"nf4 decode sweep: packed {layers} layers in {time.time() - t0:.1f}s")
+    return xs, packs, ys
+
+
+def gate_sweep(name, xs, packs, ys, layers):
+    worst = 0.0
+    for l in layers:
+        for j, (st, n, k) in enumerate(SWEEP_6144):
+            p = packs[4 * l + j][0]
+            worst = max(worst, gate_gemv_nf4(f"{name} layer {l} {st}", ys[4 * l + j], p, n, k,
+                                             sample_rows(n, 24, 100 * l + j), xs[j]))
     return worst
 
 
 def measure_headline(k_steps, warmup):
-    """The W warm-up steps and then exactly K timed steps, each step one pass over the layer's
-    four matrices (alternating the two copies), the K steps captured as one graph -- as a
-    decode step's graph holds every layer of the model, so no graph launch sits between
-    layers.  Also: the same steps with one graph per step (a graph launch per layer), and
-    block-timed kernel durations."""
+    """The decode sweep, 192 GEMV launches per token captured as one graph: W untimed then
+    exactly K timed token replays between HIP events.  Also the per-stage kernel blocks (the
+    dominant gate_up block among them), the sweep as one linear_gemv_sweep launch per token,
+    and the decode-step graph with the packed-embedding gather of a device-resident token."""
     import torch
-    layers, xs, ys, steps = setup_layer_5120(copies=2)
-    worst = gate_layer_5120(layers, xs, ys)
-    log(f"bf16 decode layer parity ok (worst ratio {worst:.3g})")
-    seq = lambda n, start: [l for i in range(n) for l in steps[(start + i) % len(steps)]]
-    warm = capture(seq(max(warmup, 1), 0))
-    timed = capture(seq(k_steps, max(warmup, 1)))
-    warm.replay()
+    import synth
+    import weight_streaming_linear_amd as wsl
+    xs, packs, ys = setup_sweep()
+    token_bytes = sum(wsl.nf4_packed_bytes(n, k) for _, n, k, _ in packs)
+    launches = [Launch(lambda p=p, n=n, k=k, j=j, y=y: wsl.linear_gemv(p, xs[j], y=y, wfmt=wsl.WSL_W_NF4, n_out=n,
+                                                                       k=k),
+                       nbytes=wsl.nf4_packed_bytes(n, k), flops=2 * n * k, name=f"nf4_gemv_{SWEEP_6144[j][0]}")
+                for (p, n, k, j), y in zip(packs, ys)]
+    for l in launches[:4]:
+        l.fn()
+    worst = gate_sweep("nf4 decode sweep", xs, packs, ys, [0])
+    g = capture(launches)
+    for _ in range(warmup):
+        g.replay()
     torch.cuda.synchronize()
+    for y in ys:
+        y.fill_(float("nan"))
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     a.record()
-    timed.replay()
+    for _ in range(k_steps):
+        g.replay()
     b.record()
     torch.cuda.synchronize()
-    gwall = a.elapsed_time(b)
-    del warm, timed
-    graphs = [capture(st) for st in steps]
-    gwall1 = time_graphs(graphs, k_steps, warmup)
-    per_kind = time_step_launches(steps, k_steps, warmup)
-    per_launch = summarize(per_kind)
-    out = {"ms_per_step": gwall / k_steps, "ms_per_step_one_graph_per_step": gwall1 / k_steps,
-           "sanity_worst_ratio": worst, "per_launch": per_launch,
-           "dominant_avg_us": per_kind[DOMINANT][0], "dominant_bytes": per_kind[DOMINANT][1].nbytes}
-    del graphs, steps, layers
+    ms = a.elapsed_time(b) / k_steps
+    worst = max(worst, gate_sweep("nf4 decode sweep (graph replay)", xs, packs, ys, [0, 23, 47]))
+    OUTPUT_SHA["nf4_decode_sweep_48x6144"] = sha256_of(ys)
+    log(f"nf4 decode sweep: {ms:.3f} ms/token (graph), {token_bytes / 1e6 / ms:.0f} GB/s, gate worst {worst:.3g}")
+
+    # one block of launches per stage kind over the 48 layers (the dominant: gate_up)
+    per_kind = time_step_launches([launches], 2 * SWEEP_LAYERS, 4)
+    kern = summarize(per_kind, {f"nf4_gemv_{st[0]}": SWEEP_LAYERS for st in SWEEP_6144})
+
+    # the same sweep as one launch per token (linear_gemv_sweep)
+    sw = wsl.GemvSweep([(p, xs[j], y, n, k) for (p, n, k, j), y in zip(packs, ys)])
+    for y in ys:
+        y.fill_(float("nan"))
+    sw()
+    torch.cuda.synchronize()
+    if sw.status() != 0:
+        refuse("linear_gemv_sweep status", float(sw.status()))
+    sw_worst = gate_sweep("nf4 decode sweep (one launch)", xs, packs, ys, [0, 23, 47])
+    if sha256_of(ys) != OUTPUT_SHA["nf4_decode_sweep_48x6144"]:
+        refuse("linear_gemv_sweep differs from the per-stage launches", float("inf"))
+    for _ in range(warmup):
+        sw()
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(k_steps):
+        sw()
+    b.record()
+    torch.cuda.synchronize()
+    sw_ms = a.elapsed_time(b) / k_steps
+
+    # decode-step graph: embedding gather of a device-resident token id + the sweep + id advance
+    emb_n = 128000
+    wemb = synth.device_weight(2, 999, emb_n, 6144)
+    emb = wsl.nf4_pack(wemb)
+    del wemb
+    tok = torch.zeros(1, dtype=torch.int64, device="cuda")
+    hid = torch.empty((1, 6144), dtype=torch.bfloat16, device="cuda")
+    step_launches = [Launch(lambda: wsl.nf4_embed_rows(emb, emb_n, 6144, tok, out=hid))] + launches + \
+        [Launch(lambda: tok.add_(1))]
+    g2 = capture(step_launches)
+    before = torch.cuda.memory_allocated()
+    step_ms = time_graphs([g2], k_steps, warmup) / k_steps
+    grew = torch.cuda.memory_allocated() - before
+    t0 = measure_launch_floor()["us"]
+    out = {
+        "ms_per_token": ms, "token_bytes": token_bytes, "sanity_worst_ratio": max(worst, sw_worst),
+        "kernels": kern, "dominant_avg_us": per_kind[DOMINANT][0], "dominant_bytes": per_kind[DOMINANT][1].nbytes,
+        "sweep_kernel": {"ms_per_token": round(sw_ms, 4), "gbs": round(token_bytes / 1e6 / sw_ms, 1),
+                         "frac_hbm": round(token_bytes / 1e6 / sw_ms / HBM_PEAK_GBS, 4),
+                         "what": "linear_gemv_sweep: the 192 stages in one launch, a device-wide barrier "
+                                 "between stages; outputs bit-identical to the per-stage launches"},
+        "decode_step_graph": {"ms_per_token": round(step_ms, 4), "tokens_per_s": round(1e3 / step_ms, 2),
+                              "what": "embedding gather (device-resident token id) + 192 GEMVs + id advance, "
+                                      "one graph", "allocator_growth_bytes": grew},
+        "launch_floor": {"t0_us": t0, "launches_per_token": len(launches),
+                         "t0_ms_per_token": round(len(launches) * t0 / 1e3, 4),
+                         "bytes_ms_at_8tbs": round(token_bytes / 8e9, 4)},
+    }
+    del g, g2, sw, packs, launches, step_launches, emb
     torch.cuda.empty_cache()
+    return out
+
+
+# ---------------------------------------------------------------- bf16 decode layer (hidden 5120)
+LAYER_5120 = [("qkv", 7168, 5120), ("o", 5120, 5120), ("gate_up", 34816, 5120), ("down", 5120, 17408)]
+LAYER_5120_UNFUSED = [("q", 5120, 5120), ("k", 1024, 5120), ("v", 1024, 5120), ("o", 5120, 5120),
+                      ("gate", 17408, 5120), ("up", 17408, 5120), ("down", 5120, 17408)]
+
+
+def setup_layer_5120(mats, copies=2, tid0=0):
+    """One dense decoder layer (hidden 5120) in bf16, `copies` distinct copies."""
+    import torch
+    import synth
+    import weight_streaming_linear_amd as wsl
+    layers = [[synth.device_weight(1, tid0 + 10 * c + j, n, k) for j, (_, n, k) in enumerate(mats)]
+              for c in range(copies)]
+    xs = [synth.device_normal_bf16(1, 100 + j, (k,)) for j, (_, n, k) in enumerate(mats)]
+    ys = [torch.empty(n, dtype=torch.float32, device="cuda") for (_, n, _) in mats]
+    steps = [[Launch(lambda w=ws_[j], x=xs[j], y=ys[j]: wsl.linear_gemv(w, x, y=y), nbytes=2 * n * k,
+                     flops=2 * n * k, name=name) for j, (name, n, k) in enumerate(mats)] for ws_ in layers]
+    return layers, xs, ys, steps
+
+
+def run_bf16_decode_layer(k_steps, warmup):
+    """bf16 decode GEMV over one dense decoder layer of hidden 5120, batch 1: q/k/v and gate/up
+    fused (4 launches per step) and as stored (7 launches), two layer copies alternating (the
+    1.32 GB exceed the 256 MB last-level cache); one graph per step, K steps."""
+    import torch
+    import weight_streaming_linear_amd as wsl
+    out = {}
+    for label, mats, tid0 in (("fused", LAYER_5120, 0), ("unfused", LAYER_5120_UNFUSED, 200)):
+        layers, xs, ys, steps = setup_layer_5120(mats, tid0=tid0)
+        worst = 0.0
+        for c, ws_ in enumerate(layers):
+            for j, (name, n, k) in enumerate(mats):
+                wsl.linear_gemv(ws_[j], xs[j], y=ys[j])
+                rows = torch.as_tensor(sample_rows(n, 48, 7 + j + 10 * c), device="cuda")
+                worst = max(worst, gate_gemv(f"bf16 layer {label} copy {c} {name}", ys[j][rows], ws_[j][rows],
+                                             xs[j], 1e-4))
+        OUTPUT_SHA[f"bf16_decode_layer_5120_{label}"] = sha256_of(ys)
+        graphs = [capture(st) for st in steps]
+        ms = time_graphs(graphs, k_steps, warmup) / k_steps
+        per_kind = time_step_launches(steps, k_steps, warmup)
+        kern = summarize(per_kind)
+        nbytes = kern["bytes_per_step"]
+        out[label] = {"launches_per_step": len(mats), "ms_per_step": round(ms, 5),
+                      "gbs": round(nbytes / 1e6 / ms, 1), "frac_hbm": round(nbytes / 1e6 / ms / HBM_PEAK_GBS, 4),
+                      "weight_bytes_per_step": nbytes, "kernel_ms_per_step": round(kern["kernel_ms_per_step"], 5),
+                      "launches": kern["launches"], "sanity_worst_ratio": worst}
+        del graphs, steps, layers
+        torch.cuda.empty_cache()
+    out["workload"] = ("bf16 decode GEMV, batch 1, one dense decoder layer, hidden 5120: fused qkv 7168x5120, o "
+                       "5120x5120, gate_up 34816x5120, down 5120x17408; unfused q, k, v, o, gate, up, down")
     return out
 
 
@@ -349,10 +501,8 @@ def run_nf4_gemv_4096(k_steps, warmup, copies=128):
         packs.append(wsl.nf4_pack(w))
         del w
     wsl.linear_gemv(packs[0], x, y=y, wfmt=wsl.WSL_W_NF4, n_out=n, k=k)
-    rows = sample_rows(n, 64, 3)
-    # the GEMV multiplies the exact c*s, the tile is bf16(c*s): 2^-8 relative per weight at most
-    worst = gate_gemv("nf4 gemv 4096", y[torch.as_tensor(rows, device="cuda")], nf4_rows_tile(packs[0], n, k, rows),
-                      x, 4e-3)
+    worst = gate_gemv_nf4("nf4 gemv 4096", y, packs[0], n, k, sample_rows(n, 64, 3), x)
+    OUTPUT_SHA["nf4_gemv_4096"] = sha256_of([y])
     nb = wsl.nf4_packed_bytes(n, k)
     steps = [[Launch(lambda p=p: wsl.linear_gemv(p, x, y=y, wfmt=wsl.WSL_W_NF4, n_out=n, k=k), nbytes=nb,
                      flops=2 * n * k, name="nf4_gemv_4096")] for p in packs]
@@ -365,73 +515,8 @@ def run_nf4_gemv_4096(k_steps, warmup, copies=128):
                            "bytes_for_75pct_at_this_t0": round(3 * t0 * 1e-6 * HBM_PEAK_GBS * 1e9)}
     out.update({"workload": "NF4 GEMV 4096x4096, fp32 out", "rotation_copies": copies, "sanity_worst_ratio": worst,
                 "frac_hbm": out["kernel_gbs"] / HBM_PEAK_GBS,
-                "frac_read_ceiling": out["kernel_gbs"] / measure_read_ceiling()["gbs"]})
+                "frac_stream_read_probe": out["kernel_gbs"] / measure_read_ceiling()["gbs"]})
     del packs
-    torch.cuda.empty_cache()
-    return out
-
-
-SWEEP_6144 = [("qkv", 8192, 6144), ("o", 6144, 6144), ("gate_up", 32768, 6144), ("down", 6144, 16384)]
-
-
-def run_nf4_decode_sweep(k_steps, warmup, layers=48):
-    """48-layer NF4 decode sweep, hidden 6144: 192 launches per token, replayed as one captured
-    graph per token; per-stage kernel durations from blocks of launches."""
-    import torch
-    import synth
-    import weight_streaming_linear_amd as wsl
-    xs = [synth.device_normal_bf16(2, 1000 + j, (k,)) for j, (_, n, k) in enumerate(SWEEP_6144)]
-    ys = [torch.empty(n, dtype=torch.float32, device="cuda") for (_, n, _) in SWEEP_6144]
-    packs = []
-    t_setup = time.time()
-    for l in range(layers):
-        for j, (name, n, k) in enumerate(SWEEP_6144):
-            w = synth.device_weight(2, 16 * l + j, n, k)
-            packs.append((wsl.nf4_pack(w), n, k, j))
-            del w
-    torch.cuda.synchronize()
-    log(f"nf4 decode sweep: packed {layers} layers in {time.time() - t_setup:.1f}s")
-    worst = 0.0
-    for j, (name, n, k) in enumerate(SWEEP_6144):
-        wsl.linear_gemv(packs[j][0], xs[j], y=ys[j], wfmt=wsl.WSL_W_NF4, n_out=n, k=k)
-        rows = sample_rows(n, 32, 11 + j)
-        worst = max(worst, gate_gemv(f"nf4 decode sweep {name}", ys[j][torch.as_tensor(rows, device="cuda")],
-                                     nf4_rows_tile(packs[j][0], n, k, rows), xs[j], 4e-3))
-    launches = [Launch(lambda p=p, n=n, k=k, j=j: wsl.linear_gemv(p, xs[j], y=ys[j], wfmt=wsl.WSL_W_NF4, n_out=n, k=k),
-                       nbytes=wsl.nf4_packed_bytes(n, k), flops=2 * n * k, name=f"nf4_gemv_{SWEEP_6144[j][0]}")
-                for (p, n, k, j) in packs]
-    g = capture(launches)
-    graph_ms = time_graphs([g], k_steps, warmup) / k_steps
-    # the same token step preceded by the packed-embedding gather of a device-resident token id
-    # (hidden 6144 table of 128000 rows), the id advanced on the device inside the graph
-    emb_n = 128000
-    wemb = synth.device_weight(2, 999, emb_n, 6144)
-    emb = wsl.nf4_pack(wemb)
-    del wemb
-    tok = torch.zeros(1, dtype=torch.int64, device="cuda")
-    hid = torch.empty((1, 6144), dtype=torch.bfloat16, device="cuda")
-    step_launches = [Launch(lambda: wsl.nf4_embed_rows(emb, emb_n, 6144, tok, out=hid))] + launches + \
-        [Launch(lambda: tok.add_(1))]
-    g2 = capture(step_launches)
-    before = torch.cuda.memory_allocated()
-    step_ms = time_graphs([g2], k_steps, warmup) / k_steps
-    grew = torch.cuda.memory_allocated() - before
-    # per stage: one block of launches over the 48 layers' matrices of that stage
-    out = summarize(time_step_launches([launches], 2 * layers, 4), {f"nf4_gemv_{st[0]}": layers for st in SWEEP_6144})
-    out.update({
-        "workload": "NF4 decode sweep, 48 layers x (qkv 8192x6144, o 6144x6144, gate_up 32768x6144, down 6144x16384)",
-        "sanity_worst_ratio": worst, "frac_hbm_kernels": out["kernel_gbs"] / HBM_PEAK_GBS,
-        "graph_ms_per_token": graph_ms, "graph_tokens_per_s": 1e3 / graph_ms,
-        "graph_gbs": out["bytes_per_step"] / 1e9 / (graph_ms / 1e3),
-        "frac_hbm_graph": out["bytes_per_step"] / 1e9 / (graph_ms / 1e3) / HBM_PEAK_GBS,
-        "frac_read_ceiling_graph": out["bytes_per_step"] / 1e9 / (graph_ms / 1e3) / measure_read_ceiling()["gbs"],
-        "launch_floor_ms_per_token": round(out["launches_per_step"] * measure_launch_floor()["us"] / 1e3, 4),
-        "launch_gap_us_per_launch": 1e3 * (graph_ms - out["kernel_ms_per_step"]) / out["launches_per_step"],
-        "decode_step_graph": {"ms_per_token": step_ms, "tokens_per_s": 1e3 / step_ms,
-                              "what": "embedding gather (device-resident token id) + 192 GEMVs + id advance, one graph",
-                              "allocator_growth_bytes": grew},
-    })
-    del g, g2, packs, launches, step_launches, emb
     torch.cuda.empty_cache()
     return out
 
@@ -456,6 +541,7 @@ def run_nf4_prefill_gemm(k_steps, warmup, copies=16):
             p = wsl.nf4_pack(w)
             if c == 0:
                 wsl.linear_gemm(p, xs[j], y=ys[j], wfmt=wsl.WSL_W_NF4, n_out=n, k=k, workspace=wss[j])
+                OUTPUT_SHA[f"nf4_prefill_gemm_m32_{name}"] = sha256_of([ys[j]])
                 cols = sample_rows(n, 48, 21 + j)
                 t = nf4_rows_tile(p, n, k, cols).float()
                 xf = xs[j].float()
@@ -466,7 +552,8 @@ def run_nf4_prefill_gemm(k_steps, warmup, copies=16):
         packs.append(pc)
     steps = [[Launch(lambda p=pc[j], j=j, n=n, k=k: wsl.linear_gemm(p, xs[j], y=ys[j], wfmt=wsl.WSL_W_NF4, n_out=n,
                                                                       k=k, workspace=wss[j]),
-                     nbytes=wsl.nf4_packed_bytes(n, k), flops=2 * m * n * k, name=f"nf4_gemm_{name}")
+                     nbytes=wsl.nf4_packed_bytes(n, k), flops=2 * m * n * k, name=f"nf4_gemm_{name}",
+                     dispatches=2 if wsl.linear_gemm_workspace_bytes(wsl.WSL_W_NF4, n, k, m) > 0 else 1)
               for j, (name, n, k) in enumerate(mats)] for pc in packs]
     out = summarize(time_step_launches(steps, k_steps, warmup))
     ai = out["flops_per_step"] / out["bytes_per_step"]
@@ -500,6 +587,7 @@ def run_bf16_verify_gemm(k_steps, warmup, copies=2):
         got = ys[j][rows][:, cols]
         worst = max(worst, check_close(f"bf16 verify gemm {name}", got, xf @ wf.t().contiguous(),
                                        xf.abs() @ wf.abs().t().contiguous(), 1e-4, ulp_rel=2.0 ** -8))
+        OUTPUT_SHA[f"bf16_verify_gemm_m8192_{name}"] = sha256_of([ys[j]])
     steps = [[Launch(lambda w=wc[j], j=j: wsl.linear_gemm(w, xs[j], y=ys[j], ofmt=wsl.WSL_OUT_BF16),
                      nbytes=2 * n * k, flops=2 * m * n * k, name=f"bf16_gemm_{name}")
               for j, (name, n, k) in enumerate(mats)] for wc in ws]
@@ -530,10 +618,11 @@ def run_nf4_embed_rows(k_steps, warmup):
         t = nf4_rows_tile(packed, n_rows, k, idss[0].cpu().numpy()[:4])
         if not torch.equal(ys[:4], t):
             refuse(f"nf4 embed rows count {count}", float("inf"))
+        OUTPUT_SHA[f"nf4_embed_rows_{count}"] = sha256_of([ys])
         nbytes = count * (k // 2 + (k // 64) * 2) + count * k * 2      # packed rows read + bf16 rows written
         launches = [Launch(lambda ids=ids: wsl.nf4_embed_rows(packed, n_rows, k, ids, out=ys), nbytes=nbytes,
                            name=f"rows_{count}") for ids in idss]
-        us = time_block(launches, k_steps, warmup)
+        us = time_block(launches, k_steps, warmup, label=f"nf4_embed_rows_{count}")
         out[f"rows_{count}"] = {"avg_us": round(us, 3), "gbs": round(nbytes / 1e3 / us, 1)}
     out["workload"] = "NF4 embedding row gather, table 128000x5120 (348 MB packed), bf16 out"
     del packed
@@ -592,6 +681,7 @@ def run_copyring_decode_sweep(k_steps, warmup, layers=48, resident_layers=29):
     torch.cuda.synchronize()
     if not all(torch.equal(g, y) for g, y in zip(got, ys)):
         refuse("copy ring decode sweep", float("inf"))
+    OUTPUT_SHA["copyring_layer0"] = sha256_of(got)
 
     def all_streamed():
         ring.gemv(host, stream_xs, stream_ys)
@@ -654,6 +744,7 @@ def run_nf4_verify_gemm(k_steps, warmup, copies=2):
         got = ys[j][rows][:, torch.as_tensor(cols, device="cuda")]
         worst = max(worst, check_close(f"nf4 verify gemm {name}", got, xf @ t.t().contiguous(),
                                        xf.abs() @ t.abs().t().contiguous(), 1e-4, ulp_rel=2.0 ** -8))
+        OUTPUT_SHA[f"nf4_verify_gemm_m8192_{name}"] = sha256_of([ys[j]])
     steps = [[Launch(lambda p=pc[j], j=j, n=n, k=k: wsl.linear_gemm(p, xs[j], y=ys[j], wfmt=wsl.WSL_W_NF4, n_out=n,
                                                                       k=k, ofmt=wsl.WSL_OUT_BF16),
                      nbytes=wsl.nf4_packed_bytes(n, k), flops=2 * m * n * k, name=f"nf4_gemm_{name}")
@@ -692,10 +783,12 @@ def run_nf4_gemm_mid_m(k_steps, warmup, copies=8):
                 xf = xs[j].float()
                 worst = max(worst, check_close(f"nf4 gemm m={m}", ys[j][:, torch.as_tensor(cols, device="cuda")],
                                                xf @ t.t().contiguous(), xf.abs() @ t.abs().t().contiguous(), 1e-4))
+                OUTPUT_SHA[f"nf4_gemm_27648x5120_m{m}"] = sha256_of([ys[j]])
         packs.append(p)
     steps = [[Launch(lambda p=p, j=j, m=m: wsl.linear_gemm(p, xs[j], y=ys[j], wfmt=wsl.WSL_W_NF4, n_out=n, k=k,
                                                            workspace=wss[j]),
-                     nbytes=wsl.nf4_packed_bytes(n, k), flops=2 * m * n * k, name=f"nf4_gemm_m{m}")
+                     nbytes=wsl.nf4_packed_bytes(n, k), flops=2 * m * n * k, name=f"nf4_gemm_m{m}",
+                     dispatches=2 if wsl.linear_gemm_workspace_bytes(wsl.WSL_W_NF4, n, k, m) > 0 else 1)
               for j, m in enumerate(ms)] for p in packs]
     out = summarize(time_step_launches(steps, k_steps, warmup))
     for j, m in enumerate(ms):
@@ -709,7 +802,7 @@ def run_nf4_gemm_mid_m(k_steps, warmup, copies=8):
     return out
 
 
-PATHS = [("nf4_gemv_4096", run_nf4_gemv_4096), ("nf4_decode_sweep_48x6144", run_nf4_decode_sweep),
+PATHS = [("bf16_decode_layer_5120", run_bf16_decode_layer), ("nf4_gemv_4096", run_nf4_gemv_4096),
          ("nf4_prefill_gemm_m32", run_nf4_prefill_gemm), ("nf4_gemm_mid_m_27648x5120", run_nf4_gemm_mid_m),
          ("bf16_verify_gemm_m8192", run_bf16_verify_gemm),
          ("nf4_verify_gemm_m8192", run_nf4_verify_gemm), ("nf4_embed_rows_128000x5120", run_nf4_embed_rows),
@@ -717,9 +810,15 @@ PATHS = [("nf4_gemv_4096", run_nf4_gemv_4096), ("nf4_decode_sweep_48x6144", run_
 
 
 # ---------------------------------------------------------------- CPU baseline (oracle)
-def cpu_baseline(budget_s=12.0):
-    """The oracle's GEMV (bf16 -> fp64 conversion + fp64 BLAS matvec) on the headline layer,
-    timed on this host's cores, repeated over the 4 matrices until about budget_s."""
+def cpu_baseline(budget_s=15.0):
+    """The oracle's decode GEMV on the headline workload, timed on this host's cores: one
+    layer of the 48-layer stack (the same seeded weights as layer 0, drawn on the device and
+    copied to the host as bf16 bits), encoded once with oracle.pack_codes (untimed: the
+    encoding is offline), then passes over the layer's four matrices through
+    oracle.dequant_exact + oracle.gemv_ref (fp64 levels * scales, fp64 BLAS matvec) until
+    about budget_s.  Reported as packed weight GB/s, like the GPU figure, and as the token
+    time it implies for the 48 layers."""
+    import torch
     import oracle
     import synth
     try:
@@ -728,21 +827,77 @@ def cpu_baseline(budget_s=12.0):
     except Exception:
         blas_threads = None
     cores = len(os.sched_getaffinity(0))
-    mats = [(synth.weight_bits(1, j, n, k), synth.act_bits(1, 100 + j, (k,))) for j, (_, n, k) in enumerate(LAYER_5120)]
-    done_bytes = 0
+    mats = []
+    t_pack = time.perf_counter()
+    for j, (_, n, k) in enumerate(SWEEP_6144):
+        w = synth.device_weight(2, j, n, k)
+        bits = w.view(torch.int16).cpu().numpy().view(np.uint16)
+        del w
+        codes, scales = oracle.pack_codes(oracle.f32_from_bf16_bits(bits))
+        x = synth.device_normal_bf16(2, 1000 + j, (k,)).view(torch.int16).cpu().numpy().view(np.uint16)
+        mats.append((codes, scales, oracle.f32_from_bf16_bits(x).astype(np.float64), oracle.packed_bytes(n, k)))
+    t_pack = time.perf_counter() - t_pack
+    torch.cuda.empty_cache()
+    done_bytes, passes = 0, 0
     t0 = time.perf_counter()
-    passes = 0
     while True:
-        for wb, xb in mats:
-            oracle.gemv_ref(oracle.f32_from_bf16_bits(wb), oracle.f32_from_bf16_bits(xb))
-            done_bytes += wb.size * 2
+        for codes, scales, x, nb in mats:
+            oracle.gemv_ref(oracle.dequant_exact(codes, scales), x)
+            done_bytes += nb
         passes += 1
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
+    layer_s = dt / passes
     return {"value": done_bytes / 1e9 / dt, "unit": "GB/s", "cores": blas_threads or cores, "kind": "oracle",
-            "sample": f"{passes} pass(es) of the headline layer's 4 bf16 matrices (660.6 MB of weights each) "
-                      f"through oracle.gemv_ref (bf16->fp64 + fp64 BLAS matvec), {dt:.1f} s; host has {cores} cores"}
+            "ms_per_token_48_layers": round(1e3 * layer_s * SWEEP_LAYERS, 1),
+            "sample": f"{passes} pass(es) over one layer of the headline stack (qkv 8192x6144, o 6144x6144, gate_up "
+                      f"32768x6144, down 6144x16384: {sum(m[3] for m in mats)} packed bytes) through "
+                      f"oracle.dequant_exact + oracle.gemv_ref (fp64), {dt:.1f} s timed; the encoding "
+                      f"(oracle.pack_codes, {t_pack:.1f} s) untimed; the 48-layer token time is 48x the layer "
+                      f"time; host has {cores} cores, BLAS threads {blas_threads}"}
+
+
+def provenance():
+    """What the line was measured with: commit (when the tree is a git checkout), a digest of
+    the sources, ROCm / HIP / torch versions, the device and the host CPU."""
+    import subprocess
+    import torch
+    info = {}
+    try:
+        r = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], stdout=subprocess.PIPE, stderr=subprocess.DEVNULL,
+                           text=True, timeout=10)
+        info["commit"] = r.stdout.strip() or None
+    except Exception:
+        info["commit"] = None
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "weight_streaming_linear_amd", "csrc", "*")) +
+                   glob.glob(os.path.join(ROOT, "include", "*.h")) + [os.path.abspath(__file__)])
+    for f in files:
+        h.update(open(f, "rb").read())
+    info["source_sha256"] = h.hexdigest()
+    try:
+        info["rocm"] = open("/opt/rocm/.info/version").read().strip()
+    except Exception:
+        info["rocm"] = None
+    info["hip_runtime"] = torch.version.hip
+    info["torch"] = torch.__version__
+    p = torch.cuda.get_device_properties(0)
+    info["device"] = {"name": p.name, "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
+                      "memory_gib": round(p.total_memory / 2 ** 30, 1)}
+    try:
+        r = subprocess.run(["rocm-smi", "--showproductname", "--showclocks"], stdout=subprocess.PIPE,
+                           stderr=subprocess.DEVNULL, text=True, timeout=20)
+        keep = [l.strip() for l in r.stdout.splitlines() if any(t in l for t in ("Card SKU", "Card Series", "sclk",
+                                                                                  "mclk", "fclk"))]
+        info["rocm_smi"] = keep[:12]
+    except Exception:
+        info["rocm_smi"] = None
+    try:
+        info["host_cpu"] = next(l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo") if l.startswith("model name"))
+    except Exception:
+        info["host_cpu"] = None
+    return info
 
 
 # ---------------------------------------------------------------- HBM traffic from rocprofv3 counters
@@ -753,20 +908,29 @@ def source_sha():
 def traffic_probe():
     """The launches that a counter run of this script sees: 3 elementwise copies of CALIB_BYTES
     (torch.neg into a second buffer: a kernel that reads and writes exactly CALIB_BYTES), then
-    4 eager launches of the headline layer's gate_up GEMV (the only GEMV dispatches of the
-    run).  No timing, no oracle."""
+    4 eager launches of the headline's dominant kernel, the NF4 gate_up GEMV (32768x6144), on
+    4 distinct packed matrices of the stack (the only GEMV dispatches of the run).  No timing,
+    no oracle."""
     import torch
+    import synth
+    import weight_streaming_linear_amd as wsl
     src = torch.empty(CALIB_BYTES // 2, dtype=torch.bfloat16, device="cuda").normal_()
     dst = torch.empty_like(src)
     for _ in range(3):
         torch.neg(src, out=dst)
     torch.cuda.synchronize()
     del src, dst
-    _, _, _, steps = setup_layer_5120(copies=2)
-    for i in range(4):
-        for l in steps[i % 2]:
-            if l.name == "gate_up":
-                l.fn()
+    n, k = 32768, 6144
+    x = synth.device_normal_bf16(2, 1002, (k,))
+    y = torch.empty(n, dtype=torch.float32, device="cuda")
+    packs = []
+    for l in range(4):
+        w = synth.device_weight(2, 16 * l + 2, n, k)
+        packs.append(wsl.nf4_pack(w))
+        del w
+    torch.cuda.synchronize()
+    for p in packs:
+        wsl.linear_gemv(p, x, y=y, wfmt=wsl.WSL_W_NF4, n_out=n, k=k)
     torch.cuda.synchronize()
     print("traffic probe done", flush=True)
 
@@ -795,7 +959,7 @@ def traffic_summarize(fetch_dir, write_dir, commands):
     """Per-launch HBM bytes of the dominant kernel from two counter runs of --traffic-probe."""
     # calibration: the elementwise negation of CALIB_BYTES (reads and writes CALIB_BYTES)
     is_calib = lambda n: "neg_kernel" in n
-    is_dom = lambda n: "gemv_bf16_kernel" in n
+    is_dom = lambda n: "gemv_nf4_team_kernel" in n
     out = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = _counter_rows(d, counter)
@@ -807,8 +971,8 @@ def traffic_summarize(fetch_dir, write_dir, commands):
         out[counter] = {"kib_per_dispatch_raw": float(np.mean(dom)), "dispatches": len(dom),
                         "calibration_copy_kib": float(np.mean(calib)), "factor": float(factor),
                         "bytes_per_launch": float(np.mean(dom) * 1024 / factor)}
-    algo = 2 * 34816 * 5120
-    res = {"kernel": "gemv_bf16_kernel<2> (gate_up 34816x5120)", "kernel_source_sha256": source_sha(),
+    algo = 32768 * 6144 // 2 + 32768 * (6144 // 64) * 2
+    res = {"kernel": DOMINANT_KERNEL, "kernel_source_sha256": source_sha(),
            "algorithmic_bytes_per_launch": algo, "counters": out,
            "bytes_per_launch": out["FETCH_SIZE"]["bytes_per_launch"] + out["WRITE_SIZE"]["bytes_per_launch"],
            "commands": commands}
@@ -924,32 +1088,64 @@ def mfma_summarize(run_dir, command):
     print("\n".join(lines))
 
 
-def trace_summarize(run_dir, title, command):
-    """Markdown summary of a rocprofv3 --kernel-trace --output-format csv run: the library's
-    dispatches grouped by kernel and grid size (one template instance serves several
-    matrix shapes, which differ in grid size), durations in microseconds."""
+def _trace_rows(run_dir):
+    """Every dispatch of a rocprofv3 --kernel-trace --output-format csv run, in start order:
+    (short kernel name, grid, workgroup, microseconds)."""
     import csv
-    groups = {}
+    rows = []
     for path in glob.glob(os.path.join(run_dir, "**", "*kernel_trace.csv"), recursive=True):
         with open(path) as f:
             for r in csv.DictReader(f):
                 name = r.get("Kernel_Name", "")
-                if "wsl::" not in name:
-                    continue
-                short = name.split("(")[0].replace("void ", "")
-                us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                short = "spin_kernel" if "spin_kernel" in name else name.split("(")[0].replace("void ", "")
                 dims = lambda pre: "x".join(r.get(f"{pre}_{a}", "1") for a in "XYZ").replace("x1x1", "").replace(
                     "x1", "") if f"{pre}_X" in r else r.get(pre, "?")
-                key = (short, dims("Grid_Size"), dims("Workgroup_Size"))
-                groups.setdefault(key, []).append(us)
-    total = sum(sum(v) for v in groups.values())
+                rows.append((int(r["Start_Timestamp"]), short, dims("Grid_Size"), dims("Workgroup_Size"),
+                             (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+    rows.sort()
+    return [r[1:] for r in rows]
+
+
+def trace_summarize(run_dir, title, command, block_log=None):
+    """Markdown summary of a rocprofv3 --kernel-trace --output-format csv run of this script.
+    With the block log the run wrote (--block-log), the dispatches of every timed block --
+    the ones that follow its spin kernel -- are attributed to the block's workload and shape;
+    the library's dispatches are also grouped by kernel and grid size.  Durations in
+    microseconds."""
+    rows = _trace_rows(run_dir)
     lines = [f"# {title}", "", "Command (run from the repository root on one MI355X, ROCm 7.2, rocprofv3):", "",
-             "```", command, "```", "",
-             "Library dispatches of the run, grouped by kernel and grid size (work-items); durations "
-             "in microseconds from the kernel trace.  Summary written by "
-             "`python bench.py --trace-summarize <run dir> <title> <command>`.", "",
-             "| kernel | grid | workgroup | calls | total (us) | average (us) | min (us) | max (us) | % of library time |",
-             "|---|---:|---:|---:|---:|---:|---:|---:|---:|"]
+             "```", command, "```", ""]
+    if block_log:
+        blocks = json.load(open(block_log))
+        # torch's spin kernel: two calibration launches come first, then one per block
+        spins = [i for i, r in enumerate(rows) if r[0] == "spin_kernel"][-len(blocks):]
+        lines += ["## Timed blocks", "",
+                  "Each block timed by the benchmark, cut from the trace: the dispatches after the block's spin "
+                  "kernel (launches x dispatches per launch).  Summary written by "
+                  "`python bench.py --trace-summarize <run dir> <title> <command> <block log>`.", "",
+                  "| block (workload / shape) | kernel | grid | dispatches | average (us) | min (us) | max (us) |",
+                  "|---|---|---:|---:|---:|---:|---:|"]
+        if len(spins) < len(blocks):
+            lines.append(f"| (trace has {len(spins)} spin kernels for {len(blocks)} blocks: not attributed) |||||||")
+        else:
+            for (label, reps, per), si in zip(blocks, spins):
+                seg = [r for r in rows[si + 1: si + 1 + reps * per] if "wsl::" in r[0]]
+                kinds = {}
+                for r in seg:
+                    kinds.setdefault((r[0], r[1]), []).append(r[3])
+                for (kname, grid), v in kinds.items():
+                    lines.append(f"| {label} | `{kname}` | {grid} | {len(v)} | {np.mean(v):.3f} | {min(v):.3f} | "
+                                 f"{max(v):.3f} |")
+        lines.append("")
+    groups = {}
+    for short, grid, wg, us in rows:
+        if "wsl::" in short:
+            groups.setdefault((short, grid, wg), []).append(us)
+    total = sum(sum(v) for v in groups.values())
+    lines += ["## All library dispatches", "",
+              "Grouped by kernel and grid size (one template instance serves several shapes).", "",
+              "| kernel | grid | workgroup | calls | total (us) | average (us) | min (us) | max (us) | % of library time |",
+              "|---|---:|---:|---:|---:|---:|---:|---:|---:|"]
     for (short, grid, wg), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
         lines.append(f"| `{short}` | {grid} | {wg} | {len(v)} | {sum(v):.1f} | {np.mean(v):.3f} | {min(v):.3f} | "
                      f"{max(v):.3f} | {100 * sum(v) / total:.2f} |")
@@ -962,8 +1158,9 @@ REPEAT_FIGURES = [
     ("value_gbs", ("value",)),
     ("ms_per_step", ("ms_per_step",)),
     ("dominant_kernel_gbs", ("roofline", "achieved")),
-    ("read_ceiling_gbs", ("read_ceiling", "gbs")),
-    ("nf4_sweep_graph_ms_per_token", ("paths", "nf4_decode_sweep_48x6144", "graph_ms_per_token")),
+    ("stream_read_probe_gbs", ("stream_read_probe", "gbs")),
+    ("sweep_kernel_ms_per_token", ("headline_detail", "sweep_kernel", "ms_per_token")),
+    ("bf16_layer_fused_gbs", ("paths", "bf16_decode_layer_5120", "fused", "gbs")),
     ("nf4_gemv_4096_us", ("paths", "nf4_gemv_4096", "launches", "nf4_gemv_4096", "avg_us")),
     ("nf4_gemm_m32_tflops", ("paths", "nf4_prefill_gemm_m32", "kernel_tflops")),
     ("bf16_gemm_m8192_tflops", ("paths", "bf16_verify_gemm_m8192", "kernel_tflops")),
@@ -998,6 +1195,8 @@ def run_repeats(args):
             cmd += ["--only", args.only]
         if args.no_cpu_baseline or r > 0:
             cmd.append("--no-cpu-baseline")
+        if args.block_log and r == 0:
+            cmd += ["--block-log", args.block_log]
         log(f"repeat {r + 1}/{args.repeats} in a fresh process")
         p = subprocess.run(cmd, stdout=subprocess.PIPE, text=True)
         if p.returncode != 0:
@@ -1017,6 +1216,16 @@ def run_repeats(args):
     out["value"] = round(rec["figures"]["value_gbs"]["median"], 2)
     out["ms_per_step"] = round(rec["figures"]["ms_per_step"]["median"], 6)
     out["repeats"] = rec
+    # determinism: every workload's outputs hash the same in every process
+    shas = [l.get("output_sha256", {}) for l in lines]
+    keys = sorted(set().union(*shas))
+    differ = [k for k in keys if len({s.get(k) for s in shas}) != 1]
+    out["determinism"] = {"processes": len(lines), "workloads": len(keys), "identical": not differ,
+                          "what": "SHA-256 of every workload's outputs, compared across the fresh processes"}
+    if differ:
+        log(f"outputs differ between processes for {differ}: refusing")
+        print(json.dumps({"error": "nondeterministic outputs", "workloads": differ}), flush=True)
+        return 3
     print(json.dumps(out), flush=True)
     return 0
 
@@ -1037,8 +1246,10 @@ def main():
     ap.add_argument("--mfma-probe", action="store_true", help="GEMM launch sequence for rocprofv3 MFMA counter runs")
     ap.add_argument("--mfma-summarize", nargs=2, metavar=("RUN_DIR", "COMMAND"))
     ap.add_argument("--traffic-commands", default="", help="the counter commands, recorded with the summary")
-    ap.add_argument("--trace-summarize", nargs=3, metavar=("RUN_DIR", "TITLE", "COMMAND"),
-                    help="markdown summary of a rocprofv3 kernel-trace CSV run")
+    ap.add_argument("--trace-summarize", nargs="+", metavar="ARG",
+                    help="RUN_DIR TITLE COMMAND [BLOCK_LOG]: markdown summary of a rocprofv3 kernel-trace CSV run")
+    ap.add_argument("--block-log", default="", help="write the timed blocks (label, launches, dispatches per "
+                                                     "launch) to this file, for --trace-summarize")
     args = ap.parse_args()
     if args.trace_summarize:
         trace_summarize(*args.trace_summarize)
@@ -1070,14 +1281,14 @@ def main():
     log(f"device {props.name} ({getattr(props, 'gcnArchName', '?')}), {props.multi_processor_count} CUs")
 
     head = measure_headline(args.steps, args.warmup)
-    per_launch = head["per_launch"]
-    value = per_launch["bytes_per_step"] / 1e9 / (head["ms_per_step"] / 1e3)
+    value = head["token_bytes"] / 1e9 / (head["ms_per_token"] / 1e3)
     achieved = head["dominant_bytes"] / 1e3 / head["dominant_avg_us"]
-    log(f"bf16 decode layer: {head['ms_per_step'] * 1e3:.1f} us/step (graph), {value:.0f} GB/s; "
-        f"kernels {per_launch['kernel_ms_per_step'] * 1e3:.1f} us/step; gate_up kernel {achieved:.0f} GB/s")
+    log(f"nf4 decode sweep: {head['ms_per_token']:.3f} ms/token, {value:.0f} GB/s; dominant gate_up kernel "
+        f"{head['dominant_avg_us']:.2f} us = {achieved:.0f} GB/s; one-launch sweep "
+        f"{head['sweep_kernel']['ms_per_token']:.3f} ms/token")
 
-    ceiling = measure_read_ceiling()
-    log(f"streaming-read ceiling: {ceiling['gbs']:.0f} GB/s")
+    probe = measure_read_ceiling()
+    log(f"stream-read probe: {probe['gbs']:.0f} GB/s")
 
     paths = {}
     if not args.no_paths:
@@ -1096,20 +1307,21 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(head["ms_per_step"], 6),
+        "ms_per_step": round(head["ms_per_token"], 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) activations; drawn on the device)",
+        "dtype": "f32",
+        "data": "synthetic (seeded N(0,0.02) weights packed to NF4 on the device, N(0,1) bf16 activations; "
+                "drawn on the device)",
         "config": {
-            "workload": "bf16 decode GEMV, batch 1, one dense decoder layer, hidden 5120: "
-                        "qkv 7168x5120, o 5120x5120, gate_up 34816x5120, down 5120x17408 (4 launches per "
-                        "step; the K timed steps replayed as one captured graph, two layer copies alternating)",
-            "weight_bytes_per_step": per_launch["bytes_per_step"],
-            "rotation_bytes": 2 * per_launch["bytes_per_step"],
+            "workload": "NF4 decode GEMV sweep, batch 1, 48-layer stack of hidden 6144: qkv 8192x6144, o 6144x6144, "
+                        "gate_up 32768x6144, down 6144x16384 per layer; 192 launches per token in decoder order, "
+                        "one graph per token",
+            "weight_format": "NF4: 4-bit codes, groups of 64 along k, one fp16 scale per group (17/32 B per weight)",
+            "activations": "bf16, fp32 accumulation, fp32 outputs",
+            "weight_bytes_per_token": head["token_bytes"],
             "parallelism": "single GPU",
-            "device": props.name,
         },
         "roofline": {
             "bound": "hbm",
@@ -1118,26 +1330,32 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic_from_file(),
-            "kernel": "gemv_bf16_kernel<2> (gate_up 34816x5120)",
+            "kernel": DOMINANT_KERNEL,
             "bytes_per_launch": head["dominant_bytes"],
             "avg_launch_us": round(head["dominant_avg_us"], 3),
         },
-        "read_ceiling": ceiling,
+        "stream_read_probe": probe,
         "headline_detail": {
-            "ms_per_step_one_graph_per_step": round(head["ms_per_step_one_graph_per_step"], 6),
-            "gbs_one_graph_per_step": round(per_launch["bytes_per_step"] / 1e9
-                                            / (head["ms_per_step_one_graph_per_step"] / 1e3), 2),
-            "frac_read_ceiling": round(value / ceiling["gbs"], 4),
-            "dominant_frac_read_ceiling": round(achieved / ceiling["gbs"], 4),
+            "frac_hbm": round(value / HBM_PEAK_GBS, 4),
+            "tokens_per_s": round(1e3 / head["ms_per_token"], 2),
+            "frac_stream_read_probe": round(value / probe["gbs"], 4),
             "sanity_worst_ratio": head["sanity_worst_ratio"],
-            "kernel_ms_per_step": round(per_launch["kernel_ms_per_step"], 6),
-            "launches": per_launch["launches"],
+            "kernel_ms_per_token": round(head["kernels"]["kernel_ms_per_step"], 5),
+            "kernels": head["kernels"]["launches"],
+            "sweep_kernel": head["sweep_kernel"],
+            "decode_step_graph": head["decode_step_graph"],
+            "launch_floor": head["launch_floor"],
         },
         "paths": paths,
     }
+    out["provenance"] = provenance()
+    out["output_sha256"] = dict(OUTPUT_SHA)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline()
+    if args.block_log:
+        with open(args.block_log, "w") as f:
+            json.dump(BLOCK_LOG, f)
     print(json.dumps(out), flush=True)
 
 
