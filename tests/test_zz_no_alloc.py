@@ -4,6 +4,8 @@ serving loops).  Checked through the C ABI against linear_gemm with a workspace 
 bit: same kernels, same splits) and against the fp64 oracle, on consecutive calls whose
 second input is smaller, so the second call runs on scratch the first one left behind."""
 
+import gc
+
 import numpy as np
 import pytest
 
@@ -102,13 +104,16 @@ def test_noalloc_under_graph_capture():
         wsl.linear_gemm_noalloc(packed, x, y, wfmt=wsl.WSL_W_NF4, n_out=n_out, k=k)
     torch.cuda.current_stream().wait_stream(s)
     g = torch.cuda.CUDAGraph()
+    gc.collect()
+    allocs = lambda: torch.cuda.memory_stats().get("allocation.all.allocated", 0)   # requests so far
     with torch.cuda.graph(g):
-        # (beginning a capture allocates torch's own bookkeeping, so measure around the call)
-        before = torch.cuda.memory_allocated()
+        # (beginning a capture allocates torch's own bookkeeping, so count around the call;
+        # requests, not bytes: a Python object freed meanwhile must not hide an allocation)
+        before = allocs()
         wsl.linear_gemm_noalloc(packed, x, y, wfmt=wsl.WSL_W_NF4, n_out=n_out, k=k)
-        grew = torch.cuda.memory_allocated() - before
+        requested = allocs() - before
     torch.cuda.synchronize()
-    assert grew == 0
+    assert requested == 0
     for _ in range(3):
         y.fill_(float("nan"))
         torch.cuda.synchronize()
