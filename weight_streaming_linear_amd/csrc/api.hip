@@ -13,7 +13,7 @@ int launch_dequant_tile(const void *packed, int64_t n_out, int64_t k, int64_t ro
 int launch_gemv_bf16(const void *w, int64_t n_out, int64_t k, const void *x, float *y, hipStream_t s);
 int launch_gemv_nf4(const void *w, int64_t n_out, int64_t k, const void *x, float *y, hipStream_t s);
 size_t sweep_ws_bytes();
-int launch_gemv_nf4_sweep(const wsl_gemv_stage *d_stages, int64_t count, void *ws, hipStream_t s);
+int launch_gemv_nf4_sweep(const wsl_gemv_stage *d_stages, int64_t count, int64_t max_k, void *ws, hipStream_t s);
 int launch_gemm_bf16(const void *w, int64_t n_out, int64_t k, const void *x, int64_t m, int64_t ldx, void *y,
                      int ofmt, int64_t ldy, void *ws, size_t ws_bytes, hipStream_t s);
 int launch_gemm_nf4(const void *w, int64_t n_out, int64_t k, const void *x, int64_t m, int64_t ldx, void *y,
@@ -103,7 +103,9 @@ int linear_gemv_sweep(int wfmt, int64_t count, const wsl_gemv_stage *h_stages, c
     int rc = wsl::check_sweep(wfmt, count, h_stages, d_stages, d_ws, ws_bytes, wsl::sweep_ws_bytes());
     if (rc != WSL_OK || count == 0) return rc;
     if ((rc = wsl::device_ok()) != WSL_OK) return rc;
-    return wsl::after_launch(wsl::launch_gemv_nf4_sweep(d_stages, count, d_ws, wsl::as_stream(stream)));
+    int64_t max_k = 0;
+    for (int64_t i = 0; i < count; ++i) max_k = h_stages[i].k > max_k ? h_stages[i].k : max_k;
+    return wsl::after_launch(wsl::launch_gemv_nf4_sweep(d_stages, count, max_k, d_ws, wsl::as_stream(stream)));
 }
 
 size_t linear_gemm_workspace_bytes(int wfmt, int64_t n_out, int64_t k, int64_t m) {

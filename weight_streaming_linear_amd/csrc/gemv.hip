@@ -21,6 +21,9 @@
 //     two codes, about half the VALU work per code).  With the loads
 //     prefetched one row group ahead, the lookups and multiply-adds are what
 //     bounds the NF4 kernel, not HBM.
+#include <atomic>
+#include <type_traits>
+
 #include "device_common.h"
 
 namespace wsl {
@@ -304,9 +307,10 @@ __device__ __forceinline__ void load_x32(const uint16_t *__restrict__ x, int64_t
     widen_x32(xv, xf);
 }
 
-// Contiguous chunk of `total` work items owned by XCD `xcd` (of 8).
-__device__ __forceinline__ void xcd_chunk(int64_t total, int xcd, int64_t &first, int64_t &count) {
-    const int64_t per = total >> 3, rem = total & 7;
+// Contiguous chunk of `total` work items owned by workgroup group `xcd` (of nx: one group
+// per XCD, workgroup b dispatched to XCD b % nx).
+__device__ __forceinline__ void xcd_chunk(int64_t total, int xcd, int nx, int64_t &first, int64_t &count) {
+    const int64_t per = total / nx, rem = total - per * nx;
     first = xcd * per + (xcd < rem ? xcd : rem);
     count = per + (xcd < rem ? 1 : 0);
 }
@@ -361,7 +365,7 @@ struct TeamStage {
     uint32_t coff, gl;
 
     __device__ __forceinline__ void init(const uint8_t *p, int64_t n_out_, int64_t k, const uint16_t *x_, float *y_,
-                                         int S_, int T_, int wave, int lane) {
+                                         int S_, int T_, int wave, int lane, int nx) {
         packed = p;
         x = x_;
         y = y_;
@@ -389,11 +393,11 @@ struct TeamStage {
         kkl = active ? kk0 : k - 32;
         coff = static_cast<uint32_t>(kkl >> 1);
         gl = static_cast<uint32_t>(kkl >> 6);
-        const int xcd = blockIdx.x & 7;
-        nloc = gridDim.x >> 3;   // the grid is a multiple of 8
+        const int xcd = blockIdx.x % nx;
+        nloc = gridDim.x / nx;   // the grid is a multiple of nx
         int64_t count;
-        xcd_chunk(supers, xcd, first, count);
-        i0 = blockIdx.x >> 3;
+        xcd_chunk(supers, xcd, nx, first, count);
+        i0 = blockIdx.x / nx;
         n = i0 < count ? (count - i0 + nloc - 1) / nloc : 0;
         cap = kRowSumCap / (T * R);
         // Parking pays off once a workgroup owns several super-groups; with one or two
@@ -421,6 +425,47 @@ struct TeamStage {
     __device__ __forceinline__ void issue_x(uint4 (&xv)[4]) const { issue_x32(x, kkl, active, xv); }
 };
 
+// The loads of one super-group in a compact form (what fetch() computes for it): kept
+// across the tail of the previous stage by the decode sweep instead of a whole geometry.
+struct FirstLoads {
+    const uint8_t *rowp;   // first row of this wave's team, at the wave's slice
+    const char *sp;        // scale block of those rows, at this lane's group
+    int64_t rowbytes;
+    bool has;
+};
+
+// `dummy`: 16-byte aligned device memory of at least 16 bytes, read instead when the
+// workgroup has no super-group in the stage (the loads are then issued all the same, so
+// that no branch decides whether they are); the sweep passes a stage's x, read-only and
+// cached (not the barrier counters, which every workgroup would then load).
+template <int R, bool WIDE>
+__device__ __forceinline__ FirstLoads first_loads(const TeamStage<R, WIDE> &st, const void *dummy) {
+    FirstLoads f;
+    f.has = st.n > 0;
+    if (!f.has) {
+        f.rowp = static_cast<const uint8_t *>(dummy);
+        f.sp = static_cast<const char *>(dummy);
+        f.rowbytes = 0;
+        return f;
+    }
+    const int64_t row0 = ((st.first + st.i0) * st.T + st.fteam) * R;
+    f.rowp = st.packed + row0 * st.rowbytes + st.coff;
+    const int64_t blk = row0 >> 4;
+    const int64_t rem = st.n_out - (blk << 4);
+    const uint32_t rb = static_cast<uint32_t>(rem < 16 ? rem : 16);
+    f.sp = reinterpret_cast<const char *>(st.scales + blk * 16 * st.groups + (row0 & 15)) + st.gl * rb * 2u;
+    f.rowbytes = st.rowbytes;
+    return f;
+}
+
+template <int R>
+__device__ __forceinline__ void issue_first(const FirstLoads &f, uint4 (&q)[R], typename ScaleBits<R>::T &sb) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) q[r] = load_stream16(f.rowp + r * f.rowbytes);
+    sb = *reinterpret_cast<const typename ScaleBits<R>::T *>(f.sp);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 template <int TAB>
 __device__ __forceinline__ float team_dot(const uint4 &q, const float (&xf)[32], const char *tab, uint32_t (&ad)[4]) {
     if constexpr (TAB == 0) return nf4_dot32(q, xf, tab, 0x3cu);
@@ -431,10 +476,19 @@ __device__ __forceinline__ float team_dot(const uint4 &q, const float (&xf)[32],
 // parked-sum flushes and the leftover row groups.  On entry qa/sa hold the loads of
 // super-group 0 (when st.n > 0), xf this wave's x slice and the table is built.
 // SKIP: the form an idle wave runs -- no loads and no math, the same barriers and the
-// same share of the parked-sum stores as the other waves.
-template <int R, int TAB, bool SKIP, bool WIDE>
-__device__ __forceinline__ void team_run(const TeamStage<R, WIDE> &st, TeamLds<R, TAB> &lds, const float (&xf)[32],
-                                         uint32_t (&ad)[4], uint4 (&qa)[R], typename ScaleBits<R>::T &sa) {
+// same share of the parked-sum stores as the other waves.  `next` (decode sweep) issues
+// the loads of whatever comes after this matrix into the buffer it is given; it is
+// called once, before the last super-group is multiplied, so that those loads are in
+// flight meanwhile.  Returns true if it was given qb/sb, false if qa/sa or not called.
+struct NoNext {
+    template <typename Q, typename S_>
+    __device__ __forceinline__ void operator()(Q &, S_ &) const {}
+};
+
+template <int R, int TAB, bool SKIP, bool WIDE, typename Next = NoNext>
+__device__ __forceinline__ bool team_run(const TeamStage<R, WIDE> &st, TeamLds<R, TAB> &lds, const float (&xf)[32],
+                                         uint32_t (&ad)[4], uint4 (&qa)[R], typename ScaleBits<R>::T &sa,
+                                         uint4 (&qb)[R], typename ScaleBits<R>::T &sb, Next next = Next()) {
     typedef typename ScaleBits<R>::T SB;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -442,11 +496,12 @@ __device__ __forceinline__ void team_run(const TeamStage<R, WIDE> &st, TeamLds<R
     const int T = st.T, S = st.S;
     int ph = 0;
     int64_t jbeg = 0;
-    auto consume = [&](int64_t j, const uint4 (&q)[R], const SB &sb) {
+    bool in_b = false;
+    auto consume = [&](int64_t j, const uint4 (&q)[R], const SB &sb_) {
         if constexpr (!SKIP) {
             float acc[R];
 #pragma unroll
-            for (int r = 0; r < R; ++r) acc[r] = scale_at<R>(sb, r) * team_dot<TAB>(q[r], xf, lds.tab, ad);
+            for (int r = 0; r < R; ++r) acc[r] = scale_at<R>(sb_, r) * team_dot<TAB>(q[r], xf, lds.tab, ad);
             const float v = reduce_rows<R>(acc, lane);
             if ((lane % span) == 0) lds.red[ph][wave][lane / span] = v;
         }
@@ -464,10 +519,13 @@ __device__ __forceinline__ void team_run(const TeamStage<R, WIDE> &st, TeamLds<R
     auto fetch = [&](int64_t j, uint4 (&q)[R], SB &s_) {
         if constexpr (!SKIP) st.fetch(j, q, s_);
     };
-    uint4 qb[R];
-    SB sb;
     const int64_t n = st.n;
-    for (jbeg = 0; jbeg < n; jbeg += st.cap) {
+    // One round of up to cap super-groups.  LAST: the matrix's last round, whose tail
+    // calls next() -- a separate copy of the body, so that no runtime branch decides
+    // whether loads are issued (with one, the compiler waits for every load in flight,
+    // the next matrix's included, before the last multiply).
+    auto round = [&](auto last_tag) {
+        constexpr bool LAST = decltype(last_tag)::value;
         const int64_t jend = (jbeg + st.cap < n) ? jbeg + st.cap : n;
         if (jbeg > 0) fetch(jbeg, qa, sa);
         int64_t j = jbeg;
@@ -483,19 +541,28 @@ __device__ __forceinline__ void team_run(const TeamStage<R, WIDE> &st, TeamLds<R
         if (j + 1 < jend) {
             fetch(j + 1, qb, sb);
             consume(j, qa, sa);
+            if constexpr (LAST) next(qa, sa);
             consume(j + 1, qb, sb);
         } else {
+            if constexpr (LAST) {
+                next(qb, sb);
+                in_b = true;
+            }
             consume(j, qa, sa);
         }
         if (st.park) {
-            __syncthreads();
+            lds_barrier();
             for (int64_t e = threadIdx.x; e < (jend - jbeg) * T * R; e += blockDim.x) {
                 const int64_t jj = jbeg + e / (T * R);
                 const int64_t rest = e - (e / (T * R)) * (T * R);
                 st.y[(st.first + st.i0 + jj * st.nloc) * T * R + rest] = lds.yl[e];
             }
-            __syncthreads();
+            lds_barrier();
         }
+    };
+    if (n > 0) {
+        for (jbeg = 0; jbeg + st.cap < n; jbeg += st.cap) round(std::false_type());
+        round(std::true_type());
     }
     // Leftover row groups [supers * T, row_groups): T per workgroup, one per team,
     // rows clamped to the matrix and scales read one row at a time.  They go to the
@@ -527,7 +594,7 @@ __device__ __forceinline__ void team_run(const TeamStage<R, WIDE> &st, TeamLds<R
         }
         const float v = reduce_rows<R>(acc, lane);
         if ((lane % span) == 0) lds.red[it & 1][wave][lane / span] = v;
-        __syncthreads();
+        lds_barrier();
         if (threadIdx.x < T * R) {
             const int tm = threadIdx.x / R, r = threadIdx.x - tm * R;
             float t = lds.red[it & 1][tm * S][r];
@@ -537,17 +604,18 @@ __device__ __forceinline__ void team_run(const TeamStage<R, WIDE> &st, TeamLds<R
         }
         ++it;
     }
+    return in_b;
 }
 
 template <int R, int TAB>
 __global__ __launch_bounds__(1024) void gemv_nf4_team_kernel(const uint8_t *__restrict__ packed, int64_t n_out,
                                                              int64_t k, const uint16_t *__restrict__ x,
-                                                             float *__restrict__ y, int S) {
+                                                             float *__restrict__ y, int S, int nx) {
     __shared__ TeamLds<R, TAB> lds;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     TeamStage<R, false> st;
-    st.init(packed, n_out, k, x, y, S, (blockDim.x >> 6) / S, wave, lane);
+    st.init(packed, n_out, k, x, y, S, (blockDim.x >> 6) / S, wave, lane, nx);
     uint32_t ad[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) ad[i] = static_cast<uint32_t>(lane & 31) << 3;
@@ -566,22 +634,23 @@ __global__ __launch_bounds__(1024) void gemv_nf4_team_kernel(const uint8_t *__re
     __syncthreads();
     float xf[32];
     widen_x32(xv, xf);
-    team_run<R, TAB, false, false>(st, lds, xf, ad, qa, sa);
+    uint4 qb[R];
+    typename ScaleBits<R>::T sb;
+    team_run<R, TAB, false, false>(st, lds, xf, ad, qa, sa, qb, sb);
 }
 
 // ---------------------------------------------------------------- decode sweep
 // Teams per workgroup for a k of S slices in a 16-wave workgroup: 16 / S, one team fewer
 // when that makes the busy waves a multiple of 4 (equal waves per SIMD; k = 6144: 4
 // teams of 3 waves rather than 5).
-__host__ __device__ __forceinline__ int sweep_teams(int S) {
-    int T = 16 / S;
+__host__ __device__ __forceinline__ int sweep_teams(int S, int waves = 16) {
+    int T = waves / S;
     if ((S * T) % 4 != 0 && T > 1 && (S * (T - 1)) % 4 == 0) --T;
     return T;
 }
 
 // Words of the sweep's synchronization workspace (each counter in its own 128-byte line).
 constexpr int kSyncGroupWord = 0;      // + 32 * g, g = 0..7: arrivals of workgroup group g
-constexpr int kSyncAllWord = 8 * 32;   // groups complete
 constexpr int kSyncExitWord = 9 * 32;  // workgroups finished
 constexpr int kSyncStatusWord = 10 * 32;
 
@@ -604,97 +673,123 @@ __device__ __forceinline__ bool sweep_stage_ok(const SweepStage &d) {
            (d.k & 63) == 0;
 }
 
-// Device-wide barrier between two stages, the b-th of the call.  Workgroups arrive per
-// group (workgroup % 8, one group per XCD): the last arrival of a group counts the
-// group as complete, and every workgroup waits until all 8 groups are.  It orders
-// execution only: no stage reads another stage's output, so no cache write-back or
-// invalidation is made here (device-scope release/acquire fences cost about 6 us per
-// barrier on this GPU, against about 0.7 us for the relaxed counters); every output is
-// visible when the kernel ends, as for any launch.  The wait is bounded: past
-// `spin_limit` polls it sets WSL_STATUS_SWEEP_TIMEOUT and goes on, so the kernel always
-// ends.  Called by one thread per workgroup.
-__device__ __forceinline__ void sweep_arrive(uint32_t *sync, uint32_t b) {
-    const uint32_t g = blockIdx.x & 7;
-    const uint32_t per = gridDim.x >> 3;
-    const uint32_t old = __hip_atomic_fetch_add(sync + kSyncGroupWord + 32 * g, 1u, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-    if (old + 1 == (b + 1) * per)
-        __hip_atomic_fetch_add(sync + kSyncAllWord, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Device-wide barrier between two stages, the b-th of the call.  Each workgroup adds one
+// to its group's counter (workgroup % 8, one group per XCD, each counter in its own cache
+// line), without waiting for the add to return; a waiter reads the 8 counters with one
+// 8-lane load per poll and goes on once every group has all its arrivals for this
+// barrier.  It orders execution only: no stage reads another stage's output, so no cache
+// write-back or invalidation is made here (device-scope release/acquire fences cost about
+// 6 us per barrier on this GPU); every output is visible when the kernel ends, as for
+// any launch.  The wait is bounded: past `spin_limit` polls it sets
+// WSL_STATUS_SWEEP_TIMEOUT and goes on, so the kernel always ends; a workgroup that has
+// given up once waits at no later barrier.
+__device__ __forceinline__ void sweep_arrive(uint32_t *sync, int nx) {
+    __hip_atomic_fetch_add(sync + kSyncGroupWord + 32 * (blockIdx.x % nx), 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// `gave_up` is set once this workgroup has abandoned a barrier; it then waits at no
-// later barrier, so a call whose workgroups are not all resident ends after one bound.
-__device__ __forceinline__ void sweep_wait(uint32_t *sync, uint32_t b, uint32_t spin_limit, bool &gave_up) {
-    const uint32_t target = 8 * (b + 1);
+// Called by all 64 lanes of one wave.
+__device__ __forceinline__ void sweep_wait(uint32_t *sync, uint32_t b, uint32_t spin_limit, int nx, bool &gave_up) {
+    const uint32_t target = (b + 1) * (gridDim.x / nx);
+    const int lane = threadIdx.x & 63;
     uint32_t polls = 0;
-    while (!gave_up && __hip_atomic_load(sync + kSyncAllWord, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+    while (!gave_up) {
+        uint32_t v = target;
+        if (lane < nx) v = __hip_atomic_load(sync + kSyncGroupWord + 32 * lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (__all(v >= target)) break;
         __builtin_amdgcn_s_sleep(1);
         if (++polls > spin_limit) {
-            __hip_atomic_fetch_or(sync + kSyncStatusWord, WSL_STATUS_SWEEP_TIMEOUT, __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_AGENT);
+            if (lane == 0)
+                __hip_atomic_fetch_or(sync + kSyncStatusWord, WSL_STATUS_SWEEP_TIMEOUT, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
             gave_up = true;
         }
     }
 }
 
 // The decode sweep: `count` NF4 GEMVs (stages) in order in one launch, one 16-wave
-// workgroup per CU for the whole call.  Each stage runs exactly as the team kernel with
-// the pair table (R = 2, T = sweep_teams(S)).  Between stages every workgroup meets a
-// device-wide barrier, so no workgroup starts a stage (nor reads its x) before every
-// workgroup has finished the previous one, as in a decode step where each stage's input
-// depends on the stage before.  The weights do not depend on earlier stages, so a
-// workgroup issues the loads of its first super-group of the next stage as soon as it
-// has arrived, and those loads are in flight while it waits.  The 64 KB pair table is built once per call instead of once
-// per stage.  On exit the last workgroup to finish returns the counters to zero.
-__global__ __launch_bounds__(1024) void gemv_nf4_sweep_kernel(const wsl_gemv_stage *__restrict__ stages, int count,
-                                                              uint32_t *__restrict__ sync, uint32_t spin_limit) {
+// workgroup per CU for the whole call.  Each stage runs as the team kernel with the pair
+// table (R = 2, T = sweep_teams(S)); waves beyond a stage's teams run its barrier-only
+// form.  Between stages every workgroup meets a device-wide barrier, so no workgroup
+// starts a stage (nor reads its x) before every workgroup has finished the previous one,
+// as in a decode step where each stage's input depends on the stage before.  The weight
+// stream does not wait for the barrier: a stage's descriptor is read a stage ahead, and
+// the loads of this workgroup's first super-group of the next stage are issued before
+// the last super-group of the current one is multiplied, so they are in flight through
+// the stage's tail, the barrier and the next x load.  The 64 KB pair table is built once
+// per call.  On exit the last workgroup to finish returns the counters to zero.
+template <int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void gemv_nf4_sweep_kernel(const wsl_gemv_stage *__restrict__ stages,
+                                                                   int count, uint32_t *__restrict__ sync,
+                                                                   uint32_t spin_limit, int nx) {
     constexpr int R = 2;
+    typedef ScaleBits<R>::T SB;
     __shared__ TeamLds<R, 1> lds;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     uint32_t ad[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) ad[i] = static_cast<uint32_t>(lane & 31) << 3;
-    TeamStage<R, true> st;
-    uint4 qa[R];
-    ScaleBits<R>::T sa;
-    bool ok = false, gave_up = false;
-    auto setup = [&](int s) {
+    auto setup = [&](int s, TeamStage<R, true> &st) -> bool {
         const SweepStage d = reinterpret_cast<const SweepStage *>(stages)[s];
-        ok = sweep_stage_ok(d);
+        const bool ok = sweep_stage_ok(d);
         const int S = ok ? static_cast<int>((d.k + 2047) / 2048) : 1;
         st.init((const uint8_t *)d.w, ok ? d.n_out : 0, ok ? d.k : 64, (const uint16_t *)d.x, (float *)d.y, S,
-                sweep_teams(S), wave, lane);
+                sweep_teams(S, WAVES), wave, lane, nx);
         if (!ok) {
             st.n = 0;
             st.row_groups = 0;
             st.supers = 0;
         }
-        if (st.n > 0) st.fetch(0, qa, sa);
+        return ok;
     };
-    setup(0);
+    TeamStage<R, true> cs;   // the stage being multiplied
+    FirstLoads nf;           // this workgroup's first loads of the next stage
+    uint4 qa[R], qb[R];
+    SB sa, sb;
+    bool ok = setup(0, cs), gave_up = false;
+    if (cs.n > 0) cs.fetch(0, qa, sa);
+    uint4 xv[4];
+    cs.issue_x(xv);
+    fill_pair_table(lds.tab);   // while the first loads are in flight
+    __syncthreads();
     for (int s = 0; s < count; ++s) {
-        uint4 xv[4];
-        if (ok) st.issue_x(xv);
-        if (s == 0) {   // the table is built while the first loads are in flight
-            fill_pair_table(lds.tab);
-            __syncthreads();
+        float xf[32];
+        widen_x32(xv, xf);
+        {   // the last stage "prefetches" the dummy
+            TeamStage<R, true> ns;
+            if (s + 1 < count) setup(s + 1, ns);
+            else ns.n = 0;
+            nf = first_loads(ns, cs.x);
         }
+        bool hooked = false;
+        auto next = [&](uint4 (&q)[R], SB &sq) {
+            issue_first<R>(nf, q, sq);
+            hooked = true;
+        };
+        bool in_b = false;
         if (ok) {
-            float xf[32];
-            widen_x32(xv, xf);
-            if (st.idle) team_run<R, 1, true, true>(st, lds, xf, ad, qa, sa);   // wave-uniform branch
-            else team_run<R, 1, false, true>(st, lds, xf, ad, qa, sa);
+            if (cs.idle) in_b = team_run<R, 1, true, true>(cs, lds, xf, ad, qa, sa, qb, sb, next);   // wave-uniform
+            else in_b = team_run<R, 1, false, true>(cs, lds, xf, ad, qa, sa, qb, sb, next);
         } else if (threadIdx.x == 0 && blockIdx.x == 0) {
             __hip_atomic_fetch_or(sync + kSyncStatusWord, WSL_STATUS_DESCRIPTOR, __ATOMIC_RELAXED,
                                   __HIP_MEMORY_SCOPE_AGENT);
         }
-        if (s + 1 < count) {
-            lds_barrier();     // this stage's LDS reads are done (its y stores may still drain)
-            if (threadIdx.x == 0) sweep_arrive(sync, static_cast<uint32_t>(s));
-            setup(s + 1);      // next stage's first loads, in flight during the wait
-            if (threadIdx.x == 0) sweep_wait(sync, static_cast<uint32_t>(s), spin_limit, gave_up);
-            lds_barrier();     // every wave waits for the wait (not for its own loads)
+        if (s + 1 == count) break;
+        if (!hooked) {   // this workgroup had no super-group of stage s
+            issue_first<R>(nf, qa, sa);
+            in_b = false;
+        }
+        lds_barrier();   // this stage's LDS reads are done (its y stores may still drain)
+        if (threadIdx.x == 0) sweep_arrive(sync, nx);
+        ok = setup(s + 1, cs);   // descriptor loads in flight during the wait
+        if (wave == 0) sweep_wait(sync, static_cast<uint32_t>(s), spin_limit, nx, gave_up);
+        lds_barrier();   // every wave waits for the wait (not for its own loads)
+        cs.issue_x(xv);
+        if (in_b) {      // the next stage's first super-group landed in the second buffer
+#pragma unroll
+            for (int r = 0; r < R; ++r) qa[r] = qb[r];
+            sa = sb;
         }
     }
     lds_barrier();
@@ -702,9 +797,8 @@ __global__ __launch_bounds__(1024) void gemv_nf4_sweep_kernel(const wsl_gemv_sta
         const uint32_t done = __hip_atomic_fetch_add(sync + kSyncExitWord, 1u, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT);
         if (done + 1 == gridDim.x) {   // every workgroup is past its last wait
-            for (int g = 0; g < 8; ++g)
+            for (int g = 0; g < nx; ++g)
                 __hip_atomic_store(sync + kSyncGroupWord + 32 * g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(sync + kSyncAllWord, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(sync + kSyncExitWord, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
@@ -792,6 +886,33 @@ int launch_gemv_bf16(const void *w, int64_t n_out, int64_t k, const void *x, flo
     return WSL_OK;
 }
 
+// Compute units and XCDs of the current device, queried once per device.  Workgroups
+// are grouped by XCD (workgroup b on XCD b % xccs) for L2 locality; the grouping is at
+// most 8-way (the sweep's barrier has 8 counters) and any grouping gives the same results.
+struct DeviceShape {
+    int cus, xccs;
+};
+
+static int device_shape(DeviceShape &out) {
+    constexpr int kDevs = 64;
+    static std::atomic<int> cus_cache[kDevs], xcc_cache[kDevs];
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevs) return WSL_E_DEVICE;
+    int cus = cus_cache[dev].load(std::memory_order_relaxed);
+    int xccs = xcc_cache[dev].load(std::memory_order_relaxed);
+    if (cus == 0) {
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+            return WSL_E_DEVICE;
+        if (hipDeviceGetAttribute(&xccs, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || xccs < 1) xccs = 1;
+        if (xccs > 8) xccs = 8;
+        xcc_cache[dev].store(xccs, std::memory_order_relaxed);
+        cus_cache[dev].store(cus, std::memory_order_relaxed);
+    }
+    out.cus = cus;
+    out.xccs = xccs;
+    return WSL_OK;
+}
+
 // NF4 plan.  k <= 32768: the team kernel with S = ceil(k / 2048) waves per team.
 // Large matrices (>= 32 Mi weights; >= 96 Mi when k <= 4096, where the 64 KB table
 // is built for few steps) take the pair table, 2 rows per row group and up to 16 / S
@@ -811,7 +932,7 @@ struct Nf4GemvPlan {
     int64_t grid;
 };
 
-static Nf4GemvPlan plan_gemv_nf4(int64_t n_out, int64_t k) {
+static Nf4GemvPlan plan_gemv_nf4(int64_t n_out, int64_t k, const DeviceShape &ds) {
     Nf4GemvPlan p{};
     const int64_t slices = (k + 2047) / 2048;
     if (slices > 16) {
@@ -843,13 +964,17 @@ static Nf4GemvPlan plan_gemv_nf4(int64_t n_out, int64_t k) {
     const int64_t rg = (n_out + p.rows - 1) / p.rows;
     const int64_t full = (n_out % p.rows == 0) ? rg : ((n_out >> 4) << 4) / p.rows;
     const int64_t supers = full / p.T;
-    const int64_t need = ((supers > 0 ? supers : 1) + 7) / 8 * 8;
-    p.grid = 256 * per_cu < need ? 256 * per_cu : need;
+    const int64_t nx = ds.xccs;
+    const int64_t need = ((supers > 0 ? supers : 1) + nx - 1) / nx * nx;
+    const int64_t most = static_cast<int64_t>(ds.cus) * per_cu / nx * nx;   // one pass over the CUs
+    p.grid = most < need ? (most > 0 ? most : nx) : need;
     return p;
 }
 
 int launch_gemv_nf4(const void *w, int64_t n_out, int64_t k, const void *x, float *y, hipStream_t s) {
-    const Nf4GemvPlan p = plan_gemv_nf4(n_out, k);
+    DeviceShape ds;
+    if (device_shape(ds) != WSL_OK) return WSL_E_DEVICE;
+    const Nf4GemvPlan p = plan_gemv_nf4(n_out, k, ds);
     const auto *wp = static_cast<const uint8_t *>(w);
     const auto *xp = static_cast<const uint16_t *>(x);
     const dim3 g(static_cast<unsigned>(p.grid)), b(64 * p.S * p.T);
@@ -857,10 +982,11 @@ int launch_gemv_nf4(const void *w, int64_t n_out, int64_t k, const void *x, floa
         if (p.rows == 4) hipLaunchKernelGGL((gemv_nf4_wide_kernel<4>), g, b, 0, s, wp, n_out, k, xp, y);
         else hipLaunchKernelGGL((gemv_nf4_wide_kernel<2>), g, b, 0, s, wp, n_out, k, xp, y);
     } else if (p.pair) {
-        hipLaunchKernelGGL((gemv_nf4_team_kernel<2, 1>), g, b, 0, s, wp, n_out, k, xp, y, p.S);
+        hipLaunchKernelGGL((gemv_nf4_team_kernel<2, 1>), g, b, 0, s, wp, n_out, k, xp, y, p.S, ds.xccs);
     } else {
-        if (p.rows == 4) hipLaunchKernelGGL((gemv_nf4_team_kernel<4, 0>), g, b, 0, s, wp, n_out, k, xp, y, p.S);
-        else hipLaunchKernelGGL((gemv_nf4_team_kernel<2, 0>), g, b, 0, s, wp, n_out, k, xp, y, p.S);
+        if (p.rows == 4)
+            hipLaunchKernelGGL((gemv_nf4_team_kernel<4, 0>), g, b, 0, s, wp, n_out, k, xp, y, p.S, ds.xccs);
+        else hipLaunchKernelGGL((gemv_nf4_team_kernel<2, 0>), g, b, 0, s, wp, n_out, k, xp, y, p.S, ds.xccs);
     }
     return WSL_OK;
 }
@@ -872,18 +998,28 @@ constexpr uint32_t kSweepSpinLimit = 1u << 20;   // polls of a stage barrier (ab
 
 size_t sweep_ws_bytes() { return kSweepWsBytes; }
 
-int launch_gemv_nf4_sweep(const wsl_gemv_stage *d_stages, int64_t count, void *ws, hipStream_t s) {
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8)
-        return WSL_E_DEVICE;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(gemv_nf4_sweep_kernel),
-                                                     1024, 0) != hipSuccess ||
-        per_cu < 1)
+// 12-wave workgroups when every stage's k fits 12 slices of 2048 (k <= 24576): a limit
+// of 170 registers per lane instead of 128, and the k = 6144 stages of a decoder (3
+// slices) use all 12 waves in 4 teams; otherwise 16 waves.
+int launch_gemv_nf4_sweep(const wsl_gemv_stage *d_stages, int64_t count, int64_t max_k, void *ws, hipStream_t s) {
+    DeviceShape ds;
+    int per_cu = 0;
+    if (device_shape(ds) != WSL_OK) return WSL_E_DEVICE;
+    const bool narrow = max_k <= 12 * 2048;
+    const void *kern = narrow ? reinterpret_cast<const void *>(gemv_nf4_sweep_kernel<12>)
+                              : reinterpret_cast<const void *>(gemv_nf4_sweep_kernel<16>);
+    const int threads = narrow ? 768 : 1024;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, 0) != hipSuccess || per_cu < 1)
         return WSL_E_LAUNCH;
-    const unsigned grid = static_cast<unsigned>(cus / 8 * 8);
-    hipLaunchKernelGGL(gemv_nf4_sweep_kernel, dim3(grid), dim3(1024), 0, s, d_stages, static_cast<int>(count),
-                       static_cast<uint32_t *>(ws), kSweepSpinLimit);
+    const int nx = ds.xccs;
+    const unsigned grid = static_cast<unsigned>(ds.cus / nx * nx);   // one workgroup per CU, all resident
+    if (grid == 0) return WSL_E_DEVICE;
+    if (narrow)
+        hipLaunchKernelGGL((gemv_nf4_sweep_kernel<12>), dim3(grid), dim3(threads), 0, s, d_stages,
+                           static_cast<int>(count), static_cast<uint32_t *>(ws), kSweepSpinLimit, nx);
+    else
+        hipLaunchKernelGGL((gemv_nf4_sweep_kernel<16>), dim3(grid), dim3(threads), 0, s, d_stages,
+                           static_cast<int>(count), static_cast<uint32_t *>(ws), kSweepSpinLimit, nx);
     return WSL_OK;
 }
 
