@@ -81,6 +81,30 @@ int main() {
         EXPECT(wsl::check_ring(WSL_W_NF4, 0, nullptr, nullptr, nullptr, nullptr, -1, 0, nullptr, 0, 0, nullptr, 0,
                                nullptr, 0, nullptr) == WSL_OK);
     }
+    {
+        // decode sweep: host descriptors, device descriptor array and workspace
+        wsl_gemv_stage st[3];
+        for (auto &e : st) e = wsl_gemv_stage{p, p, reinterpret_cast<float *>(const_cast<void *>(p)), 4, 64};
+        const size_t need = 2048;
+        EXPECT(wsl::check_sweep(WSL_W_NF4, 3, st, p, p, need, need) == WSL_OK);
+        EXPECT(wsl::check_sweep(WSL_W_NF4, 0, nullptr, nullptr, nullptr, 0, need) == WSL_OK);
+        EXPECT(wsl::check_sweep(WSL_W_BF16, 3, st, p, p, need, need) == WSL_E_FORMAT);
+        EXPECT(wsl::check_sweep(WSL_W_NF4, -1, st, p, p, need, need) == WSL_E_SHAPE);
+        EXPECT(wsl::check_sweep(WSL_W_NF4, (int64_t(1) << 24) + 1, st, p, p, need, need) == WSL_E_SHAPE);
+        EXPECT(wsl::check_sweep(WSL_W_NF4, 3, nullptr, p, p, need, need) == WSL_E_NULL);
+        EXPECT(wsl::check_sweep(WSL_W_NF4, 3, st, odd, p, need, need) == WSL_E_ALIGN);
+        EXPECT(wsl::check_sweep(WSL_W_NF4, 3, st, p, p, need - 1, need) == WSL_E_RANGE);
+        st[2].k = 32768 + 64;
+        EXPECT(wsl::check_sweep(WSL_W_NF4, 3, st, p, p, need, need) == WSL_E_SHAPE);
+        st[2].k = 96;
+        EXPECT(wsl::check_sweep(WSL_W_NF4, 3, st, p, p, need, need) == WSL_E_SHAPE);
+        st[2].k = 64;
+        st[1].x = odd;
+        EXPECT(wsl::check_sweep(WSL_W_NF4, 3, st, p, p, need, need) == WSL_E_ALIGN);
+        st[1].x = p;
+        st[0].w = nullptr;
+        EXPECT(wsl::check_sweep(WSL_W_NF4, 3, st, p, p, need, need) == WSL_E_NULL);
+    }
     std::printf("%s (%d failures)\n", fails ? "FAILED" : "ok", fails);
     return fails ? 1 : 0;
 }
