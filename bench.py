@@ -992,6 +992,65 @@ def traffic_from_file():
         return None
 
 
+# ---------------------------------------------------------------- issue/wait counters of the GEMV
+def gemv_counter_summarize(run_dirs, command):
+    """Markdown summary of SQ counter runs of --traffic-probe (several passes, one directory
+    each): for the dominant GEMV's dispatches, the mean of every counter per dispatch and
+    the ratios that say where a wave's time goes (issuing VALU / LDS / VMEM instructions,
+    waiting on anything / on LDS), instructions per weight, and the clock.  SQ cycle
+    counters are summed over the GPU; ratios between them need no unit."""
+    import csv
+    per = {}
+    xccs = 8
+    for d in run_dirs:
+        for path in glob.glob(os.path.join(d, "**", "*agent_info.csv"), recursive=True):
+            with open(path) as f:
+                for a in csv.DictReader(f):
+                    if a.get("Name", "").startswith("gfx"):
+                        xccs = int(a["Num_Xcc"])
+        disp = {}
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    if "gemv_nf4_team_kernel" not in r.get("Kernel_Name", ""):
+                        continue
+                    e = disp.setdefault(r["Dispatch_Id"], {"t": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+                    e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        for e in disp.values():
+            for c, v in e.items():
+                per.setdefault(c, []).append(v)
+    m = {c: float(np.mean(v)) for c, v in per.items()}
+    weights = 32768 * 6144
+    g = lambda c: m.get(c)
+    lines = ["# Issue and wait counters of the NF4 decode GEMV (gate_up 32768x6144, pair table)", "",
+             "Commands (run from the repository root on one MI355X, ROCm 7.2, rocprofv3), one pass per counter set:",
+             "", "```", command, "```", "",
+             "Means per dispatch of `gemv_nf4_team_kernel<2,1>` over the probe's 4 launches (counters summed over "
+             f"the GPU's {xccs} XCDs).  Summary written by `python bench.py --gemv-counter-summarize <dirs...> "
+             "<command>`.", "", "| counter | per dispatch |", "|---|---:|"]
+    for c in sorted(k for k in m if k != "t"):
+        lines.append(f"| {c} | {m[c]:.4g} |")
+    lines += ["", "| derived | value |", "|---|---:|"]
+    if g("GRBM_GUI_ACTIVE") and g("t"):
+        lines.append(f"| GPU clock during the dispatch (GRBM_GUI_ACTIVE / {xccs} / duration) | "
+                     f"{g('GRBM_GUI_ACTIVE') / xccs / g('t'):.3f} GHz |")
+    wc = g("SQ_WAVE_CYCLES")
+    for c, what in (("SQ_ACTIVE_INST_VALU", "issuing VALU"), ("SQ_ACTIVE_INST_LDS", "issuing LDS"),
+                    ("SQ_ACTIVE_INST_VMEM", "issuing VMEM"), ("SQ_ACTIVE_INST_ANY", "issuing anything"),
+                    ("SQ_WAIT_ANY", "waiting on a counter (any)"), ("SQ_WAIT_INST_ANY", "waiting to issue (any)"),
+                    ("SQ_WAIT_INST_LDS", "waiting to issue LDS")):
+        if wc and g(c) is not None:
+            lines.append(f"| share of wave time {what} ({c} / SQ_WAVE_CYCLES) | {g(c) / wc:.3f} |")
+    for c in ("SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_INSTS_VMEM_RD", "SQ_INSTS_SALU"):
+        if g(c) is not None:
+            lines.append(f"| {c} x 64 lanes per weight | {g(c) * 64 / weights:.3f} |")
+    if g("SQ_LDS_BANK_CONFLICT") is not None and g("SQ_LDS_IDX_ACTIVE"):
+        lines.append(f"| LDS bank conflicts / LDS active | {g('SQ_LDS_BANK_CONFLICT') / g('SQ_LDS_IDX_ACTIVE'):.4f} |")
+    if g("SQ_BUSY_CYCLES") and g("GRBM_GUI_ACTIVE"):
+        lines.append(f"| SQ busy / GPU active | {g('SQ_BUSY_CYCLES') / g('GRBM_GUI_ACTIVE'):.3f} |")
+    print("\n".join(lines))
+
+
 # ---------------------------------------------------------------- MFMA work from rocprofv3 counters
 MFMA_CASES = [("bf16", 8192, 17408, 5120), ("bf16", 8192, 5120, 17408), ("nf4", 8192, 17408, 5120),
               ("nf4", 8192, 5120, 17408), ("nf4", 32, 27648, 5120), ("nf4", 32, 5120, 27648)]
@@ -1248,11 +1307,16 @@ def main():
     ap.add_argument("--traffic-commands", default="", help="the counter commands, recorded with the summary")
     ap.add_argument("--trace-summarize", nargs="+", metavar="ARG",
                     help="RUN_DIR TITLE COMMAND [BLOCK_LOG]: markdown summary of a rocprofv3 kernel-trace CSV run")
+    ap.add_argument("--gemv-counter-summarize", nargs="+", metavar="ARG",
+                    help="RUN_DIR... COMMAND: issue/wait counter summary of the dominant GEMV")
     ap.add_argument("--block-log", default="", help="write the timed blocks (label, launches, dispatches per "
                                                      "launch) to this file, for --trace-summarize")
     args = ap.parse_args()
     if args.trace_summarize:
         trace_summarize(*args.trace_summarize)
+        return
+    if args.gemv_counter_summarize:
+        gemv_counter_summarize(args.gemv_counter_summarize[:-1], args.gemv_counter_summarize[-1])
         return
     if args.traffic_summarize:
         traffic_summarize(*args.traffic_summarize, args.traffic_commands)
