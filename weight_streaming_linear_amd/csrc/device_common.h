@@ -80,8 +80,6 @@ __device__ __forceinline__ void pair_addr(uint32_t &a, uint32_t w) {
         asm("v_mov_b32_sdwa %0, %1 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_3" : "+v"(a) : "v"(w));
 }
 
-// Fill the pair table (kPairTableBytes of LDS at `tab`) cooperatively; the caller
-// synchronizes the workgroup before the first lookup.
 // The 16 levels into lut[0..15] (LDS).  Lane c < 16 selects its level from the
 // literals with compare-selects, so no memory load sits in a kernel prologue.
 __device__ __forceinline__ void write_levels(float *lut) {
@@ -93,22 +91,28 @@ __device__ __forceinline__ void write_levels(float *lut) {
     }
 }
 
-// Entry i = b * 32 + copy, so a wave's 64 consecutive entries hold two byte values
-// b0 (lanes 0..31) and b0 + 1 (lanes 32..63), both wave-uniform: the four levels come
-// from scalar loads of the constant table and each lane selects its half's pair.
-// (A per-lane index would make every level a vector memory load, each followed by a
-// wait, in the prologue of every workgroup.)  blockDim.x must be a multiple of 64.
+// Fill the pair table (kPairTableBytes of LDS at `tab`) cooperatively; the caller
+// synchronizes the workgroup before the first lookup.
+// Entries by low nibble: a wave takes the byte values with low nibble L or L + 1 (L even;
+// lanes 0..31 write copy l of L, lanes 32..63 copy l - 32 of L + 1) for all 16 high
+// nibbles.  Each lane selects level(L + its half) once from the literals; level(high) is
+// a literal of the unrolled loop and the high nibble an immediate offset of the LDS
+// write, so the fill issues no memory load and needs no wait of its own: 16 writes per
+// wave for the 8 values of L (waves beyond 8 have nothing to do; fewer waves take several
+// L each).  blockDim.x must be a multiple of 64.
 __device__ __forceinline__ void fill_pair_table(char *tab) {
-    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const int wave = static_cast<int>(threadIdx.x >> 6);
     const int nw = static_cast<int>(blockDim.x >> 6);
-    const bool upper = (threadIdx.x & 32) != 0;
-    float2 *t2 = reinterpret_cast<float2 *>(tab) + (threadIdx.x & 63);
-    for (int b0 = 2 * wave; b0 < 256; b0 += 2 * nw) {
-        float lo0 = level(b0 & 15), lo1 = level((b0 + 1) & 15), hi = level(b0 >> 4);   // b0 is even
-        // pinned as scalar values, so the select below is not turned back into a
-        // per-lane table address
-        asm volatile("" : "+s"(lo0), "+s"(lo1), "+s"(hi));
-        t2[b0 * 32] = make_float2(upper ? lo1 : lo0, hi);
+    const int lane = static_cast<int>(threadIdx.x & 63);
+    for (int l2 = wave; l2 < 8; l2 += nw) {
+        const int lo = 2 * l2 + (lane >> 5);
+        uint32_t v = kLevelBits[0];
+#pragma unroll
+        for (int c = 1; c < 16; ++c) v = (lo == c) ? kLevelBits[c] : v;
+        const float lvl = __builtin_bit_cast(float, v);
+        float2 *t2 = reinterpret_cast<float2 *>(tab + lo * 256 + (lane & 31) * 8);
+#pragma unroll
+        for (int hi = 0; hi < 16; ++hi) t2[hi * 512] = make_float2(lvl, level(hi));
     }
 }
 

@@ -320,10 +320,11 @@ __device__ __forceinline__ void xcd_chunk(int64_t total, int xcd, int nx, int64_
 // S = ceil(k / 2048): the S waves of a team split the row into slices and keep their
 // 32 x values in registers for the whole matrix; team t works on row group
 // sg * T + t of super-group sg (R rows per row group).
-// Super-groups of full row groups (every row present, scales of the R rows
-// contiguous) are split into 8 contiguous chunks, one per XCD (workgroup b runs on
-// XCD b % 8), so the rows that share a 16-row scale block are read through one L2
-// and each XCD streams a contiguous range.  Workgroups are persistent over their
+// Super-groups of rows in whole 16-row scale blocks are split into 8 contiguous
+// chunks, one per XCD (workgroup b runs on XCD b % 8), so the rows that share a scale
+// block are read through one L2 and each XCD streams a contiguous range.  The wave
+// index is made wave-uniform, so a super-group's row index and its code and scale
+// addresses are scalar, plus a per-lane offset fixed for the whole matrix.  Workgroups are persistent over their
 // chunk, and the codes and scales of the next super-group are loaded before the
 // current one is multiplied; the scales stay raw fp16 until they are used.  The
 // last super-group of a round is peeled, so no load is issued past it.
@@ -331,12 +332,41 @@ __device__ __forceinline__ void xcd_chunk(int64_t total, int xcd, int nx, int64_
 // in LDS in a fixed order (one LDS-only barrier per super-group, double-buffered) --
 // the result is deterministic.  A workgroup with four or more super-groups parks the
 // finished sums of a round in LDS and writes them to y after the round, so no global
-// store sits between the loads of its loop.  Rows of a last partial 16-row block whose size is not a
-// multiple of R, and super-groups left incomplete, are done at the end with per-row
-// loads.  TAB selects the 16-entry table (0) or the replicated pair table (1).
+// store sits between the loads of its loop.  The rows of a last partial 16-row block and
+// of super-groups left incomplete are done at the end with per-row loads.  TAB selects the 16-entry table (0) or the replicated pair table (1).
 // Waves of the workgroup beyond the T teams (the decode sweep runs every matrix in
 // 16-wave workgroups) take part in the barriers only.
 constexpr int kRowSumCap = 2048;   // finished row sums parked per round
+
+// The workgroup-independent geometry of one matrix for the team GEMV, in 32-bit
+// arithmetic (n_out <= 2^30, so every count fits): computed on the host for a single
+// launch and passed by value, and on the device per decode-sweep stage.  (The 64-bit
+// divisions this replaces took about a microsecond per wave in every kernel prologue,
+// ahead of the first weight load.)
+struct TeamGeom {
+    int32_t S, T;          // waves per team, teams per workgroup
+    int32_t row_groups;    // ceil(n_out / R)
+    int32_t supers;        // super-groups: full row groups / T
+    int32_t cap;           // super-groups whose row sums a round parks in LDS
+    int32_t nloc;          // workgroups per XCD share (grid / nx)
+    int32_t per, rem;      // super-groups per XCD share: per, one more for the first rem
+};
+
+template <int R>
+__host__ __device__ __forceinline__ TeamGeom team_geom(int64_t n_out, int S, int T, uint32_t grid, uint32_t nx) {
+    TeamGeom g;
+    const uint32_t n = static_cast<uint32_t>(n_out);
+    g.S = S;
+    g.T = T;
+    g.row_groups = static_cast<int32_t>((n + R - 1) / R);
+    const uint32_t full = ((n >> 4) << 4) / R;   // rows of whole 16-row scale blocks
+    g.supers = static_cast<int32_t>(full / static_cast<uint32_t>(T));
+    g.cap = kRowSumCap / (T * R);
+    g.nloc = static_cast<int32_t>(grid / nx);
+    g.per = static_cast<int32_t>(static_cast<uint32_t>(g.supers) / nx);
+    g.rem = g.supers - g.per * static_cast<int32_t>(nx);
+    return g;
+}
 
 // LDS of the team GEMV: the level table, the cross-wave row sums (double-buffered)
 // and the parked row sums of a round.
@@ -350,7 +380,7 @@ struct TeamLds {
 // One matrix as seen by one workgroup: geometry, this wave's slice and this
 // workgroup's super-groups first + i0 + j * nloc, j = 0 .. n - 1.  WIDE: the workgroup
 // may hold more waves than the T teams need (idle waves: they run the barrier-only form
-// of team_run); the wave index is then made wave-uniform.
+// of team_run).
 template <int R, bool WIDE>
 struct TeamStage {
     typedef typename ScaleBits<R>::T SB;
@@ -362,44 +392,47 @@ struct TeamStage {
     int S, T, team, fteam;
     bool idle, active, park;
     int64_t kkl;
-    uint32_t coff, gl;
+    uint32_t coff, gl, soff;   // this lane's byte offsets: codes in a row, scale in a full block
 
     __device__ __forceinline__ void init(const uint8_t *p, int64_t n_out_, int64_t k, const uint16_t *x_, float *y_,
-                                         int S_, int T_, int wave, int lane, int nx) {
+                                         const TeamGeom &g, int wave, int lane, int nx) {
         packed = p;
         x = x_;
         y = y_;
         n_out = n_out_;
-        S = S_;
-        T = T_;
+        S = g.S;
+        T = g.T;
         groups = k >> 6;
         rowbytes = k >> 1;
-        row_groups = (n_out + R - 1) / R;
-        const int64_t full_rg = (n_out % R == 0) ? row_groups : ((n_out >> 4) << 4) / R;
-        supers = full_rg / T;
+        row_groups = g.row_groups;
+        supers = g.supers;
+        cap = g.cap;
+        nloc = g.nloc;
         scales = reinterpret_cast<const uint16_t *>(packed + n_out * rowbytes);
-        // In 16-wave workgroups the wave index is made wave-uniform, so that rows, row
-        // addresses and the idle test are scalar: the per-lane 64-bit address arithmetic
-        // otherwise takes the registers the prefetch needs (the sweep kernel runs at the
-        // 128-register limit of 16 waves per CU).
-        const int wv = WIDE ? __builtin_amdgcn_readfirstlane(wave) : wave;
-        team = wv / S;
+        // The wave index is made wave-uniform, so that rows, row addresses and the idle
+        // test are scalar: per-lane 64-bit address arithmetic costs about 30 vector
+        // instructions per super-group and the registers the prefetch needs.
+        const uint32_t wv = __builtin_amdgcn_readfirstlane(wave);
+        team = static_cast<int>(wv / static_cast<uint32_t>(S));
         idle = WIDE && team >= T;
         fteam = idle ? T - 1 : team;
-        const int slice = wv - team * S;
+        const int slice = static_cast<int>(wv) - team * S;
         // Lanes past k read valid codes of the row's last group and multiply them by x = 0.
-        const int64_t kk0 = static_cast<int64_t>(slice) * 2048 + lane * 32;
+        const int32_t kk0 = slice * 2048 + lane * 32;
         active = kk0 < k;
         kkl = active ? kk0 : k - 32;
         coff = static_cast<uint32_t>(kkl >> 1);
         gl = static_cast<uint32_t>(kkl >> 6);
-        const int xcd = blockIdx.x % nx;
-        nloc = gridDim.x / nx;   // the grid is a multiple of nx
-        int64_t count;
-        xcd_chunk(supers, xcd, nx, first, count);
-        i0 = blockIdx.x / nx;
-        n = i0 < count ? (count - i0 + nloc - 1) / nloc : 0;
-        cap = kRowSumCap / (T * R);
+        soff = gl * 32u;
+        const uint32_t b = blockIdx.x, ux = static_cast<uint32_t>(nx);
+        const uint32_t i0u = b / ux, xcd = b - i0u * ux;
+        const int32_t count = g.per + (static_cast<int32_t>(xcd) < g.rem ? 1 : 0);
+        first = static_cast<int64_t>(xcd) * g.per + (static_cast<int32_t>(xcd) < g.rem ? xcd : g.rem);
+        i0 = i0u;
+        n = static_cast<int32_t>(i0u) < count
+                ? static_cast<int64_t>(static_cast<uint32_t>(count - static_cast<int32_t>(i0u) + g.nloc - 1) /
+                                       static_cast<uint32_t>(g.nloc))
+                : 0;
         // Parking pays off once a workgroup owns several super-groups; with one or two
         // the two extra barriers of the flush cost more than the stores they move.
         park = n >= 4;
@@ -409,16 +442,16 @@ struct TeamStage {
     // loads (in bounds, and never used): with no branch around the loads, every path has
     // the same loads in flight, and the compiler's waits before the first multiply stay
     // exact (a branch that issues no loads makes it wait for every load in flight).
+    // The row index is wave-uniform (scalar) and a super-group lies in whole 16-row scale
+    // blocks, so both addresses are a scalar base plus this lane's constant offset.
     __device__ __forceinline__ void fetch(int64_t j, uint4 (&q)[R], SB &sb) const {
-        const int64_t row0 = ((first + i0 + j * nloc) * T + fteam) * R;
-        const uint8_t *rowp = packed + row0 * rowbytes;
+        const uint32_t sg = static_cast<uint32_t>(first + i0) + static_cast<uint32_t>(j) * static_cast<uint32_t>(nloc);
+        const uint32_t row0 = (sg * static_cast<uint32_t>(T) + static_cast<uint32_t>(fteam)) * R;
+        const uint8_t *rowp = packed + static_cast<int64_t>(row0) * rowbytes;
 #pragma unroll
         for (int r = 0; r < R; ++r) q[r] = load_stream16(rowp + r * rowbytes + coff);
-        const int64_t blk = row0 >> 4;
-        const int64_t rem = n_out - (blk << 4);
-        const uint32_t rb = static_cast<uint32_t>(rem < 16 ? rem : 16);
-        const uint16_t *sp = scales + blk * 16 * groups + (row0 & 15);
-        sb = *reinterpret_cast<const SB *>(reinterpret_cast<const char *>(sp) + gl * rb * 2u);
+        const char *sp = reinterpret_cast<const char *>(scales + static_cast<int64_t>(row0 >> 4) * 16 * groups + (row0 & 15));
+        sb = *reinterpret_cast<const SB *>(sp + soff);
         __builtin_amdgcn_sched_barrier(0);   // the whole prefetch is issued before the math below
     }
 
@@ -450,10 +483,7 @@ __device__ __forceinline__ FirstLoads first_loads(const TeamStage<R, WIDE> &st, 
     }
     const int64_t row0 = ((st.first + st.i0) * st.T + st.fteam) * R;
     f.rowp = st.packed + row0 * st.rowbytes + st.coff;
-    const int64_t blk = row0 >> 4;
-    const int64_t rem = st.n_out - (blk << 4);
-    const uint32_t rb = static_cast<uint32_t>(rem < 16 ? rem : 16);
-    f.sp = reinterpret_cast<const char *>(st.scales + blk * 16 * st.groups + (row0 & 15)) + st.gl * rb * 2u;
+    f.sp = reinterpret_cast<const char *>(st.scales + (row0 >> 4) * 16 * st.groups + (row0 & 15)) + st.soff;
     f.rowbytes = st.rowbytes;
     return f;
 }
@@ -610,12 +640,12 @@ __device__ __forceinline__ bool team_run(const TeamStage<R, WIDE> &st, TeamLds<R
 template <int R, int TAB>
 __global__ __launch_bounds__(1024) void gemv_nf4_team_kernel(const uint8_t *__restrict__ packed, int64_t n_out,
                                                              int64_t k, const uint16_t *__restrict__ x,
-                                                             float *__restrict__ y, int S, int nx) {
+                                                             float *__restrict__ y, TeamGeom g, int nx) {
     __shared__ TeamLds<R, TAB> lds;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     TeamStage<R, false> st;
-    st.init(packed, n_out, k, x, y, S, (blockDim.x >> 6) / S, wave, lane, nx);
+    st.init(packed, n_out, k, x, y, g, wave, lane, nx);
     uint32_t ad[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) ad[i] = static_cast<uint32_t>(lane & 31) << 3;
@@ -734,8 +764,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_nf4_sweep_kernel(const wsl_ge
         const SweepStage d = reinterpret_cast<const SweepStage *>(stages)[s];
         const bool ok = sweep_stage_ok(d);
         const int S = ok ? static_cast<int>((d.k + 2047) / 2048) : 1;
-        st.init((const uint8_t *)d.w, ok ? d.n_out : 0, ok ? d.k : 64, (const uint16_t *)d.x, (float *)d.y, S,
-                sweep_teams(S, WAVES), wave, lane, nx);
+        const int64_t n_out = ok ? d.n_out : 0;
+        st.init((const uint8_t *)d.w, n_out, ok ? d.k : 64, (const uint16_t *)d.x, (float *)d.y,
+                team_geom<R>(n_out, S, sweep_teams(S, WAVES), gridDim.x, static_cast<uint32_t>(nx)), wave, lane, nx);
         if (!ok) {
             st.n = 0;
             st.row_groups = 0;
@@ -981,12 +1012,18 @@ int launch_gemv_nf4(const void *w, int64_t n_out, int64_t k, const void *x, floa
     if (p.wide) {
         if (p.rows == 4) hipLaunchKernelGGL((gemv_nf4_wide_kernel<4>), g, b, 0, s, wp, n_out, k, xp, y);
         else hipLaunchKernelGGL((gemv_nf4_wide_kernel<2>), g, b, 0, s, wp, n_out, k, xp, y);
-    } else if (p.pair) {
-        hipLaunchKernelGGL((gemv_nf4_team_kernel<2, 1>), g, b, 0, s, wp, n_out, k, xp, y, p.S, ds.xccs);
     } else {
-        if (p.rows == 4)
-            hipLaunchKernelGGL((gemv_nf4_team_kernel<4, 0>), g, b, 0, s, wp, n_out, k, xp, y, p.S, ds.xccs);
-        else hipLaunchKernelGGL((gemv_nf4_team_kernel<2, 0>), g, b, 0, s, wp, n_out, k, xp, y, p.S, ds.xccs);
+        const uint32_t grid = static_cast<uint32_t>(p.grid), nx = static_cast<uint32_t>(ds.xccs);
+        if (p.pair) {
+            hipLaunchKernelGGL((gemv_nf4_team_kernel<2, 1>), g, b, 0, s, wp, n_out, k, xp, y,
+                               team_geom<2>(n_out, p.S, p.T, grid, nx), ds.xccs);
+        } else if (p.rows == 4) {
+            hipLaunchKernelGGL((gemv_nf4_team_kernel<4, 0>), g, b, 0, s, wp, n_out, k, xp, y,
+                               team_geom<4>(n_out, p.S, p.T, grid, nx), ds.xccs);
+        } else {
+            hipLaunchKernelGGL((gemv_nf4_team_kernel<2, 0>), g, b, 0, s, wp, n_out, k, xp, y,
+                               team_geom<2>(n_out, p.S, p.T, grid, nx), ds.xccs);
+        }
     }
     return WSL_OK;
 }
