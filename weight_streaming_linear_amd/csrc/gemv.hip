@@ -774,6 +774,14 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_nf4_sweep_kernel(const wsl_ge
         }
         return ok;
     };
+    // The first loads of stage t, whose geometry is needed a stage early; past the last
+    // stage they read the dummy (a stage's x).
+    auto first_of = [&](int t, const void *dummy) -> FirstLoads {
+        TeamStage<R, true> ns;
+        if (t < count) setup(t, ns);
+        else ns.n = 0;
+        return first_loads(ns, dummy);
+    };
     TeamStage<R, true> cs;   // the stage being multiplied
     FirstLoads nf;           // this workgroup's first loads of the next stage
     uint4 qa[R], qb[R];
@@ -782,17 +790,12 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_nf4_sweep_kernel(const wsl_ge
     if (cs.n > 0) cs.fetch(0, qa, sa);
     uint4 xv[4];
     cs.issue_x(xv);
+    nf = first_of(1, cs.x);
     fill_pair_table(lds.tab);   // while the first loads are in flight
     __syncthreads();
     for (int s = 0; s < count; ++s) {
         float xf[32];
         widen_x32(xv, xf);
-        {   // the last stage "prefetches" the dummy
-            TeamStage<R, true> ns;
-            if (s + 1 < count) setup(s + 1, ns);
-            else ns.n = 0;
-            nf = first_loads(ns, cs.x);
-        }
         bool hooked = false;
         auto next = [&](uint4 (&q)[R], SB &sq) {
             issue_first<R>(nf, q, sq);
@@ -813,7 +816,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_nf4_sweep_kernel(const wsl_ge
         }
         lds_barrier();   // this stage's LDS reads are done (its y stores may still drain)
         if (threadIdx.x == 0) sweep_arrive(sync, nx);
-        ok = setup(s + 1, cs);   // descriptor loads in flight during the wait
+        // Both geometries (the next stage's, and the first loads of the one after) are
+        // computed here, where the wait hides them, not at the start of the stage.
+        ok = setup(s + 1, cs);
+        nf = first_of(s + 2, cs.x);
         if (wave == 0) sweep_wait(sync, static_cast<uint32_t>(s), spin_limit, nx, gave_up);
         lds_barrier();   // every wave waits for the wait (not for its own loads)
         cs.issue_x(xv);
