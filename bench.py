@@ -52,9 +52,11 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, 8 TB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, 2.5 PFLOP/s
 METRIC = "GEMV effective weight GB/s (% of HBM peak); GEMM TFLOP/s (% of MFMA peak)"
 GEMV_SRC = os.path.join(ROOT, "weight_streaming_linear_amd", "csrc", "gemv.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_nf4_gate_up_32768x6144.json")
-DOMINANT = "nf4_gemv_gate_up"
-DOMINANT_KERNEL = "gemv_nf4_team_kernel<2,1> (gate_up 32768x6144)"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_nf4_sweep_48x6144.json")
+DOMINANT = "nf4_gemv_gate_up"   # the largest per-stage launch of the 192-launch form
+DOMINANT_KERNEL = "gemv_nf4_sweep_kernel<12> (48-layer hidden-6144 decode sweep, one launch per token)"
+SWEEP_KERNEL_MATCH = "gemv_nf4_sweep_kernel"
+TEAM_KERNEL_MATCH = "gemv_nf4_team_kernel"
 CALIB_BYTES = 1 << 30            # plain copy used to calibrate the byte counters
 
 
@@ -101,16 +103,21 @@ def time_block(launches, reps, warmup, label=None, dispatches=1):
     the one the launches use.  A spin kernel queued first keeps the GPU busy while the host
     enqueues the block, so the span holds the kernels and nothing of the host.  (An event
     pair around every single launch would add about 2 us of command-processor overhead to
-    each measured launch on this platform.)  Returns microseconds per launch."""
+    each measured launch on this platform.)  The spin lasts twice the host's enqueue time for
+    the block, measured on a few launches enqueued without waiting: a much longer spin lets
+    the clock settle low, and the launches that follow it run slower until it recovers.
+    Returns microseconds per launch."""
     import torch
     for i in range(warmup):
         launches[i % len(launches)].fn()
     torch.cuda.synchronize()
+    probe = min(8, max(1, reps))
     t0 = time.perf_counter()
-    launches[0].fn()
+    for i in range(probe):
+        launches[i % len(launches)].fn()
+    host_ms = 1e3 * (time.perf_counter() - t0) / probe
     torch.cuda.synchronize()
-    host_ms = 1e3 * (time.perf_counter() - t0)
-    torch.cuda._sleep(int((2.0 * host_ms * reps + 2.0) * spin_cycles_per_ms()))
+    torch.cuda._sleep(int((2.0 * host_ms * reps + 0.5) * spin_cycles_per_ms()))
     BLOCK_LOG.append((label or launches[0].name or "block", reps, dispatches))
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
@@ -340,10 +347,11 @@ def gate_sweep(name, xs, packs, ys, layers):
 
 
 def measure_headline(k_steps, warmup):
-    """The decode sweep, 192 GEMV launches per token captured as one graph: W untimed then
-    exactly K timed token replays between HIP events.  Also the per-stage kernel blocks (the
-    dominant gate_up block among them), the sweep as one linear_gemv_sweep launch per token,
-    and the decode-step graph with the packed-embedding gather of a device-resident token."""
+    """The decode sweep as one linear_gemv_sweep launch per token (the headline): W untimed
+    then exactly K timed launches between HIP events on the stream they run on.  Also the
+    same 192 GEMVs as separate launches captured in one graph per token, the per-stage kernel
+    blocks of that form (gate_up the largest), and the decode-step graph with the
+    packed-embedding gather of a device-resident token."""
     import torch
     import synth
     import weight_streaming_linear_amd as wsl
@@ -379,7 +387,7 @@ def measure_headline(k_steps, warmup):
     per_kind = time_step_launches([launches], 2 * SWEEP_LAYERS, 4)
     kern = summarize(per_kind, {f"nf4_gemv_{st[0]}": SWEEP_LAYERS for st in SWEEP_6144})
 
-    # the same sweep as one launch per token (linear_gemv_sweep)
+    # the headline: the sweep as one launch per token (linear_gemv_sweep)
     sw = wsl.GemvSweep([(p, xs[j], y, n, k) for (p, n, k, j), y in zip(packs, ys)])
     for y in ys:
         y.fill_(float("nan"))
@@ -390,15 +398,12 @@ def measure_headline(k_steps, warmup):
     sw_worst = gate_sweep("nf4 decode sweep (one launch)", xs, packs, ys, [0, 23, 47])
     if sha256_of(ys) != OUTPUT_SHA["nf4_decode_sweep_48x6144"]:
         refuse("linear_gemv_sweep differs from the per-stage launches", float("inf"))
-    for _ in range(warmup):
-        sw()
-    torch.cuda.synchronize()
-    a.record()
-    for _ in range(k_steps):
-        sw()
-    b.record()
-    torch.cuda.synchronize()
-    sw_ms = a.elapsed_time(b) / k_steps
+    sw_us = time_block([Launch(sw, nbytes=token_bytes, name="nf4_decode_sweep_kernel")], k_steps, warmup,
+                       label="nf4_decode_sweep_kernel_48x6144")
+    sw_ms = sw_us / 1e3
+    if sw.status() != 0:
+        refuse("linear_gemv_sweep status after the timed launches", float(sw.status()))
+    log(f"nf4 decode sweep: {sw_ms:.3f} ms/token (one launch), {token_bytes / 1e6 / sw_ms:.0f} GB/s")
 
     # decode-step graph: embedding gather of a device-resident token id + the sweep + id advance
     emb_n = 128000
@@ -415,12 +420,14 @@ def measure_headline(k_steps, warmup):
     grew = torch.cuda.memory_allocated() - before
     t0 = measure_launch_floor()["us"]
     out = {
-        "ms_per_token": ms, "token_bytes": token_bytes, "sanity_worst_ratio": max(worst, sw_worst),
-        "kernels": kern, "dominant_avg_us": per_kind[DOMINANT][0], "dominant_bytes": per_kind[DOMINANT][1].nbytes,
-        "sweep_kernel": {"ms_per_token": round(sw_ms, 4), "gbs": round(token_bytes / 1e6 / sw_ms, 1),
-                         "frac_hbm": round(token_bytes / 1e6 / sw_ms / HBM_PEAK_GBS, 4),
-                         "what": "linear_gemv_sweep: the 192 stages in one launch, a device-wide barrier "
-                                 "between stages; outputs bit-identical to the per-stage launches"},
+        "ms_per_token": sw_ms, "sweep_us": sw_us, "token_bytes": token_bytes,
+        "sanity_worst_ratio": max(worst, sw_worst), "kernels": kern,
+        "gate_up_avg_us": per_kind[DOMINANT][0], "gate_up_bytes": per_kind[DOMINANT][1].nbytes,
+        "graph_192_launches": {"ms_per_token": round(ms, 4), "gbs": round(token_bytes / 1e6 / ms, 1),
+                               "frac_hbm": round(token_bytes / 1e6 / ms / HBM_PEAK_GBS, 4),
+                               "what": "the same 192 GEMVs as separate linear_gemv launches captured in one "
+                                       "graph per token (stream order between stages); outputs bit-identical "
+                                       "to the one-launch sweep"},
         "decode_step_graph": {"ms_per_token": round(step_ms, 4), "tokens_per_s": round(1e3 / step_ms, 2),
                               "what": "embedding gather (device-resident token id) + 192 GEMVs + id advance, "
                                       "one graph", "allocator_growth_bytes": grew},
@@ -908,11 +915,10 @@ def source_sha():
 def traffic_probe():
     """The launches that a counter run of this script sees: 3 elementwise copies of CALIB_BYTES
     (torch.neg into a second buffer: a kernel that reads and writes exactly CALIB_BYTES), then
-    4 eager launches of the headline's dominant kernel, the NF4 gate_up GEMV (32768x6144), on
-    4 distinct packed matrices of the stack (the only GEMV dispatches of the run).  No timing,
-    no oracle."""
+    2 launches of the headline's kernel, the one-launch decode sweep over the 48-layer stack,
+    and 4 launches of the largest per-stage GEMV of the 192-launch form (gate_up 32768x6144)
+    on 4 of the stack's gate_up matrices.  No timing, no oracle."""
     import torch
-    import synth
     import weight_streaming_linear_amd as wsl
     src = torch.empty(CALIB_BYTES // 2, dtype=torch.bfloat16, device="cuda").normal_()
     dst = torch.empty_like(src)
@@ -920,17 +926,16 @@ def traffic_probe():
         torch.neg(src, out=dst)
     torch.cuda.synchronize()
     del src, dst
-    n, k = 32768, 6144
-    x = synth.device_normal_bf16(2, 1002, (k,))
-    y = torch.empty(n, dtype=torch.float32, device="cuda")
-    packs = []
-    for l in range(4):
-        w = synth.device_weight(2, 16 * l + 2, n, k)
-        packs.append(wsl.nf4_pack(w))
-        del w
+    xs, packs, ys = setup_sweep()
+    sw = wsl.GemvSweep([(p, xs[j], y, n, k) for (p, n, k, j), y in zip(packs, ys)])
+    for _ in range(2):
+        sw()
     torch.cuda.synchronize()
-    for p in packs:
-        wsl.linear_gemv(p, x, y=y, wfmt=wsl.WSL_W_NF4, n_out=n, k=k)
+    if sw.status() != 0:
+        raise SystemExit(f"sweep status {sw.status()}")
+    for l in range(4):
+        p, n, k, j = packs[4 * l + 2]
+        wsl.linear_gemv(p, xs[j], y=ys[4 * l + 2], wfmt=wsl.WSL_W_NF4, n_out=n, k=k)
     torch.cuda.synchronize()
     print("traffic probe done", flush=True)
 
@@ -956,27 +961,34 @@ def _per_dispatch(rows, match):
 
 
 def traffic_summarize(fetch_dir, write_dir, commands):
-    """Per-launch HBM bytes of the dominant kernel from two counter runs of --traffic-probe."""
+    """Per-launch HBM bytes from two counter runs of --traffic-probe: the headline's sweep
+    kernel (the figure the benchmark line carries) and the gate_up launch of the 192-launch
+    form."""
     # calibration: the elementwise negation of CALIB_BYTES (reads and writes CALIB_BYTES)
     is_calib = lambda n: "neg_kernel" in n
-    is_dom = lambda n: "gemv_nf4_team_kernel" in n
-    out = {}
-    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
-        rows = _counter_rows(d, counter)
-        calib = _per_dispatch(rows, is_calib)
-        dom = _per_dispatch(rows, is_dom)
-        if not calib or not dom:
-            raise SystemExit(f"{counter}: no calibration copy ({len(calib)}) or dominant kernel ({len(dom)}) rows")
-        factor = (np.mean(calib) * 1024) / CALIB_BYTES
-        out[counter] = {"kib_per_dispatch_raw": float(np.mean(dom)), "dispatches": len(dom),
-                        "calibration_copy_kib": float(np.mean(calib)), "factor": float(factor),
-                        "bytes_per_launch": float(np.mean(dom) * 1024 / factor)}
-    algo = 32768 * 6144 // 2 + 32768 * (6144 // 64) * 2
-    res = {"kernel": DOMINANT_KERNEL, "kernel_source_sha256": source_sha(),
-           "algorithmic_bytes_per_launch": algo, "counters": out,
-           "bytes_per_launch": out["FETCH_SIZE"]["bytes_per_launch"] + out["WRITE_SIZE"]["bytes_per_launch"],
-           "commands": commands}
-    res["ratio_to_algorithmic"] = res["bytes_per_launch"] / algo
+    token = SWEEP_LAYERS * sum(n * k // 2 + n * (k // 64) * 2 for _, n, k in SWEEP_6144)
+    gate_up = 32768 * 6144 // 2 + 32768 * (6144 // 64) * 2
+    kinds = {"sweep": (lambda n: SWEEP_KERNEL_MATCH in n, token),
+             "gate_up_launch": (lambda n: TEAM_KERNEL_MATCH in n, gate_up)}
+    res = {"kernel": DOMINANT_KERNEL, "kernel_source_sha256": source_sha(), "commands": commands}
+    for kind, (match, algo) in kinds.items():
+        out = {}
+        for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+            rows = _counter_rows(d, counter)
+            calib = _per_dispatch(rows, is_calib)
+            dom = _per_dispatch(rows, match)
+            if not calib or not dom:
+                raise SystemExit(f"{counter}: no calibration copy ({len(calib)}) or {kind} ({len(dom)}) rows")
+            factor = (np.mean(calib) * 1024) / CALIB_BYTES
+            out[counter] = {"kib_per_dispatch_raw": float(np.mean(dom)), "dispatches": len(dom),
+                            "calibration_copy_kib": float(np.mean(calib)), "factor": float(factor),
+                            "bytes_per_launch": float(np.mean(dom) * 1024 / factor)}
+        total = out["FETCH_SIZE"]["bytes_per_launch"] + out["WRITE_SIZE"]["bytes_per_launch"]
+        res[kind] = {"algorithmic_bytes_per_launch": algo, "counters": out, "bytes_per_launch": total,
+                     "ratio_to_algorithmic": total / algo}
+    res["bytes_per_launch"] = res["sweep"]["bytes_per_launch"]
+    res["algorithmic_bytes_per_launch"] = token
+    res["ratio_to_algorithmic"] = res["sweep"]["ratio_to_algorithmic"]
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(res, f, indent=1)
     print(json.dumps(res, indent=1))
@@ -995,12 +1007,17 @@ def traffic_from_file():
 # ---------------------------------------------------------------- issue/wait counters of the GEMV
 def gemv_counter_summarize(run_dirs, command):
     """Markdown summary of SQ counter runs of --traffic-probe (several passes, one directory
-    each): for the dominant GEMV's dispatches, the mean of every counter per dispatch and
-    the ratios that say where a wave's time goes (issuing VALU / LDS / VMEM instructions,
-    waiting on anything / on LDS), instructions per weight, and the clock.  SQ cycle
-    counters are summed over the GPU; ratios between them need no unit."""
+    each): for the sweep kernel's dispatches and for the gate_up launches, the mean of every
+    counter per dispatch and the ratios that say where a wave's time goes (issuing VALU /
+    LDS / VMEM instructions, waiting on anything / on LDS), instructions per weight, and the
+    clock.  SQ cycle counters are summed over the GPU; ratios between them need no unit."""
     import csv
-    per = {}
+    token_weights = SWEEP_LAYERS * sum(n * k for _, n, k in SWEEP_6144)
+    kinds = [("sweep", SWEEP_KERNEL_MATCH, token_weights,
+              "`gemv_nf4_sweep_kernel<12>`, the 48-layer decode sweep in one launch (2 launches)"),
+             ("gate_up", TEAM_KERNEL_MATCH, 32768 * 6144,
+              "`gemv_nf4_team_kernel<2,1>`, one gate_up 32768x6144 launch of the 192-launch form (4 launches)")]
+    per = {kind: {} for kind, *_ in kinds}
     xccs = 8
     for d in run_dirs:
         for path in glob.glob(os.path.join(d, "**", "*agent_info.csv"), recursive=True):
@@ -1008,46 +1025,49 @@ def gemv_counter_summarize(run_dirs, command):
                 for a in csv.DictReader(f):
                     if a.get("Name", "").startswith("gfx"):
                         xccs = int(a["Num_Xcc"])
-        disp = {}
+        disp = {kind: {} for kind, *_ in kinds}
         for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             with open(path) as f:
                 for r in csv.DictReader(f):
-                    if "gemv_nf4_team_kernel" not in r.get("Kernel_Name", ""):
-                        continue
-                    e = disp.setdefault(r["Dispatch_Id"], {"t": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
-                    e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
-        for e in disp.values():
-            for c, v in e.items():
-                per.setdefault(c, []).append(v)
-    m = {c: float(np.mean(v)) for c, v in per.items()}
-    weights = 32768 * 6144
-    g = lambda c: m.get(c)
-    lines = ["# Issue and wait counters of the NF4 decode GEMV (gate_up 32768x6144, pair table)", "",
+                    for kind, match, _, _ in kinds:
+                        if match not in r.get("Kernel_Name", ""):
+                            continue
+                        e = disp[kind].setdefault(r["Dispatch_Id"],
+                                                  {"t": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+                        e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        for kind in disp:
+            for e in disp[kind].values():
+                for c, v in e.items():
+                    per[kind].setdefault(c, []).append(v)
+    lines = ["# Issue and wait counters of the NF4 decode GEMV (48-layer hidden-6144 sweep; gate_up launch)", "",
              "Commands (run from the repository root on one MI355X, ROCm 7.2, rocprofv3), one pass per counter set:",
              "", "```", command, "```", "",
-             "Means per dispatch of `gemv_nf4_team_kernel<2,1>` over the probe's 4 launches (counters summed over "
-             f"the GPU's {xccs} XCDs).  Summary written by `python bench.py --gemv-counter-summarize <dirs...> "
-             "<command>`.", "", "| counter | per dispatch |", "|---|---:|"]
-    for c in sorted(k for k in m if k != "t"):
-        lines.append(f"| {c} | {m[c]:.4g} |")
-    lines += ["", "| derived | value |", "|---|---:|"]
-    if g("GRBM_GUI_ACTIVE") and g("t"):
-        lines.append(f"| GPU clock during the dispatch (GRBM_GUI_ACTIVE / {xccs} / duration) | "
-                     f"{g('GRBM_GUI_ACTIVE') / xccs / g('t'):.3f} GHz |")
-    wc = g("SQ_WAVE_CYCLES")
-    for c, what in (("SQ_ACTIVE_INST_VALU", "issuing VALU"), ("SQ_ACTIVE_INST_LDS", "issuing LDS"),
-                    ("SQ_ACTIVE_INST_VMEM", "issuing VMEM"), ("SQ_ACTIVE_INST_ANY", "issuing anything"),
-                    ("SQ_WAIT_ANY", "waiting on a counter (any)"), ("SQ_WAIT_INST_ANY", "waiting to issue (any)"),
-                    ("SQ_WAIT_INST_LDS", "waiting to issue LDS")):
-        if wc and g(c) is not None:
-            lines.append(f"| share of wave time {what} ({c} / SQ_WAVE_CYCLES) | {g(c) / wc:.3f} |")
-    for c in ("SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_INSTS_VMEM_RD", "SQ_INSTS_SALU"):
-        if g(c) is not None:
-            lines.append(f"| {c} x 64 lanes per weight | {g(c) * 64 / weights:.3f} |")
-    if g("SQ_LDS_BANK_CONFLICT") is not None and g("SQ_LDS_IDX_ACTIVE"):
-        lines.append(f"| LDS bank conflicts / LDS active | {g('SQ_LDS_BANK_CONFLICT') / g('SQ_LDS_IDX_ACTIVE'):.4f} |")
-    if g("SQ_BUSY_CYCLES") and g("GRBM_GUI_ACTIVE"):
-        lines.append(f"| SQ busy / GPU active | {g('SQ_BUSY_CYCLES') / g('GRBM_GUI_ACTIVE'):.3f} |")
+             f"Means per dispatch, counters summed over the GPU's {xccs} XCDs.  Summary written by "
+             "`python bench.py --gemv-counter-summarize <dirs...> <command>`.", ""]
+    for kind, _, weights, what in kinds:
+        m = {c: float(np.mean(v)) for c, v in per[kind].items()}
+        g = lambda c: m.get(c)
+        lines += [f"## {what}", "", "| counter | per dispatch |", "|---|---:|"]
+        for c in sorted(k for k in m if k != "t"):
+            lines.append(f"| {c} | {m[c]:.4g} |")
+        lines += ["", "| derived | value |", "|---|---:|"]
+        if g("GRBM_GUI_ACTIVE") and g("t"):
+            lines.append(f"| GRBM_GUI_ACTIVE / {xccs} / dispatch duration (counts dispatch overhead too: over-reads "
+                         f"the clock on a short launch) | {g('GRBM_GUI_ACTIVE') / xccs / g('t'):.3f} GHz |")
+        wc = g("SQ_WAVE_CYCLES")
+        for c, w in (("SQ_ACTIVE_INST_VALU", "issuing VALU"), ("SQ_ACTIVE_INST_LDS", "issuing LDS"),
+                     ("SQ_ACTIVE_INST_VMEM", "issuing VMEM"), ("SQ_ACTIVE_INST_ANY", "issuing anything"),
+                     ("SQ_WAIT_ANY", "waiting on a counter (any)"), ("SQ_WAIT_INST_ANY", "waiting to issue (any)"),
+                     ("SQ_WAIT_INST_LDS", "waiting to issue LDS")):
+            if wc and g(c) is not None:
+                lines.append(f"| share of wave time {w} ({c} / SQ_WAVE_CYCLES) | {g(c) / wc:.3f} |")
+        for c in ("SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_INSTS_VMEM_RD", "SQ_INSTS_SALU"):
+            if g(c) is not None:
+                lines.append(f"| {c} x 64 lanes per weight | {g(c) * 64 / weights:.3f} |")
+        if g("SQ_LDS_BANK_CONFLICT") is not None and g("SQ_LDS_IDX_ACTIVE"):
+            lines.append(f"| LDS bank conflicts / LDS active | "
+                         f"{g('SQ_LDS_BANK_CONFLICT') / g('SQ_LDS_IDX_ACTIVE'):.4f} |")
+        lines.append("")
     print("\n".join(lines))
 
 
@@ -1218,7 +1238,7 @@ REPEAT_FIGURES = [
     ("ms_per_step", ("ms_per_step",)),
     ("dominant_kernel_gbs", ("roofline", "achieved")),
     ("stream_read_probe_gbs", ("stream_read_probe", "gbs")),
-    ("sweep_kernel_ms_per_token", ("headline_detail", "sweep_kernel", "ms_per_token")),
+    ("graph_192_launches_ms_per_token", ("headline_detail", "graph_192_launches", "ms_per_token")),
     ("bf16_layer_fused_gbs", ("paths", "bf16_decode_layer_5120", "fused", "gbs")),
     ("nf4_gemv_4096_us", ("paths", "nf4_gemv_4096", "launches", "nf4_gemv_4096", "avg_us")),
     ("nf4_gemm_m32_tflops", ("paths", "nf4_prefill_gemm_m32", "kernel_tflops")),
@@ -1346,10 +1366,11 @@ def main():
 
     head = measure_headline(args.steps, args.warmup)
     value = head["token_bytes"] / 1e9 / (head["ms_per_token"] / 1e3)
-    achieved = head["dominant_bytes"] / 1e3 / head["dominant_avg_us"]
-    log(f"nf4 decode sweep: {head['ms_per_token']:.3f} ms/token, {value:.0f} GB/s; dominant gate_up kernel "
-        f"{head['dominant_avg_us']:.2f} us = {achieved:.0f} GB/s; one-launch sweep "
-        f"{head['sweep_kernel']['ms_per_token']:.3f} ms/token")
+    achieved = head["token_bytes"] / 1e3 / head["sweep_us"]   # one sweep launch per token
+    gate_up = head["gate_up_bytes"] / 1e3 / head["gate_up_avg_us"]
+    log(f"nf4 decode sweep: {head['ms_per_token']:.3f} ms/token (one launch), {value:.0f} GB/s; 192-launch graph "
+        f"{head['graph_192_launches']['ms_per_token']:.3f} ms/token; gate_up launch "
+        f"{head['gate_up_avg_us']:.2f} us = {gate_up:.0f} GB/s")
 
     probe = measure_read_ceiling()
     log(f"stream-read probe: {probe['gbs']:.0f} GB/s")
@@ -1380,8 +1401,8 @@ def main():
                 "drawn on the device)",
         "config": {
             "workload": "NF4 decode GEMV sweep, batch 1, 48-layer stack of hidden 6144: qkv 8192x6144, o 6144x6144, "
-                        "gate_up 32768x6144, down 6144x16384 per layer; 192 launches per token in decoder order, "
-                        "one graph per token",
+                        "gate_up 32768x6144, down 6144x16384 per layer; 192 GEMVs per token in decoder order, "
+                        "one linear_gemv_sweep launch per token (a device-wide barrier between stages)",
             "weight_format": "NF4: 4-bit codes, groups of 64 along k, one fp16 scale per group (17/32 B per weight)",
             "activations": "bf16, fp32 accumulation, fp32 outputs",
             "weight_bytes_per_token": head["token_bytes"],
@@ -1395,8 +1416,8 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic_from_file(),
             "kernel": DOMINANT_KERNEL,
-            "bytes_per_launch": head["dominant_bytes"],
-            "avg_launch_us": round(head["dominant_avg_us"], 3),
+            "bytes_per_launch": head["token_bytes"],
+            "avg_launch_us": round(head["sweep_us"], 3),
         },
         "stream_read_probe": probe,
         "headline_detail": {
@@ -1404,9 +1425,10 @@ def main():
             "tokens_per_s": round(1e3 / head["ms_per_token"], 2),
             "frac_stream_read_probe": round(value / probe["gbs"], 4),
             "sanity_worst_ratio": head["sanity_worst_ratio"],
-            "kernel_ms_per_token": round(head["kernels"]["kernel_ms_per_step"], 5),
-            "kernels": head["kernels"]["launches"],
-            "sweep_kernel": head["sweep_kernel"],
+            "graph_form_kernel_ms_per_token": round(head["kernels"]["kernel_ms_per_step"], 5),
+            "graph_form_kernels": head["kernels"]["launches"],
+            "gate_up_launch_gbs": round(gate_up, 1),
+            "graph_192_launches": head["graph_192_launches"],
             "decode_step_graph": head["decode_step_graph"],
             "launch_floor": head["launch_floor"],
         },
