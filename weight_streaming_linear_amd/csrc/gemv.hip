@@ -95,6 +95,34 @@ __device__ __forceinline__ float reduce_rows(const float (&a)[R], int lane) {
     }
 }
 
+// The team GEMV's reduction of two rows (fewer instructions than reduce_rows<2>): the
+// halves are exchanged and added (lanes 0-31 row 0, 32-63 row 1), summed in groups of 8
+// and then of 16 lanes (DPP), and the last lane of each 16-lane row adds the last lane of
+// the row before it (DPP row broadcast into rows 1 and 3).  Only lanes 31 and 63 end
+// with their row's total (rows 0 and 1).
+constexpr int kTwoRowsLastLane = 31;
+__device__ __forceinline__ float reduce_two_rows_last(float a0, float a1) {
+    float v = fold32(a0, a1);
+    v = sum8(v);
+    v += as_f(__builtin_amdgcn_update_dpp(0u, as_u(v), 0x128, 0xF, 0xF, true));   // row_ror:8
+    v += as_f(__builtin_amdgcn_update_dpp(0u, as_u(v), 0x142, 0xA, 0xF, true));   // row_bcast:15, rows 1 and 3
+    return v;
+}
+
+// Per-lane partial sums of a team step -> this wave's row totals, and whether this lane
+// holds one (row lane / (64 / R)).
+template <int R>
+__device__ __forceinline__ float team_reduce(const float (&acc)[R], int lane, bool &holder) {
+    constexpr int span = 64 / R;
+    if constexpr (R == 2) {
+        holder = (lane % span) == kTwoRowsLastLane;
+        return reduce_two_rows_last(acc[0], acc[1]);
+    } else {
+        holder = (lane % span) == 0;
+        return reduce_rows<R>(acc, lane);
+    }
+}
+
 // Fold the waves' row sums (LDS, fixed wave order) and store y.
 template <int R>
 __device__ __forceinline__ void finish_rows(const float (&acc)[R], float (*red)[R], int lane, int wave, int waves,
@@ -532,8 +560,9 @@ __device__ __forceinline__ bool team_run(const TeamStage<R, WIDE> &st, TeamLds<R
             float acc[R];
 #pragma unroll
             for (int r = 0; r < R; ++r) acc[r] = scale_at<R>(sb_, r) * team_dot<TAB>(q[r], xf, lds.tab, ad);
-            const float v = reduce_rows<R>(acc, lane);
-            if ((lane % span) == 0) lds.red[ph][wave][lane / span] = v;
+            bool holder;
+            const float v = team_reduce<R>(acc, lane, holder);
+            if (holder) lds.red[ph][wave][lane / span] = v;
         }
         lds_barrier();
         if (threadIdx.x < T * R) {
@@ -622,8 +651,9 @@ __device__ __forceinline__ bool team_run(const TeamStage<R, WIDE> &st, TeamLds<R
 #pragma unroll
             for (int r = 0; r < R; ++r) acc[r] = s[r] * team_dot<TAB>(q[r], xf, lds.tab, ad);
         }
-        const float v = reduce_rows<R>(acc, lane);
-        if ((lane % span) == 0) lds.red[it & 1][wave][lane / span] = v;
+        bool holder;
+        const float v = team_reduce<R>(acc, lane, holder);
+        if (holder) lds.red[it & 1][wave][lane / span] = v;
         lds_barrier();
         if (threadIdx.x < T * R) {
             const int tm = threadIdx.x / R, r = threadIdx.x - tm * R;
