@@ -611,10 +611,11 @@ __device__ __forceinline__ bool team_run(const TeamStage<R, WIDE> &st, TeamLds<R
         }
         if (st.park) {
             lds_barrier();
-            for (int64_t e = threadIdx.x; e < (jend - jbeg) * T * R; e += blockDim.x) {
-                const int64_t jj = jbeg + e / (T * R);
-                const int64_t rest = e - (e / (T * R)) * (T * R);
-                st.y[(st.first + st.i0 + jj * st.nloc) * T * R + rest] = lds.yl[e];
+            // at most cap * T * R <= kRowSumCap sums: 32-bit index arithmetic
+            const uint32_t tr = static_cast<uint32_t>(T * R), cnt = static_cast<uint32_t>(jend - jbeg) * tr;
+            for (uint32_t e = threadIdx.x; e < cnt; e += blockDim.x) {
+                const uint32_t q = e / tr, rest = e - q * tr;
+                st.y[(st.first + st.i0 + (jbeg + q) * st.nloc) * T * R + rest] = lds.yl[e];
             }
             lds_barrier();
         }
