@@ -209,3 +209,52 @@ def test_decode_sweep_kernel_graph_replays():
         torch.cuda.synchronize()
         assert all(torch.equal(st[2], w) for st, w in zip(stages, want))
         assert sw.status() == 0 and _sweep_ws_clear(sw)
+
+
+def test_decode_sweep_kernel_many_stages():
+    """A sweep longer than the stage plans the kernel keeps in LDS at once (512: two chunks
+    of 256), so later chunks are planned at stage boundaries: 1100 small stages of mixed
+    shapes, every stage equal bit for bit to its own linear_gemv launch, a sample of stages
+    against the oracle, and one device descriptor in a late chunk made invalid (skipped with
+    WSL_STATUS_DESCRIPTOR)."""
+    import ctypes
+    import torch
+    from gpu_common import to_dev_bf16
+    say("decode sweep: 1100 stages")
+    shapes = [(16, 64), (33, 128), (100, 2048), (64, 6144), (17, 16384), (48, 4096), (250, 1024)]
+    stages, bits = [], []
+    for i in range(1100):
+        n, k = shapes[i % len(shapes)]
+        wb = synth.weight_bits(116, i % 61, n, k)
+        xb = synth.act_bits(116, 200 + i % 13, (k,))
+        bits.append((wb, xb))
+        stages.append((wsl.nf4_pack(to_dev_bf16(wb)), to_dev_bf16(xb),
+                       torch.full((n,), float("nan"), dtype=torch.float32, device="cuda"), n, k))
+    ref = [torch.empty_like(st[2]) for st in stages]
+    for st, y in zip(stages, ref):
+        wsl.linear_gemv(st[0], st[1], y=y, wfmt=wsl.WSL_W_NF4, n_out=st[3], k=st[4])
+    sw = wsl.GemvSweep(stages)
+    sw()
+    torch.cuda.synchronize()
+    assert sw.status() == 0 and _sweep_ws_clear(sw)
+    for i, (st, y) in enumerate(zip(stages, ref)):
+        assert torch.equal(st[2], y), f"stage {i} {st[3]}x{st[4]} differs from its linear_gemv launch"
+    for i in (0, 255, 256, 511, 512, 767, 768, 1023, 1024, 1099):
+        wb, xb = bits[i]
+        codes, scales = oracle.pack_codes(f64(wb))
+        ok, worst, r = oracle.check_rows_f32(stages[i][2].cpu().numpy(),
+                                             *oracle.gemv_ref(oracle.dequant_exact(codes, scales), f64(xb)))
+        assert ok, f"stage {i}: row {r} worst ratio {worst}"
+    bad_stage = 800
+    size = ctypes.sizeof(wsl.WslGemvStage)
+    for st in stages:
+        st[2].fill_(float("nan"))
+    sw.d[bad_stage * size + 32:bad_stage * size + 40] = torch.tensor([65], dtype=torch.int64).view(torch.uint8).to("cuda")
+    sw()
+    torch.cuda.synchronize()
+    assert sw.status() & wsl.WSL_STATUS_DESCRIPTOR
+    assert bool(torch.isnan(stages[bad_stage][2]).all())
+    for i, (st, y) in enumerate(zip(stages, ref)):
+        if i != bad_stage:
+            assert torch.equal(st[2], y), f"stage {i} differs after the invalid descriptor"
+    sw.ws.zero_()

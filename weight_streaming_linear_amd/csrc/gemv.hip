@@ -28,6 +28,9 @@
 
 namespace wsl {
 
+// Global-address-space qualifier for pointers the kernels read back from memory.
+#define WSL_GLOBAL __attribute__((address_space(1)))
+
 constexpr int kMaxWaves = 8;
 
 // ---------------------------------------------------------------- reductions
@@ -466,6 +469,51 @@ struct TeamStage {
         park = n >= 4;
     }
 
+    // The same from a workgroup plan of a decode-sweep stage (SweepPlan, below): only the
+    // per-wave part is computed here.
+    // The plan is read from LDS into vector registers; every field is wave-uniform, and
+    // taking it into a scalar register keeps the address arithmetic of the loop scalar.
+    template <typename Plan>
+    __device__ __forceinline__ void init_plan(const Plan &p, int wave, int lane, int64_t i0_, int64_t nloc_) {
+        auto u32 = [](int32_t v) { return __builtin_amdgcn_readfirstlane(v); };
+        auto uptr = [](uint64_t v) {
+            const uint64_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int32_t>(v)));
+            const uint64_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int32_t>(v >> 32)));
+            return lo | (hi << 32);
+        };
+        // back to global-space pointers before they become the generic fields, so that the
+        // compiler still knows where they point
+        packed = (const uint8_t *)reinterpret_cast<const WSL_GLOBAL uint8_t *>(uptr((uint64_t)p.w));
+        x = (const uint16_t *)reinterpret_cast<const WSL_GLOBAL uint16_t *>(uptr((uint64_t)p.x));
+        y = (float *)reinterpret_cast<WSL_GLOBAL float *>(uptr((uint64_t)p.y));
+        const int32_t k = u32(p.k);
+        n_out = u32(p.n_out);
+        S = u32(p.S);
+        T = u32(p.T);
+        groups = k >> 6;
+        rowbytes = k >> 1;
+        row_groups = u32(p.row_groups);
+        supers = u32(p.supers);
+        cap = u32(p.cap);
+        nloc = nloc_;
+        first = u32(p.first);
+        i0 = i0_;
+        n = u32(p.n);
+        park = n >= 4;
+        scales = reinterpret_cast<const uint16_t *>(packed + n_out * rowbytes);
+        const uint32_t wv = __builtin_amdgcn_readfirstlane(wave);
+        team = static_cast<int>((wv * static_cast<uint32_t>(u32(p.inv_s))) >> 16);   // wv / S for wv < 16
+        idle = WIDE && team >= T;
+        fteam = idle ? T - 1 : team;
+        const int slice = static_cast<int>(wv) - team * S;
+        const int32_t kk0 = slice * 2048 + lane * 32;
+        active = kk0 < k;
+        kkl = active ? kk0 : k - 32;
+        coff = static_cast<uint32_t>(kkl >> 1);
+        gl = static_cast<uint32_t>(kkl >> 6);
+        soff = gl * 32u;
+    }
+
     // Loads of super-group j of this wave's team.  An idle wave loads what the last team
     // loads (in bounds, and never used): with no branch around the loads, every path has
     // the same loads in flight, and the compiler's waits before the first multiply stay
@@ -719,7 +767,6 @@ constexpr int kSyncStatusWord = 10 * 32;
 // global address space.  A pointer read from memory as a plain pointer is generic to the
 // compiler, which then emits flat loads and stores -- counted by lgkmcnt as well, so
 // every LDS-only wait would also wait for the weight loads in flight.
-#define WSL_GLOBAL __attribute__((address_space(1)))
 struct SweepStage {
     const WSL_GLOBAL uint8_t *w;
     const WSL_GLOBAL uint16_t *x;
@@ -768,6 +815,49 @@ __device__ __forceinline__ void sweep_wait(uint32_t *sync, uint32_t b, uint32_t 
     }
 }
 
+// The wave-independent geometry of a decode-sweep stage for one workgroup: what every
+// wave of the workgroup would otherwise derive for itself from the stage's descriptor
+// at every stage boundary (the descriptor load and about a dozen divisions, scalar work
+// that the CU's waves share one scalar unit for).  One lane per stage computes it; the
+// waves read it from LDS.  An invalid descriptor gives ok = 0 and no rows.
+struct SweepPlan {
+    const WSL_GLOBAL uint8_t *w;   // global address space: a generic pointer read back from
+    const WSL_GLOBAL uint16_t *x;  // memory would make the weight loads flat loads, which
+    WSL_GLOBAL float *y;           // every LDS wait would also wait for
+    int32_t n_out, k, S, T, inv_s, row_groups, supers, cap, first, n, ok, pad;
+};
+
+template <int R>
+__device__ __forceinline__ void sweep_plan(const wsl_gemv_stage *stages, int s, int waves, int nx, SweepPlan &p) {
+    const SweepStage d = reinterpret_cast<const SweepStage *>(stages)[s];
+    const bool ok = sweep_stage_ok(d);
+    const int S = ok ? static_cast<int>((d.k + 2047) / 2048) : 1;
+    const int64_t n_out = ok ? d.n_out : 0;
+    const int T = sweep_teams(S, waves);
+    const TeamGeom g = team_geom<R>(n_out, S, T, gridDim.x, static_cast<uint32_t>(nx));
+    const uint32_t b = blockIdx.x, ux = static_cast<uint32_t>(nx);
+    const uint32_t i0 = b / ux, xcd = b - i0 * ux;
+    const int32_t cnt = g.per + (static_cast<int32_t>(xcd) < g.rem ? 1 : 0);
+    p.w = d.w;
+    p.x = d.x;
+    p.y = d.y;
+    p.n_out = static_cast<int32_t>(n_out);
+    p.k = ok ? static_cast<int32_t>(d.k) : 64;
+    p.S = S;
+    p.T = T;
+    p.inv_s = (65536 + S - 1) / S;
+    p.row_groups = ok ? g.row_groups : 0;
+    p.supers = ok ? g.supers : 0;
+    p.cap = g.cap;
+    p.first = static_cast<int32_t>(xcd) * g.per + (static_cast<int32_t>(xcd) < g.rem ? static_cast<int32_t>(xcd) : g.rem);
+    p.n = (ok && static_cast<int32_t>(i0) < cnt)
+              ? static_cast<int32_t>(static_cast<uint32_t>(cnt - static_cast<int32_t>(i0) + g.nloc - 1) /
+                                     static_cast<uint32_t>(g.nloc))
+              : 0;
+    p.ok = ok ? 1 : 0;
+    p.pad = 0;
+}
+
 // The decode sweep: `count` NF4 GEMVs (stages) in order in one launch, one 16-wave
 // workgroup per CU for the whole call.  Each stage runs as the team kernel with the pair
 // table (R = 2, T = sweep_teams(S)); waves beyond a stage's teams run its barrier-only
@@ -786,8 +876,13 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_nf4_sweep_kernel(const wsl_ge
     constexpr int R = 2;
     typedef ScaleBits<R>::T SB;
     __shared__ TeamLds<R, 1> lds;
+    // Plans of the first 64 * WAVES stages (one per thread); later stages are set up from
+    // their descriptors at the stage boundary as the plans are.
+    constexpr int kPlans = 64 * WAVES;
+    __shared__ SweepPlan plans[kPlans];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
+    const int64_t i0 = blockIdx.x / nx, nloc = gridDim.x / nx;
     uint32_t ad[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) ad[i] = static_cast<uint32_t>(lane & 31) << 3;
@@ -823,6 +918,17 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_nf4_sweep_kernel(const wsl_ge
     cs.issue_x(xv);
     nf = first_of(1, cs.x);
     fill_pair_table(lds.tab);   // while the first loads are in flight
+    // The plans, one thread per stage (their descriptor loads queue behind the first loads,
+    // which the first multiply waits for anyway).  Every thread loads a descriptor (threads
+    // past the last stage load the last one again), so no branch decides whether these
+    // loads are issued -- with one, the compiler's waits for the weight loads of the stage
+    // loop below turn conservative and drain the prefetch.
+    {
+        const int t = static_cast<int>(threadIdx.x);
+        SweepPlan p;
+        sweep_plan<R>(stages, t < count ? t : count - 1, WAVES, nx, p);
+        if (t < count) plans[t] = p;
+    }
     __syncthreads();
     for (int s = 0; s < count; ++s) {
         float xf[32];
@@ -847,10 +953,22 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_nf4_sweep_kernel(const wsl_ge
         }
         lds_barrier();   // this stage's LDS reads are done (its y stores may still drain)
         if (threadIdx.x == 0) sweep_arrive(sync, nx);
-        // Both geometries (the next stage's, and the first loads of the one after) are
-        // computed here, where the wait hides them, not at the start of the stage.
-        ok = setup(s + 1, cs);
-        nf = first_of(s + 2, cs.x);
+        // The next stage's geometry and the first loads of the one after are set up here,
+        // where the wait hides them: from the workgroup's plans, or from the descriptor for
+        // stages past them.
+        if (s + 1 < kPlans) {
+            cs.init_plan(plans[s + 1], wave, lane, i0, nloc);
+            ok = __builtin_amdgcn_readfirstlane(plans[s + 1].ok) != 0;
+        } else {
+            ok = setup(s + 1, cs);
+        }
+        {
+            TeamStage<R, true> ns;
+            if (s + 2 >= count) ns.n = 0;
+            else if (s + 2 < kPlans) ns.init_plan(plans[s + 2], wave, lane, i0, nloc);
+            else setup(s + 2, ns);
+            nf = first_loads(ns, cs.x);
+        }
         if (wave == 0) sweep_wait(sync, static_cast<uint32_t>(s), spin_limit, nx, gave_up);
         lds_barrier();   // every wave waits for the wait (not for its own loads)
         cs.issue_x(xv);
