@@ -28,11 +28,10 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast
 // The k loop runs over 32-k stages held in a 4-deep LDS ring (4 x 32 KB).
 // Operands go global -> LDS directly (global_load_lds_dwordx4: a wave-wide
 // load writes 1 KB of LDS, lane L at byte 16L), so no registers are spent on
-// staging and three stages (96 KB per CU) stay in flight: enough bytes in
-// flight to cover the L2/MALL latency at the operand rate a 256 x 256 tile
-// needs.  Per stage: wait for the oldest copies (s_waitcnt vmcnt), one
-// barrier, then 2 x 8 MFMAs with the refill of the stage freed by the previous
-// iteration issued among them.
+// staging and two to three stages (64-96 KB per CU) stay in flight: enough
+// bytes in flight to cover the L2/MALL latency at the operand rate a 256 x 256
+// tile needs.  The two waves of a SIMD alternate between multiplying a stage and
+// reading the fragments of their next one (see bf16_tile).
 // LDS rows are 32 bf16 = 64 B = 4 chunks of 16 B; chunk c of row r sits at
 // c ^ ((r >> 1) & 3) ^ ((r >> 3) & 1): the fragment reads (32 rows, one chunk
 // column) are free of bank conflicts for 32 and for 64 banks.  Because a
@@ -121,7 +120,7 @@ __device__ __forceinline__ void bf16_tile(const uint16_t *__restrict__ x, const 
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
     const int half = lane >> 5, l32 = lane & 31;
-    const int64_t ktiles = k / kBK;
+    const int64_t ktiles = k / kBK;   // even: k % 64 == 0
     // Fragment reads: the lane's MI A rows (and 2 B rows) are 32 rows apart and
     // share their swizzled chunk, so one base address plus immediate offsets
     // (2048 B apart) covers the reads of a 16-k step.  They are issued from
@@ -135,14 +134,6 @@ __device__ __forceinline__ void bf16_tile(const uint16_t *__restrict__ x, const 
         offa[ks] = static_cast<uint32_t>(swz(wm * (TM / 2) + l32, ks * 2 + half));
         offb[ks] = static_cast<uint32_t>(kBM * kBK * 2 + swz(wn * 64 + l32, ks * 2 + half));
     }
-    // Per stage: issue the reads of step 0, wait; issue the reads of step 1,
-    // run the MFMAs of step 0 while they are in flight, wait; run step 1.
-    // The wait is a separate asm statement that takes the fragments as in/out
-    // operands, so no MFMA can use them before it (each fragment is named once,
-    // so the compiler has no reason to copy one before the wait).
-    // The refill's NV copies are spread among the stage's MFMAs: issued together
-    // right after the barrier they stalled the wave at issue (the vector memory
-    // queue fills) ahead of its fragment reads and MFMAs.
     using frags = u32x4[MI + 2];
     auto issue = [&](uint32_t a_addr, uint32_t b_addr, frags &f) {
         if constexpr (MI == 4) {
@@ -165,15 +156,41 @@ __device__ __forceinline__ void bf16_tile(const uint16_t *__restrict__ x, const 
                 : "v"(a_addr), "v"(b_addr));
         }
     };
-    auto landed = [&](frags &f) {
+    // The wait is a separate asm statement that takes every fragment as an in/out
+    // operand (each named once), so no MFMA can use one before it.
+    auto landed = [&](frags &f0, frags &f1) {
         if constexpr (MI == 4) {
             asm volatile("s_waitcnt lgkmcnt(0)"
-                         : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]), "+v"(f[4]), "+v"(f[5]));
+                         : "+v"(f0[0]), "+v"(f0[1]), "+v"(f0[2]), "+v"(f0[3]), "+v"(f0[4]), "+v"(f0[5]),
+                           "+v"(f1[0]), "+v"(f1[1]), "+v"(f1[2]), "+v"(f1[3]), "+v"(f1[4]), "+v"(f1[5]));
         } else {
-            asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]));
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(f0[0]), "+v"(f0[1]), "+v"(f0[2]), "+v"(f0[3]), "+v"(f1[0]), "+v"(f1[1]),
+                           "+v"(f1[2]), "+v"(f1[3]));
         }
     };
-    // One operand copy of the refill, piece q < NV (NA A-loads, then 2 B-loads).
+    // Two groups of four waves, one wave of each on every SIMD (waves are placed on
+    // the SIMDs in turn), take turns: while one group multiplies a k-stage (2 x MI x 2
+    // MFMAs that keep the SIMD's matrix pipe busy), the other reads its fragments of
+    // the next stage from LDS.  Every wave runs the same sequence -- memory phase,
+    // barrier, MFMA phase, barrier -- and the second group starts one barrier later,
+    // so the phases of the two groups alternate between consecutive barriers without
+    // any branch on the group inside the loop.  In the memory phase the fragment reads
+    // go first and the wait for this wave's copies comes after them, so the reads do
+    // not queue behind copies still arriving from L2.
+    // Ring of four stages.  A wave's copies of k-tile kt + 3 are issued one by one
+    // among the MFMAs of its stage kt, into the slot stage kt - 1 used (both groups
+    // finished reading it before the barrier that began this phase).  Its memory phase
+    // of stage kt then waits until only its copies of kt + 2 are in flight: its share
+    // of stage kt + 1 is in LDS, and the barrier that ends the phase publishes it
+    // before either group reads stage kt + 1.
+    auto bar = []() {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto lds_addr = [](char *p) { return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void *)p)); };
+    const uint32_t a0 = lds_addr(st0), a1 = lds_addr(st1), a2 = lds_addr(st2), a3 = lds_addr(st3);
     auto copy_piece = [&](int q, int64_t kt, char *sa) {
         const int64_t k0 = kt * kBK;
         if (q < NA)
@@ -181,58 +198,57 @@ __device__ __forceinline__ void bf16_tile(const uint16_t *__restrict__ x, const 
         else
             lds_copy16(bsrc[q - NA] + k0, sa + kBM * kBK * 2 + (2 * wave + q - NA) * 1024);
     };
-    auto compute_stage = [&](uint32_t base, bool refill, int64_t kn, char *dst) {
-        frags f0, f1;
-        issue(base + offa[0], base + offb[0], f0);
-        landed(f0);
-        issue(base + offa[1], base + offb[1], f1);
-        __builtin_amdgcn_sched_barrier(0);
-        constexpr int MF = 2 * MI;   // MFMAs per 16-k step
+    frags f0, f1;
+    auto stage = [&](int64_t kt, uint32_t cur, char *refill) {
+        issue(cur + offa[0], cur + offb[0], f0);
+        issue(cur + offa[1], cur + offb[1], f1);
+        landed(f0, f1);
+        if (kt + 2 < ktiles) {
+            wait_vmcnt<NV>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        bar();
+        const bool rf = kt + 3 < ktiles;
         int q = 0;
+        constexpr int MF = 2 * MI;   // MFMAs per 16-k step
 #pragma unroll
         for (int t = 0; t < 2 * MF; ++t) {
-            if (t == MF) {
-                landed(f1);
-            }
-            frags &f = t < MF ? f0 : f1;
             const int i = (t % MF) >> 1, j = t & 1;
+            const frags &f = t < MF ? f0 : f1;
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f[i]),
                                                                 __builtin_bit_cast(bf16x8, f[MI + j]), acc[i][j], 0, 0, 0);
             if ((t + 1) == (q + 1) * 2 * MF / (NV + 1) && q < NV) {
                 __builtin_amdgcn_sched_barrier(0);
-                if (refill) copy_piece(q, kn, dst);
+                if (rf) copy_piece(q, kt + 3, refill);
                 __builtin_amdgcn_sched_barrier(0);
                 ++q;
             }
         }
+        bar();
     };
-    // One k-stage: wait for this wave's copies of stage kt (copies of kt+1 and
-    // kt+2 may stay in flight), a bare barrier (no memory fence, which would also
-    // wait for those), multiply stage kt while refilling the stage freed by the
-    // previous iteration with k-tile kt+3.
-    auto lds_addr = [](char *p) { return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void *)p)); };
-    const uint32_t a0 = lds_addr(st0), a1 = lds_addr(st1), a2 = lds_addr(st2), a3 = lds_addr(st3);
-    auto step = [&](int64_t kt, uint32_t cur, char *refill) {
-        const int64_t ahead = ktiles - 1 - kt;
-        if (ahead >= 2) wait_vmcnt<2 * NV>();
-        else if (ahead == 1) wait_vmcnt<NV>();
-        else wait_vmcnt<0>();
-        __builtin_amdgcn_s_barrier();
-        compute_stage(cur, kt + 3 < ktiles, kt + 3, refill);
-    };
-    if (0 < ktiles) copy_stage(0, st0);
-    if (1 < ktiles) copy_stage(1, st1);
-    if (2 < ktiles) copy_stage(2, st2);
+    const int group = static_cast<int>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(wave))) >> 2;
+    copy_stage(0, st0);
+    copy_stage(1, st1);
+    if (2 < ktiles) {
+        copy_stage(2, st2);
+        wait_vmcnt<2 * NV>();
+    } else {
+        wait_vmcnt<NV>();
+    }
+    bar();                   // stage 0 in LDS
+    if (group != 0) bar();   // the second group runs one phase behind
     int64_t kt = 0;
     for (; kt + 4 <= ktiles; kt += 4) {
-        step(kt + 0, a0, st3);
-        step(kt + 1, a1, st0);
-        step(kt + 2, a2, st1);
-        step(kt + 3, a3, st2);
+        stage(kt + 0, a0, st3);
+        stage(kt + 1, a1, st0);
+        stage(kt + 2, a2, st1);
+        stage(kt + 3, a3, st2);
     }
-    if (kt + 0 < ktiles) step(kt + 0, a0, st3);
-    if (kt + 1 < ktiles) step(kt + 1, a1, st0);
-    if (kt + 2 < ktiles) step(kt + 2, a2, st1);
+    if (kt + 0 < ktiles) stage(kt + 0, a0, st3);
+    if (kt + 1 < ktiles) stage(kt + 1, a1, st0);
+    if (kt + 2 < ktiles) stage(kt + 2, a2, st1);
+    if (group == 0) bar();   // both groups pass the same number of barriers
 
     // 32x32 accumulator layout: element e of lane l is row 8*(e/4) + 4*(l/32) + e%4, column l%32.
 #pragma unroll
