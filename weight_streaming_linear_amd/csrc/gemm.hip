@@ -966,20 +966,16 @@ __global__ __launch_bounds__(512) void gemm_bf16_x32_kernel(const uint16_t *__re
 
 // ---------------------------------------------------------------- NF4, tiled, M > 32
 // NF4 GEMM over many positions (batch verification, long prefill): the bf16
-// kernel's 256 x 256 tiles, 8 waves of 128 x 64 and 4-stage ring, but the weight
-// half of each 32-k stage is restored on the way in.  X tiles still arrive by
-// direct global -> LDS copies three stages ahead.  Thread t restores row t/2,
-// k [16 (t % 2), +16) of the weight stage: its 8 code bytes and the group's scale
-// are loaded three stages ahead into registers, and at step kt the codes of stage
-// kt + 1 are turned into t = bf16(fp32(level * s)) through a 16-entry LDS table
-// (the four 32 KB stages leave no room for the 64 KB pair table) and written into
-// that stage's weight half.  Weight halves live in LDS arrays of their own,
-// separate from the arrays the copies fill, so the compiler sees that these
-// writes cannot alias copies in flight.  Per step: wait until the X copy of stage
-// kt and the codes of stage kt + 1 have landed (vmcnt 6 / 2 / 0 as 2, 1, 0 stages
-// remain), one barrier (an asm statement with a memory clobber, so no LDS access
-// moves across it), issue the codes and X copy of stage kt + 3, restore stage
-// kt + 1, multiply stage kt.  Each weight tile is restored once per 256 positions.
+// kernel's 256 x 256 tiles, 8 waves of 128 x 64, 4-stage X ring and ping-pong
+// schedule, but the weight half of each 32-k stage is restored on the way in.
+// X tiles still arrive by direct global -> LDS copies three stages ahead.
+// Thread t restores row t/2, k [16 (t % 2), +16) of the weight stage: its 8 code
+// bytes and the group's scale are loaded three stages ahead into registers, and in
+// the memory phase of stage kt the codes of stage kt + 1 are turned into
+// t = bf16(fp32(level * s)) through a 16-entry LDS table and written into one of two
+// weight slots.  Weight slots live in LDS arrays of their own, separate from the
+// arrays the copies fill, so the compiler sees that these writes cannot alias
+// copies in flight.  Each weight tile is restored once per 256 positions.
 // dequant8 with the table reads issued from inline asm (and waited for inside it): the
 // compiler then has no LDS access of its own to order against direct global -> LDS
 // copies in flight, which it would otherwise drain first.  lut_addr is the table's LDS
@@ -1022,7 +1018,7 @@ template <int TM>
 __device__ __forceinline__ void nf4_tile(const uint16_t *__restrict__ x, const uint8_t *__restrict__ packed, int64_t m,
                                          int64_t n_out, int64_t k, int64_t ldx, void *__restrict__ y, int ofmt,
                                          int64_t ldy, int64_t m0, int64_t n0, char *sa0, char *sa1, char *sa2,
-                                         char *sa3, char *sb0, char *sb1, char *sb2, char *sb3, const float *lut) {
+                                         char *sa3, char *sb0, char *sb1, const float *lut) {
     constexpr int MI = TM / 64;         // 32-row MFMA tiles per wave along m
     constexpr int NA = TM / 128;        // A wave-loads per wave per stage
     const int tid = threadIdx.x;
@@ -1051,18 +1047,31 @@ __device__ __forceinline__ void nf4_tile(const uint16_t *__restrict__ x, const u
     const uint32_t boff1 = static_cast<uint32_t>(swz(brow, 2 * bhp + 1));
     const uint32_t lut_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void *)lut));
 
+    const int64_t ktiles = k / kBK;   // even: k % 64 == 0
+    // Loads for k-tiles past the end are clamped to the last one: they land in a
+    // slot or register set nobody reads again, and keep the loop free of branches
+    // around loads (with them the compiler's own waits turn conservative).
+    auto tile_k0 = [&](int64_t kt) { return (kt < ktiles ? kt : ktiles - 1) * kBK; };
+    // The code and scale loads are issued from inline asm: the compiler does not
+    // track them, so it adds no waits of its own (around the loop's back edge it
+    // waited for every load in flight).  The explicit vmcnt wait of the memory phase
+    // covers them; put_b then marks the registers as written.
+    auto load_codes = [&](int64_t kt, u32x2 &q, uint32_t &sraw) {
+        const int64_t k0 = tile_k0(kt);
+        const uint8_t *cp = crow + (k0 >> 1);
+        const uint16_t *sp = srow + (k0 >> 6) * srb;
+        asm volatile("global_load_dwordx2 %0, %2, off\n\tglobal_load_ushort %1, %3, off"
+                     : "=&v"(q), "=&v"(sraw)
+                     : "v"(cp), "v"(sp));
+    };
     auto copy_a = [&](int64_t kt, char *sa) {
-        const int64_t k0 = kt * kBK;
+        const int64_t k0 = tile_k0(kt);
 #pragma unroll
         for (int i = 0; i < NA; ++i)
             lds_copy16(asrc[i] + k0, sa + (NA * wave + i) * 1024);
     };
-    auto load_codes = [&](int64_t kt, uint2 &q, uint32_t &sraw) {
-        const int64_t k0 = kt * kBK;
-        q = *reinterpret_cast<const uint2 *>(crow + (k0 >> 1));
-        sraw = srow[((k0 >> 6)) * srb];
-    };
-    auto put_b = [&](char *sb, const uint2 &q, uint32_t sraw) {
+    auto put_b = [&](char *sb, u32x2 &q, uint32_t &sraw) {
+        asm volatile("" : "+v"(q), "+v"(sraw));   // loaded: the caller waited for them
         const float s = f16_to_f32(sraw);
         const uint4 v0 = dequant8_asm(q.x, s, lut_addr);
         const uint4 v1 = dequant8_asm(q.y, s, lut_addr);
@@ -1080,7 +1089,6 @@ __device__ __forceinline__ void nf4_tile(const uint16_t *__restrict__ x, const u
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
     const int half = lane >> 5, l32 = lane & 31;
-    const int64_t ktiles = k / kBK;
     uint32_t offa[2], offb[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -1109,94 +1117,96 @@ __device__ __forceinline__ void nf4_tile(const uint16_t *__restrict__ x, const u
                 : "v"(a_addr), "v"(b_addr));
         }
     };
-    auto landed = [&](frags &f) {
+    auto landed = [&](frags &f0, frags &f1) {
         if constexpr (MI == 4) {
             asm volatile("s_waitcnt lgkmcnt(0)"
-                         : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]), "+v"(f[4]), "+v"(f[5]));
+                         : "+v"(f0[0]), "+v"(f0[1]), "+v"(f0[2]), "+v"(f0[3]), "+v"(f0[4]), "+v"(f0[5]),
+                           "+v"(f1[0]), "+v"(f1[1]), "+v"(f1[2]), "+v"(f1[3]), "+v"(f1[4]), "+v"(f1[5]));
         } else {
-            asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]));
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(f0[0]), "+v"(f0[1]), "+v"(f0[2]), "+v"(f0[3]), "+v"(f1[0]), "+v"(f1[1]),
+                           "+v"(f1[2]), "+v"(f1[3]));
         }
     };
-    // The restoration of the next weight stage runs between the two quarters of the
-    // stage's first 16-k step, so its table reads and multiplies overlap the matrix
-    // pipe instead of delaying the first MFMA after the barrier.
-    // The stage's loads for k-tile kt+3 (piece 0: this thread's codes and scale; pieces
-    // 1..NA: the wave's A copies) are spread among its MFMAs rather than issued together
-    // after the barrier, where a full vector memory queue stalled the wave at issue.
-    auto compute_stage = [&](uint32_t abase, uint32_t bbase, auto &&restore0, auto &&restore1, auto &&piece) {
-        frags f0, f1;
-        issue(abase + offa[0], bbase + offb[0], f0);
-        landed(f0);
-        issue(abase + offa[1], bbase + offb[1], f1);
+    // The bf16 kernel's ping-pong: two groups of four waves (one of each per SIMD)
+    // alternate between an MFMA phase and a memory phase, the second group one
+    // barrier behind.  The memory phase of stage kt reads the stage's fragments, then
+    // restores this thread's share of weight stage kt + 1 (table reads, multiplies,
+    // conversions: VALU work that runs beside the other group's MFMAs) and waits for
+    // its LDS writes; the barrier that ends the phase publishes that share and this
+    // wave's X copy of stage kt + 1.  Weight stages need only two slots: stage kt + 1
+    // goes into the slot of stage kt - 1, which both groups finished reading before
+    // this phase began.  The MFMA phase of stage kt issues, among its MFMAs, the code
+    // and scale loads and the X copies of k-tile kt + 3 (NV = 2 + NA vector memory
+    // operations per stage); at the memory phase of stage kt only those of kt + 2 may
+    // still be in flight.
+    constexpr int NV = NA + 2;
+    auto bar = []() {
         __builtin_amdgcn_sched_barrier(0);
-        constexpr int MF = 2 * MI;   // MFMAs per 16-k step
-        constexpr int NP = NA + 1;   // load pieces
-        int q = 0;
-#pragma unroll
-        for (int t = 0; t < 2 * MF; ++t) {
-            if (t == MF) landed(f1);
-            frags &f = t < MF ? f0 : f1;
-            const int i = (t % MF) >> 1, j = t & 1;
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f[i]),
-                                                                __builtin_bit_cast(bf16x8, f[MI + j]), acc[i][j], 0, 0, 0);
-            const bool at_piece = q < NP && t + 1 == (q + 1) * 2 * MF / (NP + 1);
-            if (at_piece || t + 1 == MF / 2 || t + 1 == MF) {
-                __builtin_amdgcn_sched_barrier(0);
-                if (at_piece) piece(q++);
-                if (t + 1 == MF / 2) restore0();
-                if (t + 1 == MF) restore1();
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
     };
     auto lds_addr = [](char *p) { return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void *)p)); };
     const uint32_t A0 = lds_addr(sa0), A1 = lds_addr(sa1), A2 = lds_addr(sa2), A3 = lds_addr(sa3);
-    const uint32_t B0 = lds_addr(sb0), B1 = lds_addr(sb1), B2 = lds_addr(sb2), B3 = lds_addr(sb3);
-    uint2 q0, q1, q2, q3;
+    const uint32_t B0 = lds_addr(sb0), B1 = lds_addr(sb1);
+    u32x2 q0, q1, q2, q3;
     uint32_t r0, r1, r2, r3;
-    // step kt: wait (A(kt) and the codes of kt+1 landed), barrier, multiply stage kt with the
-    // restoration of B(kt+1) and the loads of codes(kt+3), then A(kt+3), among its MFMAs.
-    auto step = [&](int64_t kt, uint32_t acur, uint32_t bcur, char *arefill, uint2 &qload, uint32_t &rload,
-                    char *bnext, const uint2 &qnext, const uint32_t &rnext) {
-        const int64_t ahead = ktiles - 1 - kt;
-        if (ahead >= 2) wait_vmcnt<2 * NA + 2>();
-        else if (ahead == 1) wait_vmcnt<NA>();
-        else wait_vmcnt<0>();
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        const bool refill = kt + 3 < ktiles;
-        const bool more = kt + 1 < ktiles;
-        uint4 v0;
-        compute_stage(acur, bcur, [&]() {
-            if (more) v0 = dequant8_asm(qnext.x, f16_to_f32(rnext), lut_addr);
-        }, [&]() {
-            if (more) {
-                const uint4 v1 = dequant8_asm(qnext.y, f16_to_f32(rnext), lut_addr);
-                const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void *)bnext));
-                lds_store16(base + boff0, v0);
-                lds_store16(base + boff1, v1);
+    frags f0, f1;
+    auto stage = [&](int64_t kt, uint32_t acur, uint32_t bcur, char *bnext, u32x2 &qnext, uint32_t &rnext,
+                     char *arefill, u32x2 &qload, uint32_t &rload) {
+        issue(acur + offa[0], bcur + offb[0], f0);
+        issue(acur + offa[1], bcur + offb[1], f1);
+        wait_vmcnt<NV>();
+        put_b(bnext, qnext, rnext);
+        landed(f0, f1);
+        bar();
+        constexpr int MF = 2 * MI;   // MFMAs per 16-k step
+        constexpr int NP = NA + 1;   // load pieces: the codes and scale, then the X copies
+        int q = 0;
+#pragma unroll
+        for (int t = 0; t < 2 * MF; ++t) {
+            const int i = (t % MF) >> 1, j = t & 1;
+            const frags &f = t < MF ? f0 : f1;
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f[i]),
+                                                                __builtin_bit_cast(bf16x8, f[MI + j]), acc[i][j], 0, 0, 0);
+            if (q < NP && t + 1 == (q + 1) * 2 * MF / (NP + 1)) {
+                __builtin_amdgcn_sched_barrier(0);
+                if (q == 0) load_codes(kt + 3, qload, rload);
+                else lds_copy16(asrc[q - 1] + tile_k0(kt + 3), arefill + (NA * wave + q - 1) * 1024);
+                __builtin_amdgcn_sched_barrier(0);
+                ++q;
             }
-        }, [&](int q) {
-            if (!refill) return;
-            if (q == 0) load_codes(kt + 3, qload, rload);
-            else lds_copy16(asrc[q - 1] + (kt + 3) * kBK, arefill + (NA * (threadIdx.x >> 6) + q - 1) * 1024);
-        });
+        }
+        bar();
     };
+    const int group = static_cast<int>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(wave))) >> 2;
     __syncthreads();   // lut
-    // prologue: codes and A for stages 0, 1, 2; restore B(0)
-    if (0 < ktiles) { load_codes(0, q0, r0); copy_a(0, sa0); }
-    if (1 < ktiles) { load_codes(1, q1, r1); copy_a(1, sa1); }
-    if (2 < ktiles) { load_codes(2, q2, r2); copy_a(2, sa2); }
-    if (ktiles > 0) put_b(sb0, q0, r0);
+    load_codes(0, q0, r0);
+    copy_a(0, sa0);
+    load_codes(1, q1, r1);
+    copy_a(1, sa1);
+    load_codes(2, q2, r2);
+    copy_a(2, sa2);
+    wait_vmcnt<2 * NV>();
+    put_b(sb0, q0, r0);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    bar();                   // weight stage 0 and X stage 0 in LDS
+    if (group != 0) bar();   // the second group runs one phase behind
     int64_t kt = 0;
     for (; kt + 4 <= ktiles; kt += 4) {
-        step(kt + 0, A0, B0, sa3, q3, r3, sb1, q1, r1);
-        step(kt + 1, A1, B1, sa0, q0, r0, sb2, q2, r2);
-        step(kt + 2, A2, B2, sa1, q1, r1, sb3, q3, r3);
-        step(kt + 3, A3, B3, sa2, q2, r2, sb0, q0, r0);
+        stage(kt + 0, A0, B0, sb1, q1, r1, sa3, q3, r3);
+        stage(kt + 1, A1, B1, sb0, q2, r2, sa0, q0, r0);
+        stage(kt + 2, A2, B0, sb1, q3, r3, sa1, q1, r1);
+        stage(kt + 3, A3, B1, sb0, q0, r0, sa2, q2, r2);
     }
-    if (kt + 0 < ktiles) step(kt + 0, A0, B0, sa3, q3, r3, sb1, q1, r1);
-    if (kt + 1 < ktiles) step(kt + 1, A1, B1, sa0, q0, r0, sb2, q2, r2);
-    if (kt + 2 < ktiles) step(kt + 2, A2, B2, sa1, q1, r1, sb3, q3, r3);
+    if (kt + 0 < ktiles) stage(kt + 0, A0, B0, sb1, q1, r1, sa3, q3, r3);
+    if (kt + 1 < ktiles) stage(kt + 1, A1, B1, sb0, q2, r2, sa0, q0, r0);
+    if (kt + 2 < ktiles) stage(kt + 2, A2, B0, sb1, q3, r3, sa1, q1, r1);
+    if (group == 0) bar();   // both groups pass the same number of barriers
+    // The last stages' code loads (clamped, never used) may still be in flight: keep
+    // their registers allocated until they have landed.
+    wait_vmcnt<0>();
+    asm volatile("" : "+v"(q0), "+v"(q1), "+v"(q2), "+v"(q3), "+v"(r0), "+v"(r1), "+v"(r2), "+v"(r3));
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -1224,16 +1234,14 @@ __global__ __launch_bounds__(512) void gemm_nf4_tiled_kernel(const uint16_t *__r
     __shared__ __attribute__((aligned(1024))) char sa3[kHalf];
     __shared__ __attribute__((aligned(1024))) char sb0[kHalf];
     __shared__ __attribute__((aligned(1024))) char sb1[kHalf];
-    __shared__ __attribute__((aligned(1024))) char sb2[kHalf];
-    __shared__ __attribute__((aligned(1024))) char sb3[kHalf];
     __shared__ float lut[16];
     TileItem it;
     if (!tile_item(tiles_m, tiles_n, xcd_cus, it) || it.m0 >= m) return;
     write_levels(lut);
     if (it.half < 0)
-        nf4_tile<256>(x, packed, m, n_out, k, ldx, y, ofmt, ldy, it.m0, it.n0, sa0, sa1, sa2, sa3, sb0, sb1, sb2, sb3, lut);
+        nf4_tile<256>(x, packed, m, n_out, k, ldx, y, ofmt, ldy, it.m0, it.n0, sa0, sa1, sa2, sa3, sb0, sb1, lut);
     else
-        nf4_tile<128>(x, packed, m, n_out, k, ldx, y, ofmt, ldy, it.m0, it.n0, sa0, sa1, sa2, sa3, sb0, sb1, sb2, sb3, lut);
+        nf4_tile<128>(x, packed, m, n_out, k, ldx, y, ofmt, ldy, it.m0, it.n0, sa0, sa1, sa2, sa3, sb0, sb1, lut);
 }
 
 // Sum split partials in split order (fixed, so the result is deterministic).  A
