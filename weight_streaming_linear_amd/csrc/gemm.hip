@@ -972,40 +972,59 @@ __global__ __launch_bounds__(512) void gemm_bf16_x32_kernel(const uint16_t *__re
 // Thread t restores row t/2, k [16 (t % 2), +16) of the weight stage: its 8 code
 // bytes and the group's scale are loaded three stages ahead into registers, and in
 // the memory phase of stage kt the codes of stage kt + 1 are turned into
-// t = bf16(fp32(level * s)) through a 16-entry LDS table and written into one of two
-// weight slots.  Weight slots live in LDS arrays of their own, separate from the
+// t = bf16(fp32(level * s)) through the replicated pair table (64 KB, one ds_read_b64
+// per two codes, no bank conflicts; with it the kernel's LDS is exactly 160 KB) and
+// written into one of two weight slots.  Weight slots live in LDS arrays of their own, separate from the
 // arrays the copies fill, so the compiler sees that these writes cannot alias
 // copies in flight.  Each weight tile is restored once per 256 positions.
-// dequant8 with the table reads issued from inline asm (and waited for inside it): the
-// compiler then has no LDS access of its own to order against direct global -> LDS
-// copies in flight, which it would otherwise drain first.  lut_addr is the table's LDS
-// byte address.
-__device__ __forceinline__ uint4 dequant8_asm(uint32_t w, float s, uint32_t lut_addr) {
-    const uint32_t wo = rotr32(w, 4);
-    float l0, l1, l2, l3, l4, l5, l6, l7;
+// Pair-table reads of the eight codes of one stored code word (rotated left by 2 in
+// the device layout), issued from inline asm and not waited for.  a[i] holds the
+// table's 64 KB-aligned LDS address plus this lane's copy offset; the SDWA move writes
+// code byte i into its bits 8..15.  l[i] = (level(even code), level(odd code)) of
+// byte i once the wait that follows (pair_landed) has passed.
+__device__ __forceinline__ void pair_issue4(uint32_t wmem, uint32_t (&a)[4], f32x2 (&l)[4]) {
+    const uint32_t w = rotr32(wmem, 2);
+    pair_addr<0>(a[0], w);
+    pair_addr<1>(a[1], w);
+    pair_addr<2>(a[2], w);
+    pair_addr<3>(a[3], w);
     asm volatile(
-        "ds_read_b32 %0, %8\n\t"
-        "ds_read_b32 %1, %9\n\t"
-        "ds_read_b32 %2, %10\n\t"
-        "ds_read_b32 %3, %11\n\t"
-        "ds_read_b32 %4, %12\n\t"
-        "ds_read_b32 %5, %13\n\t"
-        "ds_read_b32 %6, %14\n\t"
-        "ds_read_b32 %7, %15\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(l0), "=&v"(l1), "=&v"(l2), "=&v"(l3), "=&v"(l4), "=&v"(l5), "=&v"(l6), "=&v"(l7)
-        : "v"(lut_addr + (w & 0x3cu)), "v"(lut_addr + (wo & 0x3cu)), "v"(lut_addr + ((w >> 8) & 0x3cu)),
-          "v"(lut_addr + ((wo >> 8) & 0x3cu)), "v"(lut_addr + ((w >> 16) & 0x3cu)), "v"(lut_addr + ((wo >> 16) & 0x3cu)),
-          "v"(lut_addr + ((w >> 24) & 0x3cu)), "v"(lut_addr + ((wo >> 24) & 0x3cu)));
+        "ds_read_b64 %0, %4\n\t"
+        "ds_read_b64 %1, %5\n\t"
+        "ds_read_b64 %2, %6\n\t"
+        "ds_read_b64 %3, %7"
+        : "=&v"(l[0]), "=&v"(l[1]), "=&v"(l[2]), "=&v"(l[3])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]));
+}
+
+// Wait until at most N LDS operations are outstanding (those issued after the pair
+// reads of a and b), marking the eight entries as written.
+template <int N>
+__device__ __forceinline__ void pair_landed(f32x2 (&a)[4], f32x2 (&b)[4]) {
+    static_assert(N == 0 || N == 8 || N == 12, "LDS operations issued after the pair reads");
+    if constexpr (N == 0)
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]));
+    else if constexpr (N == 12)
+        asm volatile("s_waitcnt lgkmcnt(12)"
+                     : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]));
+    else
+        asm volatile("s_waitcnt lgkmcnt(8)"
+                     : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]));
+}
+
+// bf16(fp32(level * s)) of the eight codes of a word, even k in the low half of each pair.
+__device__ __forceinline__ uint4 scale_pairs(const f32x2 (&l)[4], float s) {
     uint4 r;
-    r.x = pack_bf16x2(l0 * s, l1 * s);
-    r.y = pack_bf16x2(l2 * s, l3 * s);
-    r.z = pack_bf16x2(l4 * s, l5 * s);
-    r.w = pack_bf16x2(l6 * s, l7 * s);
+    r.x = pack_bf16x2(l[0].x * s, l[0].y * s);
+    r.y = pack_bf16x2(l[1].x * s, l[1].y * s);
+    r.z = pack_bf16x2(l[2].x * s, l[2].y * s);
+    r.w = pack_bf16x2(l[3].x * s, l[3].y * s);
     return r;
 }
 
-// 16-byte LDS store from inline asm (see dequant8_asm).
+// 16-byte LDS store from inline asm (the compiler then has no LDS access of its own to
+// order against direct global -> LDS copies in flight, which it would drain first).
 __device__ __forceinline__ void lds_store16(uint32_t addr, uint4 v) {
     const u32x4 vv = __builtin_bit_cast(u32x4, v);
     asm volatile("ds_write_b128 %0, %1" : : "v"(addr), "v"(vv));
@@ -1018,7 +1037,7 @@ template <int TM>
 __device__ __forceinline__ void nf4_tile(const uint16_t *__restrict__ x, const uint8_t *__restrict__ packed, int64_t m,
                                          int64_t n_out, int64_t k, int64_t ldx, void *__restrict__ y, int ofmt,
                                          int64_t ldy, int64_t m0, int64_t n0, char *sa0, char *sa1, char *sa2,
-                                         char *sa3, char *sb0, char *sb1, const float *lut) {
+                                         char *sa3, char *sb0, char *sb1, char *tab) {
     constexpr int MI = TM / 64;         // 32-row MFMA tiles per wave along m
     constexpr int NA = TM / 128;        // A wave-loads per wave per stage
     const int tid = threadIdx.x;
@@ -1045,7 +1064,14 @@ __device__ __forceinline__ void nf4_tile(const uint16_t *__restrict__ x, const u
     const uint16_t *srow = scales + (gn >> 4) * 16 * groups + (gn & 15);
     const uint32_t boff0 = static_cast<uint32_t>(swz(brow, 2 * bhp));
     const uint32_t boff1 = static_cast<uint32_t>(swz(brow, 2 * bhp + 1));
-    const uint32_t lut_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void *)lut));
+    // pair-table addresses: the table's base (64 KB-aligned) plus this lane's copy offset
+    uint32_t pa[4], pb[4];
+    {
+        const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void *)tab)) +
+                              (static_cast<uint32_t>(lane & 31) << 3);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pa[i] = pb[i] = base;
+    }
 
     const int64_t ktiles = k / kBK;   // even: k % 64 == 0
     // Loads for k-tiles past the end are clamped to the last one: they land in a
@@ -1072,12 +1098,14 @@ __device__ __forceinline__ void nf4_tile(const uint16_t *__restrict__ x, const u
     };
     auto put_b = [&](char *sb, u32x2 &q, uint32_t &sraw) {
         asm volatile("" : "+v"(q), "+v"(sraw));   // loaded: the caller waited for them
+        f32x2 la[4], lb[4];
+        pair_issue4(q.x, pa, la);
+        pair_issue4(q.y, pb, lb);
+        pair_landed<0>(la, lb);
         const float s = f16_to_f32(sraw);
-        const uint4 v0 = dequant8_asm(q.x, s, lut_addr);
-        const uint4 v1 = dequant8_asm(q.y, s, lut_addr);
         const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void *)sb));
-        lds_store16(base + boff0, v0);
-        lds_store16(base + boff1, v1);
+        lds_store16(base + boff0, scale_pairs(la, s));
+        lds_store16(base + boff1, scale_pairs(lb, s));
     };
 
     f32x16 acc[MI][2];
@@ -1154,10 +1182,22 @@ __device__ __forceinline__ void nf4_tile(const uint16_t *__restrict__ x, const u
     frags f0, f1;
     auto stage = [&](int64_t kt, uint32_t acur, uint32_t bcur, char *bnext, u32x2 &qnext, uint32_t &rnext,
                      char *arefill, u32x2 &qload, uint32_t &rload) {
+        // codes of stage kt + 1 landed; their pair-table reads go ahead of the fragment
+        // reads, and the multiplies and conversions run while those are in flight
+        wait_vmcnt<NV>();
+        asm volatile("" : "+v"(qnext), "+v"(rnext));
+        f32x2 la[4], lb[4];
+        pair_issue4(qnext.x, pa, la);
+        pair_issue4(qnext.y, pb, lb);
         issue(acur + offa[0], bcur + offb[0], f0);
         issue(acur + offa[1], bcur + offb[1], f1);
-        wait_vmcnt<NV>();
-        put_b(bnext, qnext, rnext);
+        pair_landed<2 * (MI + 2)>(la, lb);
+        {
+            const float sc = f16_to_f32(rnext);
+            const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void *)bnext));
+            lds_store16(base + boff0, scale_pairs(la, sc));
+            lds_store16(base + boff1, scale_pairs(lb, sc));
+        }
         landed(f0, f1);
         bar();
         constexpr int MF = 2 * MI;   // MFMAs per 16-k step
@@ -1180,7 +1220,7 @@ __device__ __forceinline__ void nf4_tile(const uint16_t *__restrict__ x, const u
         bar();
     };
     const int group = static_cast<int>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(wave))) >> 2;
-    __syncthreads();   // lut
+    __syncthreads();   // pair table
     load_codes(0, q0, r0);
     copy_a(0, sa0);
     load_codes(1, q1, r1);
@@ -1234,14 +1274,14 @@ __global__ __launch_bounds__(512) void gemm_nf4_tiled_kernel(const uint16_t *__r
     __shared__ __attribute__((aligned(1024))) char sa3[kHalf];
     __shared__ __attribute__((aligned(1024))) char sb0[kHalf];
     __shared__ __attribute__((aligned(1024))) char sb1[kHalf];
-    __shared__ float lut[16];
+    __shared__ __attribute__((aligned(65536))) char tab[kPairTableBytes];   // bits 8..15 of its address are 0
     TileItem it;
     if (!tile_item(tiles_m, tiles_n, xcd_cus, it) || it.m0 >= m) return;
-    write_levels(lut);
+    fill_pair_table(tab);
     if (it.half < 0)
-        nf4_tile<256>(x, packed, m, n_out, k, ldx, y, ofmt, ldy, it.m0, it.n0, sa0, sa1, sa2, sa3, sb0, sb1, lut);
+        nf4_tile<256>(x, packed, m, n_out, k, ldx, y, ofmt, ldy, it.m0, it.n0, sa0, sa1, sa2, sa3, sb0, sb1, tab);
     else
-        nf4_tile<128>(x, packed, m, n_out, k, ldx, y, ofmt, ldy, it.m0, it.n0, sa0, sa1, sa2, sa3, sb0, sb1, lut);
+        nf4_tile<128>(x, packed, m, n_out, k, ldx, y, ofmt, ldy, it.m0, it.n0, sa0, sa1, sa2, sa3, sb0, sb1, tab);
 }
 
 // Sum split partials in split order (fixed, so the result is deterministic).  A
