@@ -271,8 +271,8 @@ __device__ __forceinline__ void bf16_tile(const uint16_t *__restrict__ x, const 
         }
 }
 
-// Work item -> tile, XCD-aware: XCD x = blockIdx % 8 takes the contiguous tile
-// range [start(x), start(x) + count(x)) in its dispatch order blockIdx / 8.  When
+// Work item -> tile, XCD-aware: XCD x = blockIdx % nx takes the contiguous tile
+// range [start(x), start(x) + count(x)) in its dispatch order blockIdx / nx.  When
 // the XCD's last round (count mod its CU count, one workgroup per CU) would
 // leave at least half of its CUs idle, those tiles run as two 128-row halves
 // each, so that round takes about half as long.  Tiles are ordered in bands of 8
@@ -282,10 +282,10 @@ struct TileItem {
     int64_t m0, n0;
     int half;   // -1: the whole 256-row tile; 0 / 1: its first / second 128 rows
 };
-__device__ __forceinline__ bool tile_item(int tiles_m, int tiles_n, int xcd_cus, TileItem &it) {
+__device__ __forceinline__ bool tile_item(int tiles_m, int tiles_n, int nx, int xcd_cus, TileItem &it) {
     const int ntiles = tiles_m * tiles_n;
-    const int per_xcd = ntiles >> 3, rem = ntiles & 7;
-    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int per_xcd = ntiles / nx, rem = ntiles - per_xcd * nx;
+    const int xcd = static_cast<int>(blockIdx.x) % nx, slot = static_cast<int>(blockIdx.x) / nx;
     const int count = per_xcd + (xcd < rem ? 1 : 0);
     const int start = xcd * per_xcd + (xcd < rem ? xcd : rem);
     const int r = count % xcd_cus;
@@ -315,13 +315,13 @@ __device__ __forceinline__ bool tile_item(int tiles_m, int tiles_n, int xcd_cus,
 __global__ __launch_bounds__(512) void gemm_bf16_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
                                                         int64_t m, int64_t n_out, int64_t k, int64_t ldx,
                                                         void *__restrict__ y, int ofmt, int64_t ldy,
-                                                        int tiles_m, int tiles_n, int xcd_cus) {
+                                                        int tiles_m, int tiles_n, int nx, int xcd_cus) {
     __shared__ __attribute__((aligned(1024))) char st0[kStageBytes];
     __shared__ __attribute__((aligned(1024))) char st1[kStageBytes];
     __shared__ __attribute__((aligned(1024))) char st2[kStageBytes];
     __shared__ __attribute__((aligned(1024))) char st3[kStageBytes];
     TileItem it;
-    if (!tile_item(tiles_m, tiles_n, xcd_cus, it) || it.m0 >= m) return;
+    if (!tile_item(tiles_m, tiles_n, nx, xcd_cus, it) || it.m0 >= m) return;
     if (it.half < 0)
         bf16_tile<256>(x, w, m, n_out, k, ldx, y, ofmt, ldy, it.m0, it.n0, st0, st1, st2, st3);
     else
@@ -1266,7 +1266,7 @@ __device__ __forceinline__ void nf4_tile(const uint16_t *__restrict__ x, const u
 __global__ __launch_bounds__(512) void gemm_nf4_tiled_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ packed,
                                                       int64_t m, int64_t n_out, int64_t k, int64_t ldx,
                                                       void *__restrict__ y, int ofmt, int64_t ldy, int tiles_m, int tiles_n,
-                                                      int xcd_cus) {
+                                                      int nx, int xcd_cus) {
     constexpr int kHalf = kBM * kBK * 2;   // 16 KB per operand per stage
     __shared__ __attribute__((aligned(1024))) char sa0[kHalf];
     __shared__ __attribute__((aligned(1024))) char sa1[kHalf];
@@ -1276,7 +1276,7 @@ __global__ __launch_bounds__(512) void gemm_nf4_tiled_kernel(const uint16_t *__r
     __shared__ __attribute__((aligned(1024))) char sb1[kHalf];
     __shared__ __attribute__((aligned(65536))) char tab[kPairTableBytes];   // bits 8..15 of its address are 0
     TileItem it;
-    if (!tile_item(tiles_m, tiles_n, xcd_cus, it) || it.m0 >= m) return;
+    if (!tile_item(tiles_m, tiles_n, nx, xcd_cus, it) || it.m0 >= m) return;
     fill_pair_table(tab);
     if (it.half < 0)
         nf4_tile<256>(x, packed, m, n_out, k, ldx, y, ofmt, ldy, it.m0, it.n0, sa0, sa1, sa2, sa3, sb0, sb1, tab);
@@ -1443,32 +1443,40 @@ size_t gemm_ws_bytes(int wfmt, int64_t n_out, int64_t k, int64_t m) {
 
 // CUs per XCD of the current device (one workgroup of the tiled kernels per CU),
 // cached per device; 32 on MI355X (256 CUs in 8 XCDs).
-static int xcd_cus() {
+// The device's XCDs and compute units per XCD (queried once per device): workgroup b
+// is dispatched to XCD b % nx.
+struct XcdShape {
+    int nx, cus;   // XCDs; compute units per XCD
+};
+static XcdShape xcd_shape() {
     constexpr int kDevs = 64;
-    static std::atomic<int> cache[kDevs];
+    static std::atomic<int> cache[kDevs];   // nx << 16 | cus, 0 until queried
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevs) return 32;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevs) return XcdShape{8, 32};
     int v = cache[dev].load(std::memory_order_relaxed);
     if (v == 0) {
-        int cus = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8) cus = 256;
-        v = cus / 8;
+        int cus = 0, nx = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+        if (hipDeviceGetAttribute(&nx, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || nx < 1) nx = 1;
+        if (nx > 64) nx = 64;
+        const int per = cus / nx > 0 ? cus / nx : 1;
+        v = (nx << 16) | per;
         cache[dev].store(v, std::memory_order_relaxed);
     }
-    return v;
+    return XcdShape{v >> 16, v & 0xffff};
 }
 
 // Grid of the tiled kernels: 8 XCDs times the largest per-XCD item count (whole
 // tiles plus the half tiles of a short last round), as tile_item() assigns them.
-static unsigned tile_grid(int64_t ntiles, int cus) {
+static unsigned tile_grid(int64_t ntiles, const XcdShape &xs) {
     int64_t most = 0;
-    for (int x = 0; x < 8; ++x) {
-        const int64_t count = ntiles / 8 + (x < ntiles % 8 ? 1 : 0);
-        const int64_t r = count % cus;
-        const int64_t items = count + ((r > 0 && 2 * r <= cus) ? r : 0);
+    for (int x = 0; x < xs.nx; ++x) {
+        const int64_t count = ntiles / xs.nx + (x < ntiles % xs.nx ? 1 : 0);
+        const int64_t r = count % xs.cus;
+        const int64_t items = count + ((r > 0 && 2 * r <= xs.cus) ? r : 0);
         if (items > most) most = items;
     }
-    return static_cast<unsigned>(8 * most);
+    return static_cast<unsigned>(xs.nx * most);
 }
 
 int launch_gemm_bf16(const void *w, int64_t n_out, int64_t k, const void *x, int64_t m, int64_t ldx, void *y,
@@ -1478,9 +1486,9 @@ int launch_gemm_bf16(const void *w, int64_t n_out, int64_t k, const void *x, int
     if (!use_bf16_x32(n_out, k, m)) {
         const int64_t tn = (n_out + kBN - 1) / kBN, tm = (m + kBM - 1) / kBM;
         if (tn * tm > 0x7fffffff / 4) return WSL_E_SHAPE;
-        const int cus = xcd_cus();
-        hipLaunchKernelGGL(gemm_bf16_kernel, dim3(tile_grid(tm * tn, cus)), dim3(512), 0, s, xp, wp, m, n_out, k,
-                           ldx, y, ofmt, ldy, static_cast<int>(tm), static_cast<int>(tn), cus);
+        const XcdShape xs = xcd_shape();
+        hipLaunchKernelGGL(gemm_bf16_kernel, dim3(tile_grid(tm * tn, xs)), dim3(512), 0, s, xp, wp, m, n_out, k,
+                           ldx, y, ofmt, ldy, static_cast<int>(tm), static_cast<int>(tn), xs.nx, xs.cus);
         return WSL_OK;
     }
     int splits = bf16_splits(n_out, k, m);
@@ -1513,10 +1521,10 @@ int launch_gemm_nf4(const void *w, int64_t n_out, int64_t k, const void *x, int6
     if (use_tiled(n_out, k, m)) {
         const int64_t tn = (n_out + kBN - 1) / kBN, tm = (m + kBM - 1) / kBM;
         if (tn * tm > 0x7fffffff / 4) return WSL_E_SHAPE;
-        const int cus = xcd_cus();
-        hipLaunchKernelGGL(gemm_nf4_tiled_kernel, dim3(tile_grid(tm * tn, cus)), dim3(512), 0, s,
+        const XcdShape xs = xcd_shape();
+        hipLaunchKernelGGL(gemm_nf4_tiled_kernel, dim3(tile_grid(tm * tn, xs)), dim3(512), 0, s,
                            static_cast<const uint16_t *>(x), static_cast<const uint8_t *>(w), m, n_out, k, ldx, y,
-                           ofmt, ldy, static_cast<int>(tm), static_cast<int>(tn), cus);
+                           ofmt, ldy, static_cast<int>(tm), static_cast<int>(tn), xs.nx, xs.cus);
         return WSL_OK;
     }
     int splits = nf4_splits(n_out, k, m);
