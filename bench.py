@@ -639,7 +639,7 @@ def run_nf4_embed_rows(k_steps, warmup):
 
 def run_copyring_decode_sweep(k_steps, warmup, layers=48, resident_layers=29):
     """The 48-layer NF4 decode sweep with the packed matrices in page-locked host memory,
-    streamed through two device slots (linear_gemv_streamed): every layer from the host, and
+    streamed through two device slots (linear_gemv_streamed, paced): every layer from the host, and
     a split with the first `resident_layers` layers on the device (about 6/10 of the weight
     bytes, like a model that overflows the device budget).  Tokens are timed between events on
     the compute stream; the host-to-device rate of a plain 1 GiB pinned copy is the reference."""
@@ -702,7 +702,8 @@ def run_copyring_decode_sweep(k_steps, warmup, layers=48, resident_layers=29):
         ring.gemv(host[nres:], stream_xs[nres:], stream_ys[nres:])
 
     out = {"workload": "NF4 decode sweep, 48 layers of hidden 6144, packed weights in page-locked host memory, "
-                       "two device slots", "h2d_copy_gbs": round(h2d_gbs, 1), "token_bytes": token_bytes}
+                       "two device slots, host paced two matrices ahead (WSL_RING_PACE)",
+           "h2d_copy_gbs": round(h2d_gbs, 1), "token_bytes": token_bytes}
     for name, fn, host_bytes in (("all_streamed", all_streamed, token_bytes),
                                  ("split", split, sum(wsl.nf4_packed_bytes(n, k) for _, n, k in host[nres:]))):
         for _ in range(max(1, warmup // 2)):

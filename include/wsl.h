@@ -61,7 +61,8 @@ enum {
     WSL_E_LAUNCH = 6,  /* a kernel launch failed */
     WSL_E_RANGE = 7,   /* a tile or workspace lies outside its matrix or buffer */
     WSL_E_MEMORY = 8,  /* a host buffer of a streamed call is not pinned (page-locked) host memory */
-    WSL_E_SCRATCH = 9  /* linear_gemm_noalloc: the shape needs more split workspace than its scratch holds */
+    WSL_E_SCRATCH = 9, /* linear_gemm_noalloc: the shape needs more split workspace than its scratch holds */
+    WSL_E_FLAGS = 10   /* a flags argument holds a bit the call does not define */
 };
 
 /* Weight formats. */
@@ -75,6 +76,9 @@ enum { WSL_OUT_F32 = 0, WSL_OUT_BF16 = 1 };
 #define WSL_STATUS_INDEX     4u   /* nf4_embed_rows: a requested row index was outside the matrix */
 #define WSL_STATUS_SWEEP_TIMEOUT 8u   /* linear_gemv_sweep: a stage barrier waited past its bound */
 #define WSL_STATUS_DESCRIPTOR    16u  /* linear_gemv_sweep: a device stage descriptor was invalid (skipped) */
+
+/* Flags of linear_gemv_streamed / linear_gemm_streamed. */
+#define WSL_RING_PACE 1   /* the host keeps the copies at most two matrices ahead of the kernels */
 
 /*
  * nf4_packed_bytes -- size in bytes of one packed NF4 matrix.
@@ -278,13 +282,21 @@ int nf4_embed_rows(const void *d_packed, int64_t n_rows, int64_t k, const int64_
  *   budget keeps selected packed matrices in pinned host memory and passes them
  *   through two reusable device slots to the same kernels; the 32B model of the
  *   results keeps 9.5 GiB resident and 6.7 GiB in pinned host memory.)
- * For matrix i (slot s = i % 2) the call enqueues, without waiting:
+ * For matrix i (slot s = i % 2) the call enqueues:
  *   copy_stream:    wait events[2 + s]; copy h_w[i] -> d_slot[s]; record events[s];
  *   compute_stream: wait events[s]; linear_gemv / linear_gemm on d_slot[s];
  *                   record events[2 + s].
  * So the copy of matrix i + 1 runs while matrix i is multiplied, and a slot is
  * overwritten only after the kernel that read it finished (also across calls,
- * since the events carry over).
+ * since the events carry over).  Without WSL_RING_PACE the call enqueues everything
+ * without waiting (it may be captured in a graph).  With it, before enqueueing the copy
+ * of matrix i >= 2 the host waits for events[2 + s] -- the kernel of matrix i - 2, which
+ * that copy waits for on the device anyway -- so the call returns once the kernel of
+ * matrix count - 3 has finished.  The pacing is for long streams: when hundreds of copies
+ * that each wait on a kernel of another stream are enqueued ahead, the HIP runtime can
+ * hold the host inside a copy's enqueue for milliseconds, long enough for the copy engine
+ * to run out of queued copies; kept two matrices ahead, the ring stays within a few
+ * percent of the rate of plain back-to-back copies.
  * wfmt          WSL_W_NF4 or WSL_W_BF16, the format of every h_w[i].
  * count         number of matrices (>= 0; 0 enqueues nothing).
  * h_w           host array of count pointers to page-locked host buffers (allocated
@@ -301,16 +313,18 @@ int nf4_embed_rows(const void *d_packed, int64_t n_rows, int64_t k, const int64_
  * copy_stream, compute_stream   hipStream_t (NULL = default stream); inputs and
  *               outputs are ordered on compute_stream.
  * events        host array of 4 hipEvent_t created by the caller.
+ * flags         0 or WSL_RING_PACE (other bits: WSL_E_FLAGS).
  * Every argument is validated before anything is enqueued; a HIP error while
- * enqueuing returns WSL_E_LAUNCH (earlier matrices may already be enqueued).
+ * enqueuing (or waiting, with WSL_RING_PACE) returns WSL_E_LAUNCH (earlier matrices
+ * may already be enqueued).
  */
 int linear_gemv_streamed(int wfmt, int64_t count, const void *const *h_w, const int64_t *n_out, const int64_t *k,
                          const void *const *d_x, float *const *d_y, void *const *d_slot, size_t slot_bytes,
-                         void *copy_stream, void *compute_stream, void *const *events);
+                         void *copy_stream, void *compute_stream, void *const *events, int flags);
 int linear_gemm_streamed(int wfmt, int64_t count, const void *const *h_w, const int64_t *n_out, const int64_t *k,
                          const void *const *d_x, int64_t m, int64_t ldx, void *const *d_y, int ofmt, int64_t ldy,
                          void *d_ws, size_t ws_bytes, void *const *d_slot, size_t slot_bytes,
-                         void *copy_stream, void *compute_stream, void *const *events);
+                         void *copy_stream, void *compute_stream, void *const *events, int flags);
 
 /*
  * wsl_stream_read -- measurement aid, not part of the linear path: a read-only

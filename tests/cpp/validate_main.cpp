@@ -16,7 +16,7 @@ static int fails = 0;
     } while (0)
 
 int main() {
-    alignas(16) static char buf[256];
+    alignas(256) static char buf[256];   // the strictest alignment any check asks for (the sweep workspace: 128)
     void *p = buf;
     void *odd = buf + 2;
     EXPECT(wsl::nf4_bytes(4096, 4096) == 8912896u);
@@ -68,18 +68,24 @@ int main() {
         const void *slots[2] = {p, p};
         const void *evs[4] = {p, p, p, p};
         const int64_t ns[2] = {4, 8}, ks[2] = {64, 128};
-        EXPECT(wsl::check_ring(WSL_W_NF4, 2, hw, ns, ks, xs, -1, 0, ys, 0, 0, nullptr, 0, slots, 1024, evs) == WSL_OK);
-        EXPECT(wsl::check_ring(WSL_W_NF4, 2, hw, ns, ks, xs, -1, 0, ys, 0, 0, nullptr, 0, slots, 543, evs) == WSL_E_RANGE);
-        EXPECT(wsl::check_ring(WSL_W_BF16, 2, hw, ns, ks, xs, -1, 0, ys, 0, 0, nullptr, 0, slots, 1024, evs) == WSL_E_RANGE);
-        EXPECT(wsl::check_ring(WSL_W_BF16, 2, hw, ns, ks, xs, -1, 0, ys, 0, 0, nullptr, 0, slots, 2048, evs) == WSL_OK);
-        EXPECT(wsl::check_ring(WSL_W_NF4, 2, hw, ns, ks, xs, 3, 128, ys, WSL_OUT_F32, 8, nullptr, 0, slots, 1024, evs) == WSL_OK);
-        EXPECT(wsl::check_ring(WSL_W_NF4, 2, hw, ns, ks, xs, 3, 64, ys, WSL_OUT_F32, 8, nullptr, 0, slots, 1024, evs) == WSL_E_SHAPE);
+        EXPECT(wsl::check_ring(WSL_W_NF4, 2, hw, ns, ks, xs, -1, 0, ys, 0, 0, nullptr, 0, slots, 1024, evs, 0) == WSL_OK);
+        EXPECT(wsl::check_ring(WSL_W_NF4, 2, hw, ns, ks, xs, -1, 0, ys, 0, 0, nullptr, 0, slots, 543, evs, 0) == WSL_E_RANGE);
+        EXPECT(wsl::check_ring(WSL_W_BF16, 2, hw, ns, ks, xs, -1, 0, ys, 0, 0, nullptr, 0, slots, 1024, evs, 0) == WSL_E_RANGE);
+        EXPECT(wsl::check_ring(WSL_W_BF16, 2, hw, ns, ks, xs, -1, 0, ys, 0, 0, nullptr, 0, slots, 2048, evs, 0) == WSL_OK);
+        EXPECT(wsl::check_ring(WSL_W_NF4, 2, hw, ns, ks, xs, 3, 128, ys, WSL_OUT_F32, 8, nullptr, 0, slots, 1024, evs, 0) == WSL_OK);
+        EXPECT(wsl::check_ring(WSL_W_NF4, 2, hw, ns, ks, xs, 3, 64, ys, WSL_OUT_F32, 8, nullptr, 0, slots, 1024, evs, 0) == WSL_E_SHAPE);
         const void *badslots[2] = {p, odd};
-        EXPECT(wsl::check_ring(WSL_W_NF4, 2, hw, ns, ks, xs, -1, 0, ys, 0, 0, nullptr, 0, badslots, 1024, evs) == WSL_E_ALIGN);
+        EXPECT(wsl::check_ring(WSL_W_NF4, 2, hw, ns, ks, xs, -1, 0, ys, 0, 0, nullptr, 0, badslots, 1024, evs, 0) == WSL_E_ALIGN);
         const void *hw0[2] = {p, nullptr};
-        EXPECT(wsl::check_ring(WSL_W_NF4, 2, hw0, ns, ks, xs, -1, 0, ys, 0, 0, nullptr, 0, slots, 1024, evs) == WSL_E_NULL);
+        EXPECT(wsl::check_ring(WSL_W_NF4, 2, hw0, ns, ks, xs, -1, 0, ys, 0, 0, nullptr, 0, slots, 1024, evs, 0) == WSL_E_NULL);
         EXPECT(wsl::check_ring(WSL_W_NF4, 0, nullptr, nullptr, nullptr, nullptr, -1, 0, nullptr, 0, 0, nullptr, 0,
-                               nullptr, 0, nullptr) == WSL_OK);
+                               nullptr, 0, nullptr, 0) == WSL_OK);
+        EXPECT(wsl::check_ring(WSL_W_NF4, 2, hw, ns, ks, xs, -1, 0, ys, 0, 0, nullptr, 0, slots, 1024, evs,
+                               WSL_RING_PACE) == WSL_OK);
+        EXPECT(wsl::check_ring(WSL_W_NF4, 2, hw, ns, ks, xs, -1, 0, ys, 0, 0, nullptr, 0, slots, 1024, evs, 2) ==
+               WSL_E_FLAGS);
+        EXPECT(wsl::check_ring(WSL_W_NF4, 0, nullptr, nullptr, nullptr, nullptr, -1, 0, nullptr, 0, 0, nullptr, 0,
+                               nullptr, 0, nullptr, -1) == WSL_E_FLAGS);
     }
     {
         // decode sweep: host descriptors, device descriptor array and workspace

@@ -83,18 +83,23 @@ def test_argument_errors_return_before_any_launch():
     two = (ctypes.c_void_p * 2)(4096, 8192)
     four = (ctypes.c_void_p * 4)(1, 2, 3, 4)
     shp = (ctypes.c_int64 * 1)(64)
-    assert L.linear_gemv_streamed(wsl.WSL_W_NF4, 0, None, None, None, None, None, None, 0, None, None, None) == 0
-    assert L.linear_gemv_streamed(wsl.WSL_W_NF4, -1, one, shp, shp, one, one, two, 4096, None, None, four) == 2
-    assert L.linear_gemv_streamed(9, 1, one, shp, shp, one, one, two, 4096, None, None, four) == 4
-    assert L.linear_gemv_streamed(wsl.WSL_W_NF4, 1, one, shp, shp, one, one, two, 4096, None, None, None) == 1
-    assert L.linear_gemv_streamed(wsl.WSL_W_NF4, 1, one, shp, shp, one, one, two, 100, None, None, four) == 7
+    assert L.linear_gemv_streamed(wsl.WSL_W_NF4, 0, None, None, None, None, None, None, 0, None, None, None, 0) == 0
+    assert L.linear_gemv_streamed(wsl.WSL_W_NF4, -1, one, shp, shp, one, one, two, 4096, None, None, four, 0) == 2
+    assert L.linear_gemv_streamed(9, 1, one, shp, shp, one, one, two, 4096, None, None, four, 0) == 4
+    assert L.linear_gemv_streamed(wsl.WSL_W_NF4, 1, one, shp, shp, one, one, two, 4096, None, None, None, 1) == 1
+    assert L.linear_gemv_streamed(wsl.WSL_W_NF4, 1, one, shp, shp, one, one, two, 100, None, None, four, 1) == 7
+    assert L.linear_gemv_streamed(wsl.WSL_W_NF4, 1, one, shp, shp, one, one, two, 4096, None, None, four, 2) == 10
+    assert L.linear_gemv_streamed(wsl.WSL_W_NF4, 0, None, None, None, None, None, None, 0, None, None, None, -1) == 10
     assert L.linear_gemm_streamed(wsl.WSL_W_NF4, 1, one, shp, shp, one, 0, 64, one, 0, 64, None, 0, two, 4096,
-                                  None, None, four) == 2
+                                  None, None, four, 0) == 2
+    assert L.linear_gemm_streamed(wsl.WSL_W_NF4, 1, one, shp, shp, one, 1, 64, one, 0, 64, None, 0, two, 4096,
+                                  None, None, four, 4) == 10
     assert L.wsl_stream_read(a, 0, None, None) == 0
     assert L.wsl_stream_read(None, 16, a, None) == 1
     assert L.wsl_stream_read(a, 24, a, None) == 2
     assert L.wsl_stream_read(odd, 16, a, None) == 3
     assert wsl.wsl_strerror(7).startswith("tile")
+    assert "flags" in wsl.wsl_strerror(wsl.WSL_E_FLAGS)
     assert L.nf4_codebook(None) == 1
 
 

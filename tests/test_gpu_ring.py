@@ -39,10 +39,11 @@ def _gemv_ref(wfmt, wb, xb):
     return oracle.gemv_ref(f64(wb), f64(xb))
 
 
+@pytest.mark.parametrize("pace", [True, False])
 @pytest.mark.parametrize("wfmt", [wsl.WSL_W_NF4, wsl.WSL_W_BF16])
-def test_gemv_streamed_against_oracle(wfmt):
+def test_gemv_streamed_against_oracle(wfmt, pace):
     import torch
-    say(f"ring gemv wfmt={wfmt}")
+    say(f"ring gemv wfmt={wfmt} pace={pace}")
     mats, dev, bits, nbytes = _stack(wfmt)
     xbs = [synth.act_bits(105, 100 + i, (k,)) for i, (_, k) in enumerate(SHAPES)]
     xs = [to_dev_bf16(b) for b in xbs]
@@ -51,7 +52,7 @@ def test_gemv_streamed_against_oracle(wfmt):
     ring = wsl.CopyRing(nbytes)
     for rep in range(3):               # the slots and events carry over between calls
         ys = [torch.full((n,), float("nan"), dtype=torch.float32, device="cuda") for n, _ in SHAPES]
-        ring.gemv(mats, xs, ys, wfmt=wfmt)
+        ring.gemv(mats, xs, ys, wfmt=wfmt, pace=pace)
         torch.cuda.synchronize()
         for i, (y, w, (y_ref, s_ref)) in enumerate(zip(ys, want, refs)):
             ok, worst, r = oracle.check_rows_f32(y.cpu().numpy(), y_ref, s_ref)
@@ -112,7 +113,7 @@ def test_streamed_rejects_pageable_host_memory():
         rc = ring_call(wsl.WSL_W_NF4, 1, hs, (ctypes.c_int64 * 1)(n), (ctypes.c_int64 * 1)(k),
                        wsl._ptr_array([x]), wsl._ptr_array([y]), wsl._ptr_array(ring.slots), ring.slot_bytes,
                        ctypes.c_void_p(ring.copy_stream.cuda_stream), wsl._stream(None),
-                       wsl._ptr_array([ev.cuda_event for ev in ring.events]))
+                       wsl._ptr_array([ev.cuda_event for ev in ring.events]), 0)
         wsl._check(rc, "linear_gemv_streamed")
     assert e.value.code == 8
     # the refused call left no pending error behind: a normal call still works

@@ -39,6 +39,8 @@ WSL_STATUS_SWEEP_TIMEOUT = 8
 WSL_STATUS_DESCRIPTOR = 16
 SWEEP_STATUS_OFFSET = 1280      # byte offset of the status word in the sweep workspace
 WSL_E_SCRATCH = 9
+WSL_E_FLAGS = 10
+WSL_RING_PACE = 1               # linear_*_streamed: the host keeps the copies two matrices ahead
 NOALLOC_SCRATCH_BYTES = 4 << 20
 
 
@@ -83,10 +85,10 @@ def lib():
     L.linear_gemm_noalloc.restype = ctypes.c_int
     L.nf4_embed_rows.argtypes = [vp, i64, i64, vp, i64, vp, ctypes.c_int, i64, vp, vp]
     L.nf4_embed_rows.restype = ctypes.c_int
-    L.linear_gemv_streamed.argtypes = [ctypes.c_int, i64, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
+    L.linear_gemv_streamed.argtypes = [ctypes.c_int, i64, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp, ctypes.c_int]
     L.linear_gemv_streamed.restype = ctypes.c_int
     L.linear_gemm_streamed.argtypes = [ctypes.c_int, i64, vp, vp, vp, vp, i64, i64, vp, ctypes.c_int, i64, vp, sz, vp,
-                                       sz, vp, vp, vp]
+                                       sz, vp, vp, vp, ctypes.c_int]
     L.linear_gemm_streamed.restype = ctypes.c_int
     L.wsl_stream_read.argtypes = [vp, sz, vp, vp]
     L.wsl_stream_read.restype = ctypes.c_int
@@ -373,7 +375,9 @@ class CopyRing:
 
     Matrices stay in page-locked host memory (see to_pinned); each call copies them one
     by one into the slots on the ring's copy stream while the kernels run on the compute
-    stream (torch's current stream unless given)."""
+    stream (torch's current stream unless given).  pace=True (WSL_RING_PACE) keeps the
+    host at most two matrices ahead of the kernels, so a call returns shortly before its
+    last kernels finish; pace=False enqueues everything without waiting (capturable)."""
 
     def __init__(self, slot_bytes, device="cuda"):
         import torch
@@ -401,17 +405,18 @@ class CopyRing:
         evs = _ptr_array([e.cuda_event for e in self.events])
         return hs, ns, ks, slots, evs
 
-    def gemv(self, mats, xs, ys, wfmt=WSL_W_NF4, stream=None):
+    def gemv(self, mats, xs, ys, wfmt=WSL_W_NF4, stream=None, pace=True):
         """mats: [(pinned host tensor, n_out, k)]; xs: bf16 [k] device tensors; ys: fp32 [n_out]."""
         import torch
         hs, ns, ks, slots, evs = self._common(mats, xs, ys, torch.bfloat16, (torch.float32,))
         rc = lib().linear_gemv_streamed(int(wfmt), len(mats), hs, ns, ks, _ptr_array(xs), _ptr_array(ys), slots,
                                         self.slot_bytes, ctypes.c_void_p(self.copy_stream.cuda_stream),
-                                        _stream(stream), evs)
+                                        _stream(stream), evs, WSL_RING_PACE if pace else 0)
         _check(rc, "linear_gemv_streamed")
         return ys
 
-    def gemm(self, mats, xs, ys, m, ldx, ldy, wfmt=WSL_W_NF4, ofmt=WSL_OUT_F32, workspace=None, stream=None):
+    def gemm(self, mats, xs, ys, m, ldx, ldy, wfmt=WSL_W_NF4, ofmt=WSL_OUT_F32, workspace=None, stream=None,
+             pace=True):
         import torch
         ydt = torch.float32 if ofmt == WSL_OUT_F32 else torch.bfloat16
         hs, ns, ks, slots, evs = self._common(mats, xs, ys, torch.bfloat16, (ydt,))
@@ -419,7 +424,7 @@ class CopyRing:
         rc = lib().linear_gemm_streamed(int(wfmt), len(mats), hs, ns, ks, _ptr_array(xs), int(m), int(ldx),
                                         _ptr_array(ys), int(ofmt), int(ldy), _ptr(workspace), nb, slots,
                                         self.slot_bytes, ctypes.c_void_p(self.copy_stream.cuda_stream),
-                                        _stream(stream), evs)
+                                        _stream(stream), evs, WSL_RING_PACE if pace else 0)
         _check(rc, "linear_gemm_streamed")
         return ys
 

@@ -24,10 +24,11 @@ int launch_gemm_noalloc(int wfmt, const void *w, int64_t n_out, int64_t k, const
 int check_pinned(int64_t count, const void *const *h_w);
 int ring_gemv(int wfmt, int64_t count, const void *const *h_w, const int64_t *n_out, const int64_t *k,
               const void *const *x, float *const *y, void *const *slot, hipStream_t copy, hipStream_t compute,
-              void *const *events);
+              void *const *events, int flags);
 int ring_gemm(int wfmt, int64_t count, const void *const *h_w, const int64_t *n_out, const int64_t *k,
               const void *const *x, int64_t m, int64_t ldx, void *const *y, int ofmt, int64_t ldy, void *ws,
-              size_t ws_bytes, void *const *slot, hipStream_t copy, hipStream_t compute, void *const *events);
+              size_t ws_bytes, void *const *slot, hipStream_t copy, hipStream_t compute, void *const *events,
+              int flags);
 int launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t s);
 int launch_embed_rows(const void *packed, int64_t n_rows, int64_t k, const int64_t *ids, int64_t count, void *out,
                       int ofmt, int64_t ld_out, uint32_t *status, hipStream_t s);
@@ -147,28 +148,28 @@ int nf4_embed_rows(const void *d_packed, int64_t n_rows, int64_t k, const int64_
 
 int linear_gemv_streamed(int wfmt, int64_t count, const void *const *h_w, const int64_t *n_out, const int64_t *k,
                          const void *const *d_x, float *const *d_y, void *const *d_slot, size_t slot_bytes,
-                         void *copy_stream, void *compute_stream, void *const *events) {
+                         void *copy_stream, void *compute_stream, void *const *events, int flags) {
     int rc = wsl::check_ring(wfmt, count, h_w, n_out, k, d_x, -1, 0, reinterpret_cast<const void *const *>(d_y), 0,
-                             0, nullptr, 0, d_slot, slot_bytes, events);
+                             0, nullptr, 0, d_slot, slot_bytes, events, flags);
     if (rc != WSL_OK || count == 0) return rc;
     if ((rc = wsl::device_ok()) != WSL_OK) return rc;
     if ((rc = wsl::check_pinned(count, h_w)) != WSL_OK) return rc;
     return wsl::ring_gemv(wfmt, count, h_w, n_out, k, d_x, d_y, d_slot, wsl::as_stream(copy_stream),
-                          wsl::as_stream(compute_stream), events);
+                          wsl::as_stream(compute_stream), events, flags);
 }
 
 int linear_gemm_streamed(int wfmt, int64_t count, const void *const *h_w, const int64_t *n_out, const int64_t *k,
                          const void *const *d_x, int64_t m, int64_t ldx, void *const *d_y, int ofmt, int64_t ldy,
                          void *d_ws, size_t ws_bytes, void *const *d_slot, size_t slot_bytes,
-                         void *copy_stream, void *compute_stream, void *const *events) {
+                         void *copy_stream, void *compute_stream, void *const *events, int flags) {
     int rc = wsl::check_ring(wfmt, count, h_w, n_out, k, d_x, m < 0 ? 0 : m, ldx,
                              reinterpret_cast<const void *const *>(d_y), ofmt, ldy, d_ws, ws_bytes, d_slot,
-                             slot_bytes, events);
+                             slot_bytes, events, flags);
     if (rc != WSL_OK || count == 0) return rc;
     if ((rc = wsl::device_ok()) != WSL_OK) return rc;
     if ((rc = wsl::check_pinned(count, h_w)) != WSL_OK) return rc;
     return wsl::ring_gemm(wfmt, count, h_w, n_out, k, d_x, m, ldx, d_y, ofmt, ldy, d_ws, ws_bytes, d_slot,
-                          wsl::as_stream(copy_stream), wsl::as_stream(compute_stream), events);
+                          wsl::as_stream(copy_stream), wsl::as_stream(compute_stream), events, flags);
 }
 
 int wsl_stream_read(const void *d_buf, size_t bytes, uint32_t *d_sink, void *stream) {
@@ -196,6 +197,7 @@ const char *wsl_strerror(int code) {
         case WSL_E_SCRATCH:
             return "linear_gemm_noalloc: the shape's split workspace exceeds WSL_NOALLOC_SCRATCH_BYTES "
                    "(use linear_gemm with a caller workspace)";
+        case WSL_E_FLAGS: return "a flags argument holds a bit the call does not define";
         default: return "unknown status code";
     }
 }

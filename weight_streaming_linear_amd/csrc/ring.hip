@@ -5,7 +5,7 @@
 // through two reusable device slots to the same kernels that serve resident
 // matrices.  Host code only: asynchronous copies on one stream, the kernels on
 // another, and four caller-owned events that hand each slot back and forth.
-// Nothing is allocated and nothing waits on the host.
+// Nothing is allocated; the host waits only when the caller asks for pacing.
 #include "device_common.h"
 
 namespace wsl {
@@ -33,15 +33,21 @@ int check_pinned(int64_t count, const void *const *h_w) {
 }
 
 // Enqueue the ring for count matrices; launch(i, slot, stream) enqueues the kernel of matrix i.
+// pace: before enqueueing the copy of matrix i >= 2, wait on the host for the kernel of
+// matrix i - 2 (the event that copy waits for on the device anyway).  Enqueued far ahead,
+// copies that wait on another stream's kernels can be held up inside the runtime for
+// milliseconds at a time, while the copy engine runs out of queued work.
 template <typename Launch>
 int run_ring(int wfmt, int64_t count, const void *const *h_w, const int64_t *n_out, const int64_t *k,
-             void *const *slot, hipStream_t copy, hipStream_t compute, void *const *events, Launch launch) {
+             void *const *slot, hipStream_t copy, hipStream_t compute, void *const *events, bool pace,
+             Launch launch) {
     hipEvent_t filled[2] = {static_cast<hipEvent_t>(events[0]), static_cast<hipEvent_t>(events[1])};
     hipEvent_t freed[2] = {static_cast<hipEvent_t>(events[2]), static_cast<hipEvent_t>(events[3])};
     for (int64_t i = 0; i < count; ++i) {
         const int s = static_cast<int>(i & 1);
         const size_t bytes = wfmt == WSL_W_NF4 ? nf4_packed_bytes(n_out[i], k[i])
                                                : static_cast<size_t>(n_out[i]) * static_cast<size_t>(k[i]) * 2;
+        if (pace && i >= 2 && hipEventSynchronize(freed[s]) != hipSuccess) return WSL_E_LAUNCH;
         if (hipStreamWaitEvent(copy, freed[s], 0) != hipSuccess) return WSL_E_LAUNCH;
         if (hipMemcpyAsync(slot[s], h_w[i], bytes, hipMemcpyHostToDevice, copy) != hipSuccess) return WSL_E_LAUNCH;
         if (hipEventRecord(filled[s], copy) != hipSuccess) return WSL_E_LAUNCH;
@@ -56,8 +62,8 @@ int run_ring(int wfmt, int64_t count, const void *const *h_w, const int64_t *n_o
 
 int ring_gemv(int wfmt, int64_t count, const void *const *h_w, const int64_t *n_out, const int64_t *k,
               const void *const *x, float *const *y, void *const *slot, hipStream_t copy, hipStream_t compute,
-              void *const *events) {
-    return run_ring(wfmt, count, h_w, n_out, k, slot, copy, compute, events,
+              void *const *events, int flags) {
+    return run_ring(wfmt, count, h_w, n_out, k, slot, copy, compute, events, (flags & WSL_RING_PACE) != 0,
                     [&](int64_t i, void *w, hipStream_t s) {
                         return wfmt == WSL_W_NF4 ? launch_gemv_nf4(w, n_out[i], k[i], x[i], y[i], s)
                                                  : launch_gemv_bf16(w, n_out[i], k[i], x[i], y[i], s);
@@ -66,8 +72,9 @@ int ring_gemv(int wfmt, int64_t count, const void *const *h_w, const int64_t *n_
 
 int ring_gemm(int wfmt, int64_t count, const void *const *h_w, const int64_t *n_out, const int64_t *k,
               const void *const *x, int64_t m, int64_t ldx, void *const *y, int ofmt, int64_t ldy, void *ws,
-              size_t ws_bytes, void *const *slot, hipStream_t copy, hipStream_t compute, void *const *events) {
-    return run_ring(wfmt, count, h_w, n_out, k, slot, copy, compute, events,
+              size_t ws_bytes, void *const *slot, hipStream_t copy, hipStream_t compute, void *const *events,
+              int flags) {
+    return run_ring(wfmt, count, h_w, n_out, k, slot, copy, compute, events, (flags & WSL_RING_PACE) != 0,
                     [&](int64_t i, void *w, hipStream_t s) {
                         return wfmt == WSL_W_NF4
                                    ? launch_gemm_nf4(w, n_out[i], k[i], x[i], m, ldx, y[i], ofmt, ldy, ws, ws_bytes, s)

@@ -84,8 +84,10 @@ int check_gemm(int wfmt, const void *w, int64_t n_out, int64_t k, const void *x,
 
 int check_ring(int wfmt, int64_t count, const void *const *h_w, const int64_t *n_out, const int64_t *k,
                const void *const *x, int64_t m, int64_t ldx, const void *const *y, int ofmt, int64_t ldy,
-               const void *ws, size_t ws_bytes, const void *const *slot, size_t slot_bytes, const void *const *events) {
+               const void *ws, size_t ws_bytes, const void *const *slot, size_t slot_bytes, const void *const *events,
+               int flags) {
     if (wfmt != WSL_W_BF16 && wfmt != WSL_W_NF4) return WSL_E_FORMAT;
+    if (flags & ~WSL_RING_PACE) return WSL_E_FLAGS;
     if (count < 0 || count > kMaxDim) return WSL_E_SHAPE;
     if (count == 0) return WSL_OK;
     if (!h_w || !n_out || !k || !x || !y || !slot || !events) return WSL_E_NULL;

@@ -23,12 +23,13 @@ int check_dequant_tile(const void *packed, int64_t n_out, int64_t k, int64_t row
 int check_gemv(int wfmt, const void *w, int64_t n_out, int64_t k, const void *x, const void *y);
 int check_gemm(int wfmt, const void *w, int64_t n_out, int64_t k, const void *x, int64_t m,
                int64_t ldx, const void *y, int ofmt, int64_t ldy, const void *ws, size_t ws_bytes);
-// Copy-ring arguments: the arrays, the slots, the events, and for each matrix
+// Copy-ring arguments: the flags, the arrays, the slots, the events, and for each matrix
 // check_gemv / check_gemm with the slot as the weight pointer plus the slot size.
 // m < 0 selects the GEMV checks.
 int check_ring(int wfmt, int64_t count, const void *const *h_w, const int64_t *n_out, const int64_t *k,
                const void *const *x, int64_t m, int64_t ldx, const void *const *y, int ofmt, int64_t ldy,
-               const void *ws, size_t ws_bytes, const void *const *slot, size_t slot_bytes, const void *const *events);
+               const void *ws, size_t ws_bytes, const void *const *slot, size_t slot_bytes, const void *const *events,
+               int flags);
 // Decode sweep: count in [0, 2^24], the host descriptors (each as check_gemv for NF4,
 // plus k <= 32768), the device descriptor array and the workspace.
 int check_sweep(int wfmt, int64_t count, const void *h_stages, const void *d_stages, const void *ws,
