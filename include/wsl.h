@@ -204,8 +204,10 @@ int linear_gemv_sweep(int wfmt, int64_t count, const wsl_gemv_stage *h_stages,
 
 /*
  * linear_gemm_workspace_bytes -- workspace linear_gemm can use for a shape
- * (0 if it would not split the reduction).  Passing a smaller (or NULL)
- * workspace is legal and only selects a path with less parallelism.
+ * (0 if it would not split the reduction): splits * m * n_out * 4 bytes of fp32
+ * partials, for a k split of the shared-X kernels or of the 256 x 256 tiles
+ * (a launch whose tiles would leave most compute units idle).  Passing a smaller
+ * (or NULL) workspace is legal and only selects a path with less parallelism.
  */
 size_t linear_gemm_workspace_bytes(int wfmt, int64_t n_out, int64_t k, int64_t m);
 
@@ -233,16 +235,18 @@ int linear_gemm(int wfmt, const void *d_w, int64_t n_out, int64_t k,
 /*
  * linear_gemm_noalloc -- linear_gemm for callers that cannot allocate device memory:
  * code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
- * Same arguments, kernels and results (bit for bit) as linear_gemm given a workspace of
- * linear_gemm_workspace_bytes(); instead of a caller workspace, the split-reduction
- * partials go to a scratch array of WSL_NOALLOC_SCRATCH_BYTES that the library holds in
- * device memory of every GPU it runs on, from the first call on that GPU until the process
- * ends.  The call itself allocates nothing: on its first call on a device it looks up that
- * device's copy of the array (hipGetSymbolAddress), afterwards it only enqueues kernels.
- * Returns WSL_E_SCRATCH, launching nothing, for a shape whose split workspace
- * (linear_gemm_workspace_bytes) exceeds WSL_NOALLOC_SCRATCH_BYTES (4 MiB: enough for
- * every shape at up to 32 positions with k % 256 == 0, the prefill width; more positions
- * or other k may need more); linear_gemm with a caller workspace serves those.  Every call on one GPU shares that GPU's scratch: calls
+ * Same arguments and kernels as linear_gemm; instead of a caller workspace, the
+ * split-reduction partials go to a scratch array of WSL_NOALLOC_SCRATCH_BYTES that the
+ * library holds in device memory of every GPU it runs on, from the first call on that GPU
+ * until the process ends.  The call itself allocates nothing: on its first call on a device
+ * it looks up that device's copy of the array (hipGetSymbolAddress), afterwards it only
+ * enqueues kernels.  When the shape's split workspace (linear_gemm_workspace_bytes) fits in
+ * the scratch, the results are bit for bit those of linear_gemm given that workspace.
+ * Beyond it, a shape that runs on the 256 x 256 tiles runs them without a k split (bit for
+ * bit linear_gemm without a workspace), and any other shape returns WSL_E_SCRATCH,
+ * launching nothing (4 MiB is enough for every shape at up to 32 positions with
+ * k % 256 == 0, the prefill width); linear_gemm with a caller workspace serves those.
+ * Every call on one GPU shares that GPU's scratch: calls
  * that overlap on one device (different streams, or different host threads without
  * ordering) race and may return wrong results; calls ordered on one stream do not.
  */

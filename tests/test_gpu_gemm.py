@@ -355,6 +355,61 @@ def test_gemm_nf4_tiled_mid_m(m, n_out, k, ofmt):
     assert ok, f"elem {i}: worst ratio {worst}"
 
 
+# A k split of the tiled kernels: a launch whose 256 x 256 tiles would leave most CUs idle
+# runs one work item per (tile, k range), the fp32 partials summed in split order (the
+# workspace size names the split: a multiple of M * N * 4 bytes).  Ragged M and N, a last k
+# range shorter than the others; the same call without a workspace runs unsplit.  bf16:
+# every element against the oracle; NF4: all rows, sampled columns with the tile edges.
+@pytest.mark.parametrize("wfmt,m,n_out,k", [(wsl.WSL_W_BF16, 513, 777, 12288), (wsl.WSL_W_BF16, 257, 3000, 7680),
+                                            (wsl.WSL_W_NF4, 1000, 2100, 8192), (wsl.WSL_W_NF4, 513, 4100, 12288)])
+@pytest.mark.parametrize("ofmt", [wsl.WSL_OUT_F32, wsl.WSL_OUT_BF16])
+def test_gemm_tiled_k_split(wfmt, m, n_out, k, ofmt):
+    import torch
+    say(f"gemm tiled k split wfmt={wfmt} m={m} n={n_out} k={k} ofmt={ofmt}")
+    nb = wsl.linear_gemm_workspace_bytes(wfmt, n_out, k, m)
+    assert nb > 0 and nb % (m * n_out * 4) == 0 and nb // (m * n_out * 4) >= 2, nb
+    wb = synth.weight_bits(111, n_out, n_out, k)
+    xb = synth.act_bits(111, 1000 + m, (m, k))
+    w = wsl.nf4_pack(to_dev_bf16(wb)) if wfmt == wsl.WSL_W_NF4 else to_dev_bf16(wb)
+    x = to_dev_bf16(xb)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    y_split = wsl.linear_gemm(w, x, wfmt=wfmt, n_out=n_out, k=k, ofmt=ofmt, workspace=ws)
+    y_whole = wsl.linear_gemm(w, x, wfmt=wfmt, n_out=n_out, k=k, ofmt=ofmt)
+    torch.cuda.synchronize()
+    if wfmt == wsl.WSL_W_BF16:
+        cols = np.arange(n_out)
+        t = f64(wb)
+    else:
+        cols = _sample_idx(n_out, 256, np.random.default_rng(113 + m), 160)
+        t = _tile_f64(wb[cols])
+    y_ref, s_ref = oracle.gemm_ref(f64(xb), t)
+    for name, y in (("split", y_split), ("unsplit", y_whole)):
+        ok, worst, i = _check(y[:, cols], y_ref, s_ref, ofmt)
+        assert ok, f"{name}: elem {i}: worst ratio {worst}"
+
+
+# linear_gemm_noalloc on a shape whose tiled k split would need more than the library's
+# scratch: it runs the tiled kernels unsplit (no WSL_E_SCRATCH), bit for bit what
+# linear_gemm computes without a workspace.
+def test_gemm_noalloc_tiled_runs_unsplit_beyond_scratch():
+    import torch
+    m, n_out, k = 1000, 2100, 8192
+    say(f"gemm noalloc tiled m={m} n={n_out} k={k}")
+    assert wsl.linear_gemm_workspace_bytes(wsl.WSL_W_BF16, n_out, k, m) > wsl.NOALLOC_SCRATCH_BYTES
+    wb = synth.weight_bits(112, 0, n_out, k)
+    xb = synth.act_bits(112, 1, (m, k))
+    w, x = to_dev_bf16(wb), to_dev_bf16(xb)
+    y = torch.full((m, n_out), float("nan"), dtype=torch.float32, device="cuda")
+    wsl.linear_gemm_noalloc(w, x, y)
+    y_whole = wsl.linear_gemm(w, x)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_whole)
+    cols = _sample_idx(n_out, 256, np.random.default_rng(114), 64)
+    y_ref, s_ref = oracle.gemm_ref(f64(xb), f64(wb[cols]))
+    ok, worst, i = oracle.check_rows_f32(y.cpu().numpy()[:, cols], y_ref, s_ref)
+    assert ok, f"elem {i}: worst ratio {worst}"
+
+
 def test_gemm_deterministic():
     import torch
     m, n_out, k = 32, 5120, 27648 // 4
@@ -373,10 +428,11 @@ def test_gemm_deterministic():
 
 
 # A captured linear_gemm replays to the eager result: the shared-X kernels with a k split
-# (workspace + reduction kernel) and the tiled kernels.  Each replay follows eager work of
+# (workspace + reduction kernel) and the tiled kernels, unsplit and split.  Each replay follows eager work of
 # the program's own and a synchronization, with the output poisoned first.
 @pytest.mark.parametrize("wfmt,m,n_out,k", [(wsl.WSL_W_NF4, 32, 640, 16384), (wsl.WSL_W_NF4, 300, 1000, 448),
-                                            (wsl.WSL_W_BF16, 200, 700, 1024), (wsl.WSL_W_BF16, 200, 700, 1088)])
+                                            (wsl.WSL_W_BF16, 200, 700, 1024), (wsl.WSL_W_BF16, 200, 700, 1088),
+                                            (wsl.WSL_W_BF16, 513, 777, 12288)])
 def test_gemm_graph_replays_match_eager(wfmt, m, n_out, k):
     import torch
     say(f"gemm graph wfmt={wfmt} m={m} n={n_out} k={k}")

@@ -63,14 +63,16 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // One workgroup tile: TM = 256 rows of X (each wave 128 x 64 of the output, 4 x 2
 // MFMA tiles) or TM = 128 (each wave 64 x 64, 2 x 2 tiles: the half tiles that
-// shorten the last, partly filled round of a launch).
+// shorten the last, partly filled round of a launch), over the k range [kb, kb + kl)
+// (kb and kl multiples of 64; the whole k unless the launch splits k).
 // The four ring stages are separate LDS objects and the k loop is unrolled by
 // four, so every copy and every fragment read names its stage at compile time;
 // the compiler can then tell that reading stage s does not alias the copies
 // still in flight into the other stages, and does not drain them.
 template <int TM>
 __device__ __forceinline__ void bf16_tile(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, int64_t m,
-                                          int64_t n_out, int64_t k, int64_t ldx, void *__restrict__ y, int ofmt,
+                                          int64_t n_out, int64_t k, int64_t kb, int64_t kl, int64_t ldx,
+                                          void *__restrict__ y, int ofmt,
                                           int64_t ldy, int64_t m0, int64_t n0, char *st0, char *st1, char *st2,
                                           char *st3) {
     constexpr int MI = TM / 64;         // 32-row MFMA tiles per wave along m
@@ -91,14 +93,14 @@ __device__ __forceinline__ void bf16_tile(const uint16_t *__restrict__ x, const 
         const int row = 16 * (NA * wave + i) + (lane >> 2);
         const int c = chunk_swz(row, lane & 3);                 // global chunk landing in slot lane % 4
         const int64_t gm = (m0 + row < m) ? m0 + row : m - 1;
-        asrc[i] = x + gm * ldx + c * 8;
+        asrc[i] = x + gm * ldx + kb + c * 8;
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int row = 16 * (2 * wave + i) + (lane >> 2);
         const int c = chunk_swz(row, lane & 3);
         const int64_t gn = (n0 + row < n_out) ? n0 + row : n_out - 1;
-        bsrc[i] = w + gn * k + c * 8;
+        bsrc[i] = w + gn * k + kb + c * 8;
     }
     auto copy_stage = [&](int64_t kt, char *sa) {
         char *sb = sa + kBM * kBK * 2;
@@ -120,7 +122,7 @@ __device__ __forceinline__ void bf16_tile(const uint16_t *__restrict__ x, const 
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
     const int half = lane >> 5, l32 = lane & 31;
-    const int64_t ktiles = k / kBK;   // even: k % 64 == 0
+    const int64_t ktiles = kl / kBK;   // even: kl % 64 == 0
     // Fragment reads: the lane's MI A rows (and 2 B rows) are 32 rows apart and
     // share their swizzled chunk, so one base address plus immediate offsets
     // (2048 B apart) covers the reads of a 16-k step.  They are issued from
@@ -277,12 +279,17 @@ __device__ __forceinline__ void bf16_tile(const uint16_t *__restrict__ x, const 
 // leave at least half of its CUs idle, those tiles run as two 128-row halves
 // each, so that round takes about half as long.  Tiles are ordered in bands of 8
 // m-tiles, so tiles sharing rows of X or of W run on the same XCD (one L2) at
-// about the same time.  Returns false for a work item past the XCD's end.
+// about the same time.  With k split s ways a tile is s work items (its k ranges),
+// consecutive in that order: column tn of s * tiles_n is tile column tn / s, split
+// tn % s.  Returns false for a work item past the XCD's end.
 struct TileItem {
     int64_t m0, n0;
-    int half;   // -1: the whole 256-row tile; 0 / 1: its first / second 128 rows
+    int half;    // -1: the whole 256-row tile; 0 / 1: its first / second 128 rows
+    int split;   // k range of the item
 };
-__device__ __forceinline__ bool tile_item(int tiles_m, int tiles_n, int nx, int xcd_cus, TileItem &it) {
+__device__ __forceinline__ bool tile_item(int tiles_m, int tiles_n_splits, int splits, int nx, int xcd_cus,
+                                          TileItem &it) {
+    const int tiles_n = tiles_n_splits;
     const int ntiles = tiles_m * tiles_n;
     const int per_xcd = ntiles / nx, rem = ntiles - per_xcd * nx;
     const int xcd = static_cast<int>(blockIdx.x) % nx, slot = static_cast<int>(blockIdx.x) / nx;
@@ -308,24 +315,52 @@ __device__ __forceinline__ bool tile_item(int tiles_m, int tiles_n, int nx, int 
     const int tm = b_idx * band + in_band % band_rows;
     const int tn = in_band / band_rows;
     it.m0 = static_cast<int64_t>(tm) * kBM + (it.half > 0 ? kBM / 2 : 0);
-    it.n0 = static_cast<int64_t>(tn) * kBN;
+    it.n0 = static_cast<int64_t>(tn / splits) * kBN;
+    it.split = tn % splits;
     return true;
+}
+
+// A work item's k range and destination: with ws (k split) the item writes its fp32
+// partial sums to ws[(split * m + row) * n_out + col], summed by split_reduce_kernel.
+struct SplitOut {
+    int64_t kb, kl;
+    void *y;
+    int ofmt;
+    int64_t ldy;
+};
+__device__ __forceinline__ SplitOut split_out(int split, int64_t kps, int64_t k, int64_t m, int64_t n_out, void *y,
+                                              int ofmt, int64_t ldy, float *ws) {
+    SplitOut o;
+    o.kb = static_cast<int64_t>(split) * kps;
+    o.kl = (o.kb + kps < k) ? kps : k - o.kb;
+    if (ws != nullptr) {
+        o.y = ws + static_cast<int64_t>(split) * m * n_out;
+        o.ofmt = WSL_OUT_F32;
+        o.ldy = n_out;
+    } else {
+        o.y = y;
+        o.ofmt = ofmt;
+        o.ldy = ldy;
+    }
+    return o;
 }
 
 __global__ __launch_bounds__(512) void gemm_bf16_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
                                                         int64_t m, int64_t n_out, int64_t k, int64_t ldx,
                                                         void *__restrict__ y, int ofmt, int64_t ldy,
-                                                        int tiles_m, int tiles_n, int nx, int xcd_cus) {
+                                                        int tiles_m, int tiles_n, int nx, int xcd_cus, int splits,
+                                                        int64_t kps, float *__restrict__ ws) {
     __shared__ __attribute__((aligned(1024))) char st0[kStageBytes];
     __shared__ __attribute__((aligned(1024))) char st1[kStageBytes];
     __shared__ __attribute__((aligned(1024))) char st2[kStageBytes];
     __shared__ __attribute__((aligned(1024))) char st3[kStageBytes];
     TileItem it;
-    if (!tile_item(tiles_m, tiles_n, nx, xcd_cus, it) || it.m0 >= m) return;
+    if (!tile_item(tiles_m, tiles_n * splits, splits, nx, xcd_cus, it) || it.m0 >= m) return;
+    const SplitOut o = split_out(it.split, kps, k, m, n_out, y, ofmt, ldy, ws);
     if (it.half < 0)
-        bf16_tile<256>(x, w, m, n_out, k, ldx, y, ofmt, ldy, it.m0, it.n0, st0, st1, st2, st3);
+        bf16_tile<256>(x, w, m, n_out, k, o.kb, o.kl, ldx, o.y, o.ofmt, o.ldy, it.m0, it.n0, st0, st1, st2, st3);
     else
-        bf16_tile<128>(x, w, m, n_out, k, ldx, y, ofmt, ldy, it.m0, it.n0, st0, st1, st2, st3);
+        bf16_tile<128>(x, w, m, n_out, k, o.kb, o.kl, ldx, o.y, o.ofmt, o.ldy, it.m0, it.n0, st0, st1, st2, st3);
 }
 
 // ---------------------------------------------------------------- NF4, weight-stationary
@@ -1035,7 +1070,8 @@ __device__ __forceinline__ void lds_store16(uint32_t addr, uint4 v) {
 // round); the restored weight tile is 256 rows either way.
 template <int TM>
 __device__ __forceinline__ void nf4_tile(const uint16_t *__restrict__ x, const uint8_t *__restrict__ packed, int64_t m,
-                                         int64_t n_out, int64_t k, int64_t ldx, void *__restrict__ y, int ofmt,
+                                         int64_t n_out, int64_t k, int64_t kb, int64_t kl, int64_t ldx,
+                                         void *__restrict__ y, int ofmt,
                                          int64_t ldy, int64_t m0, int64_t n0, char *sa0, char *sa1, char *sa2,
                                          char *sa3, char *sb0, char *sb1, char *tab) {
     constexpr int MI = TM / 64;         // 32-row MFMA tiles per wave along m
@@ -1073,11 +1109,11 @@ __device__ __forceinline__ void nf4_tile(const uint16_t *__restrict__ x, const u
         for (int i = 0; i < 4; ++i) pa[i] = pb[i] = base;
     }
 
-    const int64_t ktiles = k / kBK;   // even: k % 64 == 0
+    const int64_t ktiles = kl / kBK;   // even: kl % 64 == 0
     // Loads for k-tiles past the end are clamped to the last one: they land in a
     // slot or register set nobody reads again, and keep the loop free of branches
     // around loads (with them the compiler's own waits turn conservative).
-    auto tile_k0 = [&](int64_t kt) { return (kt < ktiles ? kt : ktiles - 1) * kBK; };
+    auto tile_k0 = [&](int64_t kt) { return kb + (kt < ktiles ? kt : ktiles - 1) * kBK; };
     // The code and scale loads are issued from inline asm: the compiler does not
     // track them, so it adds no waits of its own (around the loop's back edge it
     // waited for every load in flight).  The explicit vmcnt wait of the memory phase
@@ -1266,7 +1302,8 @@ __device__ __forceinline__ void nf4_tile(const uint16_t *__restrict__ x, const u
 __global__ __launch_bounds__(512) void gemm_nf4_tiled_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ packed,
                                                       int64_t m, int64_t n_out, int64_t k, int64_t ldx,
                                                       void *__restrict__ y, int ofmt, int64_t ldy, int tiles_m, int tiles_n,
-                                                      int nx, int xcd_cus) {
+                                                      int nx, int xcd_cus, int splits, int64_t kps,
+                                                      float *__restrict__ ws) {
     constexpr int kHalf = kBM * kBK * 2;   // 16 KB per operand per stage
     __shared__ __attribute__((aligned(1024))) char sa0[kHalf];
     __shared__ __attribute__((aligned(1024))) char sa1[kHalf];
@@ -1276,12 +1313,15 @@ __global__ __launch_bounds__(512) void gemm_nf4_tiled_kernel(const uint16_t *__r
     __shared__ __attribute__((aligned(1024))) char sb1[kHalf];
     __shared__ __attribute__((aligned(65536))) char tab[kPairTableBytes];   // bits 8..15 of its address are 0
     TileItem it;
-    if (!tile_item(tiles_m, tiles_n, nx, xcd_cus, it) || it.m0 >= m) return;
+    if (!tile_item(tiles_m, tiles_n * splits, splits, nx, xcd_cus, it) || it.m0 >= m) return;
     fill_pair_table(tab);
+    const SplitOut o = split_out(it.split, kps, k, m, n_out, y, ofmt, ldy, ws);
     if (it.half < 0)
-        nf4_tile<256>(x, packed, m, n_out, k, ldx, y, ofmt, ldy, it.m0, it.n0, sa0, sa1, sa2, sa3, sb0, sb1, tab);
+        nf4_tile<256>(x, packed, m, n_out, k, o.kb, o.kl, ldx, o.y, o.ofmt, o.ldy, it.m0, it.n0, sa0, sa1, sa2, sa3,
+                      sb0, sb1, tab);
     else
-        nf4_tile<128>(x, packed, m, n_out, k, ldx, y, ofmt, ldy, it.m0, it.n0, sa0, sa1, sa2, sa3, sb0, sb1, tab);
+        nf4_tile<128>(x, packed, m, n_out, k, o.kb, o.kl, ldx, o.y, o.ofmt, o.ldy, it.m0, it.n0, sa0, sa1, sa2, sa3,
+                      sb0, sb1, tab);
 }
 
 // Sum split partials in split order (fixed, so the result is deterministic).  A
@@ -1352,23 +1392,56 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float *__restri
 constexpr int kNf4Nb = 1;
 constexpr int64_t kNf4RowsPerWg = 4 * 32 * kNf4Nb;
 
+// k split of the tiled kernels.  When the 256 x 256 tiles of a launch would leave more
+// than half of the 256 CUs idle, k (a multiple of 256) is split into s ranges, one work
+// item per (tile, range), up to one round over the CUs: each item reads, or restores, only
+// its own k range of the weights, so no weight is read twice, and the fp32 partials
+// (s * M * N * 4 bytes of workspace) are summed in split order by split_reduce_kernel.
+// s minimises a time model: t_full per unit of k for a round of full tiles, t_half for a
+// last round of at most 128 tiles run as halves (unsplit launches only), and for a split
+// the partials written and read back and the output written, at 5 TB/s, plus 3 us for the
+// reduction's launch and the shorter k loops' pipeline ramp; every range is at least 512
+// long.
+struct TiledPlan {
+    int splits;
+    int64_t kps;   // k per split (k when unsplit)
+    double t;      // modelled seconds
+};
+static TiledPlan tiled_plan(int64_t n_out, int64_t k, int64_t m, double t_full, double t_half) {
+    const int64_t tiles = ((m + kBM - 1) / kBM) * ((n_out + kBN - 1) / kBN);
+    const int64_t full = tiles / 256, tail = tiles % 256;
+    double per_k = static_cast<double>(full) * t_full;
+    if (tail > 0) per_k += tail <= 128 ? t_half : t_full;
+    TiledPlan best{1, k, per_k * static_cast<double>(k)};
+    if (k % 256 != 0 || 2 * tiles > 256) return best;
+    const int64_t units = k / 256;
+    const double out = static_cast<double>(m) * static_cast<double>(n_out) * 4.0;
+    for (int64_t sp = 2; sp <= 64 && sp * tiles <= 256 && 2 * sp <= units; ++sp) {
+        const int64_t kps = ((units + sp - 1) / sp) * 256;
+        const int64_t used = (k + kps - 1) / kps;   // no empty trailing range
+        const double t = t_full * static_cast<double>(kps) + static_cast<double>(2 * used + 1) * out / 5e12 + 3e-6;
+        if (t < best.t) best = TiledPlan{static_cast<int>(used), kps, t};
+    }
+    return best;
+}
+static TiledPlan nf4_tiled_plan(int64_t n_out, int64_t k, int64_t m) { return tiled_plan(n_out, k, m, 33e-9, 23.5e-9); }
+static TiledPlan bf16_tiled_plan(int64_t n_out, int64_t k, int64_t m) { return tiled_plan(n_out, k, m, 30e-9, 21e-9); }
+
 // k a multiple of 256: the shared-X kernel for M <= 32; above that, the shared-X or the
 // tiled kernel, whichever a time model fitted to MI355X measurements puts first.  The
 // shared-X kernel streams the packed weights once per 64 positions at about 2 TB/s; a
 // round of 256 x 256 tiles (one workgroup per CU) takes about 33 ns per unit of k, and a
-// last round of at most 128 tiles, which runs as half tiles, about 23.5 ns.  Measured
-// (us, tiled / shared-X): 27648x5120 M = 64 127 / 42, M = 256 121 / 158; 5120x27648
-// M = 256 608 / 197; at M = 320, where a fixed cut at 256 took the tiled kernel,
-// 5120x27648 608 and 6144x16384 368.  Other k: the tiled kernel for M > 32, the general
-// kernel for M <= 32.
+// last round of at most 128 tiles, which runs as half tiles, about 23.5 ns; a k split
+// (tiled_plan) shortens a sparse round.  Measured (us): 27648x5120 M = 64 127 tiled / 42
+// shared-X; M = 256 121 tiled, 112 as halves, 101.5 with 2 k ranges, 158 shared-X;
+// 5120x27648 M = 256 608 tiled, 197 shared-X, 94.5 with 12 k ranges; M = 512 381
+// shared-X, 158.5 with 6; M = 1024 565 / 293 with 3; 5120x17408, 17408x5120 and
+// 6144x16384 at M = 256 127 / 119 / 121 shared-X or halves, 70 / 75 / 76 split.  Other k:
+// the tiled kernel for M > 32, the general kernel for M <= 32.
 static bool x32_faster(int64_t n_out, int64_t k, int64_t m) {
     const double packed = static_cast<double>(n_out) * static_cast<double>(k / 2 + (k / 64) * 2);
     const double t_x32 = static_cast<double>((m + 63) / 64) * packed / 2.0e12;
-    const int64_t tiles = ((m + kBM - 1) / kBM) * ((n_out + kBN - 1) / kBN);
-    const int64_t full = tiles / 256, tail = tiles % 256;
-    double per_k = static_cast<double>(full) * 33e-9;
-    if (tail > 0) per_k += tail <= 128 ? 23.5e-9 : 33e-9;
-    return t_x32 <= per_k * static_cast<double>(k);
+    return t_x32 <= nf4_tiled_plan(n_out, k, m).t;
 }
 static bool use_x32(int64_t n_out, int64_t k, int64_t m) {
     return (k % kX32Chunk) == 0 && (m <= 32 || x32_faster(n_out, k, m));
@@ -1398,7 +1471,7 @@ static int x32_splits(int64_t n_out, int64_t k, int64_t m) {
 }
 
 static int nf4_splits(int64_t n_out, int64_t k, int64_t m) {
-    if (use_tiled(n_out, k, m)) return 1;
+    if (use_tiled(n_out, k, m)) return nf4_tiled_plan(n_out, k, m).splits;
     if (use_x32(n_out, k, m)) return x32_splits(n_out, k, m);
     const int64_t waves = ((n_out + 32 * kNf4Nb - 1) / (32 * kNf4Nb)) * ((m + 31) / 32);
     const int64_t chunks = (k + 127) / 128;
@@ -1415,24 +1488,22 @@ static int64_t nf4_k_per_split(int64_t n_out, int64_t k, int64_t m, int splits) 
 
 // bf16, k a multiple of 256: the shared-X kernel for M <= 32; above that, the same kind of
 // time model as for NF4, fitted to bf16 measurements: every 64 positions re-stream the
-// 2-byte weights at about 3.2 TB/s; a round of 256 x 256 tiles takes about 30 ns per unit
-// of k, a last round of at most 128 (half) tiles about 21 ns.  Measured (us, tiled /
-// shared-X): 27648x5120 M = 64 106 / 78, M = 96 108 / 135; 5120x27648 M = 128 474 / 118,
-// M = 256 443 / 296, M = 512 446 / 600; 5120x17408 M = 256 281 / 189.  Other k: tiled.
+// 2-byte weights at about 3.6 TB/s; a round of 256 x 256 tiles takes about 30 ns per unit
+// of k, a last round of at most 128 (half) tiles about 21 ns, and a k split shortens a
+// sparse round.  Measured (us): 27648x5120 M = 64 106 tiled, 85 with 2 k ranges, 78
+// shared-X; M = 128 117 shared-X, 95 split; 5120x27648 M = 128 474 tiled, 115 shared-X,
+// 88 with 12 ranges; M = 256 443 / 291 / 103; M = 512 446 tiled, 491 shared-X, 159 with 6;
+// 5120x17408 M = 256 187 shared-X, 76 split; 1000x16384 M = 1000 91 / 59.  Other k: tiled.
 static bool bf16_x32_faster(int64_t n_out, int64_t k, int64_t m) {
     const double bytes = 2.0 * static_cast<double>(n_out) * static_cast<double>(k);
-    const double t_x32 = static_cast<double>((m + 63) / 64) * bytes / 3.2e12;
-    const int64_t tiles = ((m + kBM - 1) / kBM) * ((n_out + kBN - 1) / kBN);
-    const int64_t full = tiles / 256, tail = tiles % 256;
-    double per_k = static_cast<double>(full) * 30e-9;
-    if (tail > 0) per_k += tail <= 128 ? 21e-9 : 30e-9;
-    return t_x32 <= per_k * static_cast<double>(k);
+    const double t_x32 = static_cast<double>((m + 63) / 64) * bytes / 3.6e12;
+    return t_x32 <= bf16_tiled_plan(n_out, k, m).t;
 }
 static bool use_bf16_x32(int64_t n_out, int64_t k, int64_t m) {
     return (k % kX32Chunk) == 0 && (m <= 32 || bf16_x32_faster(n_out, k, m));
 }
 static int bf16_splits(int64_t n_out, int64_t k, int64_t m) {
-    return use_bf16_x32(n_out, k, m) ? x32_splits(n_out, k, m) : 1;
+    return use_bf16_x32(n_out, k, m) ? x32_splits(n_out, k, m) : bf16_tiled_plan(n_out, k, m).splits;
 }
 
 size_t gemm_ws_bytes(int wfmt, int64_t n_out, int64_t k, int64_t m) {
@@ -1479,16 +1550,38 @@ static unsigned tile_grid(int64_t ntiles, const XcdShape &xs) {
     return static_cast<unsigned>(xs.nx * most);
 }
 
+static void launch_split_reduce(const float *wsp, int splits, int64_t m, int64_t n_out, void *y, int ofmt,
+                                int64_t ldy, hipStream_t s) {
+    const int64_t items = (n_out % 4 == 0) ? m * n_out / 4 : m * n_out;
+    int64_t blocks = (items + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(split_reduce_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, wsp, splits, m,
+                       n_out, y, ofmt, ldy);
+}
+
+// The tiled kernels' plan for a launch: the modelled split, or none when the caller's
+// workspace cannot hold its partials.
+static TiledPlan tiled_launch_plan(int wfmt, int64_t n_out, int64_t k, int64_t m, const void *ws, size_t ws_bytes) {
+    TiledPlan pl = wfmt == WSL_W_NF4 ? nf4_tiled_plan(n_out, k, m) : bf16_tiled_plan(n_out, k, m);
+    const size_t need = static_cast<size_t>(pl.splits) * static_cast<size_t>(m) * static_cast<size_t>(n_out) * 4;
+    if (pl.splits > 1 && (ws == nullptr || ws_bytes < need)) pl = TiledPlan{1, k, pl.t};
+    return pl;
+}
+
 int launch_gemm_bf16(const void *w, int64_t n_out, int64_t k, const void *x, int64_t m, int64_t ldx, void *y,
                      int ofmt, int64_t ldy, void *ws, size_t ws_bytes, hipStream_t s) {
     const auto *wp = static_cast<const uint16_t *>(w);
     const auto *xp = static_cast<const uint16_t *>(x);
     if (!use_bf16_x32(n_out, k, m)) {
         const int64_t tn = (n_out + kBN - 1) / kBN, tm = (m + kBM - 1) / kBM;
-        if (tn * tm > 0x7fffffff / 4) return WSL_E_SHAPE;
+        const TiledPlan pl = tiled_launch_plan(WSL_W_BF16, n_out, k, m, ws, ws_bytes);
+        if (tn * tm * pl.splits > 0x7fffffff / 4) return WSL_E_SHAPE;
+        float *wsp = pl.splits > 1 ? static_cast<float *>(ws) : nullptr;
         const XcdShape xs = xcd_shape();
-        hipLaunchKernelGGL(gemm_bf16_kernel, dim3(tile_grid(tm * tn, xs)), dim3(512), 0, s, xp, wp, m, n_out, k,
-                           ldx, y, ofmt, ldy, static_cast<int>(tm), static_cast<int>(tn), xs.nx, xs.cus);
+        hipLaunchKernelGGL(gemm_bf16_kernel, dim3(tile_grid(tm * tn * pl.splits, xs)), dim3(512), 0, s, xp, wp, m,
+                           n_out, k, ldx, y, ofmt, ldy, static_cast<int>(tm), static_cast<int>(tn), xs.nx, xs.cus,
+                           pl.splits, pl.kps, wsp);
+        if (pl.splits > 1) launch_split_reduce(wsp, pl.splits, m, n_out, y, ofmt, ldy, s);
         return WSL_OK;
     }
     int splits = bf16_splits(n_out, k, m);
@@ -1506,13 +1599,7 @@ int launch_gemm_bf16(const void *w, int64_t n_out, int64_t k, const void *x, int
     else
         hipLaunchKernelGGL((gemm_bf16_x32_kernel<1>), grid, dim3(512), 0, s, wp, n_out, k, xp, m, ldx, y, ofmt, ldy,
                            wsp, kps);
-    if (splits > 1) {
-        const int64_t items = (n_out % 4 == 0) ? m * n_out / 4 : m * n_out;
-        int64_t blocks = (items + 255) / 256;
-        if (blocks > 4096) blocks = 4096;
-        hipLaunchKernelGGL(split_reduce_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, wsp, splits, m,
-                           n_out, y, ofmt, ldy);
-    }
+    if (splits > 1) launch_split_reduce(wsp, splits, m, n_out, y, ofmt, ldy, s);
     return WSL_OK;
 }
 
@@ -1520,11 +1607,15 @@ int launch_gemm_nf4(const void *w, int64_t n_out, int64_t k, const void *x, int6
                     int ofmt, int64_t ldy, void *ws, size_t ws_bytes, hipStream_t s) {
     if (use_tiled(n_out, k, m)) {
         const int64_t tn = (n_out + kBN - 1) / kBN, tm = (m + kBM - 1) / kBM;
-        if (tn * tm > 0x7fffffff / 4) return WSL_E_SHAPE;
+        const TiledPlan pl = tiled_launch_plan(WSL_W_NF4, n_out, k, m, ws, ws_bytes);
+        if (tn * tm * pl.splits > 0x7fffffff / 4) return WSL_E_SHAPE;
+        float *wsp = pl.splits > 1 ? static_cast<float *>(ws) : nullptr;
         const XcdShape xs = xcd_shape();
-        hipLaunchKernelGGL(gemm_nf4_tiled_kernel, dim3(tile_grid(tm * tn, xs)), dim3(512), 0, s,
+        hipLaunchKernelGGL(gemm_nf4_tiled_kernel, dim3(tile_grid(tm * tn * pl.splits, xs)), dim3(512), 0, s,
                            static_cast<const uint16_t *>(x), static_cast<const uint8_t *>(w), m, n_out, k, ldx, y,
-                           ofmt, ldy, static_cast<int>(tm), static_cast<int>(tn), xs.nx, xs.cus);
+                           ofmt, ldy, static_cast<int>(tm), static_cast<int>(tn), xs.nx, xs.cus, pl.splits, pl.kps,
+                           wsp);
+        if (pl.splits > 1) launch_split_reduce(wsp, pl.splits, m, n_out, y, ofmt, ldy, s);
         return WSL_OK;
     }
     int splits = nf4_splits(n_out, k, m);
@@ -1558,13 +1649,7 @@ int launch_gemm_nf4(const void *w, int64_t n_out, int64_t k, const void *x, int6
         hipLaunchKernelGGL((gemm_nf4_kernel<kNf4Nb>), grid, dim3(256), 0, s, wp, n_out, k, xp, m, ldx, y, ofmt, ldy,
                            wsp, kps);
     }
-    if (splits > 1) {
-        const int64_t items = (n_out % 4 == 0) ? m * n_out / 4 : m * n_out;
-        int64_t blocks = (items + 255) / 256;
-        if (blocks > 4096) blocks = 4096;
-        hipLaunchKernelGGL(split_reduce_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, wsp, splits, m,
-                           n_out, y, ofmt, ldy);
-    }
+    if (splits > 1) launch_split_reduce(wsp, splits, m, n_out, y, ofmt, ldy, s);
     return WSL_OK;
 }
 
@@ -1600,8 +1685,13 @@ static int scratch_ptr(void **out) {
 // every partial before split_reduce_kernel reads it, so nothing needs clearing.
 int launch_gemm_noalloc(int wfmt, const void *w, int64_t n_out, int64_t k, const void *x, int64_t m, int64_t ldx,
                         void *y, int ofmt, int64_t ldy, hipStream_t s) {
-    const size_t need = gemm_ws_bytes(wfmt, n_out, k, m);
-    if (need > kScratchBytes) return WSL_E_SCRATCH;
+    size_t need = gemm_ws_bytes(wfmt, n_out, k, m);
+    if (need > kScratchBytes) {
+        // a k split of the tiled kernels only saves time: without room they run unsplit
+        const bool tiled = wfmt == WSL_W_NF4 ? use_tiled(n_out, k, m) : !use_bf16_x32(n_out, k, m);
+        if (!tiled) return WSL_E_SCRATCH;
+        need = 0;
+    }
     void *ws = nullptr;
     if (need > 0) {
         const int rc = scratch_ptr(&ws);
