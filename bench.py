@@ -765,13 +765,14 @@ def run_nf4_verify_gemm(k_steps, warmup, copies=2):
     return out
 
 
-def run_nf4_gemm_mid_m(k_steps, warmup, copies=8):
-    """NF4 GEMM between the prefill and verification sizes: up 27648x5120 at M = 64, 128, 256
-    (prefill chunks of more than 32 positions), fp32 out."""
+def run_nf4_gemm_mid_m(k_steps, warmup, n=27648, k=5120, seed=700, copies=8):
+    """NF4 GEMM between the prefill and verification sizes: the 32B-class up (27648x5120) or
+    down (5120x27648) projection at M = 64, 128, 256 (prefill chunks of more than 32
+    positions), fp32 out, with the workspace the library asks for (a k split where it
+    pays)."""
     import torch
     import synth
     import weight_streaming_linear_amd as wsl
-    n, k = 27648, 5120
     ms = [64, 128, 256]
     xs = [synth.device_normal_bf16(3, 40 + j, (m, k)) for j, m in enumerate(ms)]
     ys = [torch.empty((m, n), dtype=torch.float32, device="cuda") for m in ms]
@@ -780,7 +781,7 @@ def run_nf4_gemm_mid_m(k_steps, warmup, copies=8):
     packs = []
     worst = 0.0
     for c in range(copies):
-        w = synth.device_weight(3, 700 + c, n, k)
+        w = synth.device_weight(3, seed + c, n, k)
         p = wsl.nf4_pack(w)
         del w
         if c == 0:
@@ -791,7 +792,7 @@ def run_nf4_gemm_mid_m(k_steps, warmup, copies=8):
                 xf = xs[j].float()
                 worst = max(worst, check_close(f"nf4 gemm m={m}", ys[j][:, torch.as_tensor(cols, device="cuda")],
                                                xf @ t.t().contiguous(), xf.abs() @ t.abs().t().contiguous(), 1e-4))
-                OUTPUT_SHA[f"nf4_gemm_27648x5120_m{m}"] = sha256_of([ys[j]])
+                OUTPUT_SHA[f"nf4_gemm_{n}x{k}_m{m}"] = sha256_of([ys[j]])
         packs.append(p)
     steps = [[Launch(lambda p=p, j=j, m=m: wsl.linear_gemm(p, xs[j], y=ys[j], wfmt=wsl.WSL_W_NF4, n_out=n, k=k,
                                                            workspace=wss[j]),
@@ -803,8 +804,10 @@ def run_nf4_gemm_mid_m(k_steps, warmup, copies=8):
         l = out["launches"][f"nf4_gemm_m{m}"]
         ai = 2 * m * n * k / wsl.nf4_packed_bytes(n, k)
         l["frac_roofline"] = l["tflops"] / min(MFMA_BF16_PEAK_TFLOPS, ai * HBM_PEAK_GBS / 1e3)
-    out.update({"workload": "NF4 GEMM up 27648x5120 at M = 64, 128, 256, fp32 out", "rotation_copies": copies,
-                "sanity_worst_ratio": worst})
+    out.update({"workload": f"NF4 GEMM {n}x{k} at M = 64, 128, 256, fp32 out", "rotation_copies": copies,
+                "sanity_worst_ratio": worst,
+                "k_splits": {str(m): wsl.linear_gemm_workspace_bytes(wsl.WSL_W_NF4, n, k, m) // (m * n * 4)
+                             for m in ms}})
     del packs
     torch.cuda.empty_cache()
     return out
@@ -812,6 +815,7 @@ def run_nf4_gemm_mid_m(k_steps, warmup, copies=8):
 
 PATHS = [("bf16_decode_layer_5120", run_bf16_decode_layer), ("nf4_gemv_4096", run_nf4_gemv_4096),
          ("nf4_prefill_gemm_m32", run_nf4_prefill_gemm), ("nf4_gemm_mid_m_27648x5120", run_nf4_gemm_mid_m),
+         ("nf4_gemm_mid_m_5120x27648", lambda ks, w: run_nf4_gemm_mid_m(ks, w, n=5120, k=27648, seed=800)),
          ("bf16_verify_gemm_m8192", run_bf16_verify_gemm),
          ("nf4_verify_gemm_m8192", run_nf4_verify_gemm), ("nf4_embed_rows_128000x5120", run_nf4_embed_rows),
          ("copyring_nf4_decode_sweep_48x6144", run_copyring_decode_sweep)]

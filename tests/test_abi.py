@@ -46,6 +46,24 @@ def test_packed_bytes_invalid():
     assert wsl.nf4_packed_bytes(-3, 64) == 0
 
 
+# The launch's choice of a k split, read on the host through the workspace it asks for:
+# splits * m * n_out * 4 bytes.  The 256 x 256 tiles split k where they are few (mid M on
+# matrices with few rows; half tiles at M <= 128), not where they fill the CUs (M = 8192)
+# nor where k % 256 != 0; the shared-X kernel (NF4 at M = 64) splits the down projection
+# and not the tall up projection.
+@pytest.mark.parametrize("wfmt,n_out,k,m,splits", [
+    (wsl.WSL_W_BF16, 5120, 27648, 256, 12), (wsl.WSL_W_NF4, 5120, 27648, 256, 12),
+    (wsl.WSL_W_NF4, 5120, 27648, 512, 6), (wsl.WSL_W_NF4, 5120, 27648, 1024, 3),
+    (wsl.WSL_W_BF16, 27648, 5120, 128, 2), (wsl.WSL_W_NF4, 27648, 5120, 256, 2),
+    (wsl.WSL_W_NF4, 27648, 5120, 128, 2), (wsl.WSL_W_NF4, 5120, 27648, 128, 12),
+    (wsl.WSL_W_NF4, 27648, 5120, 64, 0), (wsl.WSL_W_NF4, 5120, 27648, 64, 6),
+    (wsl.WSL_W_BF16, 27648, 5120, 64, 2), (wsl.WSL_W_BF16, 17408, 5120, 8192, 0),
+    (wsl.WSL_W_NF4, 5120, 17408, 8192, 0), (wsl.WSL_W_BF16, 5120, 27584, 256, 0),
+    (wsl.WSL_W_NF4, 5120, 27648, 32, 6), (wsl.WSL_W_NF4, 27648, 5120, 32, 0)])
+def test_gemm_split_choice(wfmt, n_out, k, m, splits):
+    assert wsl.linear_gemm_workspace_bytes(wfmt, n_out, k, m) == splits * m * n_out * 4
+
+
 def test_argument_errors_return_before_any_launch():
     L = wsl.lib()
     a = ctypes.c_void_p(4096)     # aligned, never dereferenced: validation fails first

@@ -357,11 +357,13 @@ def test_gemm_nf4_tiled_mid_m(m, n_out, k, ofmt):
 
 # A k split of the tiled kernels: a launch whose 256 x 256 tiles would leave most CUs idle
 # runs one work item per (tile, k range), the fp32 partials summed in split order (the
-# workspace size names the split: a multiple of M * N * 4 bytes).  Ragged M and N, a last k
-# range shorter than the others; the same call without a workspace runs unsplit.  bf16:
-# every element against the oracle; NF4: all rows, sampled columns with the tile edges.
+# workspace size names the split: a multiple of M * N * 4 bytes); with M <= 128 the items
+# are 128-row half tiles (M = 65, 100).  Ragged M and N, a last k range shorter than the
+# others; the same call without a workspace runs unsplit.  bf16: every element against the
+# oracle; NF4: all rows, sampled columns with the tile edges.
 @pytest.mark.parametrize("wfmt,m,n_out,k", [(wsl.WSL_W_BF16, 513, 777, 12288), (wsl.WSL_W_BF16, 257, 3000, 7680),
-                                            (wsl.WSL_W_NF4, 1000, 2100, 8192), (wsl.WSL_W_NF4, 513, 4100, 12288)])
+                                            (wsl.WSL_W_BF16, 65, 4100, 6144), (wsl.WSL_W_NF4, 1000, 2100, 8192),
+                                            (wsl.WSL_W_NF4, 513, 4100, 12288), (wsl.WSL_W_NF4, 100, 6000, 12288)])
 @pytest.mark.parametrize("ofmt", [wsl.WSL_OUT_F32, wsl.WSL_OUT_BF16])
 def test_gemm_tiled_k_split(wfmt, m, n_out, k, ofmt):
     import torch

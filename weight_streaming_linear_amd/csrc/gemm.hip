@@ -281,14 +281,15 @@ __device__ __forceinline__ void bf16_tile(const uint16_t *__restrict__ x, const 
 // m-tiles, so tiles sharing rows of X or of W run on the same XCD (one L2) at
 // about the same time.  With k split s ways a tile is s work items (its k ranges),
 // consecutive in that order: column tn of s * tiles_n is tile column tn / s, split
-// tn % s.  Returns false for a work item past the XCD's end.
+// tn % s.  tail_halves = false: no tail split (a launch of half tiles only, M <= 128).
+// Returns false for a work item past the XCD's end.
 struct TileItem {
     int64_t m0, n0;
     int half;    // -1: the whole 256-row tile; 0 / 1: its first / second 128 rows
     int split;   // k range of the item
 };
 __device__ __forceinline__ bool tile_item(int tiles_m, int tiles_n_splits, int splits, int nx, int xcd_cus,
-                                          TileItem &it) {
+                                          bool tail_halves, TileItem &it) {
     const int tiles_n = tiles_n_splits;
     const int ntiles = tiles_m * tiles_n;
     const int per_xcd = ntiles / nx, rem = ntiles - per_xcd * nx;
@@ -296,7 +297,7 @@ __device__ __forceinline__ bool tile_item(int tiles_m, int tiles_n_splits, int s
     const int count = per_xcd + (xcd < rem ? 1 : 0);
     const int start = xcd * per_xcd + (xcd < rem ? xcd : rem);
     const int r = count % xcd_cus;
-    const int split = (r > 0 && 2 * r <= xcd_cus) ? r : 0;
+    const int split = (tail_halves && r > 0 && 2 * r <= xcd_cus) ? r : 0;
     const int full = count - split;
     int t;
     it.half = -1;
@@ -349,13 +350,14 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(const uint16_t *__restri
                                                         int64_t m, int64_t n_out, int64_t k, int64_t ldx,
                                                         void *__restrict__ y, int ofmt, int64_t ldy,
                                                         int tiles_m, int tiles_n, int nx, int xcd_cus, int splits,
-                                                        int64_t kps, float *__restrict__ ws) {
+                                                        int64_t kps, float *__restrict__ ws, int half_only) {
     __shared__ __attribute__((aligned(1024))) char st0[kStageBytes];
     __shared__ __attribute__((aligned(1024))) char st1[kStageBytes];
     __shared__ __attribute__((aligned(1024))) char st2[kStageBytes];
     __shared__ __attribute__((aligned(1024))) char st3[kStageBytes];
     TileItem it;
-    if (!tile_item(tiles_m, tiles_n * splits, splits, nx, xcd_cus, it) || it.m0 >= m) return;
+    if (!tile_item(tiles_m, tiles_n * splits, splits, nx, xcd_cus, half_only == 0, it) || it.m0 >= m) return;
+    if (half_only) it.half = 0;
     const SplitOut o = split_out(it.split, kps, k, m, n_out, y, ofmt, ldy, ws);
     if (it.half < 0)
         bf16_tile<256>(x, w, m, n_out, k, o.kb, o.kl, ldx, o.y, o.ofmt, o.ldy, it.m0, it.n0, st0, st1, st2, st3);
@@ -1303,7 +1305,7 @@ __global__ __launch_bounds__(512) void gemm_nf4_tiled_kernel(const uint16_t *__r
                                                       int64_t m, int64_t n_out, int64_t k, int64_t ldx,
                                                       void *__restrict__ y, int ofmt, int64_t ldy, int tiles_m, int tiles_n,
                                                       int nx, int xcd_cus, int splits, int64_t kps,
-                                                      float *__restrict__ ws) {
+                                                      float *__restrict__ ws, int half_only) {
     constexpr int kHalf = kBM * kBK * 2;   // 16 KB per operand per stage
     __shared__ __attribute__((aligned(1024))) char sa0[kHalf];
     __shared__ __attribute__((aligned(1024))) char sa1[kHalf];
@@ -1313,7 +1315,8 @@ __global__ __launch_bounds__(512) void gemm_nf4_tiled_kernel(const uint16_t *__r
     __shared__ __attribute__((aligned(1024))) char sb1[kHalf];
     __shared__ __attribute__((aligned(65536))) char tab[kPairTableBytes];   // bits 8..15 of its address are 0
     TileItem it;
-    if (!tile_item(tiles_m, tiles_n * splits, splits, nx, xcd_cus, it) || it.m0 >= m) return;
+    if (!tile_item(tiles_m, tiles_n * splits, splits, nx, xcd_cus, half_only == 0, it) || it.m0 >= m) return;
+    if (half_only) it.half = 0;
     fill_pair_table(tab);
     const SplitOut o = split_out(it.split, kps, k, m, n_out, y, ofmt, ldy, ws);
     if (it.half < 0)
@@ -1401,26 +1404,31 @@ constexpr int64_t kNf4RowsPerWg = 4 * 32 * kNf4Nb;
 // last round of at most 128 tiles run as halves (unsplit launches only), and for a split
 // the partials written and read back and the output written, at 5 TB/s, plus 3 us for the
 // reduction's launch and the shorter k loops' pipeline ramp; every range is at least 512
-// long.
+// long.  With M <= 128 the split items may also be half tiles (128 rows: no MFMA work on
+// rows past M), a round of which takes t_half per unit of k.
 struct TiledPlan {
     int splits;
     int64_t kps;   // k per split (k when unsplit)
     double t;      // modelled seconds
+    bool half;     // every item a 128-row half tile
 };
 static TiledPlan tiled_plan(int64_t n_out, int64_t k, int64_t m, double t_full, double t_half) {
     const int64_t tiles = ((m + kBM - 1) / kBM) * ((n_out + kBN - 1) / kBN);
     const int64_t full = tiles / 256, tail = tiles % 256;
     double per_k = static_cast<double>(full) * t_full;
     if (tail > 0) per_k += tail <= 128 ? t_half : t_full;
-    TiledPlan best{1, k, per_k * static_cast<double>(k)};
+    TiledPlan best{1, k, per_k * static_cast<double>(k), false};
     if (k % 256 != 0 || 2 * tiles > 256) return best;
     const int64_t units = k / 256;
     const double out = static_cast<double>(m) * static_cast<double>(n_out) * 4.0;
     for (int64_t sp = 2; sp <= 64 && sp * tiles <= 256 && 2 * sp <= units; ++sp) {
         const int64_t kps = ((units + sp - 1) / sp) * 256;
         const int64_t used = (k + kps - 1) / kps;   // no empty trailing range
-        const double t = t_full * static_cast<double>(kps) + static_cast<double>(2 * used + 1) * out / 5e12 + 3e-6;
-        if (t < best.t) best = TiledPlan{static_cast<int>(used), kps, t};
+        const double extra = static_cast<double>(2 * used + 1) * out / 5e12 + 3e-6;
+        const double t = t_full * static_cast<double>(kps) + extra;
+        if (t < best.t) best = TiledPlan{static_cast<int>(used), kps, t, false};
+        const double th = t_half * static_cast<double>(kps) + extra;
+        if (m <= kBM / 2 && th < best.t) best = TiledPlan{static_cast<int>(used), kps, th, true};
     }
     return best;
 }
@@ -1429,18 +1437,19 @@ static TiledPlan bf16_tiled_plan(int64_t n_out, int64_t k, int64_t m) { return t
 
 // k a multiple of 256: the shared-X kernel for M <= 32; above that, the shared-X or the
 // tiled kernel, whichever a time model fitted to MI355X measurements puts first.  The
-// shared-X kernel streams the packed weights once per 64 positions at about 2 TB/s; a
+// shared-X kernel streams the packed weights once per 64 positions at about 1.7 TB/s; a
 // round of 256 x 256 tiles (one workgroup per CU) takes about 33 ns per unit of k, and a
 // last round of at most 128 tiles, which runs as half tiles, about 23.5 ns; a k split
 // (tiled_plan) shortens a sparse round.  Measured (us): 27648x5120 M = 64 127 tiled / 42
-// shared-X; M = 256 121 tiled, 112 as halves, 101.5 with 2 k ranges, 158 shared-X;
+// shared-X; M = 128 84 shared-X, 74 as half tiles with 2 k ranges (5120x27648: 77 / 65
+// with 12); M = 256 121 tiled, 112 as halves, 101.5 with 2 k ranges, 158 shared-X;
 // 5120x27648 M = 256 608 tiled, 197 shared-X, 94.5 with 12 k ranges; M = 512 381
 // shared-X, 158.5 with 6; M = 1024 565 / 293 with 3; 5120x17408, 17408x5120 and
 // 6144x16384 at M = 256 127 / 119 / 121 shared-X or halves, 70 / 75 / 76 split.  Other k:
 // the tiled kernel for M > 32, the general kernel for M <= 32.
 static bool x32_faster(int64_t n_out, int64_t k, int64_t m) {
     const double packed = static_cast<double>(n_out) * static_cast<double>(k / 2 + (k / 64) * 2);
-    const double t_x32 = static_cast<double>((m + 63) / 64) * packed / 2.0e12;
+    const double t_x32 = static_cast<double>((m + 63) / 64) * packed / 1.7e12;
     return t_x32 <= nf4_tiled_plan(n_out, k, m).t;
 }
 static bool use_x32(int64_t n_out, int64_t k, int64_t m) {
@@ -1491,8 +1500,8 @@ static int64_t nf4_k_per_split(int64_t n_out, int64_t k, int64_t m, int splits) 
 // 2-byte weights at about 3.6 TB/s; a round of 256 x 256 tiles takes about 30 ns per unit
 // of k, a last round of at most 128 (half) tiles about 21 ns, and a k split shortens a
 // sparse round.  Measured (us): 27648x5120 M = 64 106 tiled, 85 with 2 k ranges, 78
-// shared-X; M = 128 117 shared-X, 95 split; 5120x27648 M = 128 474 tiled, 115 shared-X,
-// 88 with 12 ranges; M = 256 443 / 291 / 103; M = 512 446 tiled, 491 shared-X, 159 with 6;
+// shared-X, 75 as half tiles with 2; M = 128 117 shared-X, 95 split, 89.5 as halves;
+// 5120x27648 M = 128 474 tiled, 115 shared-X, 88 with 12 ranges, 78 as halves; M = 256 443 / 291 / 103; M = 512 446 tiled, 491 shared-X, 159 with 6;
 // 5120x17408 M = 256 187 shared-X, 76 split; 1000x16384 M = 1000 91 / 59.  Other k: tiled.
 static bool bf16_x32_faster(int64_t n_out, int64_t k, int64_t m) {
     const double bytes = 2.0 * static_cast<double>(n_out) * static_cast<double>(k);
@@ -1564,7 +1573,7 @@ static void launch_split_reduce(const float *wsp, int splits, int64_t m, int64_t
 static TiledPlan tiled_launch_plan(int wfmt, int64_t n_out, int64_t k, int64_t m, const void *ws, size_t ws_bytes) {
     TiledPlan pl = wfmt == WSL_W_NF4 ? nf4_tiled_plan(n_out, k, m) : bf16_tiled_plan(n_out, k, m);
     const size_t need = static_cast<size_t>(pl.splits) * static_cast<size_t>(m) * static_cast<size_t>(n_out) * 4;
-    if (pl.splits > 1 && (ws == nullptr || ws_bytes < need)) pl = TiledPlan{1, k, pl.t};
+    if (pl.splits > 1 && (ws == nullptr || ws_bytes < need)) pl = TiledPlan{1, k, pl.t, false};
     return pl;
 }
 
@@ -1580,7 +1589,7 @@ int launch_gemm_bf16(const void *w, int64_t n_out, int64_t k, const void *x, int
         const XcdShape xs = xcd_shape();
         hipLaunchKernelGGL(gemm_bf16_kernel, dim3(tile_grid(tm * tn * pl.splits, xs)), dim3(512), 0, s, xp, wp, m,
                            n_out, k, ldx, y, ofmt, ldy, static_cast<int>(tm), static_cast<int>(tn), xs.nx, xs.cus,
-                           pl.splits, pl.kps, wsp);
+                           pl.splits, pl.kps, wsp, pl.half ? 1 : 0);
         if (pl.splits > 1) launch_split_reduce(wsp, pl.splits, m, n_out, y, ofmt, ldy, s);
         return WSL_OK;
     }
@@ -1614,7 +1623,7 @@ int launch_gemm_nf4(const void *w, int64_t n_out, int64_t k, const void *x, int6
         hipLaunchKernelGGL(gemm_nf4_tiled_kernel, dim3(tile_grid(tm * tn * pl.splits, xs)), dim3(512), 0, s,
                            static_cast<const uint16_t *>(x), static_cast<const uint8_t *>(w), m, n_out, k, ldx, y,
                            ofmt, ldy, static_cast<int>(tm), static_cast<int>(tn), xs.nx, xs.cus, pl.splits, pl.kps,
-                           wsp);
+                           wsp, pl.half ? 1 : 0);
         if (pl.splits > 1) launch_split_reduce(wsp, pl.splits, m, n_out, y, ofmt, ldy, s);
         return WSL_OK;
     }
