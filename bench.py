@@ -462,8 +462,9 @@ def setup_layer_5120(mats, copies=2, tid0=0):
 
 def run_bf16_decode_layer(k_steps, warmup):
     """bf16 decode GEMV over one dense decoder layer of hidden 5120, batch 1: q/k/v and gate/up
-    fused (4 launches per step) and as stored (7 launches), two layer copies alternating (the
-    1.32 GB exceed the 256 MB last-level cache); one graph per step, K steps."""
+    fused (4 launches per step), as stored (7 launches) and as stored with q/k/v and gate/up
+    each in one multi-matrix launch (4 launches), two layer copies alternating (the 1.32 GB
+    exceed the 256 MB last-level cache); one graph per step, K steps."""
     import torch
     import weight_streaming_linear_amd as wsl
     out = {}
@@ -477,19 +478,37 @@ def run_bf16_decode_layer(k_steps, warmup):
                 worst = max(worst, gate_gemv(f"bf16 layer {label} copy {c} {name}", ys[j][rows], ws_[j][rows],
                                              xs[j], 1e-4))
         OUTPUT_SHA[f"bf16_decode_layer_5120_{label}"] = sha256_of(ys)
-        graphs = [capture(st) for st in steps]
-        ms = time_graphs(graphs, k_steps, warmup) / k_steps
-        per_kind = time_step_launches(steps, k_steps, warmup)
-        kern = summarize(per_kind)
-        nbytes = kern["bytes_per_step"]
-        out[label] = {"launches_per_step": len(mats), "ms_per_step": round(ms, 5),
-                      "gbs": round(nbytes / 1e6 / ms, 1), "frac_hbm": round(nbytes / 1e6 / ms / HBM_PEAK_GBS, 4),
-                      "weight_bytes_per_step": nbytes, "kernel_ms_per_step": round(kern["kernel_ms_per_step"], 5),
-                      "launches": kern["launches"], "sanity_worst_ratio": worst}
-        del graphs, steps, layers
+        variants = [(label, steps)]
+        if label == "unfused":
+            # the same separate matrices, q/k/v and gate/up each in one linear_gemv_multi launch
+            groups = [("q_k_v", [0, 1, 2]), ("o", [3]), ("gate_up_multi", [4, 5]), ("down", [6])]
+            grouped = [[Launch(lambda ws_=ws_, g=g: wsl.linear_gemv_multi([(ws_[j], xs[j], ys[j]) for j in g]),
+                               nbytes=sum(2 * mats[j][1] * mats[j][2] for j in g),
+                               flops=sum(2 * mats[j][1] * mats[j][2] for j in g), name=name)
+                        for name, g in groups] for ws_ in layers]
+            for launch in grouped[-1]:
+                launch.fn()
+            torch.cuda.synchronize()
+            if sha256_of(ys) != OUTPUT_SHA[f"bf16_decode_layer_5120_{label}"]:
+                refuse("bf16 layer grouped launches differ from the separate launches", float("inf"))
+            variants.append(("unfused_grouped", grouped))
+        for vlabel, vsteps in variants:
+            graphs = [capture(st) for st in vsteps]
+            ms = time_graphs(graphs, k_steps, warmup) / k_steps
+            per_kind = time_step_launches(vsteps, k_steps, warmup)
+            kern = summarize(per_kind)
+            nbytes = kern["bytes_per_step"]
+            out[vlabel] = {"launches_per_step": len(vsteps[0]), "ms_per_step": round(ms, 5),
+                           "gbs": round(nbytes / 1e6 / ms, 1), "frac_hbm": round(nbytes / 1e6 / ms / HBM_PEAK_GBS, 4),
+                           "weight_bytes_per_step": nbytes, "kernel_ms_per_step": round(kern["kernel_ms_per_step"], 5),
+                           "launches": kern["launches"], "sanity_worst_ratio": worst}
+            del graphs
+        del steps, layers, variants
         torch.cuda.empty_cache()
     out["workload"] = ("bf16 decode GEMV, batch 1, one dense decoder layer, hidden 5120: fused qkv 7168x5120, o "
-                       "5120x5120, gate_up 34816x5120, down 5120x17408; unfused q, k, v, o, gate, up, down")
+                       "5120x5120, gate_up 34816x5120, down 5120x17408; unfused q, k, v, o, gate, up, down as 7 "
+                       "launches; unfused_grouped the same matrices as 4 launches (q/k/v and gate/up each one "
+                       "linear_gemv_multi)")
     return out
 
 

@@ -203,6 +203,24 @@ int linear_gemv_sweep(int wfmt, int64_t count, const wsl_gemv_stage *h_stages,
                       const wsl_gemv_stage *d_stages, void *d_ws, size_t ws_bytes, void *stream);
 
 /*
+ * linear_gemv_multi -- several independent bf16 GEMVs in one launch: y_i = W_i x_i for
+ * i < count, bit for bit what count linear_gemv calls give.  For matrices that read the
+ * same k and none of whose outputs another reads -- a layer's q, k and v projections, or
+ * its gate and up projections, kept as separate tensors (TCPP README, "What 'exact' means
+ * here": weights used as stored) -- so that they share one launch instead of paying one
+ * launch each (IPE page, "How it is benchmarked": a decode step's linear layers).
+ * wfmt      WSL_W_BF16 (WSL_W_NF4: WSL_E_FORMAT; linear_gemv_sweep serves NF4 layers).
+ * count     0 <= count <= WSL_GEMV_MULTI_MAX; 0 enqueues nothing.
+ * h_stages  host array of count descriptors (read before the call returns), each with
+ *           linear_gemv's bf16 arguments: w bf16 [n_out][k] 16-byte aligned, x bf16 [k]
+ *           16-byte aligned, y fp32 [n_out] 4-byte aligned, n_out >= 1, k >= 8,
+ *           k % 8 == 0; every descriptor has the same k (else WSL_E_SHAPE).
+ * Returns linear_gemv's errors for a bad descriptor; asynchronous on stream.
+ */
+#define WSL_GEMV_MULTI_MAX 8
+int linear_gemv_multi(int wfmt, int64_t count, const wsl_gemv_stage *h_stages, void *stream);
+
+/*
  * linear_gemm_workspace_bytes -- workspace linear_gemm can use for a shape
  * (0 if it would not split the reduction): splits * m * n_out * 4 bytes of fp32
  * partials, for a k split of the shared-X kernels or of the 256 x 256 tiles

@@ -88,6 +88,24 @@ int main() {
                                nullptr, 0, nullptr, -1) == WSL_E_FLAGS);
     }
     {
+        // several bf16 GEMVs in one launch: one k, at most WSL_GEMV_MULTI_MAX
+        wsl_gemv_stage st[WSL_GEMV_MULTI_MAX + 1];
+        for (auto &e : st) e = wsl_gemv_stage{p, p, reinterpret_cast<float *>(const_cast<void *>(p)), 16, 512};
+        EXPECT(wsl::check_multi(WSL_W_BF16, 3, st) == WSL_OK);
+        EXPECT(wsl::check_multi(WSL_W_BF16, WSL_GEMV_MULTI_MAX, st) == WSL_OK);
+        EXPECT(wsl::check_multi(WSL_W_BF16, WSL_GEMV_MULTI_MAX + 1, st) == WSL_E_SHAPE);
+        EXPECT(wsl::check_multi(WSL_W_BF16, 0, nullptr) == WSL_OK);
+        EXPECT(wsl::check_multi(WSL_W_BF16, 2, nullptr) == WSL_E_NULL);
+        EXPECT(wsl::check_multi(WSL_W_NF4, 2, st) == WSL_E_FORMAT);
+        st[1].k = 1024;
+        EXPECT(wsl::check_multi(WSL_W_BF16, 2, st) == WSL_E_SHAPE);
+        st[1].k = 516;
+        EXPECT(wsl::check_multi(WSL_W_BF16, 2, st) == WSL_E_SHAPE);
+        st[1].k = 512;
+        st[1].w = odd;
+        EXPECT(wsl::check_multi(WSL_W_BF16, 2, st) == WSL_E_ALIGN);
+    }
+    {
         // decode sweep: host descriptors, device descriptor array and workspace
         wsl_gemv_stage st[3];
         for (auto &e : st) e = wsl_gemv_stage{p, p, reinterpret_cast<float *>(const_cast<void *>(p)), 4, 64};

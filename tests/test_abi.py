@@ -116,6 +116,20 @@ def test_argument_errors_return_before_any_launch():
     assert L.wsl_stream_read(None, 16, a, None) == 1
     assert L.wsl_stream_read(a, 24, a, None) == 2
     assert L.wsl_stream_read(odd, 16, a, None) == 3
+    st = (wsl.WslGemvStage * 3)(wsl.WslGemvStage(4096, 4096, 4096, 16, 512), wsl.WslGemvStage(4096, 4096, 4096, 8, 512),
+                                wsl.WslGemvStage(4096, 4096, 4096, 4, 512))
+    assert L.linear_gemv_multi(wsl.WSL_W_BF16, 0, None, None) == 0
+    assert L.linear_gemv_multi(wsl.WSL_W_NF4, 3, st, None) == 4
+    assert L.linear_gemv_multi(wsl.WSL_W_BF16, 9, st, None) == 2
+    assert L.linear_gemv_multi(wsl.WSL_W_BF16, 3, None, None) == 1
+    st[2].k = 1024
+    assert L.linear_gemv_multi(wsl.WSL_W_BF16, 3, st, None) == 2
+    st[2].k = 512
+    st[1].x = 4100
+    assert L.linear_gemv_multi(wsl.WSL_W_BF16, 3, st, None) == 3
+    st[1].x = 4096
+    st[0].y = None
+    assert L.linear_gemv_multi(wsl.WSL_W_BF16, 3, st, None) == 1
     assert wsl.wsl_strerror(7).startswith("tile")
     assert "flags" in wsl.wsl_strerror(wsl.WSL_E_FLAGS)
     assert L.nf4_codebook(None) == 1

@@ -101,6 +101,31 @@ def test_gemv_bf16_tolerance(n_out, k, tid):
     assert ok, f"row {i}: worst ratio {worst}"
 
 
+# Several bf16 GEMVs in one launch (linear_gemv_multi): a layer's q, k and v kept as separate
+# matrices; ragged row counts with the most matrices one launch takes; a single matrix.  Each
+# output against the oracle, and bit for bit what separate linear_gemv calls give.
+@pytest.mark.parametrize("shapes", [[(5120, 5120), (1024, 5120), (1024, 5120)],
+                                    [(17, 1032), (300, 1032), (1, 1032), (4099, 1032), (2, 1032), (64, 1032),
+                                     (777, 1032), (5, 1032)],
+                                    [(333, 17408)]])
+def test_gemv_bf16_multi(shapes):
+    import torch
+    say(f"gemv bf16 multi {shapes}")
+    wbs = [synth.weight_bits(117, i, n, k) for i, (n, k) in enumerate(shapes)]
+    xbs = [synth.act_bits(117, 100 + i, (k,)) for i, (n, k) in enumerate(shapes)]
+    ws_ = [to_dev_bf16(wb) for wb in wbs]
+    xs = [to_dev_bf16(xb) for xb in xbs]
+    ys = [torch.full((n,), float("nan"), dtype=torch.float32, device="cuda") for n, _ in shapes]
+    wsl.linear_gemv_multi(list(zip(ws_, xs, ys)))
+    single = [wsl.linear_gemv(w, x) for w, x in zip(ws_, xs)]
+    torch.cuda.synchronize()
+    for i, (y, y1, wb, xb) in enumerate(zip(ys, single, wbs, xbs)):
+        y_ref, s_ref = oracle.gemv_ref(f64(wb), f64(xb))
+        ok, worst, r = oracle.check_rows_f32(y.cpu().numpy(), y_ref, s_ref)
+        assert ok, f"matrix {i} {shapes[i]}: row {r} worst ratio {worst}"
+        assert torch.equal(y, y1), f"matrix {i} differs from its own launch"
+
+
 def test_gemv_nf4_exact_cases():
     """Codes in {0, 7, 15} (levels -1, 0, +1), power-of-two scales, small integer x: every
     partial sum is an exact integer multiple of the scale, so y must equal the exact result."""

@@ -10,7 +10,8 @@ built, every call raises.
 Entry points (same names as the C ABI):
   nf4_packed_bytes, nf4_codebook, nf4_pack, nf4_dequant_tile,
   linear_gemv, linear_gemm, linear_gemm_workspace_bytes, nf4_embed_rows, wsl_strerror;
-  linear_gemm_noalloc; GemvSweep (linear_gemv_sweep, linear_gemv_sweep_workspace_bytes);
+  linear_gemm_noalloc; linear_gemv_multi; GemvSweep (linear_gemv_sweep,
+  linear_gemv_sweep_workspace_bytes);
   stream_read (wsl_stream_read); CopyRing.gemv / CopyRing.gemm (linear_gemv_streamed /
   linear_gemm_streamed, weights streamed from page-locked host memory, see to_pinned).
 """
@@ -33,7 +34,7 @@ EXPORTED = [
     "nf4_packed_bytes", "nf4_codebook", "nf4_pack", "nf4_dequant_tile", "linear_gemv",
     "linear_gemm_workspace_bytes", "linear_gemm", "nf4_embed_rows", "linear_gemv_streamed",
     "linear_gemm_streamed", "wsl_stream_read", "wsl_strerror", "linear_gemm_noalloc",
-    "linear_gemv_sweep_workspace_bytes", "linear_gemv_sweep",
+    "linear_gemv_sweep_workspace_bytes", "linear_gemv_sweep", "linear_gemv_multi",
 ]
 WSL_STATUS_SWEEP_TIMEOUT = 8
 WSL_STATUS_DESCRIPTOR = 16
@@ -81,6 +82,8 @@ def lib():
     L.linear_gemv_sweep_workspace_bytes.restype = sz
     L.linear_gemv_sweep.argtypes = [ctypes.c_int, i64, vp, vp, vp, sz, vp]
     L.linear_gemv_sweep.restype = ctypes.c_int
+    L.linear_gemv_multi.argtypes = [ctypes.c_int, i64, vp, vp]
+    L.linear_gemv_multi.restype = ctypes.c_int
     L.linear_gemm_noalloc.argtypes = [ctypes.c_int, vp, i64, i64, vp, i64, i64, vp, ctypes.c_int, i64, vp]
     L.linear_gemm_noalloc.restype = ctypes.c_int
     L.nf4_embed_rows.argtypes = [vp, i64, i64, vp, i64, vp, ctypes.c_int, i64, vp, vp]
@@ -336,6 +339,38 @@ class GemvSweep:
     def status(self):
         """The workspace's status word (reads the device: for tests and diagnostics)."""
         return int(self.ws[SWEEP_STATUS_OFFSET:SWEEP_STATUS_OFFSET + 4].view(__import__("torch").int32).item())
+
+
+GEMV_MULTI_MAX = 8
+
+
+def linear_gemv_multi(mats, stream=None):
+    """Independent bf16 GEMVs of one k in one launch (linear_gemv_multi): mats is a list of
+    (w bf16 [n_out][k], x bf16 [k], y fp32 [n_out] or None); returns the ys."""
+    import torch
+    if not mats:
+        return []
+    if len(mats) > GEMV_MULTI_MAX:
+        raise ValueError(f"{len(mats)} matrices, at most {GEMV_MULTI_MAX}")
+    dev = mats[0][0].device
+    h = (WslGemvStage * len(mats))()
+    ys = []
+    for i, (w, x, y) in enumerate(mats):
+        n_out, k = w.shape
+        _weight(w, WSL_W_BF16, n_out, k, f"w[{i}]")
+        _require(x, f"x[{i}]", (torch.bfloat16,), device=dev, contiguous=True)
+        if x.numel() < k:
+            raise ValueError(f"x[{i}]: {x.numel()} elements, k = {k}")
+        if y is None:
+            y = torch.empty(n_out, dtype=torch.float32, device=dev)
+        _require(y, f"y[{i}]", (torch.float32,), device=dev, contiguous=True)
+        if y.numel() < n_out:
+            raise ValueError(f"y[{i}]: {y.numel()} elements, n_out = {n_out}")
+        h[i] = WslGemvStage(w.data_ptr(), x.data_ptr(), y.data_ptr(), int(n_out), int(k))
+        ys.append(y)
+    rc = lib().linear_gemv_multi(WSL_W_BF16, len(mats), ctypes.byref(h), _stream(stream))
+    _check(rc, "linear_gemv_multi")
+    return ys
 
 
 def stream_read(buf, sink, stream=None):

@@ -11,6 +11,7 @@ int launch_pack(const void *w, int64_t n_out, int64_t k, void *packed, uint32_t 
 int launch_dequant_tile(const void *packed, int64_t n_out, int64_t k, int64_t row0, int64_t k0, int64_t rows,
                         int64_t cols, void *tile, int64_t ld, hipStream_t s);
 int launch_gemv_bf16(const void *w, int64_t n_out, int64_t k, const void *x, float *y, hipStream_t s);
+int launch_gemv_bf16_multi(const wsl_gemv_stage *st, int64_t count, hipStream_t s);
 int launch_gemv_nf4(const void *w, int64_t n_out, int64_t k, const void *x, float *y, hipStream_t s);
 size_t sweep_ws_bytes();
 int launch_gemv_nf4_sweep(const wsl_gemv_stage *d_stages, int64_t count, int64_t max_k, void *ws, hipStream_t s);
@@ -107,6 +108,13 @@ int linear_gemv_sweep(int wfmt, int64_t count, const wsl_gemv_stage *h_stages, c
     int64_t max_k = 0;
     for (int64_t i = 0; i < count; ++i) max_k = h_stages[i].k > max_k ? h_stages[i].k : max_k;
     return wsl::after_launch(wsl::launch_gemv_nf4_sweep(d_stages, count, max_k, d_ws, wsl::as_stream(stream)));
+}
+
+int linear_gemv_multi(int wfmt, int64_t count, const wsl_gemv_stage *h_stages, void *stream) {
+    int rc = wsl::check_multi(wfmt, count, h_stages);
+    if (rc != WSL_OK || count == 0) return rc;
+    if ((rc = wsl::device_ok()) != WSL_OK) return rc;
+    return wsl::after_launch(wsl::launch_gemv_bf16_multi(h_stages, count, wsl::as_stream(stream)));
 }
 
 size_t linear_gemm_workspace_bytes(int wfmt, int64_t n_out, int64_t k, int64_t m) {

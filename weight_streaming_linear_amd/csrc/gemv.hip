@@ -156,15 +156,14 @@ __device__ __forceinline__ float dot8(const uint4 &w, const uint4 &x, float a) {
 }
 
 // Lane slice: 8 consecutive bf16 (16 B); a wave step covers 512 k.  R rows per
-// workgroup; its waves split the k steps.
+// workgroup (rows row0 .. row0 + R - 1 of one matrix); its waves split the k steps.
 template <int R>
-__global__ __launch_bounds__(512) void gemv_bf16_kernel(const uint16_t *__restrict__ w, int64_t n_out, int64_t k,
-                                                        const uint16_t *__restrict__ x, float *__restrict__ y) {
-    __shared__ float red[kMaxWaves][R];
+__device__ __forceinline__ void bf16_rows(const uint16_t *__restrict__ w, int64_t n_out, int64_t k,
+                                          const uint16_t *__restrict__ x, float *__restrict__ y, int64_t row0,
+                                          float (*red)[R]) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int waves = blockDim.x >> 6;
-    const int64_t row0 = static_cast<int64_t>(blockIdx.x) * R;
 
     const uint16_t *rowp[R];
 #pragma unroll
@@ -196,6 +195,50 @@ __global__ __launch_bounds__(512) void gemv_bf16_kernel(const uint16_t *__restri
         for (int r = 0; r < R; ++r) acc[r] = dot8(q0[r], x0, acc[r]);
     }
     finish_rows<R>(acc, red, lane, wave, waves, row0, n_out, y);
+}
+
+template <int R>
+__global__ __launch_bounds__(512) void gemv_bf16_kernel(const uint16_t *__restrict__ w, int64_t n_out, int64_t k,
+                                                        const uint16_t *__restrict__ x, float *__restrict__ y) {
+    __shared__ float red[kMaxWaves][R];
+    bf16_rows<R>(w, n_out, k, x, y, static_cast<int64_t>(blockIdx.x) * R, red);
+}
+
+// Several independent bf16 GEMVs of one k in one launch (a layer's q, k and v, or its gate
+// and up projections, kept as separate matrices): workgroup b serves matrix i for b in
+// [first[i], first[i + 1]), rows (b - first[i]) * R .., with the same row body as a single
+// launch, so every output is bit for bit what linear_gemv gives.  The descriptors are
+// kernel arguments; the matrix is picked with compile-time indices (the index is the same
+// for the whole workgroup), which keeps the argument arrays out of scratch memory.
+constexpr int kGemvMultiMax = 8;
+struct GemvMulti {
+    const uint16_t *w[kGemvMultiMax];
+    const uint16_t *x[kGemvMultiMax];
+    float *y[kGemvMultiMax];
+    int64_t n_out[kGemvMultiMax];
+    uint32_t first[kGemvMultiMax + 1];
+    int count;
+};
+
+template <int R>
+__global__ __launch_bounds__(512) void gemv_bf16_multi_kernel(const GemvMulti a, int64_t k) {
+    __shared__ float red[kMaxWaves][R];
+    const uint32_t b = blockIdx.x;
+    const uint16_t *w = a.w[0], *x = a.x[0];
+    float *y = a.y[0];
+    int64_t n_out = a.n_out[0];
+    uint32_t first = 0;
+#pragma unroll
+    for (int i = 1; i < kGemvMultiMax; ++i) {
+        if (i < a.count && b >= a.first[i]) {
+            w = a.w[i];
+            x = a.x[i];
+            y = a.y[i];
+            n_out = a.n_out[i];
+            first = a.first[i];
+        }
+    }
+    bf16_rows<R>(w, n_out, k, x, y, static_cast<int64_t>(b - first) * R, red);
 }
 
 // ---------------------------------------------------------------- NF4
@@ -1069,6 +1112,28 @@ int launch_gemv_bf16(const void *w, int64_t n_out, int64_t k, const void *x, flo
     const auto *wp = static_cast<const uint16_t *>(w);
     const auto *xp = static_cast<const uint16_t *>(x);
     WSL_GEMV_LAUNCH(gemv_bf16_kernel, 2, grid, waves, s, wp, n_out, k, xp, y);
+    return WSL_OK;
+}
+
+// count (1 .. kGemvMultiMax) independent bf16 GEMVs of one k, validated by the caller.
+int launch_gemv_bf16_multi(const wsl_gemv_stage *st, int64_t count, hipStream_t s) {
+    int waves, r;
+    const int64_t k = st[0].k;
+    plan_gemv_bf16(k, waves, r);
+    GemvMulti a{};
+    int64_t grid = 0;
+    for (int64_t i = 0; i < count; ++i) {
+        a.w[i] = static_cast<const uint16_t *>(st[i].w);
+        a.x[i] = static_cast<const uint16_t *>(st[i].x);
+        a.y[i] = st[i].y;
+        a.n_out[i] = st[i].n_out;
+        a.first[i] = static_cast<uint32_t>(grid);
+        grid += (st[i].n_out + r - 1) / r;
+        if (grid > 0x7fffffff) return WSL_E_SHAPE;
+    }
+    a.first[count] = static_cast<uint32_t>(grid);
+    a.count = static_cast<int>(count);
+    WSL_GEMV_LAUNCH(gemv_bf16_multi_kernel, 2, grid, waves, s, a, k);
     return WSL_OK;
 }
 

@@ -126,6 +126,20 @@ int check_embed(const void *packed, int64_t n_rows, int64_t k, const void *ids, 
     return WSL_OK;
 }
 
+int check_multi(int wfmt, int64_t count, const void *h_stages) {
+    if (wfmt != WSL_W_BF16) return WSL_E_FORMAT;
+    if (count < 0 || count > WSL_GEMV_MULTI_MAX) return WSL_E_SHAPE;
+    if (count == 0) return WSL_OK;
+    if (!h_stages) return WSL_E_NULL;
+    const wsl_gemv_stage *st = static_cast<const wsl_gemv_stage *>(h_stages);
+    for (int64_t i = 0; i < count; ++i) {
+        const int rc = check_gemv(WSL_W_BF16, st[i].w, st[i].n_out, st[i].k, st[i].x, st[i].y);
+        if (rc != WSL_OK) return rc;
+        if (st[i].k != st[0].k) return WSL_E_SHAPE;
+    }
+    return WSL_OK;
+}
+
 int check_sweep(int wfmt, int64_t count, const void *h_stages, const void *d_stages, const void *ws,
                 size_t ws_bytes, size_t ws_need) {
     if (wfmt != WSL_W_NF4) return WSL_E_FORMAT;

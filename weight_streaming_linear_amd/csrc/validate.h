@@ -34,6 +34,9 @@ int check_ring(int wfmt, int64_t count, const void *const *h_w, const int64_t *n
 // plus k <= 32768), the device descriptor array and the workspace.
 int check_sweep(int wfmt, int64_t count, const void *h_stages, const void *d_stages, const void *ws,
                 size_t ws_bytes, size_t ws_need);
+// Several GEMVs in one launch: bf16 only, count in [0, WSL_GEMV_MULTI_MAX], each descriptor
+// as check_gemv, every k equal.
+int check_multi(int wfmt, int64_t count, const void *h_stages);
 int check_embed(const void *packed, int64_t n_rows, int64_t k, const void *ids, int64_t count, const void *out,
                 int ofmt, int64_t ld_out);
 
