@@ -620,6 +620,25 @@ def run_bf16_verify_gemm(k_steps, warmup, copies=2):
     out = summarize(time_step_launches(steps, k_steps, warmup))
     out.update({"workload": "bf16 GEMM M=8192: gate 17408x5120 and down 5120x17408, bf16 out",
                 "sanity_worst_ratio": worst, "frac_mfma": out["kernel_tflops"] / MFMA_BF16_PEAK_TFLOPS})
+    # Context, not a target: the vendor library (torch.matmul, hipBLASLt) on the same shapes
+    # and inputs, W^T made contiguous first, bf16 out; timed with events, 10 calls after 3.
+    vendor = {}
+    for j, (name, n, k) in enumerate(mats):
+        wt = ws[0][j].t().contiguous()
+        for _ in range(3):
+            torch.matmul(xs[j], wt, out=ys[j])
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(10):
+            torch.matmul(xs[j], wt, out=ys[j])
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 100.0
+        vendor[name] = {"avg_us": round(us, 1), "tflops": round(2 * m * n * k / us / 1e6, 1)}
+        del wt
+    out["vendor_blas_reference"] = {"what": "torch.matmul (hipBLASLt) on the same shapes, W^T contiguous, bf16 out",
+                                    **vendor}
     del ws, xs, ys
     torch.cuda.empty_cache()
     return out
