@@ -3,25 +3,26 @@
 
 Headline workload (``value``): the batch-1 NF4 decode sweep over a 48-layer stack of
 hidden size 6144 (20B class): per layer qkv 8192x6144, o 6144x6144, gate_up 32768x6144
-and down 6144x16384, packed NF4 (group 64, fp16 scales), 192 GEMV launches per token in
-decoder order on one stream, captured as one HIP graph per token (deep-fold README,
-"Метод" table: decode is an N=1 NF4 GEMV inside a graph of the whole step).  A "step"
-is one token: the W warm-up tokens and then exactly K timed tokens are replayed between
+and down 6144x16384, packed NF4 (group 64, fp16 scales), the 192 GEMVs of a token in
+decoder order in one linear_gemv_sweep launch, with a device-wide barrier between stages
+so that no stage starts before the one it follows has finished (deep-fold README, "Метод"
+table: decode is an N=1 NF4 GEMV per matrix).  A "step" is one token: the W warm-up
+tokens and then exactly K timed tokens are launched between
 HIP events; ``value`` = packed weight bytes per token (9,946,791,936 B, every byte read
 once) / wall time per token, in GB/s (1e9 B/s), every input resident in HBM before the
 timed region starts.  The 9.9 GB stack is 39x the 256 MB last-level cache, so no
 rotation copies are needed.
 
-``roofline`` describes the dominant kernel, the gate_up GEMV (gemv_nf4_team_kernel<2,1>
-on 32768x6144, 54 % of the bytes): its algorithmic bytes per launch (packed bytes)
-divided by its average duration, measured as one block of launches over the 48 layers'
-gate_up matrices between HIP events on the launch stream.  ``traffic`` is the HBM bytes
+``roofline`` describes the dominant kernel, the sweep kernel itself (one launch per token):
+its algorithmic bytes per launch (the token's packed bytes) divided by its average launch
+duration between HIP events on the launch stream.  ``traffic`` is the HBM bytes
 per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE counter runs of ``--traffic-probe``,
 scaled by what the same counters read for a plain copy of known size; null when the
 kernel source changed since the counters were taken.
 
-``paths`` holds the other workloads of the hot path measured in the same run: the sweep
-as one linear_gemv_sweep launch per token, the bf16 decode layer of hidden 5120 (fused
+``headline_detail`` holds the same 192 GEMVs as separate launches captured in one graph
+per token, each stage's launch time in that form, and the decode-step graph.  ``paths``
+holds the other workloads of the hot path measured in the same run: the bf16 decode layer of hidden 5120 (fused
 q/k/v and gate/up: 4 launches; unfused: 7), the NF4 GEMV 4096x4096, the NF4 prefill GEMM
 at 32 positions, the NF4 GEMM at 64/128/256 positions, the bf16 and NF4 verification
 GEMMs at 8192 positions, the packed-embedding gather and the copy ring.
@@ -1059,7 +1060,7 @@ def gemv_counter_summarize(run_dirs, command):
     kinds = [("sweep", SWEEP_KERNEL_MATCH, token_weights,
               "`gemv_nf4_sweep_kernel<12>`, the 48-layer decode sweep in one launch (2 launches)"),
              ("gate_up", TEAM_KERNEL_MATCH, 32768 * 6144,
-              "`gemv_nf4_team_kernel<2,1>`, one gate_up 32768x6144 launch of the 192-launch form (4 launches)")]
+              "`gemv_nf4_team_kernel<2,1,true>`, one gate_up 32768x6144 launch of the 192-launch form (4 launches)")]
     per = {kind: {} for kind, *_ in kinds}
     xccs = 8
     for d in run_dirs:

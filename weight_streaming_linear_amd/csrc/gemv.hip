@@ -629,12 +629,15 @@ __device__ __forceinline__ float team_dot(const uint4 &q, const float (&xf)[32],
 // the loads of whatever comes after this matrix into the buffer it is given; it is
 // called once, before the last super-group is multiplied, so that those loads are in
 // flight meanwhile.  Returns true if it was given qb/sb, false if qa/sa or not called.
+// EARLY: refill each buffer between the multiply and the reduction of the super-group it
+// held, so that its loads are in flight through the workgroup barrier (faster for the
+// single-matrix launch); otherwise after the reduction (faster in the decode sweep).
 struct NoNext {
     template <typename Q, typename S_>
     __device__ __forceinline__ void operator()(Q &, S_ &) const {}
 };
 
-template <int R, int TAB, bool SKIP, bool WIDE, typename Next = NoNext>
+template <int R, int TAB, bool SKIP, bool WIDE, bool EARLY = false, typename Next = NoNext>
 __device__ __forceinline__ bool team_run(const TeamStage<R, WIDE> &st, TeamLds<R, TAB> &lds, const float (&xf)[32],
                                          uint32_t (&ad)[4], uint4 (&qa)[R], typename ScaleBits<R>::T &sa,
                                          uint4 (&qb)[R], typename ScaleBits<R>::T &sb, Next next = Next()) {
@@ -646,7 +649,12 @@ __device__ __forceinline__ bool team_run(const TeamStage<R, WIDE> &st, TeamLds<R
     int ph = 0;
     int64_t jbeg = 0;
     bool in_b = false;
-    auto consume = [&](int64_t j, const uint4 (&q)[R], const SB &sb_) {
+    // A super-group is multiplied (mul: this wave's partial sums into the reduction
+    // buffer) and then reduced (reduce: the workgroup barrier, the sum over the team's
+    // waves and its store); the prefetch of a later super-group goes between the two,
+    // once the registers it overwrites have been read, so that its loads are in flight
+    // while the waves meet at the barrier.
+    auto mul = [&](const uint4 (&q)[R], const SB &sb_) {
         if constexpr (!SKIP) {
             float acc[R];
 #pragma unroll
@@ -655,6 +663,8 @@ __device__ __forceinline__ bool team_run(const TeamStage<R, WIDE> &st, TeamLds<R
             const float v = team_reduce<R>(acc, lane, holder);
             if (holder) lds.red[ph][wave][lane / span] = v;
         }
+    };
+    auto reduce = [&](int64_t j) {
         lds_barrier();
         if (threadIdx.x < T * R) {
             const int tm = threadIdx.x / R, r = threadIdx.x - tm * R;
@@ -679,26 +689,76 @@ __device__ __forceinline__ bool team_run(const TeamStage<R, WIDE> &st, TeamLds<R
         const int64_t jend = (jbeg + st.cap < n) ? jbeg + st.cap : n;
         if (jbeg > 0) fetch(jbeg, qa, sa);
         int64_t j = jbeg;
-        // Unrolled by two so that the two buffers swap without copies; the loop has its
-        // only exit at the top, so no path reaches the next iteration with a buffer's
-        // loads still pending and the next prefetch is issued without waiting for them.
-        for (; j + 2 < jend; j += 2) {
-            fetch(j + 1, qb, sb);
-            consume(j, qa, sa);
-            fetch(j + 2, qa, sa);
-            consume(j + 1, qb, sb);
-        }
-        if (j + 1 < jend) {
-            fetch(j + 1, qb, sb);
-            consume(j, qa, sa);
-            if constexpr (LAST) next(qa, sa);
-            consume(j + 1, qb, sb);
-        } else {
-            if constexpr (LAST) {
-                next(qb, sb);
-                in_b = true;
+        if constexpr (EARLY) {
+            // Unrolled by two so that the two buffers swap without copies, with the last one,
+            // two or three super-groups written out: every path between branches is straight
+            // code, each buffer is refilled right after it was multiplied, and at the loop
+            // head the two buffers are pending in the same order on every path, so the waits
+            // before each multiply leave the other buffer's loads in flight.
+            if (j + 1 < jend) {
+                fetch(j + 1, qb, sb);
+                for (; j + 3 < jend; j += 2) {   // qa: j, qb: j + 1; four or more remain
+                    mul(qa, sa);
+                    fetch(j + 2, qa, sa);
+                    reduce(j);
+                    mul(qb, sb);
+                    fetch(j + 3, qb, sb);
+                    reduce(j + 1);
+                }
+                if (j + 2 < jend) {              // three remain
+                    mul(qa, sa);
+                    fetch(j + 2, qa, sa);
+                    reduce(j);
+                    mul(qb, sb);
+                    if constexpr (LAST) {
+                        next(qb, sb);
+                        in_b = true;
+                    }
+                    reduce(j + 1);
+                    mul(qa, sa);
+                    reduce(j + 2);
+                } else {                         // two remain
+                    mul(qa, sa);
+                    if constexpr (LAST) next(qa, sa);
+                    reduce(j);
+                    mul(qb, sb);
+                    reduce(j + 1);
+                }
+            } else {                             // one remains
+                if constexpr (LAST) {
+                    next(qb, sb);
+                    in_b = true;
+                }
+                mul(qa, sa);
+                reduce(j);
             }
-            consume(j, qa, sa);
+        } else {
+            // Each buffer is refilled after the reduction of the super-group it held
+            // (the order the decode sweep measures fastest in); otherwise as above, with
+            // the last one or two super-groups written out.
+            for (; j + 2 < jend; j += 2) {
+                fetch(j + 1, qb, sb);
+                mul(qa, sa);
+                reduce(j);
+                fetch(j + 2, qa, sa);
+                mul(qb, sb);
+                reduce(j + 1);
+            }
+            if (j + 1 < jend) {
+                fetch(j + 1, qb, sb);
+                mul(qa, sa);
+                reduce(j);
+                if constexpr (LAST) next(qa, sa);
+                mul(qb, sb);
+                reduce(j + 1);
+            } else {
+                if constexpr (LAST) {
+                    next(qb, sb);
+                    in_b = true;
+                }
+                mul(qa, sa);
+                reduce(j);
+            }
         }
         if (st.park) {
             lds_barrier();
@@ -719,9 +779,9 @@ __device__ __forceinline__ bool team_run(const TeamStage<R, WIDE> &st, TeamLds<R
     // rows clamped to the matrix and scales read one row at a time.  They go to the
     // last workgroups, which own one super-group fewer than the first ones when the
     // super-groups do not divide evenly, so the leftovers do not lengthen the kernel.
-    // The first leftover round uses the reduction buffer the last consume() did not:
+    // The first leftover round uses the reduction buffer the last reduce() did not:
     // without the flush's barriers (n < 4) a team of this round may write its partials
-    // while wave 0 still reads that consume()'s partials from the other buffer.
+    // while wave 0 still reads that reduce()'s partials from the other buffer.
     const int64_t left0 = st.supers * T;
     const int64_t nleft = st.row_groups - left0;
     int it = ph;
@@ -759,7 +819,7 @@ __device__ __forceinline__ bool team_run(const TeamStage<R, WIDE> &st, TeamLds<R
     return in_b;
 }
 
-template <int R, int TAB>
+template <int R, int TAB, bool EARLY>
 __global__ __launch_bounds__(1024) void gemv_nf4_team_kernel(const uint8_t *__restrict__ packed, int64_t n_out,
                                                              int64_t k, const uint16_t *__restrict__ x,
                                                              float *__restrict__ y, TeamGeom g, int nx) {
@@ -788,7 +848,7 @@ __global__ __launch_bounds__(1024) void gemv_nf4_team_kernel(const uint8_t *__re
     widen_x32(xv, xf);
     uint4 qb[R];
     typename ScaleBits<R>::T sb;
-    team_run<R, TAB, false, false>(st, lds, xf, ad, qa, sa, qb, sb);
+    team_run<R, TAB, false, false, EARLY>(st, lds, xf, ad, qa, sa, qb, sb);
 }
 
 // ---------------------------------------------------------------- decode sweep
@@ -1234,14 +1294,20 @@ int launch_gemv_nf4(const void *w, int64_t n_out, int64_t k, const void *x, floa
         else hipLaunchKernelGGL((gemv_nf4_wide_kernel<2>), g, b, 0, s, wp, n_out, k, xp, y);
     } else {
         const uint32_t grid = static_cast<uint32_t>(p.grid), nx = static_cast<uint32_t>(ds.xccs);
-        if (p.pair) {
-            hipLaunchKernelGGL((gemv_nf4_team_kernel<2, 1>), g, b, 0, s, wp, n_out, k, xp, y,
+        // The early refill (team_run) where it measured faster: rows of up to three
+        // 2048-code slices (k <= 6144: 3-4 % on 6144x6144 and 32768x6144); at k = 16384
+        // (eight slices) it was 2 % slower.
+        if (p.pair && p.S <= 3) {
+            hipLaunchKernelGGL((gemv_nf4_team_kernel<2, 1, true>), g, b, 0, s, wp, n_out, k, xp, y,
+                               team_geom<2>(n_out, p.S, p.T, grid, nx), ds.xccs);
+        } else if (p.pair) {
+            hipLaunchKernelGGL((gemv_nf4_team_kernel<2, 1, false>), g, b, 0, s, wp, n_out, k, xp, y,
                                team_geom<2>(n_out, p.S, p.T, grid, nx), ds.xccs);
         } else if (p.rows == 4) {
-            hipLaunchKernelGGL((gemv_nf4_team_kernel<4, 0>), g, b, 0, s, wp, n_out, k, xp, y,
+            hipLaunchKernelGGL((gemv_nf4_team_kernel<4, 0, false>), g, b, 0, s, wp, n_out, k, xp, y,
                                team_geom<4>(n_out, p.S, p.T, grid, nx), ds.xccs);
         } else {
-            hipLaunchKernelGGL((gemv_nf4_team_kernel<2, 0>), g, b, 0, s, wp, n_out, k, xp, y,
+            hipLaunchKernelGGL((gemv_nf4_team_kernel<2, 0, false>), g, b, 0, s, wp, n_out, k, xp, y,
                                team_geom<2>(n_out, p.S, p.T, grid, nx), ds.xccs);
         }
     }
