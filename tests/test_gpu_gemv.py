@@ -59,9 +59,14 @@ def _sample_rows(n, rng, count):
 # Decode sweep with hidden size 6144: gate/up 6144 -> 32768, down 16384 -> 6144, qkv 6144 -> 8192,
 # o 6144 -> 6144; plus ragged large shapes (odd row count, k not a multiple of 2048).  Matrices
 # from 32 Mi weights take the pair-table kernel (from 96 Mi when k <= 4096: 28672x4096 does,
-# 20000x2112 takes the 16-entry table).
+# 20000x2112 takes the 16-entry table).  With rows of at most three 2048-code slices the pair
+# kernel refills each buffer before the workgroup barrier, with the last one, two or three
+# super-groups of a workgroup written out: 8192x6144 gives each workgroup 4, 6144x6144 3,
+# 28672x4096 7 and 32768x6144 16; 5700x6080 (712 super-groups on 256 workgroups, k not a
+# multiple of 2048, 4 leftover rows) mixes workgroups of 2 and 3.
 @pytest.mark.parametrize("n_out,k,tid", [(32768, 6144, 0), (6144, 16384, 1), (12291, 6208, 4), (8195, 6208, 2),
-                                         (20000, 2112, 3), (8192, 6144, 5), (6144, 6144, 6), (28672, 4096, 7)])
+                                         (20000, 2112, 3), (8192, 6144, 5), (6144, 6144, 6), (28672, 4096, 7),
+                                         (5700, 6080, 8)])
 def test_gemv_nf4_large_sampled(n_out, k, tid):
     import torch
     say(f"gemv nf4 large {n_out}x{k}")
