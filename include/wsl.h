@@ -352,8 +352,9 @@ int linear_gemm_streamed(int wfmt, int64_t count, const void *const *h_w, const 
  * wsl_stream_read -- measurement aid, not part of the linear path: a read-only
  * kernel that reads bytes bytes at d_buf once, with the access form of the GEMV
  * weight stream (16-byte loads that bypass the caches, 1 KB of consecutive bytes
- * per wave instruction, 4 KB per wave in flight), so that its rate over a
- * buffer much larger than the caches is the streaming-read ceiling the GB/s
+ * per wave instruction; one 8-wave workgroup per compute unit, three such
+ * loads in flight per wave), so that its rate over a buffer much larger than
+ * the caches is the streaming-read ceiling the GB/s
  * figures are compared with (a figure the pages do not give: measured on the GPU at hand).
  * d_buf    device, 16-byte aligned; bytes a multiple of 16.  bytes == 0 enqueues
  *          nothing and returns 0.

@@ -12,12 +12,15 @@ MAGIC = 0x9E3779B9
 
 
 @pytest.mark.parametrize("words,pos", [(1, 0), (256, 255), (65536 + 3, 65538), (8 * 524288 + 5, 8 * 524288 + 4),
-                                       (8 * 524288 + 5, 3 * 524288 + 17), (20 * 524288, 20 * 524288 - 1)])
+                                       (8 * 524288 + 5, 3 * 524288 + 17), (20 * 524288, 20 * 524288 - 1),
+                                       (262151, 262150), (262151, 131072)])
 def test_stream_read_reads_every_word(words, pos):
     """A buffer of zeros with the magic value in one 16-byte word: the lane that reads
-    that word XORs to the magic value and writes it to the sink.  Words past 8 grid
-    passes exercise the main loop, the rest the tail loop; without the plant the sink
-    stays untouched."""
+    that word XORs to the magic value and writes it to the sink.  Sizes from one word to
+    160 MB reach every part of the kernel: no whole 1 KB unit per wave (word loop only),
+    fewer rounds than loads in flight, the pipelined rounds with their remainder, and
+    the units and words past the last whole round; without the plant the sink stays
+    untouched."""
     import torch
     say(f"stream_read {words} words, plant at {pos}")
     buf = torch.zeros(words * 4, dtype=torch.int32, device="cuda")
