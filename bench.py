@@ -165,7 +165,8 @@ READ_CEILING = {}
 
 def measure_read_ceiling(reps=10, nbytes=2 << 30):
     """A reference streaming read on the same GPU: wsl_stream_read (16-byte loads that
-    bypass the caches, 4 KB of consecutive bytes per wave and iteration) over a 2 GiB
+    bypass the caches, 1 KB per wave instruction, three in flight per wave, one 8-wave
+    workgroup per CU) over a 2 GiB
     buffer, 8x the MALL, timed as one block of launches between HIP events.  A plain read
     kernel, not a bound: a kernel with a better access pattern can exceed it."""
     import torch
